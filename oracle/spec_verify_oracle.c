@@ -1,0 +1,413 @@
+/*
+ * spec_verify_oracle.c -- plain CPU oracle for batched draft-token verification.
+ *
+ * TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only the tests, the smoke check and
+ * the CPU-baseline leg of the benchmark load this file's library.  It shares no
+ * code, header, table or helper with the HIP path, and the HIP path never
+ * calls it.
+ *
+ * Everything here is written for a reader checking it against the pages by eye:
+ * scalar loops, all arithmetic in double precision (fp64), one full softmax per
+ * row, one left-to-right scan per request.  Nothing is blocked, fused or
+ * reordered.
+ *
+ * Sources (page title, then section):
+ *   [ANATOMY]  "Inside vLLM: Anatomy of a High-Throughput LLM Inference System"
+ *              (bilingual copy), section "Speculative Decoding": the
+ *              draft / verify / accept-reject steps and the residual and bonus
+ *              rules.
+ *   [BOOK]     "02. Speculative Decoding" (vLLM learning book), section 2
+ *              "Algorithm (Leviathan 2023)" flowchart, and the FAQ entry on why
+ *              a bonus token can be sampled when every draft is accepted.
+ *   [TRTLLM]   "TensorRT-LLM source teardown (10): speculative decoding",
+ *              section "Rejection sampling: an optional, stricter acceptance
+ *              path" (output layout [batch, D+1] padded with -1, per-request
+ *              length; target and draft must be filtered identically) and
+ *              section "MTP mechanism background" (the "Generation phase 1"
+ *              worked example: inputs E+FGH, target tokens FGXY, accepted FGX).
+ *   [KESTREL]  "Kestrel_VLLM - 32: anchoring of a speculative round", section 2
+ *              (acceptance: count leading drafts equal to the target argmax,
+ *              emit the argmax at the first mismatch) and section 3.3 (every
+ *              emitted token lies on the target's own argmax chain).
+ *   [EAGLE]    "05 - TensorRT-LLM speculative decoding and auto-deploy",
+ *              sections "Eagle-2 multi-level tree drafting" (the
+ *              paths[batch, max_decoding_tokens, max_path_len] table) and
+ *              "Target-model verification: tree attention and batched
+ *              parallelism" (each tree token is compared against the target
+ *              logits of its parent; the accepted branch is chosen).
+ *
+ * Readings where the pages leave a step open (all follow the plainest reading):
+ *   - Row i of target_logits and row i of draft_logits are both distributions
+ *     over draft token i (0-based); target row k is the bonus row.
+ *   - The acceptance test is strict: accept iff P >= Q, otherwise iff u < P/Q.
+ *     So Q == 0 always accepts.
+ *   - uniforms[b, i] (i < k) drives test i; uniforms[b, k] drives the one final
+ *     sample (residual or bonus).
+ *   - Inverse-CDF sampling walks the vocabulary in ascending index order and
+ *     picks the smallest j whose running sum exceeds u * Z.  If rounding leaves
+ *     no such j, it takes the last j with positive weight.
+ *   - If the residual mass is zero (p == q exactly at a rejected row, which a
+ *     strict test with u < 1 cannot produce), it samples from p instead.
+ *   - Temperature divides both target and draft logits.
+ *   - Argmax uses the raw logits and takes the lowest index among equal maxima.
+ *   - A draft token outside [0, V) is rejected (P and Q are reported as 0); a
+ *     path entry outside [0, N] ends the path like -1.
+ *
+ * parity unpinned: none of the pages prints numeric logits or probabilities,
+ * so exact probability values are pinned only by closed forms and by a library
+ * softmax in the tests, never by a printed example.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Element types of the logits tensors (same integer meaning as the library's
+ * public enum; written out again here, not shared). */
+#define ORACLE_DTYPE_F32 0
+#define ORACLE_DTYPE_BF16 1
+
+/* Return codes. */
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARGUMENT 1
+#define ORACLE_NO_MEMORY 2
+
+/* One logit as a double.  bf16 is the top half of an IEEE fp32 word, so the
+ * conversion is exact. */
+static double logit_at(const void *base, int dtype, size_t index)
+{
+    if (dtype == ORACLE_DTYPE_F32)
+        return (double)((const float *)base)[index];
+    uint32_t bits = (uint32_t)((const uint16_t *)base)[index] << 16;
+    float value;
+    memcpy(&value, &bits, sizeof value);
+    return (double)value;
+}
+
+/* probs[j] = softmax(row / temperature)[j], in fp64, subtracting the row
+ * maximum first.  A logit of -inf gets probability exactly 0.
+ * [ANATOMY] "Speculative Decoding": the verifier turns each of the k+1 target
+ * rows (and each draft row) into a probability distribution.  [TRTLLM]
+ * "Rejection sampling": temperature is applied identically to both sides. */
+static void softmax_row(const void *logits, int dtype, size_t row_offset, int V,
+                        double temperature, double *probs)
+{
+    double zmax = -INFINITY;
+    for (int j = 0; j < V; ++j) {
+        double z = logit_at(logits, dtype, row_offset + (size_t)j) / temperature;
+        probs[j] = z;
+        if (z > zmax)
+            zmax = z;
+    }
+    double total = 0.0;
+    for (int j = 0; j < V; ++j) {
+        probs[j] = exp(probs[j] - zmax);
+        total += probs[j];
+    }
+    for (int j = 0; j < V; ++j)
+        probs[j] /= total;
+}
+
+/* Inverse-CDF draw from the unnormalised weights w[0..V-1] with the uniform u:
+ * the smallest j with w[0] + ... + w[j] > u * Z, Z = sum of all weights.
+ * *margin receives the distance from u * Z to the nearer edge of the chosen
+ * token's CDF interval, divided by Z.
+ * [ANATOMY] "Speculative Decoding": normalise the weights to sum to 1 and
+ * sample one token from them. */
+static int32_t inverse_cdf(const double *w, int V, double u, double *margin)
+{
+    double Z = 0.0;
+    for (int j = 0; j < V; ++j)
+        Z += w[j];
+    double target = u * Z;
+    double below = 0.0; /* running sum before token j */
+    for (int j = 0; j < V; ++j) {
+        double above = below + w[j];
+        if (above > target) {
+            double lo = target - below;
+            double hi = above - target;
+            *margin = (lo < hi ? lo : hi) / Z;
+            return (int32_t)j;
+        }
+        below = above;
+    }
+    /* Rounding left u * Z at or past the total: the last positive weight. */
+    *margin = 0.0;
+    for (int j = V - 1; j >= 0; --j)
+        if (w[j] > 0.0)
+            return (int32_t)j;
+    return 0;
+}
+
+/*
+ * Stochastic verification of B linear drafts of length k.
+ *
+ *   target_logits [B, k+1, V]  (dtype)   draft_logits [B, k, V] (dtype)
+ *   draft_tokens  [B, k] int32           uniforms [B, k+1] fp32
+ *   out_tokens    [B, k+1] int32: accepted drafts, then the correction or bonus
+ *                 token, then -1 padding        ([TRTLLM] "Rejection sampling")
+ *   num_accepted  [B] int32: number of accepted draft tokens
+ *   p_at_draft, q_at_draft [B, k] (may be NULL): p_i(x_i) and q_i(x_i), fp64
+ *   margins [B, k+1] (may be NULL): for each decision actually taken, its
+ *           distance from the decision boundary (test i: |u - min(1, P/Q)|;
+ *           final sample: see inverse_cdf); +inf where no decision was taken.
+ *
+ * The steps follow [ANATOMY] "Speculative Decoding" and the [BOOK] section 2
+ * flowchart, in their order:
+ *   1. for i = 0, 1, ..., k-1 (left to right): with x = draft token i,
+ *      P = p_i(x), Q = q_i(x): accept when P >= Q; otherwise accept when
+ *      u_i < P / Q.  Stop at the first rejection.
+ *   2. rejected at row s: sample from max(0, p_s - q_s), normalised;
+ *      all k accepted: sample the bonus token from p_k ([BOOK] FAQ 2).
+ */
+int oracle_verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
+                             const int32_t *draft_tokens, const float *uniforms,
+                             double temperature, int B, int k, int V,
+                             int32_t *out_tokens, int32_t *num_accepted,
+                             double *p_at_draft, double *q_at_draft, double *margins)
+{
+    if (B < 0 || k < 0 || V < 1 || !(temperature > 0.0) || isinf(temperature))
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    double *w = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!p || !q || !w) {
+        free(p);
+        free(q);
+        free(w);
+        return ORACLE_NO_MEMORY;
+    }
+
+    for (int b = 0; b < B; ++b) {
+        const int32_t *x = draft_tokens + (size_t)b * k;
+        const float *u = uniforms + (size_t)b * (k + 1);
+        int32_t *out = out_tokens + (size_t)b * (k + 1);
+        double *margin = margins ? margins + (size_t)b * (k + 1) : NULL;
+        if (margin)
+            for (int i = 0; i <= k; ++i)
+                margin[i] = INFINITY;
+
+        /* Step 1: left-to-right accept/reject, stop at the first rejection. */
+        int s = k;
+        for (int i = 0; i < k; ++i) {
+            size_t t_row = ((size_t)b * (k + 1) + i) * (size_t)V;
+            size_t d_row = ((size_t)b * k + i) * (size_t)V;
+            softmax_row(target_logits, dtype, t_row, V, temperature, p);
+            softmax_row(draft_logits, dtype, d_row, V, temperature, q);
+            int in_range = x[i] >= 0 && x[i] < V;
+            double P = in_range ? p[x[i]] : 0.0;
+            double Q = in_range ? q[x[i]] : 0.0;
+            if (p_at_draft)
+                p_at_draft[(size_t)b * k + i] = P;
+            if (q_at_draft)
+                q_at_draft[(size_t)b * k + i] = Q;
+
+            int accepted;
+            if (!in_range)
+                accepted = 0;
+            else if (P >= Q)
+                accepted = 1;
+            else
+                accepted = (double)u[i] < P / Q;
+            if (margin) {
+                double threshold = (P >= Q) ? 1.0 : P / Q;
+                margin[i] = in_range ? fabs((double)u[i] - threshold) : INFINITY;
+            }
+            if (!accepted) {
+                s = i;
+                break;
+            }
+        }
+        /* Remaining p_at_draft / q_at_draft entries (after the stop row) are
+         * still defined: they are the same per-row probabilities. */
+        for (int i = s + 1; i < k; ++i) {
+            size_t t_row = ((size_t)b * (k + 1) + i) * (size_t)V;
+            size_t d_row = ((size_t)b * k + i) * (size_t)V;
+            int in_range = x[i] >= 0 && x[i] < V;
+            if (p_at_draft) {
+                softmax_row(target_logits, dtype, t_row, V, temperature, p);
+                p_at_draft[(size_t)b * k + i] = in_range ? p[x[i]] : 0.0;
+            }
+            if (q_at_draft) {
+                softmax_row(draft_logits, dtype, d_row, V, temperature, q);
+                q_at_draft[(size_t)b * k + i] = in_range ? q[x[i]] : 0.0;
+            }
+        }
+
+        /* Step 2: the one final token. */
+        softmax_row(target_logits, dtype, ((size_t)b * (k + 1) + s) * (size_t)V, V,
+                    temperature, p);
+        if (s < k) {
+            softmax_row(draft_logits, dtype, ((size_t)b * k + s) * (size_t)V, V,
+                        temperature, q);
+            double Z = 0.0;
+            for (int j = 0; j < V; ++j) {
+                double d = p[j] - q[j];
+                w[j] = d > 0.0 ? d : 0.0;
+                Z += w[j];
+            }
+            if (!(Z > 0.0)) /* p_s == q_s: sample from p_s */
+                memcpy(w, p, sizeof(double) * (size_t)V);
+        } else {
+            memcpy(w, p, sizeof(double) * (size_t)V);
+        }
+        double final_margin;
+        int32_t token = inverse_cdf(w, V, (double)u[k], &final_margin);
+        if (margin)
+            margin[k] = final_margin;
+
+        for (int i = 0; i < s; ++i)
+            out[i] = x[i];
+        out[s] = token;
+        for (int i = s + 1; i <= k; ++i)
+            out[i] = -1;
+        num_accepted[b] = s;
+    }
+    free(p);
+    free(q);
+    free(w);
+    return ORACLE_OK;
+}
+
+/* Index of the largest raw logit of one row; the lowest index wins a tie. */
+static int32_t argmax_row(const void *logits, int dtype, size_t row_offset, int V)
+{
+    int32_t best = 0;
+    double best_value = logit_at(logits, dtype, row_offset);
+    for (int j = 1; j < V; ++j) {
+        double v = logit_at(logits, dtype, row_offset + (size_t)j);
+        if (v > best_value) {
+            best_value = v;
+            best = (int32_t)j;
+        }
+    }
+    return best;
+}
+
+/*
+ * Greedy verification ([KESTREL] section 2, acceptance and emit steps;
+ * section 3.3): a_i = argmax of target row i for i = 0..k; the accepted count
+ * s is the number of leading draft tokens equal to a_0, a_1, ...; the output is
+ * draft[0..s-1], then a_s, then -1 padding.  When s == 0 the only token is
+ * a_0 (no row before 0 is ever read).
+ *   argmax_out [B, k+1] (may be NULL) receives every a_i.
+ */
+int oracle_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
+                         int B, int k, int V, int32_t *out_tokens, int32_t *num_accepted,
+                         int32_t *argmax_out)
+{
+    if (B < 0 || k < 0 || V < 1)
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    for (int b = 0; b < B; ++b) {
+        const int32_t *x = draft_tokens + (size_t)b * k;
+        int32_t *out = out_tokens + (size_t)b * (k + 1);
+        int32_t a[1024 + 1];
+        int32_t *arg = (k + 1 <= 1025) ? a : (int32_t *)malloc(sizeof(int32_t) * (size_t)(k + 1));
+        if (!arg)
+            return ORACLE_NO_MEMORY;
+        for (int i = 0; i <= k; ++i)
+            arg[i] = argmax_row(target_logits, dtype, ((size_t)b * (k + 1) + i) * (size_t)V, V);
+        int s = 0;
+        while (s < k && x[s] == arg[s])
+            ++s;
+        for (int i = 0; i < s; ++i)
+            out[i] = x[i];
+        out[s] = arg[s];
+        for (int i = s + 1; i <= k; ++i)
+            out[i] = -1;
+        num_accepted[b] = s;
+        if (argmax_out)
+            memcpy(argmax_out + (size_t)b * (k + 1), arg, sizeof(int32_t) * (size_t)(k + 1));
+        if (arg != a)
+            free(arg);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Tree (EAGLE-style) greedy verification ([EAGLE] both sections named above).
+ *
+ *   target_logits [B, N+1, V]: row n holds the target's distribution after
+ *                 tree node n (node 0 is the root, the last committed token).
+ *   node_tokens   [B, N+1] int32: the draft token at each node; [b, 0] unused.
+ *   paths         [B, P, L] int32: each row lists node indices from the root
+ *                 down one branch, padded with -1; a row whose first entry is
+ *                 not a node index is unused.
+ *   out_tokens    [B, L]: tokens of the accepted nodes, then the argmax at the
+ *                 last accepted node, then -1 padding.
+ *   num_accepted  [B]: accepted node count.
+ *   best_path     [B] (may be NULL): the chosen path row, -1 if none is used.
+ *   accepted_nodes [B, L] (may be NULL): the accepted node indices, -1 padded.
+ *
+ * A node is accepted when its token equals the argmax of its parent's row, and
+ * a path's accepted length m is the number of nodes accepted in a row from the
+ * root.  The chosen path has the largest m; among equal m the lowest row index.
+ */
+int oracle_verify_tree(const void *target_logits, int dtype, const int32_t *node_tokens,
+                       const int32_t *paths, int B, int N, int P, int L, int V,
+                       int32_t *out_tokens, int32_t *num_accepted, int32_t *best_path,
+                       int32_t *accepted_nodes)
+{
+    if (B < 0 || N < 0 || P < 0 || L < 1 || V < 1)
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    int32_t *a = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N + 1));
+    if (!a)
+        return ORACLE_NO_MEMORY;
+    for (int b = 0; b < B; ++b) {
+        for (int n = 0; n <= N; ++n)
+            a[n] = argmax_row(target_logits, dtype, ((size_t)b * (N + 1) + n) * (size_t)V, V);
+        const int32_t *tok = node_tokens + (size_t)b * (N + 1);
+
+        int best = -1, best_m = -1;
+        for (int p = 0; p < P; ++p) {
+            const int32_t *row = paths + ((size_t)b * P + p) * (size_t)L;
+            if (row[0] < 0 || row[0] > N)
+                continue; /* unused row */
+            int m = 0;
+            while (m + 1 < L) {
+                int32_t child = row[m + 1];
+                if (child < 0 || child > N)
+                    break;
+                if (tok[child] != a[row[m]])
+                    break;
+                ++m;
+            }
+            if (m > best_m) { /* strictly longer: lower rows win ties */
+                best_m = m;
+                best = p;
+            }
+        }
+
+        int32_t *out = out_tokens + (size_t)b * L;
+        int32_t *nodes = accepted_nodes ? accepted_nodes + (size_t)b * L : NULL;
+        for (int t = 0; t < L; ++t) {
+            out[t] = -1;
+            if (nodes)
+                nodes[t] = -1;
+        }
+        if (best < 0) { /* no usable path: the tree is the root alone */
+            out[0] = a[0];
+            num_accepted[b] = 0;
+        } else {
+            const int32_t *row = paths + ((size_t)b * P + best) * (size_t)L;
+            for (int t = 1; t <= best_m; ++t) {
+                out[t - 1] = tok[row[t]];
+                if (nodes)
+                    nodes[t - 1] = row[t];
+            }
+            out[best_m] = a[row[best_m]];
+            num_accepted[b] = best_m;
+        }
+        if (best_path)
+            best_path[b] = best;
+    }
+    free(a);
+    return ORACLE_OK;
+}

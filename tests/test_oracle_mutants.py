@@ -1,0 +1,61 @@
+"""Planted mistakes in the oracle (on the CPU only) must each fail some pin.
+
+Each mutant is a copy of the oracle's C source with one plausible mistake
+substituted (a flipped comparison, a swapped operand, a wrong row or uniform
+index, a dropped term); it is compiled into a temporary library and every pin
+in ``oracle_pins`` runs against it until one fails.  A mutant that passes every
+pin means the pins are too weak to notice that mistake.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+MUTANTS = {
+    "non-strict acceptance": ("accepted = (double)u[i] < P / Q;",
+                              "accepted = (double)u[i] <= P / Q;"),
+    "inverted ratio": ("accepted = (double)u[i] < P / Q;", "accepted = (double)u[i] < Q / P;"),
+    "residual sign": ("double d = p[j] - q[j];", "double d = q[j] - p[j];"),
+    "residual unclamped": ("w[j] = d > 0.0 ? d : 0.0;", "w[j] = d;"),
+    "residual ignores draft": ("if (s < k) {", "if (0) {"),
+    "bonus from row k-1": (
+        "softmax_row(target_logits, dtype, ((size_t)b * (k + 1) + s) * (size_t)V, V,",
+        "softmax_row(target_logits, dtype, ((size_t)b * (k + 1) + (s == k && s > 0 ? s - 1 : s)) * (size_t)V, V,"),
+    "target row shifted": ("size_t t_row = ((size_t)b * (k + 1) + i) * (size_t)V;\n            size_t d_row = ((size_t)b * k + i) * (size_t)V;\n            softmax_row",
+                           "size_t t_row = ((size_t)b * (k + 1) + i + 1) * (size_t)V;\n            size_t d_row = ((size_t)b * k + i) * (size_t)V;\n            softmax_row"),
+    "final sample uses u[s]": ("inverse_cdf(w, V, (double)u[k], &final_margin);",
+                               "inverse_cdf(w, V, (double)u[s], &final_margin);"),
+    "cdf non-strict": ("if (above > target) {", "if (above >= target) {"),
+    "temperature ignored": ("double z = logit_at(logits, dtype, row_offset + (size_t)j) / temperature;",
+                            "double z = logit_at(logits, dtype, row_offset + (size_t)j);"),
+    "argmax last tie": ("if (v > best_value) {", "if (v >= best_value) {"),
+    "greedy emits draft at stop": ("out[s] = arg[s];", "out[s] = s < k ? x[s] : arg[s];"),
+    "greedy off-by-one row": ("while (s < k && x[s] == arg[s])", "while (s < k && x[s] == arg[s + 1 <= k ? s + 1 : s])"),
+    "tree highest tie": ("if (m > best_m) { /* strictly longer", "if (m >= best_m) { /* strictly longer"),
+    "tree compares own row": ("if (tok[child] != a[row[m]])", "if (tok[child] != a[child])"),
+    "tree emits last node token": ("out[best_m] = a[row[best_m]];", "out[best_m] = tok[row[best_m]];"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SOURCE) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation anchor for {name!r} not found exactly once"
+    src = tmp_path / "mutant.c"
+    src.write_text(source.replace(old, new))
+    lib_path = oracle.compile_source(str(src), str(tmp_path / f"libmutant_{os.getpid()}.so"))
+    lib = oracle.open_library(lib_path)
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except AssertionError:
+            return  # caught
+    pytest.fail(f"planted mistake {name!r} passed every oracle pin")
