@@ -1,0 +1,204 @@
+"""Batched draft-token verification for speculative decoding on MI355X (gfx950).
+
+A thin binding over the C ABI in ``include/spec_verify.h``: the functions below
+carry the C names, check tensor shapes, dtypes and devices, pass raw device
+pointers and the current HIP stream, and return the output tensors.  Every step
+of the verification runs in the library's HIP kernels; PyTorch only provides
+device memory and the stream.  There is no CPU fallback: without the built
+library every call raises.
+
+    out, n = spec_verify_stochastic(target, draft, draft_tokens, uniforms, T)
+    out, n = spec_verify_greedy(target, draft_tokens)
+    out, n, best, nodes = spec_verify_tree(target, node_tokens, paths)
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_TREE, SpecVerifyError)
+
+__all__ = [
+    "spec_verify_stochastic", "spec_verify_greedy", "spec_verify_tree",
+    "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
+    "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE",
+]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device, stream=None) -> int:
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return s.cuda_stream
+
+
+def spec_verify_version() -> int:
+    return _lib.load().spec_verify_version()
+
+
+def spec_verify_workspace_bytes(mode: int, B: int, rows_per_request: int, V: int,
+                                dtype: int) -> int:
+    return int(_lib.load().spec_verify_workspace_bytes(mode, B, rows_per_request, V, dtype))
+
+
+class Workspace:
+    """Grow-only, zero-initialised device workspace, one buffer per device.
+
+    The library leaves its counters at zero after every completed call, so one
+    buffer serves every later call that is ordered on the same stream.
+    """
+
+    def __init__(self):
+        self._buf: dict[torch.device, torch.Tensor] = {}
+
+    def get(self, nbytes: int, device: torch.device) -> torch.Tensor:
+        buf = self._buf.get(device)
+        if buf is None or buf.numel() < nbytes:
+            # torch.zeros clears with a fill kernel (no memset node).
+            buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+            self._buf[device] = buf
+        return buf
+
+
+_default_workspace = Workspace()
+
+
+def _workspace(ws, nbytes: int, device: torch.device) -> torch.Tensor:
+    if nbytes == 0:
+        raise SpecVerifyError("spec_verify_workspace_bytes", _lib.INVALID_ARGUMENT,
+                              "shape rejected by the library")
+    if ws is None:
+        return _default_workspace.get(nbytes, device)
+    if isinstance(ws, Workspace):
+        return ws.get(nbytes, device)
+    _dev(ws, "workspace", device, torch.uint8)
+    if ws.numel() < nbytes:
+        raise SpecVerifyError("workspace", _lib.WORKSPACE_TOO_SMALL,
+                              f"need {nbytes} bytes, got {ws.numel()}")
+    return ws
+
+
+def spec_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor | None,
+                           draft_tokens: torch.Tensor | None, uniforms: torch.Tensor,
+                           temperature: float, *, out_tokens=None, num_accepted=None,
+                           p_at_draft=None, q_at_draft=None, workspace=None, stream=None):
+    """Stochastic verification; returns ``(out_tokens[B,k+1], num_accepted[B])``.
+
+    ``p_at_draft`` / ``q_at_draft`` (float32 [B, k]), when given, receive the
+    target and draft probabilities of each draft token.
+    """
+    device = target_logits.device
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, k+1, V]")
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _dev(target_logits, "target_logits", device)
+    if k > 0:
+        _dev(draft_logits, "draft_logits", device, target_logits.dtype, (B, k, V))
+        _dev(draft_tokens, "draft_tokens", device, torch.int32, (B, k))
+    else:
+        draft_logits = draft_tokens = None
+    _dev(uniforms, "uniforms", device, torch.float32, (B, k + 1))
+    if out_tokens is None:
+        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=device)
+    _dev(out_tokens, "out_tokens", device, torch.int32, (B, k + 1))
+    _dev(num_accepted, "num_accepted", device, torch.int32, (B,))
+    for name, t in (("p_at_draft", p_at_draft), ("q_at_draft", q_at_draft)):
+        if t is not None:
+            _dev(t, name, device, torch.float32, (B, k))
+    nbytes = spec_verify_workspace_bytes(MODE_STOCHASTIC, B, k + 1, V, dt)
+    ws = _workspace(workspace, nbytes, device)
+    st = _lib.load().spec_verify_stochastic(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
+        float(temperature), B, k, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(p_at_draft),
+        _ptr(q_at_draft), _ptr(ws), ws.numel(), _stream(device, stream))
+    _lib.check("spec_verify_stochastic", st)
+    return out_tokens, num_accepted
+
+
+def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor | None, *,
+                       out_tokens=None, num_accepted=None, workspace=None, stream=None):
+    """Greedy verification; returns ``(out_tokens[B,k+1], num_accepted[B])``."""
+    device = target_logits.device
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, k+1, V]")
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _dev(target_logits, "target_logits", device)
+    if k > 0:
+        _dev(draft_tokens, "draft_tokens", device, torch.int32, (B, k))
+    else:
+        draft_tokens = None
+    if out_tokens is None:
+        out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
+    if num_accepted is None:
+        num_accepted = torch.empty((B,), dtype=torch.int32, device=device)
+    _dev(out_tokens, "out_tokens", device, torch.int32, (B, k + 1))
+    _dev(num_accepted, "num_accepted", device, torch.int32, (B,))
+    nbytes = spec_verify_workspace_bytes(MODE_GREEDY, B, k + 1, V, dt)
+    ws = _workspace(workspace, nbytes, device)
+    st = _lib.load().spec_verify_greedy(
+        _ptr(target_logits), dt, _ptr(draft_tokens), B, k, V, _ptr(out_tokens),
+        _ptr(num_accepted), _ptr(ws), ws.numel(), _stream(device, stream))
+    _lib.check("spec_verify_greedy", st)
+    return out_tokens, num_accepted
+
+
+def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,
+                     paths: torch.Tensor, *, out_tokens=None, num_accepted=None,
+                     best_path=None, accepted_nodes=None, workspace=None, stream=None):
+    """Tree verification; returns ``(out_tokens[B,L], num_accepted[B], best_path[B],
+    accepted_nodes[B,L])``."""
+    device = target_logits.device
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3 or paths.dim() != 3:
+        raise ValueError("target_logits must be [B, N+1, V] and paths [B, P, L]")
+    B, N1, V = target_logits.shape
+    _, P, L = paths.shape
+    _dev(target_logits, "target_logits", device)
+    _dev(node_tokens, "node_tokens", device, torch.int32, (B, N1))
+    _dev(paths, "paths", device, torch.int32, (B, P, L))
+    outs = []
+    for name, t, shape in (("out_tokens", out_tokens, (B, L)),
+                           ("num_accepted", num_accepted, (B,)),
+                           ("best_path", best_path, (B,)),
+                           ("accepted_nodes", accepted_nodes, (B, L))):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=device)
+        outs.append(_dev(t, name, device, torch.int32, shape))
+    nbytes = spec_verify_workspace_bytes(MODE_TREE, B, N1, V, dt)
+    ws = _workspace(workspace, nbytes, device)
+    st = _lib.load().spec_verify_tree(
+        _ptr(target_logits), dt, _ptr(node_tokens), _ptr(paths), B, N1 - 1, P, L, V,
+        _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(outs[3]), _ptr(ws), ws.numel(),
+        _stream(device, stream))
+    _lib.check("spec_verify_tree", st)
+    return tuple(outs)

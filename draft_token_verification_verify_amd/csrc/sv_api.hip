@@ -1,0 +1,195 @@
+// sv_api.hip -- the C ABI: host-side validation, launch geometry, launches.
+//
+// Every check runs on the host before anything is enqueued, and reads only
+// shapes, pointers and scalars (never device data): a rejected call launches
+// nothing and touches no output, so a caller can capture calls in a graph.
+// Host-side, fail-closed validation follows the shape guards described on the
+// page "TensorRT-LLM source teardown (10): speculative decoding", section
+// "Rejection sampling".
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/spec_verify.h"
+#include "sv_common.hpp"
+#include "sv_launch.hpp"
+
+namespace {
+
+int elem_bytes_of(int dtype) {
+    if (dtype == SPEC_VERIFY_F32) return 4;
+    if (dtype == SPEC_VERIFY_BF16) return 2;
+    return 0;
+}
+
+// Rows are 16-byte aligned and hold whole 16-byte vectors.
+bool vec_ok(const void* p, int V, int eb) {
+    return p == nullptr || ((reinterpret_cast<uintptr_t>(p) % 16 == 0) &&
+                            ((size_t)V * (size_t)eb) % 16 == 0);
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_HIP_ERROR; }
+
+// Profiling hook state (see spec_verify_profile_events).
+void* const* g_events = nullptr;
+int g_event_pairs = 0;
+int g_event_next = 0;
+
+sv::KernelEvents next_events() {
+    sv::KernelEvents ev;
+    if (g_events && g_event_pairs > 0) {
+        const int i = g_event_next;
+        g_event_next = (i + 1) % g_event_pairs;
+        ev.begin = (hipEvent_t)g_events[2 * i];
+        ev.end = (hipEvent_t)g_events[2 * i + 1];
+    }
+    return ev;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify_version(void) { return 100; }
+
+const char* spec_verify_status_string(int status) {
+    switch (status) {
+        case SPEC_VERIFY_OK: return "ok";
+        case SPEC_VERIFY_INVALID_ARGUMENT: return "invalid argument";
+        case SPEC_VERIFY_UNSUPPORTED_DTYPE: return "unsupported dtype";
+        case SPEC_VERIFY_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case SPEC_VERIFY_LIMIT_EXCEEDED: return "limit exceeded";
+        case SPEC_VERIFY_HIP_ERROR: return "HIP launch error";
+        default: return "unknown status";
+    }
+}
+
+size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype) {
+    const int eb = elem_bytes_of(dtype);
+    if (eb == 0 || mode < 0 || mode > 2 || V > SPEC_VERIFY_MAX_VOCAB) return 0;
+    if (mode != 2 && rows_per_request - 1 > SPEC_VERIFY_MAX_K) return 0;
+    if (mode == 2 && rows_per_request > SPEC_VERIFY_MAX_TREE_ROWS) return 0;
+    sv::Geometry g;
+    if (!sv::make_geometry(mode, B, rows_per_request, V, eb, &g)) return 0;
+    return g.bytes;
+}
+
+int spec_verify_profile_events(void* const* events, int n_pairs) {
+    if (n_pairs < 0 || (n_pairs > 0 && events == nullptr)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    g_events = n_pairs > 0 ? events : nullptr;
+    g_event_pairs = n_pairs;
+    g_event_next = 0;
+    return SPEC_VERIFY_OK;
+}
+
+int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    if (workspace == nullptr && workspace_bytes != 0) return SPEC_VERIFY_INVALID_ARGUMENT;
+    return finish(sv::run_fill_zero(workspace, workspace_bytes, (hipStream_t)stream));
+}
+
+int spec_verify_stochastic(const void* target_logits, const void* draft_logits, int dtype,
+                           const int32_t* draft_tokens, const float* uniforms,
+                           float temperature, int B, int k, int V, int32_t* out_tokens,
+                           int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const int eb = elem_bytes_of(dtype);
+    if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
+    if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!target_logits || !uniforms || !out_tokens || !num_accepted || !workspace)
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    sv::Geometry g;
+    if (!sv::make_geometry(0, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if ((long long)B * g.R * g.S > 0x7fffffffLL || (long long)B * g.S2 > 0x7fffffffLL)
+        return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (workspace_bytes < g.bytes) return SPEC_VERIFY_WORKSPACE_TOO_SMALL;
+
+    sv::StochasticCall c;
+    c.target = target_logits;
+    c.draft = k > 0 ? draft_logits : nullptr;
+    c.dtype = dtype;
+    c.vec = vec_ok(target_logits, V, eb) && vec_ok(c.draft, V, eb);
+    c.draft_tokens = draft_tokens;
+    c.uniforms = uniforms;
+    c.temperature = temperature;
+    c.B = B;
+    c.k = k;
+    c.V = V;
+    c.out_tokens = out_tokens;
+    c.num_accepted = num_accepted;
+    c.p_at_draft = p_at_draft;
+    c.q_at_draft = q_at_draft;
+    c.workspace = workspace;
+    return finish(sv::run_stochastic(c, g, (hipStream_t)stream, next_events()));
+}
+
+int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draft_tokens, int B,
+                       int k, int V, int32_t* out_tokens, int32_t* num_accepted,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    const int eb = elem_bytes_of(dtype);
+    if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
+    if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!target_logits || !out_tokens || !num_accepted || !workspace)
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (k > 0 && !draft_tokens) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    sv::Geometry g;
+    if (!sv::make_geometry(1, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if ((long long)B * g.R * g.S > 0x7fffffffLL) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (workspace_bytes < g.bytes) return SPEC_VERIFY_WORKSPACE_TOO_SMALL;
+
+    sv::GreedyCall c;
+    c.target = target_logits;
+    c.dtype = dtype;
+    c.vec = vec_ok(target_logits, V, eb);
+    c.draft_tokens = draft_tokens;
+    c.B = B;
+    c.k = k;
+    c.V = V;
+    c.out_tokens = out_tokens;
+    c.num_accepted = num_accepted;
+    c.workspace = workspace;
+    return finish(sv::run_greedy(c, g, (hipStream_t)stream, next_events()));
+}
+
+int spec_verify_tree(const void* target_logits, int dtype, const int32_t* node_tokens,
+                     const int32_t* paths, int B, int N, int P, int L, int V,
+                     int32_t* out_tokens, int32_t* num_accepted, int32_t* best_path,
+                     int32_t* accepted_nodes, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+    const int eb = elem_bytes_of(dtype);
+    if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
+    if (B < 1 || N < 0 || P < 0 || L < 1 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!target_logits || !node_tokens || !out_tokens || !num_accepted || !workspace)
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (P > 0 && !paths) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (N + 1 > SPEC_VERIFY_MAX_TREE_ROWS || P > SPEC_VERIFY_MAX_PATHS ||
+        L > SPEC_VERIFY_MAX_PATH_LEN || (long long)P * L > SPEC_VERIFY_MAX_PATH_TABLE ||
+        V > SPEC_VERIFY_MAX_VOCAB)
+        return SPEC_VERIFY_LIMIT_EXCEEDED;
+    sv::Geometry g;
+    if (!sv::make_geometry(2, B, N + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if ((long long)B * g.R * g.S > 0x7fffffffLL) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (workspace_bytes < g.bytes) return SPEC_VERIFY_WORKSPACE_TOO_SMALL;
+
+    sv::TreeCall c;
+    c.target = target_logits;
+    c.dtype = dtype;
+    c.vec = vec_ok(target_logits, V, eb);
+    c.node_tokens = node_tokens;
+    c.paths = paths;
+    c.B = B;
+    c.N = N;
+    c.P = P;
+    c.L = L;
+    c.V = V;
+    c.out_tokens = out_tokens;
+    c.num_accepted = num_accepted;
+    c.best_path = best_path;
+    c.accepted_nodes = accepted_nodes;
+    c.workspace = workspace;
+    return finish(sv::run_tree(c, g, (hipStream_t)stream, next_events()));
+}
+
+}  // extern "C"

@@ -1,0 +1,205 @@
+// sv_common.hpp -- shared device helpers, launch geometry and workspace layout of
+// the verification kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;           // one workgroup = 4 wave64s
+constexpr int kWaves = kThreads / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kSampleSegVecs = 4;       // 16-byte vectors per thread in a sampler chunk
+constexpr int kMaxK = 64;               // longest linear draft
+constexpr int kTreeLdsPathEntries = 4096;  // path tables up to this many entries go to LDS
+
+// ---------------------------------------------------------------------------
+// Launch geometry and workspace layout.  A pure function of the call's shape
+// (never of pointer values), so sizing and launching always agree.
+// ---------------------------------------------------------------------------
+struct Geometry {
+    int R;           // logits rows streamed per request
+    int S;           // chunks per row in the streaming kernel
+    int chunk;       // elements per chunk (multiple of 2048)
+    int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8
+    int S2;          // stop-row chunks per request (stochastic sampler)
+    int chunk2;      // elements per stop-row chunk
+    size_t off_ticket_a, off_ticket_b, off_partials, off_stop, off_mass, bytes;
+};
+
+struct StopInfo {      // per request, written by the streaming kernel's epilogue
+    int32_t s;         // number of accepted drafts = stop row
+    int32_t pad;
+    float mt, st;      // max logit and sum of exp2((x - mt) * c) of target row s
+    float md, sd;      // same for draft row s (unused when s == k)
+    float pad2[2];
+};
+static_assert(sizeof(StopInfo) == 32, "StopInfo layout");
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// mode: 0 stochastic, 1 greedy, 2 tree; rows_per_request: k+1 or N+1.
+inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem_bytes,
+                          Geometry* g) {
+    if (B < 1 || rows_per_request < 1 || V < 1 || (elem_bytes != 2 && elem_bytes != 4))
+        return false;
+    const int epv = 16 / elem_bytes;  // elements per 16-byte vector
+    g->R = (mode == 0) ? 2 * rows_per_request - 1 : rows_per_request;
+    const long long rows = (long long)B * g->R;
+    // Largest per-thread vector count whose tile count still fills the chip
+    // several times over; small problems fall back to smaller tiles.
+    int U = 8;
+    for (; U > 1; U >>= 1) {
+        long long ce = (long long)kThreads * U * epv;
+        long long tiles = rows * ((V + ce - 1) / ce);
+        if (tiles >= 2048) break;
+    }
+    g->U = U;
+    g->chunk = kThreads * U * epv;
+    g->S = (V + g->chunk - 1) / g->chunk;
+    g->chunk2 = kThreads * kSampleSegVecs * epv;
+    g->S2 = (mode == 0) ? (V + g->chunk2 - 1) / g->chunk2 : 0;
+
+    size_t off = 0;
+    g->off_ticket_a = off;
+    off = align_up(off + sizeof(uint32_t) * (size_t)B, 256);
+    g->off_ticket_b = off;
+    off = align_up(off + sizeof(uint32_t) * (size_t)B, 256);
+    g->off_partials = off;
+    off = align_up(off + 8 * (size_t)rows * (size_t)g->S, 256);
+    g->off_stop = off;
+    off = align_up(off + (mode == 0 ? sizeof(StopInfo) * (size_t)B : 0), 256);
+    g->off_mass = off;
+    off = align_up(off + (mode == 0 ? sizeof(double) * (size_t)B * (size_t)g->S2 : 0), 256);
+    g->bytes = off;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
+// Element access.  bf16 logits are carried as raw uint16 bit patterns; widening
+// to fp32 is a 16-bit shift (exact).
+// ---------------------------------------------------------------------------
+struct bf16_t { uint16_t bits; };
+
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static constexpr int kPerVec = 4;
+    __device__ static inline float load(const float* p, size_t i) { return p[i]; }
+    __device__ static inline void widen(const uint4& v, float* out) {
+        out[0] = __uint_as_float(v.x);
+        out[1] = __uint_as_float(v.y);
+        out[2] = __uint_as_float(v.z);
+        out[3] = __uint_as_float(v.w);
+    }
+};
+
+template <> struct Elem<bf16_t> {
+    static constexpr int kPerVec = 8;
+    __device__ static inline float load(const bf16_t* p, size_t i) {
+        return __uint_as_float((uint32_t)p[i].bits << 16);
+    }
+    __device__ static inline void widen(const uint4& v, float* out) {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            out[2 * q] = __uint_as_float(w[q] << 16);
+            out[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+        }
+    }
+};
+
+__device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Softmax statistics (m, s): m = max raw logit, s = sum exp2((x - m) * c).
+// Merging two pairs rescales both sums to the larger maximum; an empty side
+// (m = -inf, s = 0) contributes nothing and never produces a NaN.
+// ---------------------------------------------------------------------------
+__device__ inline void merge_ms(float& m, float& s, float m2, float s2, float c) {
+    float M = fmaxf(m, m2);
+    float Ms = (M == -INFINITY) ? 0.f : M;
+    s = s * fast_exp2((m - Ms) * c) + s2 * fast_exp2((m2 - Ms) * c);
+    m = M;
+}
+
+// Argmax pairs: larger value wins, the lower index wins a tie.
+__device__ inline void merge_argmax(float& v, int& i, float v2, int i2) {
+    bool take = (v2 > v) || (v2 == v && i2 < i);
+    v = take ? v2 : v;
+    i = take ? i2 : i;
+}
+
+// Fixed-order reductions (same result on every run).
+__device__ inline void wave_reduce_ms(float& m, float& s, float c) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float m2 = __shfl_xor(m, off, 64);
+        float s2 = __shfl_xor(s, off, 64);
+        merge_ms(m, s, m2, s2, c);
+    }
+}
+
+__device__ inline void wave_reduce_argmax(float& v, int& i) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        float v2 = __shfl_xor(v, off, 64);
+        int i2 = __shfl_xor(i, off, 64);
+        merge_argmax(v, i, v2, i2);
+    }
+}
+
+__device__ inline double wave_reduce_sum(double x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// Inclusive prefix sum over the workgroup in thread order (deterministic).
+// `wave_tot` is LDS scratch of kWaves doubles.  Returns the inclusive prefix;
+// *total receives the workgroup total.
+__device__ inline double block_inclusive_scan(double x, double* wave_tot, double* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        double y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) wave_tot[wave] = x;
+    __syncthreads();
+    double before = 0.0, all = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        double t = wave_tot[w];
+        if (w < wave) before += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + x;
+}
+
+// Take an arrival ticket on `counter` after thread 0 has written this
+// workgroup's contribution (only thread 0 writes what other workgroups read).
+// Returns true in every thread of the last of `expected` arrivals; those
+// threads then see every other arrival's writes.  The last arrival resets the
+// counter to zero (atomically, where the other arrivals incremented it).
+__device__ inline bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
+    if (threadIdx.x == 0) {
+        __threadfence();  // release thread 0's writes at device scope
+        uint32_t prev = atomicAdd(counter, 1u);
+        int last = (prev == expected - 1);
+        if (last) atomicExch(counter, 0u);
+        *lds_flag = last;
+    }
+    __syncthreads();
+    bool last = *lds_flag != 0;
+    if (last) __threadfence();
+    return last;
+}
+
+}  // namespace sv

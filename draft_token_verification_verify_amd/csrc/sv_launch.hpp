@@ -1,0 +1,67 @@
+// sv_launch.hpp -- validated call descriptions passed from the C ABI layer to the
+// kernel launchers (internal; not part of the public header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+struct StochasticCall {
+    const void* target;
+    const void* draft;
+    int dtype;  // 0 f32, 1 bf16
+    bool vec;   // rows are 16-byte aligned and V is a whole number of vectors
+    const int32_t* draft_tokens;
+    const float* uniforms;
+    float temperature;
+    int B, k, V;
+    int32_t* out_tokens;
+    int32_t* num_accepted;
+    float* p_at_draft;
+    float* q_at_draft;
+    void* workspace;
+};
+
+struct GreedyCall {
+    const void* target;
+    int dtype;
+    bool vec;
+    const int32_t* draft_tokens;
+    int B, k, V;
+    int32_t* out_tokens;
+    int32_t* num_accepted;
+    void* workspace;
+};
+
+struct TreeCall {
+    const void* target;
+    int dtype;
+    bool vec;
+    const int32_t* node_tokens;
+    const int32_t* paths;
+    int B, N, P, L, V;
+    int32_t* out_tokens;
+    int32_t* num_accepted;
+    int32_t* best_path;
+    int32_t* accepted_nodes;
+    void* workspace;
+};
+
+// Optional events recorded around the streaming kernel (both null = none).
+struct KernelEvents {
+    hipEvent_t begin = nullptr, end = nullptr;
+};
+
+hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
+                          const KernelEvents& ev);
+hipError_t run_greedy(const GreedyCall& call, const Geometry& g, hipStream_t st,
+                      const KernelEvents& ev);
+hipError_t run_tree(const TreeCall& call, const Geometry& g, hipStream_t st,
+                    const KernelEvents& ev);
+hipError_t run_fill_zero(void* ptr, size_t bytes, hipStream_t st);
+
+}  // namespace sv

@@ -38,7 +38,7 @@ __all__ = [
     "StochasticCase", "GreedyCase", "TreeCase",
     "gaussian_stochastic", "zipf_stochastic", "gaussian_greedy", "random_tree_case",
     "c1", "c2_greedy", "c2_stochastic", "c3", "c4", "c5",
-    "bf16_bits", "bits_to_float",
+    "bf16_bits", "bits_to_float", "to_device",
 ]
 
 
@@ -53,6 +53,17 @@ def bf16_bits(x: np.ndarray) -> np.ndarray:
 def bits_to_float(bits: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def to_device(a: np.ndarray, dtype: str | None = None, device="cuda"):
+    """Copy a NumPy array to a torch device tensor; ``dtype="bf16"`` reinterprets
+    uint16 bit patterns as torch.bfloat16."""
+    import torch
+
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
 @dataclass

@@ -1,0 +1,199 @@
+/*
+ * spec_verify.h -- C ABI of the batched draft-token verification library
+ * (speculative decoding) for AMD Instinct MI355X (gfx950).
+ *
+ * Three verification calls, one per mode, plus sizing and status helpers.
+ * Every pointer argument named *_logits, *_tokens, uniforms, paths, out_*,
+ * num_accepted, best_path, accepted_nodes, p_at_draft, q_at_draft and
+ * workspace is a DEVICE pointer owned by the caller.  The library never
+ * allocates, frees or synchronises; it never reads device data on the host.
+ * Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ * default stream); outputs are valid once the stream has reached that point.
+ * Inputs are never modified.  Shapes are plain integers, layouts are dense and
+ * row-major with the vocabulary innermost.
+ *
+ * Errors are fail-closed: every argument is checked on the host before any
+ * launch; on an error nothing is launched and no output is touched.
+ *
+ * Data preconditions (documented, not checked on the device): logits hold no
+ * NaN and each row has at least one finite value (-inf is allowed); uniforms lie
+ * in [0, 1).  Out-of-range ids are tolerated with a defined result: a draft
+ * token outside [0, V) is rejected (stochastic) or never matches (greedy); a
+ * path entry outside [0, N] ends that path like -1.
+ *
+ * Sources (page title, section):
+ *   "Inside vLLM: Anatomy of a High-Throughput LLM Inference System",
+ *     "Speculative Decoding" -- the accept / reject / residual / bonus rules.
+ *   "02. Speculative Decoding" (vLLM learning book), section 2 flowchart -- the
+ *     test r < min(1, p(x_i) / q(x_i)) and the residual (p - q)+ / Z.
+ *   "TensorRT-LLM source teardown (10): speculative decoding", "Rejection
+ *     sampling" -- accepted_tokens [batch, D+1] (accepted drafts, correction or
+ *     bonus token, then -1 padding) plus a per-request count; host-side
+ *     fail-closed shape guards that never read device values.
+ *   "Kestrel_VLLM - 32", section 2 -- greedy acceptance by argmax match.
+ *   "05 - TensorRT-LLM speculative decoding and auto-deploy", "Eagle-2
+ *     multi-level tree drafting" -- paths[batch, max_decoding_tokens,
+ *     max_path_len].
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Stable integer enums: values are never renumbered. */
+enum spec_verify_dtype {
+    SPEC_VERIFY_F32 = 0,  /* IEEE binary32 logits */
+    SPEC_VERIFY_BF16 = 1  /* bfloat16 logits (upper half of a binary32) */
+};
+
+enum spec_verify_mode {
+    SPEC_VERIFY_MODE_STOCHASTIC = 0,
+    SPEC_VERIFY_MODE_GREEDY = 1,
+    SPEC_VERIFY_MODE_TREE = 2
+};
+
+enum spec_verify_status {
+    SPEC_VERIFY_OK = 0,
+    SPEC_VERIFY_INVALID_ARGUMENT = 1,   /* null pointer, bad size, bad temperature */
+    SPEC_VERIFY_UNSUPPORTED_DTYPE = 2,
+    SPEC_VERIFY_WORKSPACE_TOO_SMALL = 3,
+    SPEC_VERIFY_LIMIT_EXCEEDED = 4,     /* k, N, P, L or V beyond the limits below */
+    SPEC_VERIFY_HIP_ERROR = 5           /* a launch failed; see hipGetLastError */
+};
+
+/* Limits checked on the host. */
+#define SPEC_VERIFY_MAX_K 64          /* draft length of the linear modes */
+#define SPEC_VERIFY_MAX_TREE_ROWS 1024 /* N + 1 */
+#define SPEC_VERIFY_MAX_PATHS 1024    /* P */
+#define SPEC_VERIFY_MAX_PATH_LEN 64   /* L */
+#define SPEC_VERIFY_MAX_PATH_TABLE 16384 /* P * L */
+#define SPEC_VERIFY_MAX_VOCAB (1 << 30)
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int spec_verify_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *spec_verify_status_string(int status);
+
+/*
+ * Bytes of device workspace one call of `mode` needs for a batch of B
+ * requests with `rows_per_request` target rows each (k + 1 for the linear
+ * modes, N + 1 for the tree mode) over a vocabulary of V in `dtype`.
+ * Returns 0 for arguments the corresponding call would reject.
+ *
+ * The workspace holds per-request arrival counters, per-chunk partial
+ * reductions and per-request sampling state.  It must be zero-filled before
+ * its first use (spec_verify_workspace_init does that); every call leaves the
+ * counters zeroed again when it completes, so one workspace serves any number
+ * of later calls of any mode and shape whose size fits, provided calls that
+ * share it are ordered on one stream.
+ */
+size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype);
+
+/*
+ * Zero-fill `workspace_bytes` bytes of a fresh workspace on `stream` with a fill
+ * kernel (no memset node).  Call once after allocating it.
+ */
+int spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Profiling hook.  After this call, every verification call records
+ * events[2 * i] on its stream immediately before its streaming kernel (the one
+ * that reads every logits row) and events[2 * i + 1] immediately after it, with
+ * i advancing by one per call and wrapping at n_pairs.  The events are
+ * hipEvent_t handles (passed as void*) that the caller created and destroys.
+ * Pass NULL and 0 to switch the hook off.  The hook is process-wide and not
+ * thread-safe; it exists so that a benchmark can time that kernel alone on the
+ * stream it runs on.
+ */
+int spec_verify_profile_events(void *const *events, int n_pairs);
+
+/*
+ * Stochastic verification (speculative sampling) of B linear drafts of length k.
+ *
+ *   target_logits [B, k+1, V] dtype  -- row i (i < k) is the target distribution
+ *                  for draft token i; row k is the bonus row.
+ *   draft_logits  [B, k, V] dtype    -- row i is the draft distribution that
+ *                  proposed draft token i (may be NULL when k == 0).
+ *   draft_tokens  [B, k] int32 (may be NULL when k == 0).
+ *   uniforms      [B, k+1] float32 in [0, 1): uniforms[b, i] (i < k) drives test
+ *                  i; uniforms[b, k] drives the one final (residual or bonus)
+ *                  sample.
+ *   temperature   > 0 and finite: both logits tensors are divided by it before
+ *                  the softmax (the two sides are filtered identically).
+ *
+ * Per request, with p_i = softmax(target row i / T), q_i = softmax(draft row
+ * i / T), P = p_i(x_i), Q = q_i(x_i): test i accepts when P >= Q or
+ * u_i * Q < P (the strict test u < min(1, P/Q)); s = the first rejected i, or
+ * k.  The final token is the inverse-CDF draw with u_k over token ids in
+ * ascending order (the smallest j whose running weight exceeds u_k * Z) from
+ * the weights max(0, p_s - q_s) when s < k, or p_k when s == k.
+ *
+ * Outputs:
+ *   out_tokens   [B, k+1] int32: draft[0..s-1], the final token, then -1.
+ *   num_accepted [B] int32: s.
+ *   p_at_draft, q_at_draft [B, k] float32 or NULL: P and Q of every draft
+ *                 position (0 for an out-of-range draft id).
+ *
+ * The call launches two kernels: a single-pass streaming kernel that reads every
+ * logits row once and decides s, and a sampler that reads only each request's
+ * stop row(s).
+ */
+int spec_verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
+                           const int32_t *draft_tokens, const float *uniforms,
+                           float temperature, int B, int k, int V,
+                           int32_t *out_tokens, int32_t *num_accepted,
+                           float *p_at_draft, float *q_at_draft,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy verification of B linear drafts of length k.
+ *
+ *   target_logits [B, k+1, V] dtype; draft_tokens [B, k] int32 (NULL if k == 0).
+ *
+ * a_i = argmax of raw target row i (lowest index among equal maxima);
+ * s = number of leading i with draft_tokens[b, i] == a_i.
+ *   out_tokens   [B, k+1] int32: draft[0..s-1], a_s, then -1.
+ *   num_accepted [B] int32: s.
+ */
+int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
+                       int B, int k, int V, int32_t *out_tokens, int32_t *num_accepted,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Tree (EAGLE-style) greedy verification.
+ *
+ *   target_logits [B, N+1, V] dtype -- row n: target distribution after node n
+ *                  (node 0 is the root, the last committed token).
+ *   node_tokens   [B, N+1] int32 -- draft token of node n; [b, 0] is ignored.
+ *   paths         [B, P, L] int32 -- node indices from the root down one branch,
+ *                  -1 padded; a row whose first entry is not in [0, N] is unused.
+ *
+ * A path's accepted length m is the number of its nodes, from the root down,
+ * whose token equals the argmax of the previous node's row, counted until the
+ * first mismatch.  The chosen row has the largest m, the lowest row index among
+ * equal m.
+ *   out_tokens     [B, L] int32: tokens of the m accepted nodes, the argmax of
+ *                  the last accepted node's row, then -1.  With no usable row:
+ *                  the root row's argmax, then -1.
+ *   num_accepted   [B] int32: m.
+ *   best_path      [B] int32 or NULL: the chosen row, -1 if no row is usable.
+ *   accepted_nodes [B, L] int32 or NULL: the m accepted node indices, then -1
+ *                  (the rows a caller keeps when it compacts its KV cache).
+ */
+int spec_verify_tree(const void *target_logits, int dtype, const int32_t *node_tokens,
+                     const int32_t *paths, int B, int N, int P, int L, int V,
+                     int32_t *out_tokens, int32_t *num_accepted, int32_t *best_path,
+                     int32_t *accepted_nodes, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

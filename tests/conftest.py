@@ -20,3 +20,11 @@ def oracle_lib():
     if not os.path.exists(os.path.join(ROOT, "oracle", "libspec_verify_oracle.so")):
         oracle.build(force=True)
     return None  # None selects the default oracle build
+
+
+def pytest_runtest_logstart(nodeid, location):
+    # Name each test on stderr before it runs, so a run that dies on the GPU
+    # still shows which case was in flight.
+    if "gpu" in nodeid or "smoke" in nodeid:
+        sys.__stderr__.write(f"[start] {nodeid}\n")
+        sys.__stderr__.flush()

@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad calls on
+the host before any launch (no GPU needed: every call here fails validation)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from draft_token_verification_verify_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from draft_token_verification_verify_amd import build
+
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*[a-z_ 0-9*]+?\b(spec_verify_[a-z_]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_header_declares_the_exported_set():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.spec_verify_version() >= 100
+    for code in range(6):
+        assert lib.spec_verify_status_string(code)
+    assert lib.spec_verify_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizing(lib):
+    ws = lib.spec_verify_workspace_bytes
+    assert ws(_lib.MODE_STOCHASTIC, 64, 4, 128256, _lib.BF16) > 0
+    assert ws(_lib.MODE_GREEDY, 8, 5, 32000, _lib.BF16) > 0
+    assert ws(_lib.MODE_TREE, 32, 61, 128256, _lib.BF16) > 0
+    assert ws(_lib.MODE_STOCHASTIC, 1, 1, 1, _lib.F32) > 0  # k = 0, V = 1
+    assert ws(3, 1, 2, 10, _lib.F32) == 0           # unknown mode
+    assert ws(_lib.MODE_STOCHASTIC, 1, 2, 10, 7) == 0  # unknown dtype
+    assert ws(_lib.MODE_STOCHASTIC, 0, 2, 10, _lib.F32) == 0
+    assert ws(_lib.MODE_STOCHASTIC, 1, 66, 10, _lib.F32) == 0  # k = 65
+    assert ws(_lib.MODE_TREE, 1, 1025, 10, _lib.F32) == 0
+    # larger batches never need less
+    assert ws(_lib.MODE_STOCHASTIC, 128, 4, 128256, _lib.BF16) >= ws(
+        _lib.MODE_STOCHASTIC, 64, 4, 128256, _lib.BF16)
+
+
+def stoch(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dtype=_lib.BF16, x=FAKE, u=FAKE, T=1.0, B=2, k=3, V=100,
+             out=FAKE, acc=FAKE, p=None, q=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_verify_stochastic(a["t"], a["d"], a["dtype"], a["x"], a["u"], a["T"], a["B"],
+                                      a["k"], a["V"], a["out"], a["acc"], a["p"], a["q"], a["ws"],
+                                      a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), _lib.UNSUPPORTED_DTYPE),
+    (dict(B=0), _lib.INVALID_ARGUMENT),
+    (dict(k=-1), _lib.INVALID_ARGUMENT),
+    (dict(V=0), _lib.INVALID_ARGUMENT),
+    (dict(T=0.0), _lib.INVALID_ARGUMENT),
+    (dict(T=-1.0), _lib.INVALID_ARGUMENT),
+    (dict(T=math.inf), _lib.INVALID_ARGUMENT),
+    (dict(T=math.nan), _lib.INVALID_ARGUMENT),
+    (dict(t=None), _lib.INVALID_ARGUMENT),
+    (dict(u=None), _lib.INVALID_ARGUMENT),
+    (dict(out=None), _lib.INVALID_ARGUMENT),
+    (dict(acc=None), _lib.INVALID_ARGUMENT),
+    (dict(ws=None), _lib.INVALID_ARGUMENT),
+    (dict(d=None), _lib.INVALID_ARGUMENT),
+    (dict(x=None), _lib.INVALID_ARGUMENT),
+    (dict(k=65), _lib.LIMIT_EXCEEDED),
+    (dict(wsb=16), _lib.WORKSPACE_TOO_SMALL),
+])
+def test_stochastic_rejects(lib, kw, code):
+    assert stoch(lib, **kw) == code
+
+
+def test_stochastic_k0_needs_no_draft_pointers_but_checks_workspace(lib):
+    # With k = 0 the draft pointers may be NULL; a too-small workspace still fails
+    # on the host, so nothing is launched here.
+    assert stoch(lib, k=0, d=None, x=None, wsb=8) == _lib.WORKSPACE_TOO_SMALL
+
+
+def greedy(lib, **kw):
+    a = dict(t=FAKE, dtype=_lib.F32, x=FAKE, B=2, k=3, V=100, out=FAKE, acc=FAKE, ws=FAKE,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_verify_greedy(a["t"], a["dtype"], a["x"], a["B"], a["k"], a["V"], a["out"],
+                                  a["acc"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), _lib.UNSUPPORTED_DTYPE),
+    (dict(B=-3), _lib.INVALID_ARGUMENT),
+    (dict(t=None), _lib.INVALID_ARGUMENT),
+    (dict(x=None), _lib.INVALID_ARGUMENT),
+    (dict(k=100), _lib.LIMIT_EXCEEDED),
+    (dict(wsb=0), _lib.WORKSPACE_TOO_SMALL),
+])
+def test_greedy_rejects(lib, kw, code):
+    assert greedy(lib, **kw) == code
+
+
+def tree(lib, **kw):
+    a = dict(t=FAKE, dtype=_lib.BF16, nt=FAKE, paths=FAKE, B=2, N=60, P=60, L=7, V=1000,
+             out=FAKE, acc=FAKE, best=None, nodes=None, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_verify_tree(a["t"], a["dtype"], a["nt"], a["paths"], a["B"], a["N"], a["P"],
+                                a["L"], a["V"], a["out"], a["acc"], a["best"], a["nodes"], a["ws"],
+                                a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=-1), _lib.UNSUPPORTED_DTYPE),
+    (dict(L=0), _lib.INVALID_ARGUMENT),
+    (dict(N=-1), _lib.INVALID_ARGUMENT),
+    (dict(nt=None), _lib.INVALID_ARGUMENT),
+    (dict(paths=None), _lib.INVALID_ARGUMENT),
+    (dict(N=1024), _lib.LIMIT_EXCEEDED),
+    (dict(P=1025), _lib.LIMIT_EXCEEDED),
+    (dict(L=65), _lib.LIMIT_EXCEEDED),
+    (dict(P=1000, L=20), _lib.LIMIT_EXCEEDED),
+    (dict(wsb=100), _lib.WORKSPACE_TOO_SMALL),
+])
+def test_tree_rejects(lib, kw, code):
+    assert tree(lib, **kw) == code
+
+
+def test_workspace_init_rejects_null(lib):
+    assert lib.spec_verify_workspace_init(None, 64, None) == _lib.INVALID_ARGUMENT

@@ -1,0 +1,140 @@
+"""GPU parity: greedy and tree verification through the C ABI, bit-exact against
+the oracle (argmax over raw logits, lowest index on ties)."""
+import numpy as np
+import pytest
+
+import draft_token_verification_verify_amd as sv
+from draft_token_verification_verify_amd import workloads as wl
+from tests import gpu_helpers as H
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+
+def check_greedy(case):
+    gpu = H.run_greedy(case)
+    ref = oracle.greedy(case.target, case.draft_tokens)
+    np.testing.assert_array_equal(gpu["num_accepted"], ref["num_accepted"], err_msg=case.name)
+    np.testing.assert_array_equal(gpu["out_tokens"], ref["out_tokens"], err_msg=case.name)
+    return gpu, ref
+
+
+def tied_greedy(seed, B, k, V, dtype, corrupt=0.3):
+    """Logits rounded to halves (many equal maxima), drafts = the argmax chain with
+    a fraction replaced."""
+    rng = np.random.default_rng(seed)
+    t32 = (np.round(rng.normal(0, 2.0, (B, k + 1, V)) * 2) / 2).astype(np.float32)
+    target = wl.bf16_bits(t32) if dtype == "bf16" else t32
+    tf = wl.bits_to_float(target) if dtype == "bf16" else target
+    a = np.argmax(tf, axis=2)
+    x = a[:, :k].astype(np.int32).copy()
+    m = rng.random((B, k)) < corrupt
+    x[m] = rng.integers(0, V, int(m.sum()))
+    return wl.GreedyCase(f"tied-{dtype}-B{B}-k{k}-V{V}", B, k, V, dtype, target, x)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_c2_greedy(seed):
+    check_greedy(wl.c2_greedy(seed))
+
+
+@pytest.mark.parametrize("B,k,V,dtype", [
+    (8, 4, 32000, "bf16"),
+    (4, 3, 128256, "bf16"),
+    (3, 2, 50001, "f32"),     # unaligned rows: scalar path
+    (5, 6, 77777, "bf16"),    # unaligned rows: scalar path
+    (16, 8, 4096, "f32"),
+    (7, 0, 9000, "bf16"),     # k = 0: plain argmax of row 0
+    (2, 64, 300, "bf16"),     # longest draft
+    (3, 2, 1, "f32"),         # V = 1
+])
+def test_tied_logits(B, k, V, dtype):
+    for seed in (0, 1):
+        check_greedy(tied_greedy(seed, B, k, V, dtype))
+
+
+def test_no_draft_accepted_reads_row_zero_only():
+    case = tied_greedy(3, 8, 4, 1000, "f32", corrupt=0.0)
+    tf = case.target
+    a0 = np.argmax(tf[:, 0, :], axis=1)
+    case.draft_tokens[:, 0] = (a0 + 1) % case.V
+    gpu, _ = check_greedy(case)
+    assert np.all(gpu["num_accepted"] == 0)
+    np.testing.assert_array_equal(gpu["out_tokens"][:, 0], a0)
+    assert np.all(gpu["out_tokens"][:, 1:] == -1)
+
+
+def test_all_negative_infinity_but_one():
+    rng = np.random.default_rng(9)
+    B, k, V = 4, 3, 20000
+    t = np.full((B, k + 1, V), -np.inf, np.float32)
+    hot = rng.integers(0, V, (B, k + 1))
+    for b in range(B):
+        for i in range(k + 1):
+            t[b, i, hot[b, i]] = 1.0
+    x = hot[:, :k].astype(np.int32)
+    check_greedy(wl.GreedyCase("one-finite", B, k, V, "f32", t, x))
+
+
+# ---- tree -------------------------------------------------------------------------
+
+def check_tree(case, rows=None):
+    gpu = H.run_tree(case)
+    sel = slice(None) if rows is None else rows
+    ref = oracle.tree(case.target[sel], case.node_tokens[sel], case.paths[sel])
+    for key in ("num_accepted", "out_tokens", "best_path", "accepted_nodes"):
+        np.testing.assert_array_equal(gpu[key][sel], ref[key], err_msg=f"{case.name}: {key}")
+    return gpu, ref
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c5_full_size(seed):
+    gpu, _ = check_tree(wl.c5(seed))
+    assert gpu["num_accepted"].max() >= 1
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_small_trees_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    case = wl.random_tree_case(seed, 6, 20, 4, 3000, "bf16", P=20, max_children=4)
+    # coarse logits: many tied maxima, and tokens that match often
+    t = np.round(wl.bits_to_float(case.target) / 3).astype(np.float32)
+    case.target = wl.bf16_bits(t)
+    a = np.argmax(wl.bits_to_float(case.target), axis=2)
+    for b in range(case.B):
+        for n in range(1, case.N + 1):
+            if rng.random() < 0.8:
+                case.node_tokens[b, n] = a[b, case.parents[b, n]]
+    check_tree(case)
+
+
+def test_tree_special_rows():
+    rng = np.random.default_rng(2)
+    case = wl.random_tree_case(3, 5, 12, 3, 2048, "f32", P=16)
+    case.paths[0, :, :] = -1                  # no usable row: root argmax only
+    case.paths[1, 0, 2] = 99                  # out-of-range entry ends that path
+    case.paths[2, 3:, :] = rng.integers(-5, 0, (13, case.L))  # unused rows
+    check_tree(case)
+
+
+def test_tree_large_path_table_in_global_memory():
+    """P * L above the LDS staging limit: the path walk reads global memory."""
+    case = wl.random_tree_case(4, 2, 600, 8, 512, "bf16", P=1000, max_children=10)
+    assert case.P * case.L > 4096
+    check_tree(case)
+
+
+def test_shared_workspace_across_modes():
+    ws = sv.Workspace()
+    c_s = wl.c3(11, B=8)
+    c_g = wl.c2_greedy(11)
+    c_t = wl.c5(11, B=4)
+    for _ in range(2):
+        g = H.run_stochastic(c_s, workspace=ws)
+        H.compare_stochastic(g, H.oracle_stochastic(c_s), label=c_s.name)
+        g = H.run_greedy(c_g, workspace=ws)
+        r = oracle.greedy(c_g.target, c_g.draft_tokens)
+        np.testing.assert_array_equal(g["out_tokens"], r["out_tokens"])
+        g = H.run_tree(c_t, workspace=ws)
+        r = oracle.tree(c_t.target, c_t.node_tokens, c_t.paths)
+        np.testing.assert_array_equal(g["out_tokens"], r["out_tokens"])

@@ -1,0 +1,133 @@
+"""GPU parity: stochastic verification through the C ABI against the fp64 oracle.
+
+Bar: out_tokens and num_accepted equal to the oracle on every request none of
+whose decisions lies within 1e-6 of its threshold or CDF boundary (those are
+counted and must stay below 1e-4 of the rows); p(x_i) and q(x_i) within 1e-5
+relative.
+"""
+import numpy as np
+import pytest
+import torch
+
+import draft_token_verification_verify_amd as sv
+from draft_token_verification_verify_amd import workloads as wl
+from tests import gpu_helpers as H
+from tests.oracle_pins import CHI2_DF7_P001, chi2_stat, lib_softmax, sample_from
+
+pytestmark = pytest.mark.gpu
+
+
+def check(case, rows=None):
+    gpu = H.run_stochastic(case)
+    ref = H.oracle_stochastic(case, rows)
+    amb, dis = H.compare_stochastic(gpu, ref, rows, case.name)
+    n_rows = case.B * (case.k + 1) if rows is None else len(rows) * (case.k + 1)
+    assert amb <= max(1, 1e-4 * n_rows), f"{case.name}: {amb} ambiguous requests"
+    return gpu, ref, amb, dis
+
+
+SMALL = [
+    # (name, factory) -- sizes that span several chunks and end in a ragged chunk
+    ("bf16-V40000-k3", lambda s: wl.gaussian_stochastic(s, 4, 3, 40000, "bf16", target_sd=3.0,
+                                                        draft_noise_sd=1.0)),
+    ("f32-V50001-k2-unaligned", lambda s: wl.gaussian_stochastic(s, 3, 2, 50001, "f32",
+                                                                 target_sd=2.0,
+                                                                 draft_noise_sd=0.7)),
+    ("bf16-V77777-k4-unaligned", lambda s: wl.gaussian_stochastic(s, 2, 4, 77777, "bf16",
+                                                                  target_sd=2.0,
+                                                                  draft_noise_sd=1.0,
+                                                                  temperature=1.7)),
+    ("f32-V33000-k0", lambda s: wl.gaussian_stochastic(s, 5, 0, 33000, "f32", target_sd=2.0,
+                                                       draft_noise_sd=1.0)),
+    ("bf16-V6000-k8", lambda s: wl.gaussian_stochastic(s, 6, 8, 6000, "bf16", target_sd=1.5,
+                                                       draft_noise_sd=0.3, temperature=0.6)),
+    ("zipf-bf16-V128256-B8", lambda s: wl.c3(s, B=8)),
+    ("zipf-f32-V151936-B4", lambda s: wl.c4(s, B=4)),
+    ("f32-V1-k3", lambda s: wl.gaussian_stochastic(s, 3, 3, 1, "f32", target_sd=1.0,
+                                                   draft_noise_sd=1.0)),
+    ("f32-V9-k5", lambda s: wl.gaussian_stochastic(s, 64, 5, 9, "f32", target_sd=1.0,
+                                                   draft_noise_sd=1.0)),
+]
+
+
+@pytest.mark.parametrize("name,factory", SMALL, ids=[n for n, _ in SMALL])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_small_shapes(name, factory, seed):
+    check(factory(seed))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_c1_all_seeds(seed):
+    check(wl.c1(seed))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_c2_stochastic(seed):
+    check(wl.c2_stochastic(seed))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c3_full_size(seed):
+    """B=64, k=3, V=128256 bf16, T=0.8: the timed workload, every request checked."""
+    gpu, ref, amb, dis = check(wl.c3(seed))
+    assert 0 < gpu["num_accepted"].mean() < 3
+
+
+def test_c4_full_size_sampled_requests():
+    """B=256, k=5, V=151936 fp32 on the GPU; the oracle checks 40 sampled requests."""
+    case = wl.c4(0)
+    rows = np.sort(np.random.default_rng(5).choice(case.B, 40, replace=False))
+    check(case, rows)
+
+
+def test_identical_draft_accepts_everything():
+    case = wl.gaussian_stochastic(3, 16, 4, 20000, "bf16", target_sd=2.0, draft_noise_sd=1.0)
+    case.draft = case.target[:, :case.k, :].copy()
+    gpu, ref, _, _ = check(case)
+    assert np.all(gpu["num_accepted"] == case.k)
+
+
+def test_disjoint_support_rejects_first():
+    case = wl.gaussian_stochastic(4, 8, 3, 4096, "f32", target_sd=1.0, draft_noise_sd=1.0)
+    case.target[:, :, 1::2] = -np.inf
+    case.draft[:, :, 0::2] = -np.inf
+    case.draft_tokens = (case.draft_tokens | 1).astype(np.int32)
+    gpu, ref, _, _ = check(case)
+    assert np.all(gpu["num_accepted"] == 0)
+    assert np.all(gpu["out_tokens"][:, 0] % 2 == 0)
+
+
+def test_out_of_range_drafts_are_rejected():
+    case = wl.gaussian_stochastic(5, 4, 3, 5000, "bf16", target_sd=1.0, draft_noise_sd=0.1)
+    case.draft_tokens[:, 1] = np.array([5000, -1, 1 << 30, -7], np.int32)
+    case.uniforms[:] = 0.0  # tests before position 1 accept
+    gpu, ref, _, _ = check(case)
+    assert np.all(gpu["num_accepted"] <= 1)
+
+
+def test_repeat_calls_are_bit_identical():
+    case = wl.c3(7, B=16)
+    a = H.run_stochastic(case)
+    b = H.run_stochastic(case)
+    for key in a:
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_emitted_tokens_distributed_as_p():
+    """Chi-squared on the GPU path, V=8, k=2, 10^6 trials (same law as the oracle pin)."""
+    rng = np.random.default_rng(16)
+    V, k, n = 8, 2, 1_000_000
+    tl = rng.normal(0, 1.2, (k + 1, V)).astype(np.float32)
+    dl = (tl[:k] + rng.normal(0, 1.0, (k, V))).astype(np.float32)
+    p, q = lib_softmax(tl), lib_softmax(dl)
+    x = np.stack([sample_from(rng, q[i], n) for i in range(k)], axis=1)
+    u = rng.random((n, k + 1), dtype=np.float32)
+    dev = torch.device("cuda", 0)
+    t = torch.from_numpy(tl).to(dev).expand(n, k + 1, V).contiguous()
+    d = torch.from_numpy(dl).to(dev).expand(n, k, V).contiguous()
+    out, s = sv.spec_verify_stochastic(t, d, torch.from_numpy(x).to(dev),
+                                       torch.from_numpy(u).to(dev), 1.0)
+    out, s = out.cpu().numpy(), s.cpu().numpy()
+    assert chi2_stat(np.bincount(out[:, 0], minlength=V), p[0]) < CHI2_DF7_P001
+    assert chi2_stat(np.bincount(out[s >= 1, 1], minlength=V), p[1]) < CHI2_DF7_P001
+    assert chi2_stat(np.bincount(out[s >= 2, 2], minlength=V), p[2]) < CHI2_DF7_P001
