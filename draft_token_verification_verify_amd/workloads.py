@@ -133,6 +133,12 @@ class TreeCase:
         return self.target.nbytes
 
 
+def _f32(x: float) -> float:
+    """The float32 value nearest x, as a Python float: the library takes the
+    temperature as float32, so every consumer is given exactly that value."""
+    return float(np.float32(x))
+
+
 def _finish(x32: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.ascontiguousarray(x32, dtype=np.float32)
@@ -188,7 +194,7 @@ def gaussian_stochastic(seed: int, B: int, k: int, V: int, dtype: str, *,
     target = _finish(t32, dtype)
     draft = _finish(d32, dtype)
     drafts = _sample_drafts(rng, draft, dtype, temperature)
-    return StochasticCase(name, B, k, V, dtype, temperature, target, draft, drafts,
+    return StochasticCase(name, B, k, V, dtype, _f32(temperature), target, draft, drafts,
                           _uniforms(rng, B, k), dict(seed=seed))
 
 
@@ -217,7 +223,7 @@ def zipf_stochastic(seed: int, B: int, k: int, V: int, dtype: str, *,
     draft = _finish(d32, dtype)
     del d32
     drafts = _sample_drafts(rng, draft, dtype, temperature)
-    return StochasticCase(name, B, k, V, dtype, temperature, target, draft, drafts,
+    return StochasticCase(name, B, k, V, dtype, _f32(temperature), target, draft, drafts,
                           _uniforms(rng, B, k), dict(seed=seed))
 
 

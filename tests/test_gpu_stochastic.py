@@ -1,9 +1,11 @@
 """GPU parity: stochastic verification through the C ABI against the fp64 oracle.
 
 Bar: out_tokens and num_accepted equal to the oracle on every request none of
-whose decisions lies within 1e-6 of its threshold or CDF boundary (those are
-counted and must stay below 1e-4 of the rows); p(x_i) and q(x_i) within 1e-5
-relative.
+whose decisions lies within 1e-6 of its threshold or CDF boundary; requests that
+do (ambiguous) may differ, and the ones that differ are counted and must stay
+below 1e-4 of the rows; p(x_i) and q(x_i) within 1e-5 relative.  The ambiguous
+count itself is reported, not bounded: with V ~ 10^5 CDF edges a 1e-6 band
+around each edge covers a few percent of [0, 1) on heavy-tailed rows.
 """
 import numpy as np
 import pytest
@@ -22,7 +24,8 @@ def check(case, rows=None):
     ref = H.oracle_stochastic(case, rows)
     amb, dis = H.compare_stochastic(gpu, ref, rows, case.name)
     n_rows = case.B * (case.k + 1) if rows is None else len(rows) * (case.k + 1)
-    assert amb <= max(1, 1e-4 * n_rows), f"{case.name}: {amb} ambiguous requests"
+    print(f"{case.name}: {amb} ambiguous requests, {dis} differ (rows {n_rows})")
+    assert dis <= 1e-4 * n_rows, f"{case.name}: {dis} ambiguous requests differ"
     return gpu, ref, amb, dis
 
 
@@ -71,6 +74,22 @@ def test_c3_full_size(seed):
     """B=64, k=3, V=128256 bf16, T=0.8: the timed workload, every request checked."""
     gpu, ref, amb, dis = check(wl.c3(seed))
     assert 0 < gpu["num_accepted"].mean() < 3
+
+
+def test_c3_disagreements_over_many_seeds():
+    """Twelve seeds of the timed workload (768 requests, 3072 rows): requests that
+    differ from the oracle stay below 1e-4 of the rows."""
+    tot_rows = tot_dis = tot_amb = 0
+    for seed in range(12):
+        case = wl.c3(100 + seed)
+        gpu = H.run_stochastic(case)
+        ref = H.oracle_stochastic(case)
+        amb, dis = H.compare_stochastic(gpu, ref, None, case.name)
+        tot_rows += case.rows
+        tot_dis += dis
+        tot_amb += amb
+    print(f"c3 x12: {tot_amb} ambiguous requests, {tot_dis} differ, {tot_rows} rows")
+    assert tot_dis <= 1e-4 * tot_rows
 
 
 def test_c4_full_size_sampled_requests():
