@@ -11,7 +11,7 @@ namespace sv {
 constexpr int kThreads = 256;           // one workgroup = 4 wave64s
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSampleSegVecs = 4;       // 16-byte vectors per thread in a sampler chunk
+constexpr int kSampleSeg = 16;          // elements per thread in a sampler chunk
 constexpr int kMaxK = 64;               // longest linear draft
 constexpr int kTreeLdsPathEntries = 4096;  // path tables up to this many entries go to LDS
 
@@ -29,12 +29,30 @@ struct Geometry {
     size_t off_ticket_a, off_ticket_b, off_partials, off_stop, off_mass, bytes;
 };
 
+// log2(e) / temperature, the factor that turns a logit difference into a
+// base-2 exponent.  The fp32 pair (hi, lo) carries it to ~2^-48 relative, so an
+// exponent computed as fma(d, hi, d * lo) is rounded once (0.5 ulp); c64 feeds
+// the fp64 paths.
+struct Scale {
+    float hi, lo;
+    double c64;
+};
+
+// Per (row, chunk) softmax statistics: m = max raw logit of the chunk, s = sum of
+// 2^((x - m) * c) over the chunk, accumulated in fp64.
+struct StatPartial {
+    float m;
+    float pad;
+    double s;
+};
+static_assert(sizeof(StatPartial) == 16, "StatPartial layout");
+
 struct StopInfo {      // per request, written by the streaming kernel's epilogue
     int32_t s;         // number of accepted drafts = stop row
+    float mt;          // max logit of target row s
+    float md;          // max logit of draft row s (unused when s == k)
     int32_t pad;
-    float mt, st;      // max logit and sum of exp2((x - mt) * c) of target row s
-    float md, sd;      // same for draft row s (unused when s == k)
-    float pad2[2];
+    double st, sd;     // sum of 2^((x - max) * c) of those rows (fp64)
 };
 static_assert(sizeof(StopInfo) == 32, "StopInfo layout");
 
@@ -59,7 +77,7 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     g->U = U;
     g->chunk = kThreads * U * epv;
     g->S = (V + g->chunk - 1) / g->chunk;
-    g->chunk2 = kThreads * kSampleSegVecs * epv;
+    g->chunk2 = kThreads * kSampleSeg;
     g->S2 = (mode == 0) ? (V + g->chunk2 - 1) / g->chunk2 : 0;
 
     size_t off = 0;
@@ -68,7 +86,7 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     g->off_ticket_b = off;
     off = align_up(off + sizeof(uint32_t) * (size_t)B, 256);
     g->off_partials = off;
-    off = align_up(off + 8 * (size_t)rows * (size_t)g->S, 256);
+    off = align_up(off + 16 * (size_t)rows * (size_t)g->S, 256);
     g->off_stop = off;
     off = align_up(off + (mode == 0 ? sizeof(StopInfo) * (size_t)B : 0), 256);
     g->off_mass = off;
@@ -115,16 +133,14 @@ __device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const u
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ---------------------------------------------------------------------------
-// Softmax statistics (m, s): m = max raw logit, s = sum exp2((x - m) * c).
-// Merging two pairs rescales both sums to the larger maximum; an empty side
-// (m = -inf, s = 0) contributes nothing and never produces a NaN.
-// ---------------------------------------------------------------------------
-__device__ inline void merge_ms(float& m, float& s, float m2, float s2, float c) {
-    float M = fmaxf(m, m2);
-    float Ms = (M == -INFINITY) ? 0.f : M;
-    s = s * fast_exp2((m - Ms) * c) + s2 * fast_exp2((m2 - Ms) * c);
-    m = M;
+// Base-2 exponent of a logit difference d = x - m, rounded once.
+__device__ inline float scaled(float d, const Scale& k) { return fmaf(d, k.hi, d * k.lo); }
+
+// 2^((x - m) * c) in fp64 (accurate to a few ulp of double); 0 for x = -inf.
+// Kept out of line: it sits on rare branches of otherwise short loops.
+__device__ __noinline__ double exp2_accurate(float x, float m, const Scale& k) {
+    if (x == -INFINITY) return 0.0;
+    return exp2(((double)x - (double)m) * k.c64);
 }
 
 // Argmax pairs: larger value wins, the lower index wins a tie.
@@ -135,13 +151,10 @@ __device__ inline void merge_argmax(float& v, int& i, float v2, int i2) {
 }
 
 // Fixed-order reductions (same result on every run).
-__device__ inline void wave_reduce_ms(float& m, float& s, float c) {
+__device__ inline float wave_max(float v) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        float m2 = __shfl_xor(m, off, 64);
-        float s2 = __shfl_xor(s, off, 64);
-        merge_ms(m, s, m2, s2, c);
-    }
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
 }
 
 __device__ inline void wave_reduce_argmax(float& v, int& i) {
@@ -157,6 +170,30 @@ __device__ inline double wave_reduce_sum(double x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
+}
+
+// Workgroup max / sum; `sh` is LDS scratch of kWaves entries.  Every thread
+// gets the result.
+__device__ inline float block_max(float v, float* sh) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, sh[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ inline double block_sum(double v, double* sh) {
+    v = wave_reduce_sum(v);
+    if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = sh[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r += sh[w];
+    __syncthreads();
+    return r;
 }
 
 // Inclusive prefix sum over the workgroup in thread order (deterministic).

@@ -11,19 +11,28 @@
 // Two kernels:
 //   stats:   one workgroup per (request, logits row, vocabulary chunk).  Reads
 //            its chunk once with 16-byte loads and reduces it to softmax
-//            statistics (max m, sum of exp2((x - m) * log2(e) / T)).  The last
-//            workgroup of a request to finish (arrival ticket) merges the
-//            chunks of every row, gathers p_i(x_i) and q_i(x_i), runs the k
-//            tests (independent given the uniforms), takes the first failure as
-//            the stop row s and writes the accepted drafts, the -1 padding and
-//            num_accepted.
+//            statistics: the chunk max m and s = sum of 2^((x - m) * log2(e)/T).
+//            Each thread sums its own elements against its own maximum (so a
+//            row's largest logits, each usually the maximum of its thread,
+//            contribute an exact 1) in fp64, and threads are merged with fp64
+//            scale factors.  The last workgroup of a request to finish (arrival
+//            ticket) merges the chunks of every row, computes p_i(x_i) and
+//            q_i(x_i) in fp64, runs the k tests (independent given the
+//            uniforms), takes the first failure as the stop row s and writes the
+//            accepted drafts, the -1 padding and num_accepted.
 //   sample:  one workgroup per (request, stop-row chunk).  Computes the chunk's
 //            share of the final distribution's mass (residual max(0, p_s - q_s)
-//            or bonus p_k), in fp64.  The last workgroup of a request picks the
-//            chunk holding u_k * Z by a prefix sum over the chunk masses, then
-//            the token inside that chunk by a prefix sum over per-thread
-//            segments and a walk through one segment (ascending vocabulary
-//            order: the smallest j whose running mass exceeds u_k * Z).
+//            or bonus p_k) in fp64; tokens within 2^-8 of the row maximum take an
+//            fp64 exponential, the rest fp32.  The last workgroup of a request
+//            picks the chunk holding u_k * Z by a prefix sum over the chunk
+//            masses, then the token inside that chunk by a prefix sum over
+//            per-thread segments and a walk through one segment (ascending
+//            vocabulary order: the smallest j whose running mass exceeds u_k * Z).
+//
+// Accuracy matters beyond the decisions themselves: a vocabulary of ~10^5 has
+// ~10^5 CDF edges, so a relative error e in the cumulative weights moves the
+// drawn token on a fraction ~V * e of the draws.  The fp64 paths above keep e
+// near 1e-10.
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 
@@ -35,8 +44,8 @@ struct StatsArgs {
     const int32_t* draft_tokens;
     const float* uniforms;
     int B, k, V, S, chunk;
-    float c;                 // log2(e) / temperature
-    float2* partials;        // [B, 2k+1, S]
+    Scale sc;                // log2(e) / temperature
+    StatPartial* partials;   // [B, 2k+1, S]
     uint32_t* tickets;       // [B]
     StopInfo* stop;          // [B]
     int32_t* out_tokens;     // [B, k+1]
@@ -54,39 +63,47 @@ __device__ inline const T* stats_row(const StatsArgs& a, int b, int r) {
     return static_cast<const T*>(a.draft) + ((size_t)b * a.k + (r - a.k - 1)) * (size_t)a.V;
 }
 
+// p(x) = 2^((x - M) * c) / S in fp64; 0 when x or the whole row is -inf.
+__device__ inline double prob_of(float x, float M, double S, const Scale& k) {
+    if (M == -INFINITY || !(S > 0.0)) return 0.0;
+    return exp2_accurate(x, M, k) / S;
+}
+
 // Per-request epilogue, run by the last workgroup of request b.
 template <typename T>
 __device__ void stats_epilogue(const StatsArgs& a, int b) {
-    __shared__ float sh_m[2 * kMaxK + 1], sh_s[2 * kMaxK + 1];
+    __shared__ float sh_m[2 * kMaxK + 1];
+    __shared__ double sh_s[2 * kMaxK + 1];
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
     const int k = a.k, R = 2 * k + 1;
     for (int r = threadIdx.x; r < R; r += kThreads) {
-        float m = -INFINITY, s = 0.f;
-        const float2* p = a.partials + ((size_t)b * R + r) * a.S;
-        for (int ch = 0; ch < a.S; ++ch) {  // fixed chunk order
-            float2 v = p[ch];
-            merge_ms(m, s, v.x, v.y, a.c);
-        }
-        sh_m[r] = m;
-        sh_s[r] = s;
+        const StatPartial* p = a.partials + ((size_t)b * R + r) * a.S;
+        float M = -INFINITY;
+        for (int ch = 0; ch < a.S; ++ch) M = fmaxf(M, p[ch].m);
+        double S = 0.0;
+        if (M != -INFINITY)
+            for (int ch = 0; ch < a.S; ++ch)  // fixed chunk order
+                S += p[ch].s * exp2_accurate(p[ch].m, M, a.sc);
+        sh_m[r] = M;
+        sh_s[r] = S;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < k; i += kThreads) {
         const int32_t x = a.draft_tokens[(size_t)b * k + i];
         const float u = a.uniforms[(size_t)b * (k + 1) + i];
-        float P = 0.f, Q = 0.f;
+        double P = 0.0, Q = 0.0;
         int acc = 0;
         if (x >= 0 && x < a.V) {
-            float xt = Elem<T>::load(stats_row<T>(a, b, i), x);
-            float xd = Elem<T>::load(stats_row<T>(a, b, k + 1 + i), x);
-            P = fast_exp2((xt - sh_m[i]) * a.c) / sh_s[i];
-            Q = fast_exp2((xd - sh_m[k + 1 + i]) * a.c) / sh_s[k + 1 + i];
-            acc = (P >= Q) || (u * Q < P);  // strict u < min(1, P/Q) without a division
+            const float xt = Elem<T>::load(stats_row<T>(a, b, i), x);
+            const float xd = Elem<T>::load(stats_row<T>(a, b, k + 1 + i), x);
+            P = prob_of(xt, sh_m[i], sh_s[i], a.sc);
+            Q = prob_of(xd, sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
+            acc = (P >= Q) || ((double)u * Q < P);  // strict u < min(1, P/Q), no division
         }
         sh_acc[i] = acc;
-        if (a.p_at_draft) a.p_at_draft[(size_t)b * k + i] = P;
-        if (a.q_at_draft) a.q_at_draft[(size_t)b * k + i] = Q;
+        if (a.p_at_draft) a.p_at_draft[(size_t)b * k + i] = (float)P;
+        if (a.q_at_draft) a.q_at_draft[(size_t)b * k + i] = (float)Q;
     }
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -95,12 +112,11 @@ __device__ void stats_epilogue(const StatsArgs& a, int b) {
             if (!sh_acc[i]) { s = i; break; }
         StopInfo si;
         si.s = s;
-        si.pad = 0;
         si.mt = sh_m[s];
         si.st = sh_s[s];
         si.md = (s < k) ? sh_m[k + 1 + s] : 0.f;
-        si.sd = (s < k) ? sh_s[k + 1 + s] : 1.f;
-        si.pad2[0] = si.pad2[1] = 0.f;
+        si.sd = (s < k) ? sh_s[k + 1 + s] : 1.0;
+        si.pad = 0;
         a.stop[b] = si;
         a.num_accepted[b] = s;
         sh_stop = s;
@@ -127,7 +143,9 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
     const int lo = ch * a.chunk;
     const int hi = min(a.V, lo + a.chunk);
 
-    float m, s = 0.f;
+    // Each thread: its maximum m, then sum 2^((x - m) * c) over its elements in fp64.
+    float m = -INFINITY;
+    double s = 0.0;
     if constexpr (VEC) {
         // The chunk is whole 16-byte vectors (V % EPV == 0, rows 16-byte aligned).
         const int nvec = (hi - lo) / EPV;
@@ -143,7 +161,6 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
                 for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
             }
         }
-        m = -INFINITY;
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -152,33 +169,27 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) s += fast_exp2((x[j][e] - ms) * a.c);
+            for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[j][e] - ms, a.sc));
     } else {
-        m = -INFINITY;
-        for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
-            float x = Elem<T>::load(row, j);
-            if (x > m) {
-                s = s * fast_exp2((m - x) * a.c);
-                m = x;
-            }
-            const float ms = (m == -INFINITY) ? 0.f : m;
-            s += fast_exp2((x - ms) * a.c);
-        }
+        for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, Elem<T>::load(row, j));
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        for (int j = lo + threadIdx.x; j < hi; j += kThreads)
+            s += (double)fast_exp2(scaled(Elem<T>::load(row, j) - ms, a.sc));
     }
 
-    wave_reduce_ms(m, s, a.c);
-    __shared__ float red_m[kWaves], red_s[kWaves];
+    // Workgroup: common maximum, then each thread's sum rescaled in fp64.
+    __shared__ float red_f[kWaves];
+    __shared__ double red_d[kWaves];
     __shared__ int last_flag;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red_m[wave] = m;
-        red_s[wave] = s;
-    }
-    __syncthreads();
+    const float M = block_max(m, red_f);
+    const double f = (m == -INFINITY) ? 0.0 : exp2_accurate(m, M, a.sc);
+    const double S = block_sum(s * f, red_d);
     if (threadIdx.x == 0) {
-        float M = red_m[0], Ssum = red_s[0];
-        for (int w = 1; w < kWaves; ++w) merge_ms(M, Ssum, red_m[w], red_s[w], a.c);
-        a.partials[tile] = make_float2(M, Ssum);
+        StatPartial p;
+        p.m = M;
+        p.pad = 0.f;
+        p.s = S;
+        a.partials[tile] = p;
     }
     if (arrive_last(a.tickets + b, (uint32_t)(R * a.S), &last_flag))
         stats_epilogue<T>(a, b);
@@ -191,40 +202,50 @@ struct SampleArgs {
     const void* draft;
     const float* uniforms;
     int B, k, V, S2, chunk2;
-    float c;
+    Scale sc;
     const StopInfo* stop;  // [B]
     double* mass;          // [B, S2]
     uint32_t* tickets;     // [B]
     int32_t* out_tokens;   // [B, k+1]
 };
 
-// Weight of one token in the final draw: the residual max(0, p - q) when the
-// request stopped on a rejection, else the target probability.
+// Weight of one token in the final draw, in fp64: the residual max(0, p - q)
+// when the request stopped on a rejection, else the target probability.  Tokens
+// within 2^-8 of their row's maximum (the few that carry most of the mass) take
+// the fp64 exponential; the others the fp32 one, whose error is then negligible
+// against the total.
 struct Weigher {
-    float mt, inv_st, md, inv_sd, c;
+    float mt, md;
+    double inv_st, inv_sd;
+    Scale sc;
     bool residual;
-    __device__ inline float operator()(float xt, float xd) const {
-        float p = fast_exp2((xt - mt) * c) * inv_st;
+    __device__ inline double e_of(float x, float m) const {
+        const float a = scaled(x - m, sc);
+        if (a > -8.f) return exp2_accurate(x, m, sc);
+        return (double)fast_exp2(a);
+    }
+    __device__ inline double operator()(float xt, float xd) const {
+        const double p = e_of(xt, mt) * inv_st;
         if (!residual) return p;
-        float q = fast_exp2((xd - md) * c) * inv_sd;
-        return fmaxf(p - q, 0.f);
+        const double q = e_of(xd, md) * inv_sd;
+        return p > q ? p - q : 0.0;
     }
 };
 
-// Weights of this thread's segment (kSampleSegVecs consecutive 16-byte vectors,
-// or the scalar equivalent) of chunk `ch`: w[] in ascending token order,
-// first token id in *j0, count in *n.
+// Weights of this thread's segment (kSampleSeg consecutive tokens) of the chunk
+// [lo, hi): w[] in ascending token order, first token id in *j0, count in *n.
 template <typename T, bool VEC>
 __device__ inline void segment_weights(const T* trow, const T* drow, const Weigher& W, int V,
-                                       int lo, int hi, float* w, int* j0, int* n) {
+                                       int lo, int hi, double* w, int* j0, int* n) {
     constexpr int EPV = Elem<T>::kPerVec;
-    constexpr int SEG = kSampleSegVecs * EPV;
+    constexpr int SEG = kSampleSeg;
+    constexpr int NV = SEG / EPV;
     const int start = lo + threadIdx.x * SEG;
     *j0 = start;
     *n = max(0, min(SEG, hi - start));
     if constexpr (VEC) {
 #pragma unroll
-        for (int v = 0; v < kSampleSegVecs; ++v) {
+        for (int v = 0; v < NV; ++v) {
             const int j = start + v * EPV;
             float xt[EPV], xd[EPV];
             if (j < hi) {
@@ -237,7 +258,7 @@ __device__ inline void segment_weights(const T* trow, const T* drow, const Weigh
                 for (int e = 0; e < EPV; ++e) w[v * EPV + e] = W(xt[e], xd[e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) w[v * EPV + e] = 0.f;
+                for (int e = 0; e < EPV; ++e) w[v * EPV + e] = 0.0;
             }
         }
     } else {
@@ -249,7 +270,7 @@ __device__ inline void segment_weights(const T* trow, const T* drow, const Weigh
                 float xd = W.residual ? Elem<T>::load(drow, j) : 0.f;
                 w[e] = W(xt, xd);
             } else {
-                w[e] = 0.f;
+                w[e] = 0.0;
             }
         }
     }
@@ -259,13 +280,13 @@ __device__ inline void segment_weights(const T* trow, const T* drow, const Weigh
 template <typename T, bool VEC>
 __device__ double chunk_mass(const T* trow, const T* drow, const Weigher& W, int V, int lo,
                              int hi, double* red) {
-    constexpr int SEG = kSampleSegVecs * Elem<T>::kPerVec;
-    float w[SEG];
+    constexpr int SEG = kSampleSeg;
+    double w[SEG];
     int j0, n;
     segment_weights<T, VEC>(trow, drow, W, V, lo, hi, w, &j0, &n);
     double acc = 0.0;
 #pragma unroll
-    for (int e = 0; e < SEG; ++e) acc += (double)w[e];
+    for (int e = 0; e < SEG; ++e) acc += w[e];
     acc = wave_reduce_sum(acc);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     __syncthreads();
@@ -281,7 +302,7 @@ __device__ double chunk_mass(const T* trow, const T* drow, const Weigher& W, int
 template <typename T, bool VEC>
 __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const T* drow,
                                 Weigher W) {
-    constexpr int SEG = kSampleSegVecs * Elem<T>::kPerVec;
+    constexpr int SEG = kSampleSeg;
     __shared__ double sh_wave[kWaves];
     __shared__ double sh_red[kWaves];
     __shared__ int sh_first;
@@ -367,12 +388,12 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
     // Token selection inside the chosen chunk.
     const int c = sh_chunk;
     const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    float w[SEG];
+    double w[SEG];
     int j0, n;
     segment_weights<T, VEC>(trow, drow, W, a.V, lo, hi, w, &j0, &n);
     double seg = 0.0;
 #pragma unroll
-    for (int e = 0; e < SEG; ++e) seg += (double)w[e];
+    for (int e = 0; e < SEG; ++e) seg += w[e];
     double chunk_total;
     double incl = block_inclusive_scan(seg, sh_wave, &chunk_total);
     const double base = sh_base, tau = sh_tau;
@@ -388,8 +409,8 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
         int tok = -1, last_pos = -1;
         for (int e = 0; e < SEG; ++e) {
             if (e >= n) break;
-            if (w[e] > 0.f) last_pos = j0 + e;
-            run += (double)w[e];
+            if (w[e] > 0.0) last_pos = j0 + e;
+            run += w[e];
             if (run > tau) { tok = j0 + e; break; }
         }
         sh_token = (tok >= 0) ? tok : last_pos;
@@ -399,7 +420,7 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
         // Rounding left u * Z past this chunk's total: the chunk's last positive weight.
         int last_pos = -1;
         for (int e = 0; e < SEG; ++e)
-            if (e < n && w[e] > 0.f) last_pos = j0 + e;
+            if (e < n && w[e] > 0.0) last_pos = j0 + e;
         if (last_pos >= 0) atomicMax(&sh_token, last_pos);
         __syncthreads();
     }
@@ -420,10 +441,10 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a) {
     si.s = min(max(si.s, 0), k);  // never index outside the request's rows
     Weigher W;
     W.mt = si.mt;
-    W.inv_st = 1.f / si.st;
+    W.inv_st = 1.0 / si.st;
     W.md = si.md;
-    W.inv_sd = 1.f / si.sd;
-    W.c = a.c;
+    W.inv_sd = 1.0 / si.sd;
+    W.sc = a.sc;
     W.residual = si.s < k;
     const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + si.s) * (size_t)a.V;
     const T* drow = W.residual
@@ -473,8 +494,10 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.V = call.V;
     a.S = g.S;
     a.chunk = g.chunk;
-    a.c = kLog2e / call.temperature;
-    a.partials = reinterpret_cast<float2*>(ws + g.off_partials);
+    a.sc.c64 = 1.4426950408889634074 / (double)call.temperature;
+    a.sc.hi = (float)a.sc.c64;
+    a.sc.lo = (float)(a.sc.c64 - (double)a.sc.hi);
+    a.partials = reinterpret_cast<StatPartial*>(ws + g.off_partials);
     a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_ticket_a);
     a.stop = reinterpret_cast<StopInfo*>(ws + g.off_stop);
     a.out_tokens = call.out_tokens;
@@ -491,7 +514,7 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     s.V = call.V;
     s.S2 = g.S2;
     s.chunk2 = g.chunk2;
-    s.c = a.c;
+    s.sc = a.sc;
     s.stop = a.stop;
     s.mass = reinterpret_cast<double*>(ws + g.off_mass);
     s.tickets = reinterpret_cast<uint32_t*>(ws + g.off_ticket_b);
