@@ -94,7 +94,9 @@ int spec_verify_stochastic(const void* target_logits, const void* draft_logits, 
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!(temperature >= SPEC_VERIFY_MIN_TEMPERATURE) ||
+        !(temperature <= SPEC_VERIFY_MAX_TEMPERATURE))
+        return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!target_logits || !uniforms || !out_tokens || !num_accepted || !workspace)
         return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace sv {
@@ -132,6 +133,18 @@ template <> struct Elem<bf16_t> {
 __device__ inline uint4 load16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// hi is c rounded toward zero and, when c is a float itself, one step lower, so
+// lo = c - hi is strictly positive: then d = -inf gives -inf (never inf - inf).
+inline Scale make_scale(float temperature) {
+    Scale k;
+    k.c64 = 1.4426950408889634074 / (double)temperature;
+    float hi = (float)k.c64;
+    if ((double)hi >= k.c64) hi = nextafterf(hi, 0.f);
+    k.hi = hi;
+    k.lo = (float)(k.c64 - (double)hi);
+    return k;
+}
 
 // Base-2 exponent of a logit difference d = x - m, rounded once.
 __device__ inline float scaled(float d, const Scale& k) { return fmaf(d, k.hi, d * k.lo); }

@@ -494,9 +494,7 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.V = call.V;
     a.S = g.S;
     a.chunk = g.chunk;
-    a.sc.c64 = 1.4426950408889634074 / (double)call.temperature;
-    a.sc.hi = (float)a.sc.c64;
-    a.sc.lo = (float)(a.sc.c64 - (double)a.sc.hi);
+    a.sc = make_scale(call.temperature);
     a.partials = reinterpret_cast<StatPartial*>(ws + g.off_partials);
     a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_ticket_a);
     a.stop = reinterpret_cast<StopInfo*>(ws + g.off_stop);

@@ -73,6 +73,8 @@ enum spec_verify_status {
 #define SPEC_VERIFY_MAX_PATH_LEN 64   /* L */
 #define SPEC_VERIFY_MAX_PATH_TABLE 16384 /* P * L */
 #define SPEC_VERIFY_MAX_VOCAB (1 << 30)
+#define SPEC_VERIFY_MIN_TEMPERATURE 1e-20f /* keeps log2(e)/T finite in fp32 */
+#define SPEC_VERIFY_MAX_TEMPERATURE 1e20f
 
 /* Library version as major * 10000 + minor * 100 + patch. */
 int spec_verify_version(void);
@@ -124,8 +126,10 @@ int spec_verify_profile_events(void *const *events, int n_pairs);
  *   uniforms      [B, k+1] float32 in [0, 1): uniforms[b, i] (i < k) drives test
  *                  i; uniforms[b, k] drives the one final (residual or bonus)
  *                  sample.
- *   temperature   > 0 and finite: both logits tensors are divided by it before
- *                  the softmax (the two sides are filtered identically).
+ *   temperature   in [SPEC_VERIFY_MIN_TEMPERATURE, SPEC_VERIFY_MAX_TEMPERATURE]
+ *                  (else INVALID_ARGUMENT): both logits tensors are divided by
+ *                  it before the softmax (the two sides are filtered
+ *                  identically).
  *
  * Per request, with p_i = softmax(target row i / T), q_i = softmax(draft row
  * i / T), P = p_i(x_i), Q = q_i(x_i): test i accepts when P >= Q or

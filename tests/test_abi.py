@@ -79,6 +79,8 @@ def stoch(lib, **kw):
     (dict(T=-1.0), _lib.INVALID_ARGUMENT),
     (dict(T=math.inf), _lib.INVALID_ARGUMENT),
     (dict(T=math.nan), _lib.INVALID_ARGUMENT),
+    (dict(T=1e-21), _lib.INVALID_ARGUMENT),
+    (dict(T=1e21), _lib.INVALID_ARGUMENT),
     (dict(t=None), _lib.INVALID_ARGUMENT),
     (dict(u=None), _lib.INVALID_ARGUMENT),
     (dict(out=None), _lib.INVALID_ARGUMENT),

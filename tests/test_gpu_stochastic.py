@@ -50,6 +50,14 @@ SMALL = [
                                                    draft_noise_sd=1.0)),
     ("f32-V9-k5", lambda s: wl.gaussian_stochastic(s, 64, 5, 9, "f32", target_sd=1.0,
                                                    draft_noise_sd=1.0)),
+    ("bf16-V20000-k3-T0.001", lambda s: wl.gaussian_stochastic(s, 8, 3, 20000, "bf16",
+                                                               target_sd=2.0,
+                                                               draft_noise_sd=0.5,
+                                                               temperature=1e-3)),
+    ("f32-V20000-k3-T37.5", lambda s: wl.gaussian_stochastic(s, 8, 3, 20000, "f32",
+                                                             target_sd=2.0,
+                                                             draft_noise_sd=0.5,
+                                                             temperature=37.5)),
 ]
 
 
