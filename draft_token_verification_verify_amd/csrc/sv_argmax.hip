@@ -181,15 +181,19 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxArgs a) {
     if constexpr (VEC) {
         const int nvec = (hi - lo) / EPV;
         const uint4* base = reinterpret_cast<const uint4*>(row + lo);
+        // All U loads issue back to back: slots past the chunk's end reload its
+        // last vector (in bounds) and are masked afterwards.
+        uint4 raw[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
         float x[U][EPV];
         int first[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int v = threadIdx.x + j * kThreads;
-            if (v < nvec) {
-                Elem<T>::widen(base[v], x[j]);
-                first[j] = lo + v * EPV;
-            } else {
+            Elem<T>::widen(raw[j], x[j]);
+            first[j] = lo + v * EPV;
+            if (v >= nvec) {
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
                 first[j] = INT_MAX - EPV;

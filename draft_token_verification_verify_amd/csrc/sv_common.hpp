@@ -240,7 +240,8 @@ __device__ inline double block_inclusive_scan(double x, double* wave_tot, double
 // counter to zero (atomically, where the other arrivals incremented it).
 __device__ inline bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
     if (threadIdx.x == 0) {
-        __threadfence();  // release thread 0's writes at device scope
+        // Release thread 0's writes at device scope, then take the ticket.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         uint32_t prev = atomicAdd(counter, 1u);
         int last = (prev == expected - 1);
         if (last) atomicExch(counter, 0u);
@@ -248,7 +249,7 @@ __device__ inline bool arrive_last(uint32_t* counter, uint32_t expected, int* ld
     }
     __syncthreads();
     bool last = *lds_flag != 0;
-    if (last) __threadfence();
+    if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every arrival's writes
     return last;
 }
 

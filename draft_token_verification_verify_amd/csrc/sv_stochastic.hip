@@ -150,16 +150,18 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
         // The chunk is whole 16-byte vectors (V % EPV == 0, rows 16-byte aligned).
         const int nvec = (hi - lo) / EPV;
         const uint4* base = reinterpret_cast<const uint4*>(row + lo);
+        // All U loads issue back to back: slots past the chunk's end reload its
+        // last vector (in bounds) and are masked to -inf afterwards.
+        uint4 raw[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
         float x[U][EPV];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int v = threadIdx.x + j * kThreads;
-            if (v < nvec) {
-                Elem<T>::widen(base[v], x[j]);
-            } else {
+            Elem<T>::widen(raw[j], x[j]);
+            if ((int)threadIdx.x + j * kThreads >= nvec)
 #pragma unroll
                 for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
-            }
         }
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -243,36 +245,35 @@ __device__ inline void segment_weights(const T* trow, const T* drow, const Weigh
     const int start = lo + threadIdx.x * SEG;
     *j0 = start;
     *n = max(0, min(SEG, hi - start));
+    // Loads issue back to back from in-bounds (clamped) positions; positions
+    // past the chunk's end get weight 0.  drow == trow when there is no residual.
     if constexpr (VEC) {
+        uint4 rt[NV], rd[NV];
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            const int j = start + v * EPV;
+            const int j = min(start + v * EPV, hi - EPV);
+            rt[v] = load16(trow + j);
+            rd[v] = load16(drow + j);
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
             float xt[EPV], xd[EPV];
-            if (j < hi) {
-                Elem<T>::widen(load16(trow + j), xt);
-                if (W.residual) Elem<T>::widen(load16(drow + j), xd);
-                else
+            Elem<T>::widen(rt[v], xt);
+            Elem<T>::widen(rd[v], xd);
+            const bool in = start + v * EPV < hi;
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) xd[e] = 0.f;
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) w[v * EPV + e] = W(xt[e], xd[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) w[v * EPV + e] = 0.0;
-            }
+            for (int e = 0; e < EPV; ++e) w[v * EPV + e] = in ? W(xt[e], xd[e]) : 0.0;
         }
     } else {
+        float xt[SEG], xd[SEG];
 #pragma unroll
         for (int e = 0; e < SEG; ++e) {
-            const int j = start + e;
-            if (j < hi) {
-                float xt = Elem<T>::load(trow, j);
-                float xd = W.residual ? Elem<T>::load(drow, j) : 0.f;
-                w[e] = W(xt, xd);
-            } else {
-                w[e] = 0.0;
-            }
+            const int j = min(start + e, hi - 1);
+            xt[e] = Elem<T>::load(trow, j);
+            xd[e] = Elem<T>::load(drow, j);
         }
+#pragma unroll
+        for (int e = 0; e < SEG; ++e) w[e] = (start + e < hi) ? W(xt[e], xd[e]) : 0.0;
     }
     (void)V;
 }
@@ -380,9 +381,9 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
             __syncthreads();
         }
         // Make thread 0's fresh masses visible to every wave before rereading.
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
-        __threadfence();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
 
     // Token selection inside the chosen chunk.
