@@ -9,7 +9,7 @@
 #include <math.h>
 #include <stdint.h>
 
-#include "../../include/spec_verify.h"
+#include "spec_verify.h"
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 

@@ -12,30 +12,24 @@
 // parent's row; the branch of paths[b, P, L] with the most nodes accepted from
 // the root down is kept (lowest path row on ties).
 //
-// One kernel per mode: one workgroup per (request, row, vocabulary chunk)
+// Two kernels per call: one workgroup per (request, row, vocabulary chunk)
 // streams its chunk once with 16-byte loads and reduces it to (max, lowest
-// index of the max).  The last workgroup of each request (arrival ticket)
-// merges the chunks of every row in chunk order and runs the mode's epilogue:
-// the leading-match count (greedy), or the path walk with the path table, the
-// node tokens and the argmax vector staged in LDS (tree).
+// index of the max); then one workgroup per request merges the chunks of every
+// row in chunk order and runs the mode's epilogue: the leading-match count
+// (greedy), or the path walk with the path table, the node tokens and the
+// argmax vector staged in LDS (tree).
 #include <limits.h>
 
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
+#include "sv_stream.hpp"
 
 namespace sv {
-
-struct ArgPartial {
-    float v;
-    int i;
-};
-static_assert(sizeof(ArgPartial) == 8, "ArgPartial layout");
 
 struct ArgmaxArgs {
     const void* target;
     int B, R, V, S, chunk;
-    ArgPartial* partials;  // [B, R, S]
-    uint32_t* tickets;     // [B]
+    Partial16* partials;  // [B, R, S]: f0 = chunk max, f1 = its lowest index (int bits)
     // greedy
     const int32_t* draft_tokens;  // [B, k]
     int k;
@@ -50,142 +44,36 @@ struct ArgmaxArgs {
     int32_t* accepted_nodes;
 };
 
-__device__ inline ArgPartial merge_row(const ArgmaxArgs& a, int b, int r) {
-    const ArgPartial* p = a.partials + ((size_t)b * a.R + r) * a.S;
-    float v = -INFINITY;
-    int i = INT_MAX;
-    for (int ch = 0; ch < a.S; ++ch) {  // fixed chunk order
-        ArgPartial q = p[ch];
-        merge_argmax(v, i, q.v, q.i);
+// Streaming argmax of every target row (lowest index among equal maxima), then
+// the greedy (MODE 1) or tree (MODE 2) epilogue per request.
+template <typename T, int U, int MODE>
+struct ArgmaxOp : ArgmaxArgs {
+    __device__ const T* row(int b, int r) const {
+        return static_cast<const T*>(target) + ((size_t)b * R + r) * (size_t)V;
     }
-    ArgPartial out;
-    out.v = v;
-    out.i = i;
-    return out;
-}
 
-__device__ void greedy_epilogue(const ArgmaxArgs& a, int b) {
-    __shared__ int sh_a[kMaxK + 1];
-    const int k = a.k;
-    for (int r = threadIdx.x; r <= k; r += kThreads) sh_a[r] = merge_row(a, b, r).i;
-    __syncthreads();
-    __shared__ int sh_s;
-    if (threadIdx.x == 0) {
-        int s = 0;
-        while (s < k && a.draft_tokens[(size_t)b * k + s] == sh_a[s]) ++s;
-        sh_s = s;
-        a.num_accepted[b] = s;
-    }
-    __syncthreads();
-    const int s = sh_s;
-    for (int i = threadIdx.x; i <= k; i += kThreads) {
-        int32_t v = -1;
-        if (i < s) v = a.draft_tokens[(size_t)b * k + i];
-        else if (i == s) v = sh_a[s];
-        a.out_tokens[(size_t)b * (k + 1) + i] = v;
-    }
-}
-
-__device__ void tree_epilogue(const ArgmaxArgs& a, int b) {
-    extern __shared__ int dyn[];
-    const int N = a.N, P = a.P, L = a.L;
-    int* sh_a = dyn;             // [N+1] argmax of each node's row
-    int* sh_tok = dyn + (N + 1); // [N+1] node tokens
-    int* sh_paths = dyn + 2 * (N + 1);
-    for (int n = threadIdx.x; n <= N; n += kThreads) {
-        sh_a[n] = merge_row(a, b, n).i;
-        sh_tok[n] = a.node_tokens[(size_t)b * (N + 1) + n];
-    }
-    const int32_t* gpaths = a.paths + (size_t)b * P * L;
-    if (a.paths_in_lds)
-        for (int q = threadIdx.x; q < P * L; q += kThreads) sh_paths[q] = gpaths[q];
-    __syncthreads();
-    const int32_t* paths = a.paths_in_lds ? (const int32_t*)sh_paths : gpaths;
-
-    int best_m = -1, best_p = INT_MAX;
-    for (int p = threadIdx.x; p < P; p += kThreads) {
-        const int32_t* row = paths + (size_t)p * L;
-        const int r0 = row[0];
-        if (r0 < 0 || r0 > N) continue;  // unused row
-        int m = 0;
-        while (m + 1 < L) {
-            const int child = row[m + 1];
-            if (child < 0 || child > N) break;
-            if (sh_tok[child] != sh_a[row[m]]) break;
-            ++m;
+    __device__ void finish(float v, int i, float* f0, float* f1, double* d) const {
+        wave_reduce_argmax(v, i);
+        __shared__ float red_v[kWaves];
+        __shared__ int red_i[kWaves];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) {
+            red_v[wave] = v;
+            red_i[wave] = i;
         }
-        if (m > best_m) {  // p ascends within a thread: strictly longer only
-            best_m = m;
-            best_p = p;
-        }
+        __syncthreads();
+        v = red_v[0];
+        i = red_i[0];
+        for (int w = 1; w < kWaves; ++w) merge_argmax(v, i, red_v[w], red_i[w]);
+        __syncthreads();
+        *f0 = v;
+        *f1 = __int_as_float(i);
+        *d = 0.0;
     }
-    // Workgroup reduction: longest m, then lowest path row.
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        int m2 = __shfl_xor(best_m, off, 64);
-        int p2 = __shfl_xor(best_p, off, 64);
-        bool take = (m2 > best_m) || (m2 == best_m && p2 < best_p);
-        best_m = take ? m2 : best_m;
-        best_p = take ? p2 : best_p;
-    }
-    __shared__ int red_m[kWaves], red_p[kWaves];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red_m[wave] = best_m;
-        red_p[wave] = best_p;
-    }
-    __syncthreads();
-    best_m = red_m[0];
-    best_p = red_p[0];
-    for (int w = 1; w < kWaves; ++w) {
-        bool take = (red_m[w] > best_m) || (red_m[w] == best_m && red_p[w] < best_p);
-        best_m = take ? red_m[w] : best_m;
-        best_p = take ? red_p[w] : best_p;
-    }
-    const bool none = best_m < 0;
-    const int m = none ? 0 : best_m;
-    const int32_t* row = none ? nullptr : paths + (size_t)best_p * L;
-    for (int t = threadIdx.x; t < L; t += kThreads) {
-        int32_t tok = -1, node = -1;
-        if (none) {
-            if (t == 0) tok = sh_a[0];
-        } else if (t < m) {
-            node = row[t + 1];
-            tok = sh_tok[node];
-        } else if (t == m) {
-            tok = sh_a[row[m]];
-        }
-        a.out_tokens[(size_t)b * L + t] = tok;
-        if (a.accepted_nodes) a.accepted_nodes[(size_t)b * L + t] = node;
-    }
-    if (threadIdx.x == 0) {
-        a.num_accepted[b] = m;
-        if (a.best_path) a.best_path[b] = none ? -1 : best_p;
-    }
-}
 
-// MODE 1: greedy, MODE 2: tree.
-template <typename T, int U, bool VEC, int MODE>
-__global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxArgs a) {
-    constexpr int EPV = Elem<T>::kPerVec;
-    const int tile = blockIdx.x;
-    const int ch = tile % a.S;
-    const int rr = tile / a.S;
-    const int b = rr / a.R;
-    const T* row = static_cast<const T*>(a.target) + (size_t)rr * (size_t)a.V;
-    const int lo = ch * a.chunk;
-    const int hi = min(a.V, lo + a.chunk);
-
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    if constexpr (VEC) {
-        const int nvec = (hi - lo) / EPV;
-        const uint4* base = reinterpret_cast<const uint4*>(row + lo);
-        // All U loads issue back to back: slots past the chunk's end reload its
-        // last vector (in bounds) and are masked afterwards.
-        uint4 raw[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
+    __device__ void tile(int, int, int lo, int, const uint4* raw, int nvec, float* f0, float* f1,
+                         double* d) const {
+        constexpr int EPV = Elem<T>::kPerVec;
         float x[U][EPV];
         int first[U];
 #pragma unroll
@@ -193,76 +81,209 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxArgs a) {
             const int v = threadIdx.x + j * kThreads;
             Elem<T>::widen(raw[j], x[j]);
             first[j] = lo + v * EPV;
-            if (v >= nvec) {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
-                first[j] = INT_MAX - EPV;
-            }
         }
+        if (nvec < U * kThreads) {  // ragged last chunk of a row: mask the padding
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+                if ((int)threadIdx.x + j * kThreads >= nvec) {
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
+                    first[j] = INT_MAX - EPV;
+                }
+        }
+        float bv = -INFINITY;
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int e = 0; e < EPV; ++e) bv = fmaxf(bv, x[j][e]);
         // Lowest index holding the maximum: walk from the highest slot down.
+        int bi = INT_MAX;
 #pragma unroll
         for (int j = U - 1; j >= 0; --j)
 #pragma unroll
             for (int e = EPV - 1; e >= 0; --e) bi = (x[j][e] == bv) ? first[j] + e : bi;
-    } else {
+        finish(bv, bi, f0, f1, d);
+    }
+
+    __device__ void tile_scalar(int b, int r, int lo, int hi, float* f0, float* f1,
+                                double* d) const {
+        const T* p = row(b, r);
+        float bv = -INFINITY;
+        int bi = INT_MAX;
         for (int j = lo + threadIdx.x; j < hi; j += kThreads) {
-            float x = Elem<T>::load(row, j);
+            const float x = Elem<T>::load(p, j);
             if (x > bv || bi == INT_MAX) {
                 bv = x;
                 bi = j;
             }
         }
+        finish(bv, bi, f0, f1, d);
     }
 
-    wave_reduce_argmax(bv, bi);
-    __shared__ float red_v[kWaves];
-    __shared__ int red_i[kWaves];
-    __shared__ int last_flag;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red_v[wave] = bv;
-        red_i[wave] = bi;
+    __device__ int row_argmax(int b, int r) const {
+        const Partial16* p = partials + ((size_t)b * R + r) * S;
+        float v = -INFINITY;
+        int i = INT_MAX;
+        for (int ch = 0; ch < S; ++ch)  // fixed chunk order
+            merge_argmax(v, i, p[ch].f0, __float_as_int(p[ch].f1));
+        return i;
     }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        float v = red_v[0];
-        int i = red_i[0];
-        for (int w = 1; w < kWaves; ++w) merge_argmax(v, i, red_v[w], red_i[w]);
-        ArgPartial p;
-        p.v = v;
-        p.i = i;
-        a.partials[tile] = p;
+
+    __device__ void epilogue(int b) const {
+        if constexpr (MODE == 1) greedy_epilogue(b);
+        else tree_epilogue(b);
+        __syncthreads();
+        clear_partials(partials + (size_t)b * R * S, R * S);  // workspace back to zero
     }
-    if (arrive_last(a.tickets + b, (uint32_t)(a.R * a.S), &last_flag)) {
-        if constexpr (MODE == 1) greedy_epilogue(a, b);
-        else tree_epilogue(a, b);
+
+    __device__ void greedy_epilogue(int b) const {
+        __shared__ int sh_a[kMaxK + 1];
+        __shared__ int sh_s;
+        for (int r = threadIdx.x; r <= k; r += kThreads) sh_a[r] = row_argmax(b, r);
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int s = 0;
+            while (s < k && draft_tokens[(size_t)b * k + s] == sh_a[s]) ++s;
+            sh_s = s;
+            num_accepted[b] = s;
+        }
+        __syncthreads();
+        const int s = sh_s;
+        for (int i = threadIdx.x; i <= k; i += kThreads) {
+            int32_t v = -1;
+            if (i < s) v = draft_tokens[(size_t)b * k + i];
+            else if (i == s) v = sh_a[s];
+            out_tokens[(size_t)b * (k + 1) + i] = v;
+        }
     }
+
+    __device__ void tree_epilogue(int b) const {
+        extern __shared__ int dyn[];
+        int* sh_a = dyn;              // [N+1] argmax of each node's row
+        int* sh_tok = dyn + (N + 1);  // [N+1] node tokens
+        int* sh_paths = dyn + 2 * (N + 1);
+        for (int n = threadIdx.x; n <= N; n += kThreads) {
+            sh_a[n] = row_argmax(b, n);
+            sh_tok[n] = node_tokens[(size_t)b * (N + 1) + n];
+        }
+        const int32_t* gpaths = paths + (size_t)b * P * L;
+        if (paths_in_lds)
+            for (int q = threadIdx.x; q < P * L; q += kThreads) sh_paths[q] = gpaths[q];
+        __syncthreads();
+        const int32_t* pt = paths_in_lds ? (const int32_t*)sh_paths : gpaths;
+
+        int best_m = -1, best_p = INT_MAX;
+        for (int p = threadIdx.x; p < P; p += kThreads) {
+            const int32_t* rowp = pt + (size_t)p * L;
+            const int r0 = rowp[0];
+            if (r0 < 0 || r0 > N) continue;  // unused row
+            int m = 0;
+            while (m + 1 < L) {
+                const int child = rowp[m + 1];
+                if (child < 0 || child > N) break;
+                if (sh_tok[child] != sh_a[rowp[m]]) break;
+                ++m;
+            }
+            if (m > best_m) {  // p ascends within a thread: strictly longer only
+                best_m = m;
+                best_p = p;
+            }
+        }
+        // Workgroup reduction: longest m, then lowest path row.
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+            const int m2 = __shfl_xor(best_m, off, 64);
+            const int p2 = __shfl_xor(best_p, off, 64);
+            const bool take = (m2 > best_m) || (m2 == best_m && p2 < best_p);
+            best_m = take ? m2 : best_m;
+            best_p = take ? p2 : best_p;
+        }
+        __shared__ int red_m[kWaves], red_p[kWaves];
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        if (lane == 0) {
+            red_m[wave] = best_m;
+            red_p[wave] = best_p;
+        }
+        __syncthreads();
+        best_m = red_m[0];
+        best_p = red_p[0];
+        for (int w = 1; w < kWaves; ++w) {
+            const bool take = (red_m[w] > best_m) || (red_m[w] == best_m && red_p[w] < best_p);
+            best_m = take ? red_m[w] : best_m;
+            best_p = take ? red_p[w] : best_p;
+        }
+        const bool none = best_m < 0;
+        const int m = none ? 0 : best_m;
+        const int32_t* rowp = none ? nullptr : pt + (size_t)best_p * L;
+        for (int t = threadIdx.x; t < L; t += kThreads) {
+            int32_t tok = -1, node = -1;
+            if (none) {
+                if (t == 0) tok = sh_a[0];
+            } else if (t < m) {
+                node = rowp[t + 1];
+                tok = sh_tok[node];
+            } else if (t == m) {
+                tok = sh_a[rowp[m]];
+            }
+            out_tokens[(size_t)b * L + t] = tok;
+            if (accepted_nodes) accepted_nodes[(size_t)b * L + t] = node;
+        }
+        if (threadIdx.x == 0) {
+            num_accepted[b] = m;
+            if (best_path) best_path[b] = none ? -1 : best_p;
+        }
+    }
+};
+
+template <typename T, int U, bool VEC, int MODE>
+__global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxArgs a) {
+    ArgmaxOp<T, U, MODE> op;
+    static_cast<ArgmaxArgs&>(op) = a;
+    if constexpr (VEC) stream_tile_vec<T, U>(op);
+    else stream_tile_scalar<T>(op);
 }
 
-template <typename T, bool VEC, int MODE>
-static hipError_t launch_argmax(const ArgmaxArgs& a, int U, size_t lds, hipStream_t st) {
-    const dim3 grid((unsigned)((long long)a.B * a.R * a.S)), block(kThreads);
-    switch (U) {
-        case 8: argmax_kernel<T, 8, VEC, MODE><<<grid, block, lds, st>>>(a); break;
-        case 4: argmax_kernel<T, 4, VEC, MODE><<<grid, block, lds, st>>>(a); break;
-        case 2: argmax_kernel<T, 2, VEC, MODE><<<grid, block, lds, st>>>(a); break;
-        default: argmax_kernel<T, 1, VEC, MODE><<<grid, block, lds, st>>>(a); break;
-    }
+// One workgroup per request.  (T and U do not matter to the epilogue.)
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void argmax_epilogue_kernel(ArgmaxArgs a) {
+    ArgmaxOp<float, 1, MODE> op;
+    static_cast<ArgmaxArgs&>(op) = a;
+    op.epilogue(blockIdx.x);
+}
+
+template <typename T, int U, bool VEC, int MODE>
+static hipError_t launch_argmax_u(const ArgmaxArgs& a, hipStream_t st) {
+    const unsigned n_tiles = (unsigned)((long long)a.B * a.R * a.S);
+    argmax_kernel<T, U, VEC, MODE><<<dim3(n_tiles), dim3(kThreads), 0, st>>>(a);
     return hipGetLastError();
 }
 
+template <typename T, bool VEC, int MODE>
+static hipError_t launch_argmax(const ArgmaxArgs& a, int U, hipStream_t st) {
+    switch (U) {
+        case 8: return launch_argmax_u<T, 8, VEC, MODE>(a, st);
+        case 4: return launch_argmax_u<T, 4, VEC, MODE>(a, st);
+        case 2: return launch_argmax_u<T, 2, VEC, MODE>(a, st);
+        default: return launch_argmax_u<T, 1, VEC, MODE>(a, st);
+    }
+}
+
+// Streaming kernel (timed by the profiling events), then the epilogue kernel.
 template <int MODE>
 static hipError_t dispatch(const ArgmaxArgs& a, int dtype, bool vec, int U, size_t lds,
-                           hipStream_t st) {
+                           hipStream_t st, const KernelEvents& ev) {
+    hipError_t e;
+    if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
     if (dtype == 1)
-        return vec ? launch_argmax<bf16_t, true, MODE>(a, U, lds, st)
-                   : launch_argmax<bf16_t, false, MODE>(a, U, lds, st);
-    return vec ? launch_argmax<float, true, MODE>(a, U, lds, st)
-               : launch_argmax<float, false, MODE>(a, U, lds, st);
+        e = vec ? launch_argmax<bf16_t, true, MODE>(a, U, st)
+                : launch_argmax<bf16_t, false, MODE>(a, U, st);
+    else
+        e = vec ? launch_argmax<float, true, MODE>(a, U, st)
+                : launch_argmax<float, false, MODE>(a, U, st);
+    if (e != hipSuccess) return e;
+    if (ev.end && (e = hipEventRecord(ev.end, st)) != hipSuccess) return e;
+    argmax_epilogue_kernel<MODE><<<dim3((unsigned)a.B), dim3(kThreads), lds, st>>>(a);
+    return hipGetLastError();
 }
 
 static ArgmaxArgs base_args(const void* target, int B, int R, int V, const Geometry& g,
@@ -275,8 +296,7 @@ static ArgmaxArgs base_args(const void* target, int B, int R, int V, const Geome
     a.V = V;
     a.S = g.S;
     a.chunk = g.chunk;
-    a.partials = reinterpret_cast<ArgPartial*>(ws + g.off_partials);
-    a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_ticket_a);
+    a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
     return a;
 }
 
@@ -287,10 +307,7 @@ hipError_t run_greedy(const GreedyCall& c, const Geometry& g, hipStream_t st,
     a.k = c.k;
     a.out_tokens = c.out_tokens;
     a.num_accepted = c.num_accepted;
-    hipError_t e;
-    if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
-    if ((e = dispatch<1>(a, c.dtype, c.vec, g.U, 0, st)) != hipSuccess) return e;
-    return ev.end ? hipEventRecord(ev.end, st) : hipSuccess;
+    return dispatch<1>(a, c.dtype, c.vec, g.U, 0, st, ev);
 }
 
 hipError_t run_tree(const TreeCall& c, const Geometry& g, hipStream_t st,
@@ -308,10 +325,7 @@ hipError_t run_tree(const TreeCall& c, const Geometry& g, hipStream_t st,
     a.accepted_nodes = c.accepted_nodes;
     const size_t lds = sizeof(int) * (2 * (size_t)(c.N + 1) +
                                       (a.paths_in_lds ? (size_t)c.P * c.L : 0));
-    hipError_t e;
-    if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
-    if ((e = dispatch<2>(a, c.dtype, c.vec, g.U, lds, st)) != hipSuccess) return e;
-    return ev.end ? hipEventRecord(ev.end, st) : hipSuccess;
+    return dispatch<2>(a, c.dtype, c.vec, g.U, lds, st, ev);
 }
 
 // ---------------------------------------------------------------------------

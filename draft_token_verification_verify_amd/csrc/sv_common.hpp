@@ -7,6 +7,24 @@
 #include <math.h>
 #include <stdint.h>
 
+#ifndef SV_COHERENT_TICKETS
+#define SV_COHERENT_TICKETS 1
+#endif
+// Tile shape: the largest per-thread vector count (at most SV_MAX_U) whose tile
+// count reaches SV_MIN_TILES.
+#ifndef SV_MAX_U
+#define SV_MAX_U 8
+#endif
+#ifndef SV_MIN_TILES
+#define SV_MIN_TILES 2048
+#endif
+// Distance in uint32 words between two requests' arrival counters: each counter
+// gets its own cache line, so atomics on different requests do not queue on one
+// line.
+#ifndef SV_TICKET_STRIDE
+#define SV_TICKET_STRIDE 64
+#endif
+
 namespace sv {
 
 constexpr int kThreads = 256;           // one workgroup = 4 wave64s
@@ -15,6 +33,12 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kSampleSeg = 16;          // elements per thread in a sampler chunk
 constexpr int kMaxK = 64;               // longest linear draft
 constexpr int kTreeLdsPathEntries = 4096;  // path tables up to this many entries go to LDS
+constexpr int kTicketStride = SV_TICKET_STRIDE;
+
+// Arrival counter of request b.
+__host__ __device__ inline uint32_t* ticket_of(uint32_t* base, int b) {
+    return base + (size_t)b * kTicketStride;
+}
 
 // ---------------------------------------------------------------------------
 // Launch geometry and workspace layout.  A pure function of the call's shape
@@ -27,7 +51,7 @@ struct Geometry {
     int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8
     int S2;          // stop-row chunks per request (stochastic sampler)
     int chunk2;      // elements per stop-row chunk
-    size_t off_ticket_a, off_ticket_b, off_partials, off_stop, off_mass, bytes;
+    size_t off_tickets, off_partials, off_mass, bytes;
 };
 
 // log2(e) / temperature, the factor that turns a logit difference into a
@@ -38,24 +62,6 @@ struct Scale {
     float hi, lo;
     double c64;
 };
-
-// Per (row, chunk) softmax statistics: m = max raw logit of the chunk, s = sum of
-// 2^((x - m) * c) over the chunk, accumulated in fp64.
-struct StatPartial {
-    float m;
-    float pad;
-    double s;
-};
-static_assert(sizeof(StatPartial) == 16, "StatPartial layout");
-
-struct StopInfo {      // per request, written by the streaming kernel's epilogue
-    int32_t s;         // number of accepted drafts = stop row
-    float mt;          // max logit of target row s
-    float md;          // max logit of draft row s (unused when s == k)
-    int32_t pad;
-    double st, sd;     // sum of 2^((x - max) * c) of those rows (fp64)
-};
-static_assert(sizeof(StopInfo) == 32, "StopInfo layout");
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -69,11 +75,11 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     const long long rows = (long long)B * g->R;
     // Largest per-thread vector count whose tile count still fills the chip
     // several times over; small problems fall back to smaller tiles.
-    int U = 8;
+    int U = SV_MAX_U;
     for (; U > 1; U >>= 1) {
         long long ce = (long long)kThreads * U * epv;
         long long tiles = rows * ((V + ce - 1) / ce);
-        if (tiles >= 2048) break;
+        if (tiles >= SV_MIN_TILES) break;
     }
     g->U = U;
     g->chunk = kThreads * U * epv;
@@ -82,14 +88,10 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     g->S2 = (mode == 0) ? (V + g->chunk2 - 1) / g->chunk2 : 0;
 
     size_t off = 0;
-    g->off_ticket_a = off;
-    off = align_up(off + sizeof(uint32_t) * (size_t)B, 256);
-    g->off_ticket_b = off;
-    off = align_up(off + sizeof(uint32_t) * (size_t)B, 256);
+    g->off_tickets = off;  // sampler arrival counters (stochastic only), one line each
+    off = align_up(off + (mode == 0 ? sizeof(uint32_t) * kTicketStride * (size_t)B : 0), 256);
     g->off_partials = off;
     off = align_up(off + 16 * (size_t)rows * (size_t)g->S, 256);
-    g->off_stop = off;
-    off = align_up(off + (mode == 0 ? sizeof(StopInfo) * (size_t)B : 0), 256);
     g->off_mass = off;
     off = align_up(off + (mode == 0 ? sizeof(double) * (size_t)B * (size_t)g->S2 : 0), 256);
     g->bytes = off;
@@ -233,6 +235,19 @@ __device__ inline double block_inclusive_scan(double x, double* wave_tot, double
     return before + x;
 }
 
+// Values that one workgroup writes and another reads within the same launch
+// (partials, masses, stop state) travel through the device-coherent level:
+// agent-scope relaxed atomic accesses (sc1 on gfx950), which neither stay dirty
+// in one XCD's L2 nor hit stale lines in another's.
+template <typename T>
+__device__ inline void store_coherent(T* p, T v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ inline T load_coherent(const T* p) {
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Take an arrival ticket on `counter` after thread 0 has written this
 // workgroup's contribution (only thread 0 writes what other workgroups read).
 // Returns true in every thread of the last of `expected` arrivals; those
@@ -240,8 +255,15 @@ __device__ inline double block_inclusive_scan(double x, double* wave_tot, double
 // counter to zero (atomically, where the other arrivals incremented it).
 __device__ inline bool arrive_last(uint32_t* counter, uint32_t expected, int* lds_flag) {
     if (threadIdx.x == 0) {
+#if SV_COHERENT_TICKETS
+        // Thread 0's coherent stores complete before the ticket is taken.
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#else
         // Release thread 0's writes at device scope, then take the ticket.
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+#endif
         uint32_t prev = atomicAdd(counter, 1u);
         int last = (prev == expected - 1);
         if (last) atomicExch(counter, 0u);
@@ -249,7 +271,9 @@ __device__ inline bool arrive_last(uint32_t* counter, uint32_t expected, int* ld
     }
     __syncthreads();
     bool last = *lds_flag != 0;
+#if !SV_COHERENT_TICKETS
     if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // see every arrival's writes
+#endif
     return last;
 }
 

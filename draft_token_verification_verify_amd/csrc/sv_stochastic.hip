@@ -15,19 +15,24 @@
 //            Each thread sums its own elements against its own maximum (so a
 //            row's largest logits, each usually the maximum of its thread,
 //            contribute an exact 1) in fp64, and threads are merged with fp64
-//            scale factors.  The last workgroup of a request to finish (arrival
-//            ticket) merges the chunks of every row, computes p_i(x_i) and
-//            q_i(x_i) in fp64, runs the k tests (independent given the
-//            uniforms), takes the first failure as the stop row s and writes the
-//            accepted drafts, the -1 padding and num_accepted.
-//   sample:  one workgroup per (request, stop-row chunk).  Computes the chunk's
-//            share of the final distribution's mass (residual max(0, p_s - q_s)
-//            or bonus p_k) in fp64; tokens within 2^-8 of the row maximum take an
-//            fp64 exponential, the rest fp32.  The last workgroup of a request
-//            picks the chunk holding u_k * Z by a prefix sum over the chunk
-//            masses, then the token inside that chunk by a prefix sum over
-//            per-thread segments and a walk through one segment (ascending
-//            vocabulary order: the smallest j whose running mass exceeds u_k * Z).
+//            scale factors.  A tile of a test row also publishes the raw logit
+//            of the tested draft token when that token falls inside it.
+//   sample:  one workgroup per (request, stop-row chunk).  Every workgroup of a
+//            request first merges that request's partials (chunk order, fp64),
+//            computes p_i(x_i) and q_i(x_i), runs the k tests (independent given
+//            the uniforms) and takes the first failure as the stop row s; the
+//            chunk-0 workgroup writes the accepted drafts, the -1 padding,
+//            num_accepted and the probabilities.  Each workgroup then computes
+//            its chunk's share of the final distribution's mass (residual
+//            max(0, p_s - q_s) or bonus p_k) in fp64 -- tokens within 2^-8 of
+//            the row maximum take an fp64 exponential, the rest fp32 -- and the
+//            last of the request's workgroups (arrival ticket) picks the chunk
+//            holding u_k * Z by a prefix sum over the chunk masses, then the
+//            token inside that chunk by a prefix sum over per-thread segments
+//            and a walk through one segment (ascending vocabulary order: the
+//            smallest j whose running mass exceeds u_k * Z).
+// The streaming kernel has no atomics or fences: the kernel boundary publishes
+// its partials to the sampler.
 //
 // Accuracy matters beyond the decisions themselves: a vocabulary of ~10^5 has
 // ~10^5 CDF edges, so a relative error e in the cumulative weights moves the
@@ -35,33 +40,27 @@
 // near 1e-10.
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
+#include "sv_stream.hpp"
 
 namespace sv {
 
-struct StatsArgs {
+struct CallArgs {
     const void* target;
     const void* draft;
     const int32_t* draft_tokens;
     const float* uniforms;
-    int B, k, V, S, chunk;
+    int B, k, V;
+    int R, S, chunk;         // streaming geometry: rows per request, chunks per row
+    int S2, chunk2;          // sampler geometry: chunks per stop row
     Scale sc;                // log2(e) / temperature
-    StatPartial* partials;   // [B, 2k+1, S]
-    uint32_t* tickets;       // [B]
-    StopInfo* stop;          // [B]
+    Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, f1 = tested logit or NaN, d = sum
+    uint32_t* tickets;       // per request (padded): sampler arrivals
+    double* mass;            // [B, S2]
     int32_t* out_tokens;     // [B, k+1]
     int32_t* num_accepted;   // [B]
     float* p_at_draft;       // [B, k] or null
     float* q_at_draft;       // [B, k] or null
 };
-
-// Row r of request b in the streaming order: rows 0..k are target rows, rows
-// k+1..2k are draft rows 0..k-1.
-template <typename T>
-__device__ inline const T* stats_row(const StatsArgs& a, int b, int r) {
-    if (r <= a.k)
-        return static_cast<const T*>(a.target) + ((size_t)b * (a.k + 1) + r) * (size_t)a.V;
-    return static_cast<const T*>(a.draft) + ((size_t)b * a.k + (r - a.k - 1)) * (size_t)a.V;
-}
 
 // p(x) = 2^((x - M) * c) / S in fp64; 0 when x or the whole row is -inf.
 __device__ inline double prob_of(float x, float M, double S, const Scale& k) {
@@ -69,24 +68,130 @@ __device__ inline double prob_of(float x, float M, double S, const Scale& k) {
     return exp2_accurate(x, M, k) / S;
 }
 
-// Per-request epilogue, run by the last workgroup of request b.
-template <typename T>
-__device__ void stats_epilogue(const StatsArgs& a, int b) {
-    __shared__ float sh_m[2 * kMaxK + 1];
+// ---------------------------------------------------------------------------
+// Streaming statistics.  Row order within request b: r = 0..k target rows,
+// r = k+1..2k draft rows 0..k-1.
+// ---------------------------------------------------------------------------
+template <typename T, int U>
+struct StatsOp : CallArgs {
+    __device__ const T* row(int b, int r) const {
+        if (r <= k) return static_cast<const T*>(target) + ((size_t)b * (k + 1) + r) * (size_t)V;
+        return static_cast<const T*>(draft) + ((size_t)b * k + (r - k - 1)) * (size_t)V;
+    }
+
+    // Draft token tested on row r of request b, or -1 for the bonus row.
+    __device__ int token_of_row(int b, int r) const {
+        if (r == k) return -1;
+        const int i = (r < k) ? r : r - k - 1;
+        return draft_tokens[(size_t)b * k + i];
+    }
+
+    // Workgroup reduction of per-thread (max m, fp64 sum s against m) into the
+    // tile's (M, S): every thread's sum is rescaled to the common M with an fp64
+    // exponential, then summed in fixed order.
+    __device__ void finish(float m, double s, float gx, float* f0, float* f1, double* d) const {
+        __shared__ float red_f[kWaves];
+        __shared__ double red_d[kWaves];
+        const float M = block_max(m, red_f);
+        const double f = (m == -INFINITY) ? 0.0 : exp2_accurate(m, M, sc);
+        const double Ssum = block_sum(s * f, red_d);
+        *f0 = M;
+        *f1 = gx;
+        *d = Ssum;
+    }
+
+    __device__ void tile(int b, int r, int lo, int hi, const uint4* raw, int nvec, float* f0,
+                         float* f1, double* d) const {
+        constexpr int EPV = Elem<T>::kPerVec;
+        // Thread 0 fetches the tested token's logit early (it is in this tile's
+        // lines, so the load overlaps the arithmetic).
+        float gx = __builtin_nanf("");
+        if (threadIdx.x == 0) {
+            const int x = token_of_row(b, r);
+            if (x >= lo && x < hi) gx = Elem<T>::load(row(b, r), x);
+        }
+        float x[U][EPV];
+#pragma unroll
+        for (int j = 0; j < U; ++j) Elem<T>::widen(raw[j], x[j]);
+        if (nvec < U * kThreads) {  // ragged last chunk of a row: mask the padding
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+                if ((int)threadIdx.x + j * kThreads >= nvec)
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
+        }
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) m = fmaxf(m, x[j][e]);
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        double s = 0.0;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[j][e] - ms, sc));
+        finish(m, s, gx, f0, f1, d);
+    }
+
+    __device__ void tile_scalar(int b, int r, int lo, int hi, float* f0, float* f1,
+                                double* d) const {
+        const T* p = row(b, r);
+        float gx = __builtin_nanf("");
+        if (threadIdx.x == 0) {
+            const int x = token_of_row(b, r);
+            if (x >= lo && x < hi) gx = Elem<T>::load(p, x);
+        }
+        float m = -INFINITY;
+        for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, Elem<T>::load(p, j));
+        const float ms = (m == -INFINITY) ? 0.f : m;
+        double s = 0.0;
+        for (int j = lo + threadIdx.x; j < hi; j += kThreads)
+            s += (double)fast_exp2(scaled(Elem<T>::load(p, j) - ms, sc));
+        finish(m, s, gx, f0, f1, d);
+    }
+};
+
+template <typename T, int U, bool VEC>
+__global__ __launch_bounds__(kThreads) void stats_kernel(CallArgs a) {
+    StatsOp<T, U> op;
+    static_cast<CallArgs&>(op) = a;
+    if constexpr (VEC) stream_tile_vec<T, U>(op);
+    else stream_tile_scalar<T>(op);
+}
+
+// ---------------------------------------------------------------------------
+// Sampler: decision, stop-row mass, final draw.
+// ---------------------------------------------------------------------------
+
+// The request's decision, computed by every sampler workgroup of the request
+// from the streaming partials (fixed chunk order, fp64).
+struct Decision {
+    int s;
+    float mt, md;
+    double st, sd;
+};
+
+__device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
+    __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1];
     __shared__ double sh_s[2 * kMaxK + 1];
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
-    const int k = a.k, R = 2 * k + 1;
+    const int k = a.k, R = a.R, S = a.S;
     for (int r = threadIdx.x; r < R; r += kThreads) {
-        const StatPartial* p = a.partials + ((size_t)b * R + r) * a.S;
-        float M = -INFINITY;
-        for (int ch = 0; ch < a.S; ++ch) M = fmaxf(M, p[ch].m);
-        double S = 0.0;
+        const Partial16* p = a.partials + ((size_t)b * R + r) * S;
+        float M = -INFINITY, g = __builtin_nanf("");
+        for (int ch = 0; ch < S; ++ch) {
+            M = fmaxf(M, p[ch].f0);
+            if (!__builtin_isnan(p[ch].f1)) g = p[ch].f1;
+        }
+        double Ssum = 0.0;
         if (M != -INFINITY)
-            for (int ch = 0; ch < a.S; ++ch)  // fixed chunk order
-                S += p[ch].s * exp2_accurate(p[ch].m, M, a.sc);
+            for (int ch = 0; ch < S; ++ch)  // fixed chunk order
+                Ssum += p[ch].d * exp2_accurate(p[ch].f0, M, a.sc);
         sh_m[r] = M;
-        sh_s[r] = S;
+        sh_s[r] = Ssum;
+        sh_g[r] = g;
     }
     __syncthreads();
     for (int i = threadIdx.x; i < k; i += kThreads) {
@@ -95,121 +200,39 @@ __device__ void stats_epilogue(const StatsArgs& a, int b) {
         double P = 0.0, Q = 0.0;
         int acc = 0;
         if (x >= 0 && x < a.V) {
-            const float xt = Elem<T>::load(stats_row<T>(a, b, i), x);
-            const float xd = Elem<T>::load(stats_row<T>(a, b, k + 1 + i), x);
-            P = prob_of(xt, sh_m[i], sh_s[i], a.sc);
-            Q = prob_of(xd, sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
+            P = prob_of(sh_g[i], sh_m[i], sh_s[i], a.sc);
+            Q = prob_of(sh_g[k + 1 + i], sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
             acc = (P >= Q) || ((double)u * Q < P);  // strict u < min(1, P/Q), no division
         }
         sh_acc[i] = acc;
-        if (a.p_at_draft) a.p_at_draft[(size_t)b * k + i] = (float)P;
-        if (a.q_at_draft) a.q_at_draft[(size_t)b * k + i] = (float)Q;
+        if (write_outputs) {
+            if (a.p_at_draft) a.p_at_draft[(size_t)b * k + i] = (float)P;
+            if (a.q_at_draft) a.q_at_draft[(size_t)b * k + i] = (float)Q;
+        }
     }
     __syncthreads();
     if (threadIdx.x == 0) {
         int s = k;
         for (int i = 0; i < k; ++i)
             if (!sh_acc[i]) { s = i; break; }
-        StopInfo si;
-        si.s = s;
-        si.mt = sh_m[s];
-        si.st = sh_s[s];
-        si.md = (s < k) ? sh_m[k + 1 + s] : 0.f;
-        si.sd = (s < k) ? sh_s[k + 1 + s] : 1.0;
-        si.pad = 0;
-        a.stop[b] = si;
-        a.num_accepted[b] = s;
         sh_stop = s;
+        if (write_outputs) a.num_accepted[b] = s;
     }
     __syncthreads();
     const int s = sh_stop;
-    for (int i = threadIdx.x; i <= k; i += kThreads) {
-        if (i < s) a.out_tokens[(size_t)b * (k + 1) + i] = a.draft_tokens[(size_t)b * k + i];
-        else if (i > s) a.out_tokens[(size_t)b * (k + 1) + i] = -1;
-        // out_tokens[b, s] is written by the sampler.
-    }
-}
-
-template <typename T, int U, bool VEC>
-__global__ __launch_bounds__(kThreads) void stats_kernel(StatsArgs a) {
-    constexpr int EPV = Elem<T>::kPerVec;
-    const int R = 2 * a.k + 1;
-    const int tile = blockIdx.x;
-    const int ch = tile % a.S;
-    const int rr = tile / a.S;
-    const int r = rr % R;
-    const int b = rr / R;
-    const T* row = stats_row<T>(a, b, r);
-    const int lo = ch * a.chunk;
-    const int hi = min(a.V, lo + a.chunk);
-
-    // Each thread: its maximum m, then sum 2^((x - m) * c) over its elements in fp64.
-    float m = -INFINITY;
-    double s = 0.0;
-    if constexpr (VEC) {
-        // The chunk is whole 16-byte vectors (V % EPV == 0, rows 16-byte aligned).
-        const int nvec = (hi - lo) / EPV;
-        const uint4* base = reinterpret_cast<const uint4*>(row + lo);
-        // All U loads issue back to back: slots past the chunk's end reload its
-        // last vector (in bounds) and are masked to -inf afterwards.
-        uint4 raw[U];
-#pragma unroll
-        for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
-        float x[U][EPV];
-#pragma unroll
-        for (int j = 0; j < U; ++j) {
-            Elem<T>::widen(raw[j], x[j]);
-            if ((int)threadIdx.x + j * kThreads >= nvec)
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) x[j][e] = -INFINITY;
+    if (write_outputs)
+        for (int i = threadIdx.x; i <= k; i += kThreads) {
+            if (i < s) a.out_tokens[(size_t)b * (k + 1) + i] = a.draft_tokens[(size_t)b * k + i];
+            else if (i > s) a.out_tokens[(size_t)b * (k + 1) + i] = -1;
+            // out_tokens[b, s] is written by the final draw.
         }
-#pragma unroll
-        for (int j = 0; j < U; ++j)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) m = fmaxf(m, x[j][e]);
-        const float ms = (m == -INFINITY) ? 0.f : m;
-#pragma unroll
-        for (int j = 0; j < U; ++j)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[j][e] - ms, a.sc));
-    } else {
-        for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, Elem<T>::load(row, j));
-        const float ms = (m == -INFINITY) ? 0.f : m;
-        for (int j = lo + threadIdx.x; j < hi; j += kThreads)
-            s += (double)fast_exp2(scaled(Elem<T>::load(row, j) - ms, a.sc));
-    }
-
-    // Workgroup: common maximum, then each thread's sum rescaled in fp64.
-    __shared__ float red_f[kWaves];
-    __shared__ double red_d[kWaves];
-    __shared__ int last_flag;
-    const float M = block_max(m, red_f);
-    const double f = (m == -INFINITY) ? 0.0 : exp2_accurate(m, M, a.sc);
-    const double S = block_sum(s * f, red_d);
-    if (threadIdx.x == 0) {
-        StatPartial p;
-        p.m = M;
-        p.pad = 0.f;
-        p.s = S;
-        a.partials[tile] = p;
-    }
-    if (arrive_last(a.tickets + b, (uint32_t)(R * a.S), &last_flag))
-        stats_epilogue<T>(a, b);
+    out->s = s;
+    out->mt = sh_m[s];
+    out->st = sh_s[s];
+    out->md = (s < k) ? sh_m[k + 1 + s] : 0.f;
+    out->sd = (s < k) ? sh_s[k + 1 + s] : 1.0;
+    __syncthreads();
 }
-
-// ---------------------------------------------------------------------------
-
-struct SampleArgs {
-    const void* target;
-    const void* draft;
-    const float* uniforms;
-    int B, k, V, S2, chunk2;
-    Scale sc;
-    const StopInfo* stop;  // [B]
-    double* mass;          // [B, S2]
-    uint32_t* tickets;     // [B]
-    int32_t* out_tokens;   // [B, k+1]
-};
 
 // Weight of one token in the final draw, in fp64: the residual max(0, p - q)
 // when the request stopped on a rejection, else the target probability.  Tokens
@@ -301,8 +324,8 @@ __device__ double chunk_mass(const T* trow, const T* drow, const Weigher& W, int
 }
 
 template <typename T, bool VEC>
-__device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const T* drow,
-                                Weigher W) {
+__device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow, const T* drow,
+                             Weigher W) {
     constexpr int SEG = kSampleSeg;
     __shared__ double sh_wave[kWaves];
     __shared__ double sh_red[kWaves];
@@ -320,7 +343,7 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
         double grp = 0.0;
         for (int g = 0; g < G; ++g) {
             const int c = threadIdx.x * G + g;
-            if (c < a.S2) grp += mass[c];
+            if (c < a.S2) grp += load_coherent(&mass[c]);
         }
         double incl = block_inclusive_scan(grp, sh_wave, &Z);
         if (Z > 0.0 || pass == 1) {
@@ -342,13 +365,14 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
                 for (int g = 0; g < G; ++g) {
                     const int c = threadIdx.x * G + g;
                     if (c >= a.S2) break;
-                    if (mass[c] > 0.0) { lastc = c; lastbase = run; }
-                    if (run + mass[c] > tau) {
+                    const double mc = load_coherent(&mass[c]);
+                    if (mc > 0.0) { lastc = c; lastbase = run; }
+                    if (run + mc > tau) {
                         lastc = c;
                         lastbase = run;
                         break;
                     }
-                    run += mass[c];
+                    run += mc;
                 }
                 // Rounding can leave the walk short of tau: stay in this group.
                 if (lastc >= 0) {
@@ -363,8 +387,9 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
                 int lastc = 0;
                 double lastbase = 0.0;
                 for (int c = 0; c < a.S2; ++c) {
-                    if (mass[c] > 0.0) { lastc = c; lastbase = run; }
-                    run += mass[c];
+                    const double mc = load_coherent(&mass[c]);
+                    if (mc > 0.0) { lastc = c; lastbase = run; }
+                    run += mc;
                 }
                 sh_chunk = lastc;
                 sh_base = lastbase;
@@ -377,7 +402,7 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
             double mc = chunk_mass<T, VEC>(trow, drow, W, a.V, lo, hi, sh_red);
-            if (threadIdx.x == 0) mass[c] = mc;
+            if (threadIdx.x == 0) store_coherent(&mass[c], mc);
             __syncthreads();
         }
         // Make thread 0's fresh masses visible to every wave before rereading.
@@ -428,55 +453,66 @@ __device__ void sample_epilogue(const SampleArgs& a, int b, const T* trow, const
     if (threadIdx.x == 0) {
         int tok = sh_token;
         if (tok < 0) tok = lo;  // no positive weight anywhere: unreachable with finite logits
-        a.out_tokens[(size_t)b * (k + 1) + min(max(a.stop[b].s, 0), k)] = tok;
+        a.out_tokens[(size_t)b * (k + 1) + s_row] = tok;
     }
+    // Leave this request's part of the workspace zero for later calls (every
+    // other workgroup of the request has read the partials and stored its mass
+    // before taking its ticket).
+    __syncthreads();
+    for (int c = threadIdx.x; c < a.S2; c += kThreads) mass[c] = 0.0;
+    clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
 }
 
+
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_kernel(SampleArgs a) {
+__global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     const int tile = blockIdx.x;
     const int b = tile / a.S2;
     const int ch = tile % a.S2;
-    StopInfo si = a.stop[b];
     const int k = a.k;
-    si.s = min(max(si.s, 0), k);  // never index outside the request's rows
+    Decision dc;
+    decide(a, b, ch == 0, &dc);
     Weigher W;
-    W.mt = si.mt;
-    W.inv_st = 1.0 / si.st;
-    W.md = si.md;
-    W.inv_sd = 1.0 / si.sd;
+    W.mt = dc.mt;
+    W.inv_st = 1.0 / dc.st;
+    W.md = dc.md;
+    W.inv_sd = 1.0 / dc.sd;
     W.sc = a.sc;
-    W.residual = si.s < k;
-    const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + si.s) * (size_t)a.V;
+    W.residual = dc.s < k;
+    const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + dc.s) * (size_t)a.V;
     const T* drow = W.residual
-        ? static_cast<const T*>(a.draft) + ((size_t)b * k + si.s) * (size_t)a.V
+        ? static_cast<const T*>(a.draft) + ((size_t)b * k + dc.s) * (size_t)a.V
         : trow;
     __shared__ double red[kWaves];
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    double mc = chunk_mass<T, VEC>(trow, drow, W, a.V, lo, hi, red);
-    if (threadIdx.x == 0) a.mass[(size_t)b * a.S2 + ch] = mc;
-    if (arrive_last(a.tickets + b, (uint32_t)a.S2, &last_flag))
-        sample_epilogue<T, VEC>(a, b, trow, drow, W);
+    const double mc = chunk_mass<T, VEC>(trow, drow, W, a.V, lo, hi, red);
+    if (threadIdx.x == 0) store_coherent(&a.mass[(size_t)b * a.S2 + ch], mc);
+    if (arrive_last(ticket_of(a.tickets, b), (uint32_t)a.S2, &last_flag))
+        sample_final<T, VEC>(a, b, dc.s, trow, drow, W);
 }
 
 // ---------------------------------------------------------------------------
 
-template <typename T, bool VEC>
-static hipError_t launch_stats(const StatsArgs& a, int U, hipStream_t st) {
-    const int R = 2 * a.k + 1;
-    const dim3 grid((unsigned)((long long)a.B * R * a.S)), block(kThreads);
-    switch (U) {
-        case 8: stats_kernel<T, 8, VEC><<<grid, block, 0, st>>>(a); break;
-        case 4: stats_kernel<T, 4, VEC><<<grid, block, 0, st>>>(a); break;
-        case 2: stats_kernel<T, 2, VEC><<<grid, block, 0, st>>>(a); break;
-        default: stats_kernel<T, 1, VEC><<<grid, block, 0, st>>>(a); break;
-    }
+template <typename T, int U, bool VEC>
+static hipError_t launch_stats_u(const CallArgs& a, hipStream_t st) {
+    const unsigned n_tiles = (unsigned)((long long)a.B * a.R * a.S);
+    stats_kernel<T, U, VEC><<<dim3(n_tiles), dim3(kThreads), 0, st>>>(a);
     return hipGetLastError();
 }
 
 template <typename T, bool VEC>
-static hipError_t launch_sample(const SampleArgs& a, hipStream_t st) {
+static hipError_t launch_stats(const CallArgs& a, int U, hipStream_t st) {
+    switch (U) {
+        case 8: return launch_stats_u<T, 8, VEC>(a, st);
+        case 4: return launch_stats_u<T, 4, VEC>(a, st);
+        case 2: return launch_stats_u<T, 2, VEC>(a, st);
+        default: return launch_stats_u<T, 1, VEC>(a, st);
+    }
+}
+
+template <typename T, bool VEC>
+static hipError_t launch_sample(const CallArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
     sample_kernel<T, VEC><<<grid, block, 0, st>>>(a);
     return hipGetLastError();
@@ -485,7 +521,7 @@ static hipError_t launch_sample(const SampleArgs& a, hipStream_t st) {
 hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
                           const KernelEvents& ev) {
     char* ws = static_cast<char*>(call.workspace);
-    StatsArgs a;
+    CallArgs a;
     a.target = call.target;
     a.draft = call.draft;
     a.draft_tokens = call.draft_tokens;
@@ -493,31 +529,19 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.B = call.B;
     a.k = call.k;
     a.V = call.V;
+    a.R = g.R;
     a.S = g.S;
     a.chunk = g.chunk;
+    a.S2 = g.S2;
+    a.chunk2 = g.chunk2;
     a.sc = make_scale(call.temperature);
-    a.partials = reinterpret_cast<StatPartial*>(ws + g.off_partials);
-    a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_ticket_a);
-    a.stop = reinterpret_cast<StopInfo*>(ws + g.off_stop);
+    a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
+    a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_tickets);
+    a.mass = reinterpret_cast<double*>(ws + g.off_mass);
     a.out_tokens = call.out_tokens;
     a.num_accepted = call.num_accepted;
     a.p_at_draft = call.p_at_draft;
     a.q_at_draft = call.q_at_draft;
-
-    SampleArgs s;
-    s.target = call.target;
-    s.draft = call.draft;
-    s.uniforms = call.uniforms;
-    s.B = call.B;
-    s.k = call.k;
-    s.V = call.V;
-    s.S2 = g.S2;
-    s.chunk2 = g.chunk2;
-    s.sc = a.sc;
-    s.stop = a.stop;
-    s.mass = reinterpret_cast<double*>(ws + g.off_mass);
-    s.tickets = reinterpret_cast<uint32_t*>(ws + g.off_ticket_b);
-    s.out_tokens = call.out_tokens;
 
     hipError_t e;
     if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
@@ -530,8 +554,8 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     if (e != hipSuccess) return e;
     if (ev.end && (e = hipEventRecord(ev.end, st)) != hipSuccess) return e;
     if (call.dtype == 1)
-        return call.vec ? launch_sample<bf16_t, true>(s, st) : launch_sample<bf16_t, false>(s, st);
-    return call.vec ? launch_sample<float, true>(s, st) : launch_sample<float, false>(s, st);
+        return call.vec ? launch_sample<bf16_t, true>(a, st) : launch_sample<bf16_t, false>(a, st);
+    return call.vec ? launch_sample<float, true>(a, st) : launch_sample<float, false>(a, st);
 }
 
 }  // namespace sv

@@ -1,0 +1,82 @@
+// sv_stream.hpp -- the tile loop shared by the streaming kernels (softmax
+// statistics and argmax).
+//
+// A tile is one chunk of one logits row: 256 threads x U 16-byte vectors, one
+// workgroup per tile, tiles numbered request-major t = (b * R + r) * S + ch.
+// Each workgroup issues all of its loads at once, reduces the tile and writes
+// one 16-byte partial; nothing else.  The per-request merge of the partials
+// happens in the next kernel of the call, after the kernel boundary has made
+// every partial visible (no atomics or fences on the streaming path).
+#pragma once
+
+#include "sv_common.hpp"
+
+namespace sv {
+
+// Partial of one tile: meaning depends on the op (see the ops).
+struct Partial16 {
+    float f0;
+    float f1;
+    double d;
+};
+static_assert(sizeof(Partial16) == 16, "Partial16 layout");
+
+// One workgroup per tile, rows 16-byte aligned (V a whole number of vectors).
+//   Op::row(b, r) -> const T* row start
+//   Op::tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d): reduce the tile held in
+//     raw[U] (this thread's vectors; slots >= nvec are padding); the returned
+//     values are published by thread 0.
+template <typename T, int U, class Op>
+__device__ void stream_tile_vec(const Op& op) {
+    constexpr int EPV = Elem<T>::kPerVec;
+    const int t = blockIdx.x;
+    const int ch = t % op.S, rr = t / op.S;
+    const int r = rr % op.R, b = rr / op.R;
+    const int lo = ch * op.chunk, hi = min(op.V, lo + op.chunk);
+    const int nvec = (hi - lo) / EPV;
+    const uint4* base = reinterpret_cast<const uint4*>(op.row(b, r) + lo);
+    // All U loads issue back to back: slots past the chunk's end reload its last
+    // vector (in bounds) and are masked by the op.
+    uint4 raw[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
+    float f0, f1;
+    double d;
+    op.tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d);
+    if (threadIdx.x == 0) {
+        Partial16 p;
+        p.f0 = f0;
+        p.f1 = f1;
+        p.d = d;
+        op.partials[t] = p;
+    }
+}
+
+// Same for rows that are not 16-byte aligned: scalar loads.
+template <typename T, class Op>
+__device__ void stream_tile_scalar(const Op& op) {
+    const int t = blockIdx.x;
+    const int ch = t % op.S, rr = t / op.S;
+    const int r = rr % op.R, b = rr / op.R;
+    const int lo = ch * op.chunk, hi = min(op.V, lo + op.chunk);
+    float f0, f1;
+    double d;
+    op.tile_scalar(b, r, lo, hi, &f0, &f1, &d);
+    if (threadIdx.x == 0) {
+        Partial16 p;
+        p.f0 = f0;
+        p.f1 = f1;
+        p.d = d;
+        op.partials[t] = p;
+    }
+}
+
+// Zero a request's partials once every reader has read them, so that the
+// workspace is all zero again when the call completes (a later call of another
+// shape may place its arrival counters there).
+__device__ inline void clear_partials(Partial16* p, int n) {
+    for (int i = threadIdx.x; i < n; i += kThreads)
+        *reinterpret_cast<uint4*>(p + i) = make_uint4(0, 0, 0, 0);
+}
+
+}  // namespace sv

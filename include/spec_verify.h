@@ -90,10 +90,11 @@ const char *spec_verify_status_string(int status);
  *
  * The workspace holds per-request arrival counters, per-chunk partial
  * reductions and per-request sampling state.  It must be zero-filled before
- * its first use (spec_verify_workspace_init does that); every call leaves the
- * counters zeroed again when it completes, so one workspace serves any number
- * of later calls of any mode and shape whose size fits, provided calls that
- * share it are ordered on one stream.
+ * its first use (spec_verify_workspace_init does that); every call leaves all
+ * of it zero-filled again when it completes, so one workspace serves any
+ * number of later calls of any mode and shape whose size fits, provided calls
+ * that share it are ordered on one stream.  (A call cut short by a device
+ * fault leaves it undefined: zero it again.)
  */
 size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype);
 

@@ -138,3 +138,36 @@ def test_shared_workspace_across_modes():
         g = H.run_tree(c_t, workspace=ws)
         r = oracle.tree(c_t.target, c_t.node_tokens, c_t.paths)
         np.testing.assert_array_equal(g["out_tokens"], r["out_tokens"])
+
+
+def test_workspace_is_zero_after_every_call_and_reusable_across_shapes():
+    """One workspace across calls of different modes and shapes (growing and
+    shrinking B, k, V); each result matches the oracle and the workspace reads
+    back all zero after each call."""
+    import torch
+
+    ws = torch.zeros(1 << 22, dtype=torch.uint8, device="cuda")
+    seq = [
+        ("s", wl.gaussian_stochastic(1, 2, 4, 7777, "bf16", target_sd=2.0, draft_noise_sd=1.0)),
+        ("s", wl.gaussian_stochastic(2, 9, 0, 33000, "f32", target_sd=2.0, draft_noise_sd=1.0)),
+        ("g", wl.c2_greedy(3)),
+        ("s", wl.c3(4, B=3, V=20000)),
+        ("t", wl.c5(5, B=3, V=9000)),
+        ("s", wl.gaussian_stochastic(6, 17, 2, 4096, "bf16", target_sd=2.0, draft_noise_sd=1.0)),
+        ("g", tied_greedy(7, 11, 3, 5001, "f32")),
+        ("s", wl.gaussian_stochastic(8, 1, 1, 50001, "f32", target_sd=2.0, draft_noise_sd=1.0)),
+    ]
+    for kind, case in seq:
+        if kind == "s":
+            g = H.run_stochastic(case, workspace=ws)
+            H.compare_stochastic(g, H.oracle_stochastic(case), label=case.name)
+        elif kind == "g":
+            g = H.run_greedy(case, workspace=ws)
+            r = oracle.greedy(case.target, case.draft_tokens)
+            np.testing.assert_array_equal(g["out_tokens"], r["out_tokens"])
+        else:
+            g = H.run_tree(case, workspace=ws)
+            r = oracle.tree(case.target, case.node_tokens, case.paths)
+            np.testing.assert_array_equal(g["out_tokens"], r["out_tokens"])
+        torch.cuda.synchronize()
+        assert int(torch.count_nonzero(ws)) == 0, f"workspace not zero after {case.name}"
