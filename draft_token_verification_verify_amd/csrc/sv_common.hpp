@@ -21,6 +21,9 @@
 // Distance in uint32 words between two requests' arrival counters: each counter
 // gets its own cache line, so atomics on different requests do not queue on one
 // line.
+#ifndef SV_SAMPLER_WGS
+#define SV_SAMPLER_WGS 1024
+#endif
 #ifndef SV_TICKET_STRIDE
 #define SV_TICKET_STRIDE 64
 #endif
@@ -30,7 +33,6 @@ namespace sv {
 constexpr int kThreads = 256;           // one workgroup = 4 wave64s
 constexpr int kWaves = kThreads / 64;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSampleSeg = 16;          // elements per thread in a sampler chunk
 constexpr int kMaxK = 64;               // longest linear draft
 constexpr int kTreeLdsPathEntries = 4096;  // path tables up to this many entries go to LDS
 constexpr int kTicketStride = SV_TICKET_STRIDE;
@@ -84,7 +86,13 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     g->U = U;
     g->chunk = kThreads * U * epv;
     g->S = (V + g->chunk - 1) / g->chunk;
-    g->chunk2 = kThreads * kSampleSeg;
+    // Sampler: 16, 32 or 64 consecutive tokens per thread; the smallest that
+    // keeps the sampler to about one round of resident workgroups.
+    int nsub = 1;
+    while (nsub < 4 && (long long)B * ((V + kThreads * 16 * nsub - 1) / (kThreads * 16 * nsub)) >
+                           SV_SAMPLER_WGS)
+        nsub <<= 1;
+    g->chunk2 = kThreads * 16 * nsub;
     g->S2 = (mode == 0) ? (V + g->chunk2 - 1) / g->chunk2 : 0;
 
     size_t off = 0;

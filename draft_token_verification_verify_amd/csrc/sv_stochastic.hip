@@ -172,28 +172,67 @@ struct Decision {
     double st, sd;
 };
 
+constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the merge
+
+// Row statistics of request b: sh_m[r] = row max, sh_s[r] = sum of
+// 2^((x - max) * c) in fp64 (chunks merged in order), sh_g[r] = tested logit.
+__device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s, float* sh_g) {
+    const int R = a.R, S = a.S, n = R * S;
+    const Partial16* p = a.partials + (size_t)b * n;
+    for (int r = threadIdx.x; r < R; r += kThreads) sh_g[r] = __builtin_nanf("");
+    __syncthreads();
+    if (n <= kMergeLds) {
+        // Every thread takes a few partials: one fp64 exponential each.
+        __shared__ float pm[kMergeLds];
+        __shared__ double ps[kMergeLds];
+        for (int t = threadIdx.x; t < n; t += kThreads) {
+            const Partial16 q = p[t];
+            pm[t] = q.f0;
+            ps[t] = q.d;
+            if (!__builtin_isnan(q.f1)) sh_g[t / S] = q.f1;  // one chunk per row holds it
+        }
+        __syncthreads();
+        for (int r = threadIdx.x; r < R; r += kThreads) {
+            float M = -INFINITY;
+            for (int ch = 0; ch < S; ++ch) M = fmaxf(M, pm[r * S + ch]);
+            sh_m[r] = M;
+        }
+        __syncthreads();
+        for (int t = threadIdx.x; t < n; t += kThreads) {
+            const float M = sh_m[t / S];
+            ps[t] = (M == -INFINITY) ? 0.0 : ps[t] * exp2_accurate(pm[t], M, a.sc);
+        }
+        __syncthreads();
+        for (int r = threadIdx.x; r < R; r += kThreads) {
+            double acc = 0.0;
+            for (int ch = 0; ch < S; ++ch) acc += ps[r * S + ch];  // fixed chunk order
+            sh_s[r] = acc;
+        }
+    } else {
+        for (int r = threadIdx.x; r < R; r += kThreads) {
+            const Partial16* q = p + (size_t)r * S;
+            float M = -INFINITY;
+            for (int ch = 0; ch < S; ++ch) {
+                M = fmaxf(M, q[ch].f0);
+                if (!__builtin_isnan(q[ch].f1)) sh_g[r] = q[ch].f1;
+            }
+            double acc = 0.0;
+            if (M != -INFINITY)
+                for (int ch = 0; ch < S; ++ch) acc += q[ch].d * exp2_accurate(q[ch].f0, M, a.sc);
+            sh_m[r] = M;
+            sh_s[r] = acc;
+        }
+    }
+    __syncthreads();
+}
+
 __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
     __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1];
     __shared__ double sh_s[2 * kMaxK + 1];
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
-    const int k = a.k, R = a.R, S = a.S;
-    for (int r = threadIdx.x; r < R; r += kThreads) {
-        const Partial16* p = a.partials + ((size_t)b * R + r) * S;
-        float M = -INFINITY, g = __builtin_nanf("");
-        for (int ch = 0; ch < S; ++ch) {
-            M = fmaxf(M, p[ch].f0);
-            if (!__builtin_isnan(p[ch].f1)) g = p[ch].f1;
-        }
-        double Ssum = 0.0;
-        if (M != -INFINITY)
-            for (int ch = 0; ch < S; ++ch)  // fixed chunk order
-                Ssum += p[ch].d * exp2_accurate(p[ch].f0, M, a.sc);
-        sh_m[r] = M;
-        sh_s[r] = Ssum;
-        sh_g[r] = g;
-    }
-    __syncthreads();
+    const int k = a.k;
+    merge_rows(a, b, sh_m, sh_s, sh_g);
     for (int i = threadIdx.x; i < k; i += kThreads) {
         const int32_t x = a.draft_tokens[(size_t)b * k + i];
         const float u = a.uniforms[(size_t)b * (k + 1) + i];
@@ -257,81 +296,76 @@ struct Weigher {
     }
 };
 
-// Weights of this thread's segment (kSampleSeg consecutive tokens) of the chunk
-// [lo, hi): w[] in ascending token order, first token id in *j0, count in *n.
-template <typename T, bool VEC>
-__device__ inline void segment_weights(const T* trow, const T* drow, const Weigher& W, int V,
-                                       int lo, int hi, double* w, int* j0, int* n) {
+constexpr int kSub = 16;  // tokens per sub-step of a sampler segment
+
+// Visit this thread's contiguous segment of the chunk [lo, hi) -- tokens
+// [lo + t * NSUB * 16, ...) -- in ascending order, 16 tokens per sub-step with
+// all loads of a sub-step issued together (clamped in bounds); f(j, w) is
+// called for every token of the segment inside the chunk.  drow == trow when
+// there is no residual.
+template <typename T, bool VEC, int NSUB, class F>
+__device__ inline void visit_segment(const T* trow, const T* drow, const Weigher& W, int lo,
+                                     int hi, F&& f) {
     constexpr int EPV = Elem<T>::kPerVec;
-    constexpr int SEG = kSampleSeg;
-    constexpr int NV = SEG / EPV;
-    const int start = lo + threadIdx.x * SEG;
-    *j0 = start;
-    *n = max(0, min(SEG, hi - start));
-    // Loads issue back to back from in-bounds (clamped) positions; positions
-    // past the chunk's end get weight 0.  drow == trow when there is no residual.
-    if constexpr (VEC) {
-        uint4 rt[NV], rd[NV];
+    constexpr int NV = kSub / EPV;
+    const int start = lo + (int)threadIdx.x * (NSUB * kSub);
+#pragma unroll 1
+    for (int sub = 0; sub < NSUB; ++sub) {
+        const int s0 = start + sub * kSub;
+        if constexpr (VEC) {
+            uint4 rt[NV], rd[NV];
 #pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            const int j = min(start + v * EPV, hi - EPV);
-            rt[v] = load16(trow + j);
-            rd[v] = load16(drow + j);
+            for (int v = 0; v < NV; ++v) {
+                const int j = max(lo, min(s0 + v * EPV, hi - EPV));
+                rt[v] = load16(trow + j);
+                rd[v] = load16(drow + j);
+            }
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                float xt[EPV], xd[EPV];
+                Elem<T>::widen(rt[v], xt);
+                Elem<T>::widen(rd[v], xd);
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    const int j = s0 + v * EPV + e;
+                    if (j < hi) f(j, W(xt[e], xd[e]));
+                }
+            }
+        } else {
+            float xt[kSub], xd[kSub];
+#pragma unroll
+            for (int e = 0; e < kSub; ++e) {
+                const int j = max(lo, min(s0 + e, hi - 1));
+                xt[e] = Elem<T>::load(trow, j);
+                xd[e] = Elem<T>::load(drow, j);
+            }
+#pragma unroll
+            for (int e = 0; e < kSub; ++e)
+                if (s0 + e < hi) f(s0 + e, W(xt[e], xd[e]));
         }
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-            float xt[EPV], xd[EPV];
-            Elem<T>::widen(rt[v], xt);
-            Elem<T>::widen(rd[v], xd);
-            const bool in = start + v * EPV < hi;
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) w[v * EPV + e] = in ? W(xt[e], xd[e]) : 0.0;
-        }
-    } else {
-        float xt[SEG], xd[SEG];
-#pragma unroll
-        for (int e = 0; e < SEG; ++e) {
-            const int j = min(start + e, hi - 1);
-            xt[e] = Elem<T>::load(trow, j);
-            xd[e] = Elem<T>::load(drow, j);
-        }
-#pragma unroll
-        for (int e = 0; e < SEG; ++e) w[e] = (start + e < hi) ? W(xt[e], xd[e]) : 0.0;
     }
-    (void)V;
 }
 
-template <typename T, bool VEC>
-__device__ double chunk_mass(const T* trow, const T* drow, const Weigher& W, int V, int lo,
-                             int hi, double* red) {
-    constexpr int SEG = kSampleSeg;
-    double w[SEG];
-    int j0, n;
-    segment_weights<T, VEC>(trow, drow, W, V, lo, hi, w, &j0, &n);
-    double acc = 0.0;
-#pragma unroll
-    for (int e = 0; e < SEG; ++e) acc += w[e];
-    acc = wave_reduce_sum(acc);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    __syncthreads();
-    if (lane == 0) red[wave] = acc;
-    __syncthreads();
-    double tot = 0.0;
-#pragma unroll
-    for (int q = 0; q < kWaves; ++q) tot += red[q];
-    __syncthreads();
-    return tot;
+// Sum of this thread's segment weights, and of the whole chunk (workgroup).
+template <typename T, bool VEC, int NSUB>
+__device__ double chunk_mass(const T* trow, const T* drow, const Weigher& W, int lo, int hi,
+                             double* seg_out, double* red) {
+    double seg = 0.0;
+    visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int, double w) { seg += w; });
+    *seg_out = seg;
+    return block_sum(seg, red);
 }
 
-template <typename T, bool VEC>
+// The last workgroup of request b: chunk holding u_k * Z, then the token in it.
+template <typename T, bool VEC, int NSUB>
 __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow, const T* drow,
                              Weigher W) {
-    constexpr int SEG = kSampleSeg;
     __shared__ double sh_wave[kWaves];
     __shared__ double sh_red[kWaves];
     __shared__ int sh_first;
     __shared__ double sh_base, sh_tau;
     __shared__ int sh_chunk;
+    __shared__ int sh_token;
     const int k = a.k;
     double* mass = a.mass + (size_t)b * a.S2;
     const double u = (double)a.uniforms[(size_t)b * (k + 1) + k];
@@ -345,20 +379,18 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
             const int c = threadIdx.x * G + g;
             if (c < a.S2) grp += load_coherent(&mass[c]);
         }
-        double incl = block_inclusive_scan(grp, sh_wave, &Z);
+        const double incl = block_inclusive_scan(grp, sh_wave, &Z);
         if (Z > 0.0 || pass == 1) {
             const double tau = u * Z;
-            if (threadIdx.x == 0) sh_first = kThreads;
-            __syncthreads();
-            if (incl > tau) atomicMin(&sh_first, (int)threadIdx.x);
-            __syncthreads();
             if (threadIdx.x == 0) {
+                sh_first = kThreads;
                 sh_tau = tau;
                 sh_chunk = -1;
             }
             __syncthreads();
-            int first = sh_first;
-            if (first < kThreads && (int)threadIdx.x == first) {
+            if (incl > tau) atomicMin(&sh_first, (int)threadIdx.x);
+            __syncthreads();
+            if ((int)threadIdx.x == sh_first) {
                 double run = incl - grp;
                 int lastc = -1;
                 double lastbase = 0.0;
@@ -399,54 +431,50 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
         }
         // Z == 0: the residual vanished (p_s == q_s); draw from p_s instead.
         W.residual = false;
+        drow = trow;
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-            double mc = chunk_mass<T, VEC>(trow, drow, W, a.V, lo, hi, sh_red);
+            double seg;
+            const double mc = chunk_mass<T, VEC, NSUB>(trow, drow, W, lo, hi, &seg, sh_red);
             if (threadIdx.x == 0) store_coherent(&mass[c], mc);
-            __syncthreads();
         }
-        // Make thread 0's fresh masses visible to every wave before rereading.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
 
-    // Token selection inside the chosen chunk.
+    // Token selection inside the chosen chunk: prefix over the per-thread
+    // segments, then one thread walks its segment.
     const int c = sh_chunk;
     const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    double w[SEG];
-    int j0, n;
-    segment_weights<T, VEC>(trow, drow, W, a.V, lo, hi, w, &j0, &n);
     double seg = 0.0;
-#pragma unroll
-    for (int e = 0; e < SEG; ++e) seg += w[e];
+    visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int, double w) { seg += w; });
     double chunk_total;
-    double incl = block_inclusive_scan(seg, sh_wave, &chunk_total);
+    const double incl = block_inclusive_scan(seg, sh_wave, &chunk_total);
     const double base = sh_base, tau = sh_tau;
-    if (threadIdx.x == 0) sh_first = kThreads;
+    if (threadIdx.x == 0) {
+        sh_first = kThreads;
+        sh_token = -1;
+    }
     __syncthreads();
     if (base + incl > tau) atomicMin(&sh_first, (int)threadIdx.x);
-    __syncthreads();
-    __shared__ int sh_token;
-    if (threadIdx.x == 0) sh_token = -1;
     __syncthreads();
     if ((int)threadIdx.x == sh_first) {
         double run = base + (incl - seg);
         int tok = -1, last_pos = -1;
-        for (int e = 0; e < SEG; ++e) {
-            if (e >= n) break;
-            if (w[e] > 0.0) last_pos = j0 + e;
-            run += w[e];
-            if (run > tau) { tok = j0 + e; break; }
-        }
+        visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int j, double w) {
+            if (tok >= 0) return;
+            if (w > 0.0) last_pos = j;
+            run += w;
+            if (run > tau) tok = j;
+        });
         sh_token = (tok >= 0) ? tok : last_pos;
     }
     __syncthreads();
     if (sh_token < 0) {
         // Rounding left u * Z past this chunk's total: the chunk's last positive weight.
         int last_pos = -1;
-        for (int e = 0; e < SEG; ++e)
-            if (e < n && w[e] > 0.0) last_pos = j0 + e;
+        visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int j, double w) {
+            if (w > 0.0) last_pos = j;
+        });
         if (last_pos >= 0) atomicMax(&sh_token, last_pos);
         __syncthreads();
     }
@@ -459,12 +487,11 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
     // other workgroup of the request has read the partials and stored its mass
     // before taking its ticket).
     __syncthreads();
-    for (int c = threadIdx.x; c < a.S2; c += kThreads) mass[c] = 0.0;
+    for (int cc = threadIdx.x; cc < a.S2; cc += kThreads) mass[cc] = 0.0;
     clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
 }
 
-
-template <typename T, bool VEC>
+template <typename T, bool VEC, int NSUB>
 __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     const int tile = blockIdx.x;
     const int b = tile / a.S2;
@@ -486,10 +513,11 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     __shared__ double red[kWaves];
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    const double mc = chunk_mass<T, VEC>(trow, drow, W, a.V, lo, hi, red);
+    double seg;
+    const double mc = chunk_mass<T, VEC, NSUB>(trow, drow, W, lo, hi, &seg, red);
     if (threadIdx.x == 0) store_coherent(&a.mass[(size_t)b * a.S2 + ch], mc);
     if (arrive_last(ticket_of(a.tickets, b), (uint32_t)a.S2, &last_flag))
-        sample_final<T, VEC>(a, b, dc.s, trow, drow, W);
+        sample_final<T, VEC, NSUB>(a, b, dc.s, trow, drow, W);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,7 +542,11 @@ static hipError_t launch_stats(const CallArgs& a, int U, hipStream_t st) {
 template <typename T, bool VEC>
 static hipError_t launch_sample(const CallArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
-    sample_kernel<T, VEC><<<grid, block, 0, st>>>(a);
+    switch (a.chunk2 / (kThreads * kSub)) {
+        case 4: sample_kernel<T, VEC, 4><<<grid, block, 0, st>>>(a); break;
+        case 2: sample_kernel<T, VEC, 2><<<grid, block, 0, st>>>(a); break;
+        default: sample_kernel<T, VEC, 1><<<grid, block, 0, st>>>(a); break;
+    }
     return hipGetLastError();
 }
 
