@@ -55,7 +55,8 @@ struct CallArgs {
     Scale sc;                // log2(e) / temperature
     Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, f1 = tested logit or NaN, d = sum
     uint32_t* tickets;       // per request (padded): sampler arrivals
-    double* mass;            // [B, S2]
+    double* mass;            // [B, S2]: stop-row mass per sampler chunk
+    double* segs;            // [B, S2, 256]: stop-row mass per thread segment
     int32_t* out_tokens;     // [B, k+1]
     int32_t* num_accepted;   // [B]
     float* p_at_draft;       // [B, k] or null
@@ -232,10 +233,15 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
     const int k = a.k;
+    const int i = threadIdx.x;  // test i runs in thread i (k <= 64)
+    int32_t x = 0;
+    float u = 0.f;
+    if (i < k) {  // issued before the merge so the loads overlap it
+        x = a.draft_tokens[(size_t)b * k + i];
+        u = a.uniforms[(size_t)b * (k + 1) + i];
+    }
     merge_rows(a, b, sh_m, sh_s, sh_g);
-    for (int i = threadIdx.x; i < k; i += kThreads) {
-        const int32_t x = a.draft_tokens[(size_t)b * k + i];
-        const float u = a.uniforms[(size_t)b * (k + 1) + i];
+    if (i < k) {
         double P = 0.0, Q = 0.0;
         int acc = 0;
         if (x >= 0 && x < a.V) {
@@ -252,17 +258,17 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     __syncthreads();
     if (threadIdx.x == 0) {
         int s = k;
-        for (int i = 0; i < k; ++i)
-            if (!sh_acc[i]) { s = i; break; }
+        for (int j = 0; j < k; ++j)
+            if (!sh_acc[j]) { s = j; break; }
         sh_stop = s;
         if (write_outputs) a.num_accepted[b] = s;
     }
     __syncthreads();
     const int s = sh_stop;
     if (write_outputs)
-        for (int i = threadIdx.x; i <= k; i += kThreads) {
-            if (i < s) a.out_tokens[(size_t)b * (k + 1) + i] = a.draft_tokens[(size_t)b * k + i];
-            else if (i > s) a.out_tokens[(size_t)b * (k + 1) + i] = -1;
+        for (int j = threadIdx.x; j <= k; j += kThreads) {
+            if (j < s) a.out_tokens[(size_t)b * (k + 1) + j] = a.draft_tokens[(size_t)b * k + j];
+            else if (j > s) a.out_tokens[(size_t)b * (k + 1) + j] = -1;
             // out_tokens[b, s] is written by the final draw.
         }
     out->s = s;
@@ -296,198 +302,193 @@ struct Weigher {
     }
 };
 
-constexpr int kSub = 16;  // tokens per sub-step of a sampler segment
+constexpr int kSub = 16;  // tokens per sampler sub-step
 
-// Visit this thread's contiguous segment of the chunk [lo, hi) -- tokens
-// [lo + t * NSUB * 16, ...) -- in ascending order, 16 tokens per sub-step with
-// all loads of a sub-step issued together (clamped in bounds); f(j, w) is
-// called for every token of the segment inside the chunk.  drow == trow when
-// there is no residual.
-template <typename T, bool VEC, int NSUB, class F>
-__device__ inline void visit_segment(const T* trow, const T* drow, const Weigher& W, int lo,
-                                     int hi, F&& f) {
-    constexpr int EPV = Elem<T>::kPerVec;
-    constexpr int NV = kSub / EPV;
-    const int start = lo + (int)threadIdx.x * (NSUB * kSub);
+// Sum of the weights of this thread's segment of the chunk [lo, hi): the
+// NSUB * 16 consecutive tokens from lo + t * NSUB * 16.  Each pass issues up to
+// four 16-byte loads per row back to back (clamped in bounds; slots past hi are
+// masked).  drow == trow when there is no residual.
+template <typename T, bool VEC, int NSUB>
+__device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, int lo, int hi) {
+    constexpr int SEG = NSUB * kSub;
+    const int start = lo + (int)threadIdx.x * SEG;
+    double seg = 0.0;
+    if constexpr (VEC) {
+        constexpr int EPV = Elem<T>::kPerVec;
+        constexpr int NV = SEG / EPV;                  // vectors per row in the segment
+        constexpr int NVP = NV < 4 ? NV : 4;           // vectors per row per pass
 #pragma unroll 1
-    for (int sub = 0; sub < NSUB; ++sub) {
-        const int s0 = start + sub * kSub;
-        if constexpr (VEC) {
-            uint4 rt[NV], rd[NV];
+        for (int v0 = 0; v0 < NV; v0 += NVP) {
+            uint4 rt[NVP], rd[NVP];
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
-                const int j = max(lo, min(s0 + v * EPV, hi - EPV));
+            for (int v = 0; v < NVP; ++v) {
+                const int j = max(lo, min(start + (v0 + v) * EPV, hi - EPV));
                 rt[v] = load16(trow + j);
                 rd[v] = load16(drow + j);
             }
 #pragma unroll
-            for (int v = 0; v < NV; ++v) {
+            for (int v = 0; v < NVP; ++v) {
                 float xt[EPV], xd[EPV];
                 Elem<T>::widen(rt[v], xt);
                 Elem<T>::widen(rd[v], xd);
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const int j = s0 + v * EPV + e;
-                    if (j < hi) f(j, W(xt[e], xd[e]));
-                }
+                for (int e = 0; e < EPV; ++e)
+                    if (start + (v0 + v) * EPV + e < hi) seg += W(xt[e], xd[e]);
             }
-        } else {
+        }
+    } else {
+#pragma unroll 1
+        for (int s0 = 0; s0 < SEG; s0 += kSub) {
             float xt[kSub], xd[kSub];
 #pragma unroll
             for (int e = 0; e < kSub; ++e) {
-                const int j = max(lo, min(s0 + e, hi - 1));
+                const int j = max(lo, min(start + s0 + e, hi - 1));
                 xt[e] = Elem<T>::load(trow, j);
                 xd[e] = Elem<T>::load(drow, j);
             }
 #pragma unroll
             for (int e = 0; e < kSub; ++e)
-                if (s0 + e < hi) f(s0 + e, W(xt[e], xd[e]));
+                if (start + s0 + e < hi) seg += W(xt[e], xd[e]);
         }
     }
+    return seg;
 }
 
-// Sum of this thread's segment weights, and of the whole chunk (workgroup).
-template <typename T, bool VEC, int NSUB>
-__device__ double chunk_mass(const T* trow, const T* drow, const Weigher& W, int lo, int hi,
-                             double* seg_out, double* red) {
-    double seg = 0.0;
-    visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int, double w) { seg += w; });
-    *seg_out = seg;
-    return block_sum(seg, red);
+// Wait until this thread's global stores have completed.
+__device__ inline void wait_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// The last workgroup of request b: chunk holding u_k * Z, then the token in it.
+// The last workgroup of request b: the chunk holding u_k * Z (prefix over the
+// chunk masses), the thread segment inside it (prefix over the stored segment
+// sums), then the token inside that segment (prefix over its weights, one token
+// per lane of wave 0).  Each level takes the first entry whose running mass
+// exceeds u_k * Z; where rounding leaves every running mass at or below it, the
+// last entry with positive mass.
 template <typename T, bool VEC, int NSUB>
 __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow, const T* drow,
                              Weigher W) {
+    constexpr int SEG = NSUB * kSub;
+    static_assert(SEG <= 64, "one segment per wave");
     __shared__ double sh_wave[kWaves];
-    __shared__ double sh_red[kWaves];
-    __shared__ int sh_first;
-    __shared__ double sh_base, sh_tau;
+    __shared__ int sh_first, sh_last;
+    __shared__ double sh_base, sh_run0;
     __shared__ int sh_chunk;
-    __shared__ int sh_token;
     const int k = a.k;
+    const int tid = threadIdx.x;
     double* mass = a.mass + (size_t)b * a.S2;
+    double* segs = a.segs + (size_t)b * a.S2 * kThreads;
     const double u = (double)a.uniforms[(size_t)b * (k + 1) + k];
 
-    // Chunk selection: thread t owns a contiguous group of chunk masses.
+    // Chunk masses: thread t owns a contiguous group of G chunks.
     const int G = (a.S2 + kThreads - 1) / kThreads;
-    double Z = 0.0;
-    for (int pass = 0; pass < 2; ++pass) {
-        double grp = 0.0;
-        for (int g = 0; g < G; ++g) {
-            const int c = threadIdx.x * G + g;
-            if (c < a.S2) grp += load_coherent(&mass[c]);
-        }
-        const double incl = block_inclusive_scan(grp, sh_wave, &Z);
-        if (Z > 0.0 || pass == 1) {
-            const double tau = u * Z;
-            if (threadIdx.x == 0) {
-                sh_first = kThreads;
-                sh_tau = tau;
-                sh_chunk = -1;
-            }
-            __syncthreads();
-            if (incl > tau) atomicMin(&sh_first, (int)threadIdx.x);
-            __syncthreads();
-            if ((int)threadIdx.x == sh_first) {
-                double run = incl - grp;
-                int lastc = -1;
-                double lastbase = 0.0;
-                for (int g = 0; g < G; ++g) {
-                    const int c = threadIdx.x * G + g;
-                    if (c >= a.S2) break;
-                    const double mc = load_coherent(&mass[c]);
-                    if (mc > 0.0) { lastc = c; lastbase = run; }
-                    if (run + mc > tau) {
-                        lastc = c;
-                        lastbase = run;
-                        break;
-                    }
-                    run += mc;
-                }
-                // Rounding can leave the walk short of tau: stay in this group.
-                if (lastc >= 0) {
-                    sh_chunk = lastc;
-                    sh_base = lastbase;
-                }
-            }
-            __syncthreads();
-            if (sh_chunk < 0 && threadIdx.x == 0) {
-                // u * Z at or past the total (rounding): the last chunk with mass.
-                double run = 0.0;
-                int lastc = 0;
-                double lastbase = 0.0;
-                for (int c = 0; c < a.S2; ++c) {
-                    const double mc = load_coherent(&mass[c]);
-                    if (mc > 0.0) { lastc = c; lastbase = run; }
-                    run += mc;
-                }
-                sh_chunk = lastc;
-                sh_base = lastbase;
-            }
-            __syncthreads();
-            break;
-        }
-        // Z == 0: the residual vanished (p_s == q_s); draw from p_s instead.
+    double grp = 0.0, Z = 0.0;
+    for (int g = 0; g < G; ++g) {
+        const int c = tid * G + g;
+        if (c < a.S2) grp += load_coherent(&mass[c]);
+    }
+    double incl = block_inclusive_scan(grp, sh_wave, &Z);
+    bool recompute = false;
+    if (!(Z > 0.0)) {
+        // The residual vanished (p_s == q_s): draw from p_s instead.
         W.residual = false;
         drow = trow;
+        recompute = true;
+        __shared__ double sh_red[kWaves];
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-            double seg;
-            const double mc = chunk_mass<T, VEC, NSUB>(trow, drow, W, lo, hi, &seg, sh_red);
-            if (threadIdx.x == 0) store_coherent(&mass[c], mc);
+            const double mc = block_sum(segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi), sh_red);
+            if (tid == 0) store_coherent(&mass[c], mc);
         }
+        wait_stores();
         __syncthreads();
+        grp = 0.0;
+        for (int g = 0; g < G; ++g) {
+            const int c = tid * G + g;
+            if (c < a.S2) grp += load_coherent(&mass[c]);
+        }
+        incl = block_inclusive_scan(grp, sh_wave, &Z);
     }
+    const double tau = u * Z;
+    if (tid == 0) {
+        sh_first = kThreads;
+        sh_last = -1;
+    }
+    __syncthreads();
+    if (incl > tau) atomicMin(&sh_first, tid);
+    if (grp > 0.0) atomicMax(&sh_last, tid);
+    __syncthreads();
+    {
+        const bool over = sh_first < kThreads;
+        const int owner = over ? sh_first : max(sh_last, 0);
+        if (tid == owner) {
+            double run = incl - grp;
+            int pick = -1, lastpos = -1;
+            double pick_base = 0.0, last_base = 0.0;
+            for (int g = 0; g < G; ++g) {
+                const int c = tid * G + g;
+                if (c >= a.S2) break;
+                const double mc = load_coherent(&mass[c]);
+                if (mc > 0.0) { lastpos = c; last_base = run; }
+                if (over && mc > 0.0 && run + mc > tau) { pick = c; pick_base = run; break; }
+                run += mc;
+            }
+            if (pick < 0) { pick = max(lastpos, tid * G); pick_base = last_base; }
+            sh_chunk = pick;
+            sh_base = pick_base;
+        }
+    }
+    __syncthreads();
 
-    // Token selection inside the chosen chunk: prefix over the per-thread
-    // segments, then one thread walks its segment.
+    // Segment inside the chunk.
     const int c = sh_chunk;
     const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    double seg = 0.0;
-    visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int, double w) { seg += w; });
+    const double seg = recompute ? segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi)
+                                 : load_coherent(&segs[(size_t)c * kThreads + tid]);
     double chunk_total;
-    const double incl = block_inclusive_scan(seg, sh_wave, &chunk_total);
-    const double base = sh_base, tau = sh_tau;
-    if (threadIdx.x == 0) {
+    const double sincl = sh_base + block_inclusive_scan(seg, sh_wave, &chunk_total);
+    if (tid == 0) {
         sh_first = kThreads;
-        sh_token = -1;
+        sh_last = -1;
     }
     __syncthreads();
-    if (base + incl > tau) atomicMin(&sh_first, (int)threadIdx.x);
+    if (sincl > tau && seg > 0.0) atomicMin(&sh_first, tid);
+    if (seg > 0.0) atomicMax(&sh_last, tid);
     __syncthreads();
-    if ((int)threadIdx.x == sh_first) {
-        double run = base + (incl - seg);
-        int tok = -1, last_pos = -1;
-        visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int j, double w) {
-            if (tok >= 0) return;
-            if (w > 0.0) last_pos = j;
-            run += w;
-            if (run > tau) tok = j;
-        });
-        sh_token = (tok >= 0) ? tok : last_pos;
-    }
+    const bool over = sh_first < kThreads;
+    const int t = over ? sh_first : max(sh_last, 0);
+    if (tid == t) sh_run0 = sincl - seg;
     __syncthreads();
-    if (sh_token < 0) {
-        // Rounding left u * Z past this chunk's total: the chunk's last positive weight.
-        int last_pos = -1;
-        visit_segment<T, VEC, NSUB>(trow, drow, W, lo, hi, [&](int j, double w) {
-            if (w > 0.0) last_pos = j;
-        });
-        if (last_pos >= 0) atomicMax(&sh_token, last_pos);
-        __syncthreads();
+
+    // Token inside the segment: lane l of wave 0 weighs token lo + t * SEG + l.
+    if (tid < 64) {
+        const int lane = tid;
+        const int j = lo + t * SEG + lane;
+        double w = 0.0;
+        if (lane < SEG && j < hi) w = W(Elem<T>::load(trow, j), Elem<T>::load(drow, j));
+        double x = w;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double y = __shfl_up(x, off, 64);
+            if (lane >= off) x += y;
+        }
+        const double run = sh_run0 + x;
+        const unsigned long long hit = __ballot(over && w > 0.0 && run > tau);
+        const unsigned long long pos = __ballot(w > 0.0);
+        int sel;
+        if (hit) sel = __ffsll((long long)hit) - 1;
+        else if (pos) sel = 63 - __clzll((long long)pos);
+        else sel = 0;  // no positive weight anywhere: unreachable with finite logits
+        if (lane == 0) a.out_tokens[(size_t)b * (k + 1) + s_row] = lo + t * SEG + sel;
     }
-    if (threadIdx.x == 0) {
-        int tok = sh_token;
-        if (tok < 0) tok = lo;  // no positive weight anywhere: unreachable with finite logits
-        a.out_tokens[(size_t)b * (k + 1) + s_row] = tok;
-    }
+
     // Leave this request's part of the workspace zero for later calls (every
-    // other workgroup of the request has read the partials and stored its mass
-    // before taking its ticket).
-    __syncthreads();
-    for (int cc = threadIdx.x; cc < a.S2; cc += kThreads) mass[cc] = 0.0;
+    // other workgroup of the request has finished reading and writing it before
+    // taking its ticket).
+    for (int cc = tid; cc < a.S2; cc += kThreads) mass[cc] = 0.0;
+    for (size_t i = tid; i < (size_t)a.S2 * kThreads; i += kThreads) segs[i] = 0.0;
     clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
 }
 
@@ -513,9 +514,13 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     __shared__ double red[kWaves];
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    double seg;
-    const double mc = chunk_mass<T, VEC, NSUB>(trow, drow, W, lo, hi, &seg, red);
+    const double seg = segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi);
+    store_coherent(&a.segs[((size_t)b * a.S2 + ch) * kThreads + threadIdx.x], seg);
+    const double mc = block_sum(seg, red);
     if (threadIdx.x == 0) store_coherent(&a.mass[(size_t)b * a.S2 + ch], mc);
+    // Every thread's stores complete before the ticket is taken.
+    wait_stores();
+    __syncthreads();
     if (arrive_last(ticket_of(a.tickets, b), (uint32_t)a.S2, &last_flag))
         sample_final<T, VEC, NSUB>(a, b, dc.s, trow, drow, W);
 }
@@ -570,6 +575,7 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
     a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_tickets);
     a.mass = reinterpret_cast<double*>(ws + g.off_mass);
+    a.segs = reinterpret_cast<double*>(ws + g.off_segs);
     a.out_tokens = call.out_tokens;
     a.num_accepted = call.num_accepted;
     a.p_at_draft = call.p_at_draft;
