@@ -53,7 +53,7 @@ struct Geometry {
     int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8
     int S2;          // stop-row chunks per request (stochastic sampler)
     int chunk2;      // elements per stop-row chunk
-    size_t off_tickets, off_partials, off_mass, off_segs, bytes;
+    size_t off_tickets, off_partials, off_segs, bytes;
 };
 
 // log2(e) / temperature, the factor that turns a logit difference into a
@@ -100,10 +100,8 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     off = align_up(off + (mode == 0 ? sizeof(uint32_t) * kTicketStride * (size_t)B : 0), 256);
     g->off_partials = off;
     off = align_up(off + 16 * (size_t)rows * (size_t)g->S, 256);
-    g->off_mass = off;
-    off = align_up(off + (mode == 0 ? sizeof(double) * (size_t)B * (size_t)g->S2 : 0), 256);
     g->off_segs = off;
-    off = align_up(off + sizeof(double) * (size_t)B * (size_t)g->S2 * kThreads, 256);
+    off = align_up(off + sizeof(double) * (size_t)B * (size_t)g->S2 * (g->chunk2 / 64), 256);
     g->bytes = off;
     return true;
 }

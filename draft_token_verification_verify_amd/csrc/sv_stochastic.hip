@@ -15,22 +15,22 @@
 //            Each thread sums its own elements against its own maximum (so a
 //            row's largest logits, each usually the maximum of its thread,
 //            contribute an exact 1) in fp64, and threads are merged with fp64
-//            scale factors.  A tile of a test row also publishes the raw logit
-//            of the tested draft token when that token falls inside it.
+//            scale factors.
 //   sample:  one workgroup per (request, stop-row chunk).  Every workgroup of a
 //            request first merges that request's partials (chunk order, fp64),
-//            computes p_i(x_i) and q_i(x_i), runs the k tests (independent given
-//            the uniforms) and takes the first failure as the stop row s; the
-//            chunk-0 workgroup writes the accepted drafts, the -1 padding,
-//            num_accepted and the probabilities.  Each workgroup then computes
-//            its chunk's share of the final distribution's mass (residual
-//            max(0, p_s - q_s) or bonus p_k) in fp64 -- tokens within 2^-8 of
-//            the row maximum take an fp64 exponential, the rest fp32 -- and the
-//            last of the request's workgroups (arrival ticket) picks the chunk
-//            holding u_k * Z by a prefix sum over the chunk masses, then the
-//            token inside that chunk by a prefix sum over per-thread segments
-//            and a walk through one segment (ascending vocabulary order: the
-//            smallest j whose running mass exceeds u_k * Z).
+//            gathers the tested logits, computes p_i(x_i) and q_i(x_i), runs the
+//            k tests (independent given the uniforms) and takes the first
+//            failure as the stop row s; the chunk-0 workgroup writes the
+//            accepted drafts, the -1 padding, num_accepted and the
+//            probabilities.  Each workgroup then weighs its chunk of the final
+//            distribution (residual max(0, p_s - q_s) or bonus p_k) in fp64 --
+//            tokens within 2^-8 of the row maximum take an fp64 exponential,
+//            the rest fp32 -- and stores the mass of every 64-token segment.
+//            The last of the request's workgroups (arrival ticket) finds the
+//            segment holding u_k * Z by a prefix sum over the segment masses,
+//            then the token inside it by a wave-wide prefix sum (ascending
+//            vocabulary order: the smallest j whose running mass exceeds
+//            u_k * Z).
 // The streaming kernel has no atomics or fences: the kernel boundary publishes
 // its partials to the sampler.
 //
@@ -53,10 +53,9 @@ struct CallArgs {
     int R, S, chunk;         // streaming geometry: rows per request, chunks per row
     int S2, chunk2;          // sampler geometry: chunks per stop row
     Scale sc;                // log2(e) / temperature
-    Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, f1 = tested logit or NaN, d = sum
+    Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, d = sum (f1 unused)
     uint32_t* tickets;       // per request (padded): sampler arrivals
-    double* mass;            // [B, S2]: stop-row mass per sampler chunk
-    double* segs;            // [B, S2, 256]: stop-row mass per thread segment
+    double* segs;            // [B, S2 * chunk2 / 64]: stop-row mass per 64-token segment
     int32_t* out_tokens;     // [B, k+1]
     int32_t* num_accepted;   // [B]
     float* p_at_draft;       // [B, k] or null
@@ -80,37 +79,23 @@ struct StatsOp : CallArgs {
         return static_cast<const T*>(draft) + ((size_t)b * k + (r - k - 1)) * (size_t)V;
     }
 
-    // Draft token tested on row r of request b, or -1 for the bonus row.
-    __device__ int token_of_row(int b, int r) const {
-        if (r == k) return -1;
-        const int i = (r < k) ? r : r - k - 1;
-        return draft_tokens[(size_t)b * k + i];
-    }
-
     // Workgroup reduction of per-thread (max m, fp64 sum s against m) into the
     // tile's (M, S): every thread's sum is rescaled to the common M with an fp64
     // exponential, then summed in fixed order.
-    __device__ void finish(float m, double s, float gx, float* f0, float* f1, double* d) const {
+    __device__ void finish(float m, double s, float* f0, float* f1, double* d) const {
         __shared__ float red_f[kWaves];
         __shared__ double red_d[kWaves];
         const float M = block_max(m, red_f);
         const double f = (m == -INFINITY) ? 0.0 : exp2_accurate(m, M, sc);
         const double Ssum = block_sum(s * f, red_d);
         *f0 = M;
-        *f1 = gx;
+        *f1 = 0.f;
         *d = Ssum;
     }
 
     __device__ void tile(int b, int r, int lo, int hi, const uint4* raw, int nvec, float* f0,
                          float* f1, double* d) const {
         constexpr int EPV = Elem<T>::kPerVec;
-        // Thread 0 fetches the tested token's logit early (it is in this tile's
-        // lines, so the load overlaps the arithmetic).
-        float gx = __builtin_nanf("");
-        if (threadIdx.x == 0) {
-            const int x = token_of_row(b, r);
-            if (x >= lo && x < hi) gx = Elem<T>::load(row(b, r), x);
-        }
         float x[U][EPV];
 #pragma unroll
         for (int j = 0; j < U; ++j) Elem<T>::widen(raw[j], x[j]);
@@ -132,24 +117,19 @@ struct StatsOp : CallArgs {
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[j][e] - ms, sc));
-        finish(m, s, gx, f0, f1, d);
+        finish(m, s, f0, f1, d);
     }
 
     __device__ void tile_scalar(int b, int r, int lo, int hi, float* f0, float* f1,
                                 double* d) const {
         const T* p = row(b, r);
-        float gx = __builtin_nanf("");
-        if (threadIdx.x == 0) {
-            const int x = token_of_row(b, r);
-            if (x >= lo && x < hi) gx = Elem<T>::load(p, x);
-        }
         float m = -INFINITY;
         for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, Elem<T>::load(p, j));
         const float ms = (m == -INFINITY) ? 0.f : m;
         double s = 0.0;
         for (int j = lo + threadIdx.x; j < hi; j += kThreads)
             s += (double)fast_exp2(scaled(Elem<T>::load(p, j) - ms, sc));
-        finish(m, s, gx, f0, f1, d);
+        finish(m, s, f0, f1, d);
     }
 };
 
@@ -176,12 +156,10 @@ struct Decision {
 constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the merge
 
 // Row statistics of request b: sh_m[r] = row max, sh_s[r] = sum of
-// 2^((x - max) * c) in fp64 (chunks merged in order), sh_g[r] = tested logit.
-__device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s, float* sh_g) {
+// 2^((x - max) * c) in fp64 (chunks merged in order).
+__device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) {
     const int R = a.R, S = a.S, n = R * S;
     const Partial16* p = a.partials + (size_t)b * n;
-    for (int r = threadIdx.x; r < R; r += kThreads) sh_g[r] = __builtin_nanf("");
-    __syncthreads();
     if (n <= kMergeLds) {
         // Every thread takes a few partials: one fp64 exponential each.
         __shared__ float pm[kMergeLds];
@@ -190,7 +168,6 @@ __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s, 
             const Partial16 q = p[t];
             pm[t] = q.f0;
             ps[t] = q.d;
-            if (!__builtin_isnan(q.f1)) sh_g[t / S] = q.f1;  // one chunk per row holds it
         }
         __syncthreads();
         for (int r = threadIdx.x; r < R; r += kThreads) {
@@ -213,10 +190,7 @@ __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s, 
         for (int r = threadIdx.x; r < R; r += kThreads) {
             const Partial16* q = p + (size_t)r * S;
             float M = -INFINITY;
-            for (int ch = 0; ch < S; ++ch) {
-                M = fmaxf(M, q[ch].f0);
-                if (!__builtin_isnan(q[ch].f1)) sh_g[r] = q[ch].f1;
-            }
+            for (int ch = 0; ch < S; ++ch) M = fmaxf(M, q[ch].f0);
             double acc = 0.0;
             if (M != -INFINITY)
                 for (int ch = 0; ch < S; ++ch) acc += q[ch].d * exp2_accurate(q[ch].f0, M, a.sc);
@@ -227,20 +201,34 @@ __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s, 
     __syncthreads();
 }
 
+template <typename T>
 __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
     __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1];
     __shared__ double sh_s[2 * kMaxK + 1];
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
     const int k = a.k;
+    // Wave 1 gathers the tested logits target[b, i, x_i] and draft[b, i, x_i]
+    // while wave 0 merges the partials.
+    if (threadIdx.x >= 64 && threadIdx.x < 64 + k) {
+        const int i = threadIdx.x - 64;
+        const int32_t x = a.draft_tokens[(size_t)b * k + i];
+        float gt = -INFINITY, gd = -INFINITY;
+        if (x >= 0 && x < a.V) {
+            gt = Elem<T>::load(static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + i) * (size_t)a.V, x);
+            gd = Elem<T>::load(static_cast<const T*>(a.draft) + ((size_t)b * k + i) * (size_t)a.V, x);
+        }
+        sh_g[i] = gt;
+        sh_g[k + 1 + i] = gd;
+    }
     const int i = threadIdx.x;  // test i runs in thread i (k <= 64)
     int32_t x = 0;
     float u = 0.f;
-    if (i < k) {  // issued before the merge so the loads overlap it
+    if (i < k) {
         x = a.draft_tokens[(size_t)b * k + i];
         u = a.uniforms[(size_t)b * (k + 1) + i];
     }
-    merge_rows(a, b, sh_m, sh_s, sh_g);
+    merge_rows(a, b, sh_m, sh_s);
     if (i < k) {
         double P = 0.0, Q = 0.0;
         int acc = 0;
@@ -361,55 +349,67 @@ __device__ inline void wait_stores() {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// The last workgroup of request b: the chunk holding u_k * Z (prefix over the
-// chunk masses), the thread segment inside it (prefix over the stored segment
-// sums), then the token inside that segment (prefix over its weights, one token
-// per lane of wave 0).  Each level takes the first entry whose running mass
-// exceeds u_k * Z; where rounding leaves every running mass at or below it, the
-// last entry with positive mass.
+// The stop row's mass is kept per 64-token segment (segment f covers tokens
+// [64 f, 64 f + 64)), in vocabulary order: the 4 / NSUB threads that weigh one
+// segment add their sums (in thread order) and the first of them stores it.
+constexpr int kStoredSeg = 64;
+constexpr int kRegSegs = 10;  // stored segments a thread of the final draw keeps in registers
+
+template <int NSUB>
+__device__ inline void store_segment(double* req_segs, int ch, int chunk2, double seg) {
+    constexpr int P = kStoredSeg / (NSUB * kSub);  // threads per stored segment
+    static_assert(P >= 1 && P * NSUB * kSub == kStoredSeg, "segment split");
+    if constexpr (P >= 2) seg += __shfl_down(seg, 1, 64);
+    if constexpr (P >= 4) seg += __shfl_down(seg, 2, 64);
+    if (threadIdx.x % P == 0)
+        store_coherent(&req_segs[(size_t)ch * (chunk2 / kStoredSeg) + threadIdx.x / P], seg);
+}
+
+// The last workgroup of request b draws the token.  The request's n stored
+// segment sums are split into 256 runs of G = ceil(n / 256) consecutive sums,
+// one run per thread: a prefix sum over the runs finds the run holding u_k * Z,
+// its owner walks it to the segment, and wave 0 walks that segment's tokens
+// with a wave-wide prefix sum, one token per lane.  Each level takes the first
+// entry with positive weight whose running mass exceeds u_k * Z; where rounding
+// leaves every running mass at or below it, the last entry with positive weight.
 template <typename T, bool VEC, int NSUB>
 __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow, const T* drow,
                              Weigher W) {
-    constexpr int SEG = NSUB * kSub;
-    static_assert(SEG <= 64, "one segment per wave");
     __shared__ double sh_wave[kWaves];
-    __shared__ int sh_first, sh_last;
-    __shared__ double sh_base, sh_run0;
-    __shared__ int sh_chunk;
+    __shared__ int sh_first, sh_last, sh_seg;
+    __shared__ double sh_run0;
     const int k = a.k;
     const int tid = threadIdx.x;
-    double* mass = a.mass + (size_t)b * a.S2;
-    double* segs = a.segs + (size_t)b * a.S2 * kThreads;
+    const int n = a.S2 * (a.chunk2 / kStoredSeg);
+    const int G = (n + kThreads - 1) / kThreads;
+    const int first = tid * G;
+    const int len = max(0, min(G, n - first));   // this thread's run: [first, first + len)
+    double* segs = a.segs + (size_t)b * n;
     const double u = (double)a.uniforms[(size_t)b * (k + 1) + k];
 
-    // Chunk masses: thread t owns a contiguous group of G chunks.
-    const int G = (a.S2 + kThreads - 1) / kThreads;
-    double grp = 0.0, Z = 0.0;
-    for (int g = 0; g < G; ++g) {
-        const int c = tid * G + g;
-        if (c < a.S2) grp += load_coherent(&mass[c]);
-    }
-    double incl = block_inclusive_scan(grp, sh_wave, &Z);
-    bool recompute = false;
-    if (!(Z > 0.0)) {
+    double v[kRegSegs];
+    double grp, incl, Z;
+    for (int pass = 0;; ++pass) {
+        // All loads of the run are issued together (clamped in bounds, masked).
+#pragma unroll
+        for (int g = 0; g < kRegSegs; ++g) v[g] = load_coherent(segs + min(first + g, n - 1));
+#pragma unroll
+        for (int g = 0; g < kRegSegs; ++g) v[g] = (g < len) ? v[g] : 0.0;
+        grp = 0.0;
+#pragma unroll
+        for (int g = 0; g < kRegSegs; ++g) grp += v[g];
+        for (int g = kRegSegs; g < len; ++g) grp += load_coherent(segs + first + g);
+        incl = block_inclusive_scan(grp, sh_wave, &Z);
+        if (Z > 0.0 || pass == 1) break;
         // The residual vanished (p_s == q_s): draw from p_s instead.
         W.residual = false;
         drow = trow;
-        recompute = true;
-        __shared__ double sh_red[kWaves];
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-            const double mc = block_sum(segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi), sh_red);
-            if (tid == 0) store_coherent(&mass[c], mc);
+            store_segment<NSUB>(segs, c, a.chunk2, segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi));
         }
         wait_stores();
         __syncthreads();
-        grp = 0.0;
-        for (int g = 0; g < G; ++g) {
-            const int c = tid * G + g;
-            if (c < a.S2) grp += load_coherent(&mass[c]);
-        }
-        incl = block_inclusive_scan(grp, sh_wave, &Z);
     }
     const double tau = u * Z;
     if (tid == 0) {
@@ -417,57 +417,48 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
         sh_last = -1;
     }
     __syncthreads();
-    if (incl > tau) atomicMin(&sh_first, tid);
+    if (grp > 0.0 && incl > tau) atomicMin(&sh_first, tid);
     if (grp > 0.0) atomicMax(&sh_last, tid);
     __syncthreads();
-    {
-        const bool over = sh_first < kThreads;
-        const int owner = over ? sh_first : max(sh_last, 0);
-        if (tid == owner) {
-            double run = incl - grp;
-            int pick = -1, lastpos = -1;
-            double pick_base = 0.0, last_base = 0.0;
-            for (int g = 0; g < G; ++g) {
-                const int c = tid * G + g;
-                if (c >= a.S2) break;
-                const double mc = load_coherent(&mass[c]);
-                if (mc > 0.0) { lastpos = c; last_base = run; }
-                if (over && mc > 0.0 && run + mc > tau) { pick = c; pick_base = run; break; }
-                run += mc;
-            }
-            if (pick < 0) { pick = max(lastpos, tid * G); pick_base = last_base; }
-            sh_chunk = pick;
-            sh_base = pick_base;
-        }
-    }
-    __syncthreads();
-
-    // Segment inside the chunk.
-    const int c = sh_chunk;
-    const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    const double seg = recompute ? segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi)
-                                 : load_coherent(&segs[(size_t)c * kThreads + tid]);
-    double chunk_total;
-    const double sincl = sh_base + block_inclusive_scan(seg, sh_wave, &chunk_total);
-    if (tid == 0) {
-        sh_first = kThreads;
-        sh_last = -1;
-    }
-    __syncthreads();
-    if (sincl > tau && seg > 0.0) atomicMin(&sh_first, tid);
-    if (seg > 0.0) atomicMax(&sh_last, tid);
-    __syncthreads();
     const bool over = sh_first < kThreads;
-    const int t = over ? sh_first : max(sh_last, 0);
-    if (tid == t) sh_run0 = sincl - seg;
+    const int owner = over ? sh_first : max(sh_last, 0);
+    if (tid == owner) {
+        double run = incl - grp, pick_base = 0.0, last_base = 0.0;
+        int pick = -1, lastpos = -1;
+#pragma unroll
+        for (int g = 0; g < kRegSegs; ++g) {
+            if (pick < 0) {
+                const double w = v[g];  // zero past the run
+                if (w > 0.0) {
+                    lastpos = g;
+                    last_base = run;
+                    if (over && run + w > tau) { pick = g; pick_base = run; }
+                }
+                run += w;
+            }
+        }
+        for (int g = kRegSegs; g < len && pick < 0; ++g) {
+            const double w = load_coherent(segs + first + g);
+            if (w > 0.0) {
+                lastpos = g;
+                last_base = run;
+                if (over && run + w > tau) { pick = g; pick_base = run; }
+            }
+            run += w;
+        }
+        if (pick < 0) { pick = max(lastpos, 0); pick_base = last_base; }
+        sh_seg = min(first + pick, n - 1);
+        sh_run0 = pick_base;
+    }
     __syncthreads();
 
-    // Token inside the segment: lane l of wave 0 weighs token lo + t * SEG + l.
+    // Token inside the segment: lane l of wave 0 weighs token 64 f + l.
     if (tid < 64) {
         const int lane = tid;
-        const int j = lo + t * SEG + lane;
+        const int base_tok = sh_seg * kStoredSeg;
+        const int j = base_tok + lane;
         double w = 0.0;
-        if (lane < SEG && j < hi) w = W(Elem<T>::load(trow, j), Elem<T>::load(drow, j));
+        if (j < a.V) w = W(Elem<T>::load(trow, j), Elem<T>::load(drow, j));
         double x = w;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -481,14 +472,13 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
         if (hit) sel = __ffsll((long long)hit) - 1;
         else if (pos) sel = 63 - __clzll((long long)pos);
         else sel = 0;  // no positive weight anywhere: unreachable with finite logits
-        if (lane == 0) a.out_tokens[(size_t)b * (k + 1) + s_row] = lo + t * SEG + sel;
+        if (lane == 0) a.out_tokens[(size_t)b * (k + 1) + s_row] = base_tok + sel;
     }
 
     // Leave this request's part of the workspace zero for later calls (every
     // other workgroup of the request has finished reading and writing it before
     // taking its ticket).
-    for (int cc = tid; cc < a.S2; cc += kThreads) mass[cc] = 0.0;
-    for (size_t i = tid; i < (size_t)a.S2 * kThreads; i += kThreads) segs[i] = 0.0;
+    for (int g = 0; g < len; ++g) segs[first + g] = 0.0;
     clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
 }
 
@@ -499,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     const int ch = tile % a.S2;
     const int k = a.k;
     Decision dc;
-    decide(a, b, ch == 0, &dc);
+    decide<T>(a, b, ch == 0, &dc);
     Weigher W;
     W.mt = dc.mt;
     W.inv_st = 1.0 / dc.st;
@@ -511,13 +501,10 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     const T* drow = W.residual
         ? static_cast<const T*>(a.draft) + ((size_t)b * k + dc.s) * (size_t)a.V
         : trow;
-    __shared__ double red[kWaves];
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
     const double seg = segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi);
-    store_coherent(&a.segs[((size_t)b * a.S2 + ch) * kThreads + threadIdx.x], seg);
-    const double mc = block_sum(seg, red);
-    if (threadIdx.x == 0) store_coherent(&a.mass[(size_t)b * a.S2 + ch], mc);
+    store_segment<NSUB>(a.segs + (size_t)b * a.S2 * (a.chunk2 / kStoredSeg), ch, a.chunk2, seg);
     // Every thread's stores complete before the ticket is taken.
     wait_stores();
     __syncthreads();
@@ -574,7 +561,6 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.sc = make_scale(call.temperature);
     a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
     a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_tickets);
-    a.mass = reinterpret_cast<double*>(ws + g.off_mass);
     a.segs = reinterpret_cast<double*>(ws + g.off_segs);
     a.out_tokens = call.out_tokens;
     a.num_accepted = call.num_accepted;
