@@ -101,7 +101,11 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     g->off_partials = off;
     off = align_up(off + 16 * (size_t)rows * (size_t)g->S, 256);
     g->off_segs = off;
-    off = align_up(off + sizeof(double) * (size_t)B * (size_t)g->S2 * (g->chunk2 / 64), 256);
+    // Stop-row segment masses: per request 256 runs of ceil(n / 256) slots for
+    // its n = S2 * chunk2 / 64 segments of 64 tokens.
+    const long long nseg = (long long)g->S2 * (g->chunk2 / 64);
+    off = align_up(off + sizeof(double) * (size_t)B * (size_t)((nseg + kThreads - 1) / kThreads) *
+                             kThreads, 256);
     g->bytes = off;
     return true;
 }
@@ -173,25 +177,97 @@ __device__ inline void merge_argmax(float& v, int& i, float v2, int i2) {
     i = take ? i2 : i;
 }
 
-// Fixed-order reductions (same result on every run).
+// ---------------------------------------------------------------------------
+// Cross-lane steps on DPP (lane permutations applied by the VALU operand
+// network, no LDS round trip).  A wave64 is four rows of 16 lanes.
+// ---------------------------------------------------------------------------
+namespace dpp {
+constexpr int kQuadSwap1 = 0xB1;      // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;      // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kRowHalfMirror = 0x141; // lane i <- lane 7 - i within each 8 lanes
+constexpr int kRowMirror = 0x140;     // lane i <- lane 15 - i within each row
+constexpr int kRowShr = 0x110;        // + n: lane i <- lane i - n in the row (else 0)
+constexpr int kRowShl = 0x100;        // + n: lane i <- lane i + n in the row (else 0)
+constexpr int kRowBcast15 = 0x142;    // row r + 1 <- lane 15 of row r
+constexpr int kRowBcast31 = 0x143;    // rows 2, 3 <- lane 31
+}  // namespace dpp
+
+// Lanes of disabled rows, and lanes whose source is outside their row, get 0.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline int dpp_i32(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xf, true);
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline float dpp_f32(float v) {
+    return __int_as_float(dpp_i32<CTRL, ROW_MASK>(__float_as_int(v)));
+}
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ inline double dpp_f64(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)dpp_i32<CTRL, ROW_MASK>((int)(unsigned)b);
+    const unsigned hi = (unsigned)dpp_i32<CTRL, ROW_MASK>((int)(unsigned)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline double readlane_f64(double v, int lane) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline float readlane_f32(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Fixed-order reductions (same result on every run); every lane gets the
+// result.  Within a row the butterfly leaves identical bits in all 16 lanes;
+// the four row results are then combined in row order.
 __device__ inline float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    v = fmaxf(v, dpp_f32<dpp::kQuadSwap1>(v));
+    v = fmaxf(v, dpp_f32<dpp::kQuadSwap2>(v));
+    v = fmaxf(v, dpp_f32<dpp::kRowHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<dpp::kRowMirror>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 __device__ inline void wave_reduce_argmax(float& v, int& i) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        float v2 = __shfl_xor(v, off, 64);
-        int i2 = __shfl_xor(i, off, 64);
-        merge_argmax(v, i, v2, i2);
+#define SV_ARGMAX_STEP(CTRL)                                                   \
+    {                                                                          \
+        const float v2 = dpp_f32<CTRL>(v);                                     \
+        const int i2 = dpp_i32<CTRL>(i);                                       \
+        merge_argmax(v, i, v2, i2);                                            \
     }
+    SV_ARGMAX_STEP(dpp::kQuadSwap1)
+    SV_ARGMAX_STEP(dpp::kQuadSwap2)
+    SV_ARGMAX_STEP(dpp::kRowHalfMirror)
+    SV_ARGMAX_STEP(dpp::kRowMirror)
+#undef SV_ARGMAX_STEP
+    float bv = readlane_f32(v, 0);
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r)
+        merge_argmax(bv, bi, readlane_f32(v, 16 * r), __builtin_amdgcn_readlane(i, 16 * r));
+    v = bv;
+    i = bi;
 }
 
 __device__ inline double wave_reduce_sum(double x) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    x += dpp_f64<dpp::kQuadSwap1>(x);
+    x += dpp_f64<dpp::kQuadSwap2>(x);
+    x += dpp_f64<dpp::kRowHalfMirror>(x);
+    x += dpp_f64<dpp::kRowMirror>(x);
+    return (readlane_f64(x, 0) + readlane_f64(x, 16)) + (readlane_f64(x, 32) + readlane_f64(x, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes in lane order: a scan inside each row
+// of 16, then the row totals carried forward by row broadcasts.
+__device__ inline double wave_inclusive_scan(double x) {
+    x += dpp_f64<dpp::kRowShr + 1>(x);
+    x += dpp_f64<dpp::kRowShr + 2>(x);
+    x += dpp_f64<dpp::kRowShr + 4>(x);
+    x += dpp_f64<dpp::kRowShr + 8>(x);
+    x += dpp_f64<dpp::kRowBcast15, 0xa>(x);
+    x += dpp_f64<dpp::kRowBcast31, 0xc>(x);
     return x;
 }
 
@@ -224,11 +300,7 @@ __device__ inline double block_sum(double v, double* sh) {
 // *total receives the workgroup total.
 __device__ inline double block_inclusive_scan(double x, double* wave_tot, double* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        double y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    x = wave_inclusive_scan(x);
     if (lane == 63) wave_tot[wave] = x;
     __syncthreads();
     double before = 0.0, all = 0.0;

@@ -55,7 +55,7 @@ struct CallArgs {
     Scale sc;                // log2(e) / temperature
     Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, d = sum (f1 unused)
     uint32_t* tickets;       // per request (padded): sampler arrivals
-    double* segs;            // [B, S2 * chunk2 / 64]: stop-row mass per 64-token segment
+    double* segs;            // per request: stop-row mass per 64-token segment, run-major
     int32_t* out_tokens;     // [B, k+1]
     int32_t* num_accepted;   // [B]
     float* p_at_draft;       // [B, k] or null
@@ -350,55 +350,71 @@ __device__ inline void wait_stores() {
 }
 
 // The stop row's mass is kept per 64-token segment (segment f covers tokens
-// [64 f, 64 f + 64)), in vocabulary order: the 4 / NSUB threads that weigh one
-// segment add their sums (in thread order) and the first of them stores it.
+// [64 f, 64 f + 64)).  A request's n segments are split into 256 runs of
+// G = ceil(n / 256) consecutive segments; segment f is stored at
+// (f % G) * 256 + f / G, so that the final draw's thread t, which owns run t,
+// reads slot g of all runs with one coalesced load per g.
 constexpr int kStoredSeg = 64;
-constexpr int kRegSegs = 10;  // stored segments a thread of the final draw keeps in registers
+constexpr int kRegSegs = 10;  // run slots a thread of the final draw keeps in registers
 
+struct SegLayout {
+    int n;  // stored segments per request
+    int G;  // run length
+    __device__ SegLayout(const CallArgs& a)
+        : n(a.S2 * (a.chunk2 / kStoredSeg)), G((a.S2 * (a.chunk2 / kStoredSeg) + kThreads - 1) / kThreads) {}
+    __device__ size_t per_request() const { return (size_t)G * kThreads; }
+    __device__ size_t slot(int f) const { return (size_t)(f % G) * kThreads + f / G; }
+};
+
+// The 4 / NSUB threads that weigh one segment add their sums (in thread order;
+// the partner lanes are in the same DPP row) and the first of them stores it.
 template <int NSUB>
-__device__ inline void store_segment(double* req_segs, int ch, int chunk2, double seg) {
+__device__ inline void store_segment(double* req_segs, const SegLayout& L, int ch, int chunk2,
+                                     double seg) {
     constexpr int P = kStoredSeg / (NSUB * kSub);  // threads per stored segment
     static_assert(P >= 1 && P * NSUB * kSub == kStoredSeg, "segment split");
-    if constexpr (P >= 2) seg += __shfl_down(seg, 1, 64);
-    if constexpr (P >= 4) seg += __shfl_down(seg, 2, 64);
-    if (threadIdx.x % P == 0)
-        store_coherent(&req_segs[(size_t)ch * (chunk2 / kStoredSeg) + threadIdx.x / P], seg);
+    if constexpr (P >= 2) seg += dpp_f64<dpp::kRowShl + 1>(seg);
+    if constexpr (P >= 4) seg += dpp_f64<dpp::kRowShl + 2>(seg);
+    if (threadIdx.x % P == 0) {
+        const int f = ch * (chunk2 / kStoredSeg) + threadIdx.x / P;
+        store_coherent(&req_segs[L.slot(f)], seg);
+    }
 }
 
-// The last workgroup of request b draws the token.  The request's n stored
-// segment sums are split into 256 runs of G = ceil(n / 256) consecutive sums,
-// one run per thread: a prefix sum over the runs finds the run holding u_k * Z,
-// its owner walks it to the segment, and wave 0 walks that segment's tokens
-// with a wave-wide prefix sum, one token per lane.  Each level takes the first
-// entry with positive weight whose running mass exceeds u_k * Z; where rounding
-// leaves every running mass at or below it, the last entry with positive weight.
+// The last workgroup of request b draws the token: a prefix sum over the runs
+// finds the run holding u_k * Z, its owner walks it to the segment, and wave 0
+// walks that segment's tokens with a wave-wide prefix sum, one token per lane.
+// Each level takes the first entry with positive weight whose running mass
+// exceeds u_k * Z; where rounding leaves every running mass at or below it, the
+// last entry with positive weight.
 template <typename T, bool VEC, int NSUB>
 __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow, const T* drow,
                              Weigher W) {
     __shared__ double sh_wave[kWaves];
-    __shared__ int sh_first, sh_last, sh_seg;
+    __shared__ int sh_first[kWaves], sh_last[kWaves], sh_seg;
     __shared__ double sh_run0;
     const int k = a.k;
-    const int tid = threadIdx.x;
-    const int n = a.S2 * (a.chunk2 / kStoredSeg);
-    const int G = (n + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const SegLayout L(a);
+    const int n = L.n, G = L.G;
     const int first = tid * G;
-    const int len = max(0, min(G, n - first));   // this thread's run: [first, first + len)
-    double* segs = a.segs + (size_t)b * n;
+    const int len = max(0, min(G, n - first));   // this thread's run: segments [first, first + len)
+    double* segs = a.segs + (size_t)b * L.per_request();
     const double u = (double)a.uniforms[(size_t)b * (k + 1) + k];
 
     double v[kRegSegs];
     double grp, incl, Z;
     for (int pass = 0;; ++pass) {
-        // All loads of the run are issued together (clamped in bounds, masked).
+        // Slot g of every run is one coalesced load; all loads issue together.
 #pragma unroll
-        for (int g = 0; g < kRegSegs; ++g) v[g] = load_coherent(segs + min(first + g, n - 1));
+        for (int g = 0; g < kRegSegs; ++g)
+            v[g] = load_coherent(segs + (size_t)min(g, G - 1) * kThreads + tid);
 #pragma unroll
         for (int g = 0; g < kRegSegs; ++g) v[g] = (g < len) ? v[g] : 0.0;
         grp = 0.0;
 #pragma unroll
         for (int g = 0; g < kRegSegs; ++g) grp += v[g];
-        for (int g = kRegSegs; g < len; ++g) grp += load_coherent(segs + first + g);
+        for (int g = kRegSegs; g < len; ++g) grp += load_coherent(segs + (size_t)g * kThreads + tid);
         incl = block_inclusive_scan(grp, sh_wave, &Z);
         if (Z > 0.0 || pass == 1) break;
         // The residual vanished (p_s == q_s): draw from p_s instead.
@@ -406,22 +422,30 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
         drow = trow;
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-            store_segment<NSUB>(segs, c, a.chunk2, segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi));
+            store_segment<NSUB>(segs, L, c, a.chunk2, segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi));
         }
         wait_stores();
         __syncthreads();
     }
     const double tau = u * Z;
-    if (tid == 0) {
-        sh_first = kThreads;
-        sh_last = -1;
+    // First run whose running mass exceeds tau, and last run with positive mass.
+    {
+        const unsigned long long over_m = __ballot(grp > 0.0 && incl > tau);
+        const unsigned long long pos_m = __ballot(grp > 0.0);
+        if (lane == 0) {
+            sh_first[wave] = over_m ? wave * 64 + __ffsll((long long)over_m) - 1 : kThreads;
+            sh_last[wave] = pos_m ? wave * 64 + 63 - __clzll((long long)pos_m) : -1;
+        }
     }
     __syncthreads();
-    if (grp > 0.0 && incl > tau) atomicMin(&sh_first, tid);
-    if (grp > 0.0) atomicMax(&sh_last, tid);
-    __syncthreads();
-    const bool over = sh_first < kThreads;
-    const int owner = over ? sh_first : max(sh_last, 0);
+    int first_over = kThreads, last_pos = -1;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        first_over = min(first_over, sh_first[w]);
+        last_pos = max(last_pos, sh_last[w]);
+    }
+    const bool over = first_over < kThreads;
+    const int owner = over ? first_over : max(last_pos, 0);
     if (tid == owner) {
         double run = incl - grp, pick_base = 0.0, last_base = 0.0;
         int pick = -1, lastpos = -1;
@@ -438,7 +462,7 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
             }
         }
         for (int g = kRegSegs; g < len && pick < 0; ++g) {
-            const double w = load_coherent(segs + first + g);
+            const double w = load_coherent(segs + (size_t)g * kThreads + tid);
             if (w > 0.0) {
                 lastpos = g;
                 last_base = run;
@@ -453,19 +477,12 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
     __syncthreads();
 
     // Token inside the segment: lane l of wave 0 weighs token 64 f + l.
-    if (tid < 64) {
-        const int lane = tid;
+    if (wave == 0) {
         const int base_tok = sh_seg * kStoredSeg;
         const int j = base_tok + lane;
         double w = 0.0;
         if (j < a.V) w = W(Elem<T>::load(trow, j), Elem<T>::load(drow, j));
-        double x = w;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double y = __shfl_up(x, off, 64);
-            if (lane >= off) x += y;
-        }
-        const double run = sh_run0 + x;
+        const double run = sh_run0 + wave_inclusive_scan(w);
         const unsigned long long hit = __ballot(over && w > 0.0 && run > tau);
         const unsigned long long pos = __ballot(w > 0.0);
         int sel;
@@ -478,7 +495,7 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
     // Leave this request's part of the workspace zero for later calls (every
     // other workgroup of the request has finished reading and writing it before
     // taking its ticket).
-    for (int g = 0; g < len; ++g) segs[first + g] = 0.0;
+    for (int g = 0; g < G; ++g) segs[(size_t)g * kThreads + tid] = 0.0;
     clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
 }
 
@@ -504,7 +521,8 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
     const double seg = segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi);
-    store_segment<NSUB>(a.segs + (size_t)b * a.S2 * (a.chunk2 / kStoredSeg), ch, a.chunk2, seg);
+    const SegLayout L(a);
+    store_segment<NSUB>(a.segs + (size_t)b * L.per_request(), L, ch, a.chunk2, seg);
     // Every thread's stores complete before the ticket is taken.
     wait_stores();
     __syncthreads();
