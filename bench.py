@@ -10,8 +10,9 @@ in device memory.  Inputs rotate over enough copies (>= 1 GiB in total) that the
 
 Prints ONE JSON line: throughput in verified rows/s (B * (k+1) per step), the
 roofline of the streaming kernel (algorithmic bytes = one read of each logits
-tensor, timed alone with HIP events on its own stream), and the CPU oracle's
-rate on a bounded sample of the same workload.
+tensor, over that kernel's own start/end event timestamps in a second run of the
+timed steps), and the CPU oracle's rate on a bounded sample of the same
+workload.
 """
 from __future__ import annotations
 
@@ -162,8 +163,11 @@ def time_steps(step, steps: int, warmup: int) -> float:
 
 
 def time_streaming_kernel(step, steps: int, warmup: int):
-    """Per-launch durations (ms) of the streaming kernel, from events the library
-    records around it on the stream it runs on."""
+    """Per-launch durations (ms) of the streaming kernel over a second run of the
+    same steps, in which the library attaches a start/stop event pair to each
+    streaming-kernel launch (the kernel's own start and end timestamps, on the
+    stream it runs on).  Attached events add a few microseconds between the
+    kernels of a step, so the step rate comes from the plain run."""
     import torch
 
     from draft_token_verification_verify_amd import _lib

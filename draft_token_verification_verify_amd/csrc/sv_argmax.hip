@@ -252,19 +252,22 @@ __global__ __launch_bounds__(kThreads) void argmax_epilogue_kernel(ArgmaxArgs a)
 }
 
 template <typename T, int U, bool VEC, int MODE>
-static hipError_t launch_argmax_u(const ArgmaxArgs& a, hipStream_t st) {
+static hipError_t launch_argmax_u(const ArgmaxArgs& a, hipStream_t st, const KernelEvents& ev) {
     const unsigned n_tiles = (unsigned)((long long)a.B * a.R * a.S);
-    argmax_kernel<T, U, VEC, MODE><<<dim3(n_tiles), dim3(kThreads), 0, st>>>(a);
+    // The events (when set) take the kernel's own start and end timestamps.
+    hipExtLaunchKernelGGL(argmax_kernel<T, U, VEC, MODE>, dim3(n_tiles), dim3(kThreads), 0, st,
+                          ev.begin, ev.end, 0, a);
     return hipGetLastError();
 }
 
 template <typename T, bool VEC, int MODE>
-static hipError_t launch_argmax(const ArgmaxArgs& a, int U, hipStream_t st) {
+static hipError_t launch_argmax(const ArgmaxArgs& a, int U, hipStream_t st,
+                                const KernelEvents& ev) {
     switch (U) {
-        case 8: return launch_argmax_u<T, 8, VEC, MODE>(a, st);
-        case 4: return launch_argmax_u<T, 4, VEC, MODE>(a, st);
-        case 2: return launch_argmax_u<T, 2, VEC, MODE>(a, st);
-        default: return launch_argmax_u<T, 1, VEC, MODE>(a, st);
+        case 8: return launch_argmax_u<T, 8, VEC, MODE>(a, st, ev);
+        case 4: return launch_argmax_u<T, 4, VEC, MODE>(a, st, ev);
+        case 2: return launch_argmax_u<T, 2, VEC, MODE>(a, st, ev);
+        default: return launch_argmax_u<T, 1, VEC, MODE>(a, st, ev);
     }
 }
 
@@ -273,15 +276,13 @@ template <int MODE>
 static hipError_t dispatch(const ArgmaxArgs& a, int dtype, bool vec, int U, size_t lds,
                            hipStream_t st, const KernelEvents& ev) {
     hipError_t e;
-    if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
     if (dtype == 1)
-        e = vec ? launch_argmax<bf16_t, true, MODE>(a, U, st)
-                : launch_argmax<bf16_t, false, MODE>(a, U, st);
+        e = vec ? launch_argmax<bf16_t, true, MODE>(a, U, st, ev)
+                : launch_argmax<bf16_t, false, MODE>(a, U, st, ev);
     else
-        e = vec ? launch_argmax<float, true, MODE>(a, U, st)
-                : launch_argmax<float, false, MODE>(a, U, st);
+        e = vec ? launch_argmax<float, true, MODE>(a, U, st, ev)
+                : launch_argmax<float, false, MODE>(a, U, st, ev);
     if (e != hipSuccess) return e;
-    if (ev.end && (e = hipEventRecord(ev.end, st)) != hipSuccess) return e;
     argmax_epilogue_kernel<MODE><<<dim3((unsigned)a.B), dim3(kThreads), lds, st>>>(a);
     return hipGetLastError();
 }

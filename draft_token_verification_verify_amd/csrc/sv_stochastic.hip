@@ -533,19 +533,21 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
 // ---------------------------------------------------------------------------
 
 template <typename T, int U, bool VEC>
-static hipError_t launch_stats_u(const CallArgs& a, hipStream_t st) {
+static hipError_t launch_stats_u(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
     const unsigned n_tiles = (unsigned)((long long)a.B * a.R * a.S);
-    stats_kernel<T, U, VEC><<<dim3(n_tiles), dim3(kThreads), 0, st>>>(a);
+    // The events (when set) take the kernel's own start and end timestamps.
+    hipExtLaunchKernelGGL(stats_kernel<T, U, VEC>, dim3(n_tiles), dim3(kThreads), 0, st, ev.begin,
+                          ev.end, 0, a);
     return hipGetLastError();
 }
 
 template <typename T, bool VEC>
-static hipError_t launch_stats(const CallArgs& a, int U, hipStream_t st) {
+static hipError_t launch_stats(const CallArgs& a, int U, hipStream_t st, const KernelEvents& ev) {
     switch (U) {
-        case 8: return launch_stats_u<T, 8, VEC>(a, st);
-        case 4: return launch_stats_u<T, 4, VEC>(a, st);
-        case 2: return launch_stats_u<T, 2, VEC>(a, st);
-        default: return launch_stats_u<T, 1, VEC>(a, st);
+        case 8: return launch_stats_u<T, 8, VEC>(a, st, ev);
+        case 4: return launch_stats_u<T, 4, VEC>(a, st, ev);
+        case 2: return launch_stats_u<T, 2, VEC>(a, st, ev);
+        default: return launch_stats_u<T, 1, VEC>(a, st, ev);
     }
 }
 
@@ -586,15 +588,13 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.q_at_draft = call.q_at_draft;
 
     hipError_t e;
-    if (ev.begin && (e = hipEventRecord(ev.begin, st)) != hipSuccess) return e;
     if (call.dtype == 1)
-        e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st)
-                     : launch_stats<bf16_t, false>(a, g.U, st);
+        e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st, ev)
+                     : launch_stats<bf16_t, false>(a, g.U, st, ev);
     else
-        e = call.vec ? launch_stats<float, true>(a, g.U, st)
-                     : launch_stats<float, false>(a, g.U, st);
+        e = call.vec ? launch_stats<float, true>(a, g.U, st, ev)
+                     : launch_stats<float, false>(a, g.U, st, ev);
     if (e != hipSuccess) return e;
-    if (ev.end && (e = hipEventRecord(ev.end, st)) != hipSuccess) return e;
     if (call.dtype == 1)
         return call.vec ? launch_sample<bf16_t, true>(a, st) : launch_sample<bf16_t, false>(a, st);
     return call.vec ? launch_sample<float, true>(a, st) : launch_sample<float, false>(a, st);

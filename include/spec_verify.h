@@ -105,10 +105,11 @@ size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V,
 int spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Profiling hook.  After this call, every verification call records
- * events[2 * i] on its stream immediately before its streaming kernel (the one
- * that reads every logits row) and events[2 * i + 1] immediately after it, with
- * i advancing by one per call and wrapping at n_pairs.  The events are
+ * Profiling hook.  After this call, every verification call launches its
+ * streaming kernel (the one that reads every logits row) with events[2 * i] and
+ * events[2 * i + 1] attached as the kernel's start and stop events
+ * (hipExtLaunchKernel: they take the kernel's own start and end timestamps),
+ * with i advancing by one per call and wrapping at n_pairs.  The events are
  * hipEvent_t handles (passed as void*) that the caller created and destroys.
  * Pass NULL and 0 to switch the hook off.  The hook is process-wide and not
  * thread-safe; it exists so that a benchmark can time that kernel alone on the
