@@ -267,14 +267,16 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     __syncthreads();
 }
 
-// Weight of one token in the final draw, in fp64: the residual max(0, p - q)
-// when the request stopped on a rejection, else the target probability.  Tokens
-// within 2^-8 of their row's maximum (the few that carry most of the mass) take
-// the fp64 exponential; the others the fp32 one, whose error is then negligible
-// against the total.
+// Weight of one token in the final draw, in fp64, scaled by the target row's
+// softmax sum S_t (the scale cancels against the total Z): the residual
+// S_t * max(0, p - q) = max(0, e_t - r e_d) with r = S_t / S_d when the request
+// stopped on a rejection, else S_t * p = e_t.  Here e = 2^((x - row max) * c).
+// Tokens within 2^-8 of their row's maximum (the few that carry most of the
+// mass) take the fp64 exponential; the others the fp32 one, whose error is
+// then negligible against the total.
 struct Weigher {
     float mt, md;
-    double inv_st, inv_sd;
+    double r;
     Scale sc;
     bool residual;
     __device__ inline double e_of(float x, float m) const {
@@ -282,11 +284,14 @@ struct Weigher {
         if (a > -8.f) return exp2_accurate(x, m, sc);
         return (double)fast_exp2(a);
     }
+    template <bool RESID>
+    __device__ inline double w(float xt, float xd) const {
+        const double et = e_of(xt, mt);
+        if constexpr (!RESID) return et;
+        return fmax(fma(-r, e_of(xd, md), et), 0.0);
+    }
     __device__ inline double operator()(float xt, float xd) const {
-        const double p = e_of(xt, mt) * inv_st;
-        if (!residual) return p;
-        const double q = e_of(xd, md) * inv_sd;
-        return p > q ? p - q : 0.0;
+        return residual ? w<true>(xt, xd) : w<false>(xt, xd);
     }
 };
 
@@ -295,8 +300,10 @@ constexpr int kSub = 16;  // tokens per sampler sub-step
 // Sum of the weights of this thread's segment of the chunk [lo, hi): the
 // NSUB * 16 consecutive tokens from lo + t * NSUB * 16.  Each pass issues up to
 // four 16-byte loads per row back to back (clamped in bounds; slots past hi are
-// masked).  drow == trow when there is no residual.
-template <typename T, bool VEC, int NSUB>
+// masked); the draft row is read only for a residual.  The per-token bound test
+// stays a branch even in full chunks: it keeps the compiler from interleaving
+// all of the segment's tokens, whose registers would cost occupancy.
+template <typename T, bool VEC, int NSUB, bool RESID>
 __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, int lo, int hi) {
     constexpr int SEG = NSUB * kSub;
     const int start = lo + (int)threadIdx.x * SEG;
@@ -312,16 +319,17 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
             for (int v = 0; v < NVP; ++v) {
                 const int j = max(lo, min(start + (v0 + v) * EPV, hi - EPV));
                 rt[v] = load16(trow + j);
-                rd[v] = load16(drow + j);
+                if constexpr (RESID) rd[v] = load16(drow + j);
             }
 #pragma unroll
             for (int v = 0; v < NVP; ++v) {
                 float xt[EPV], xd[EPV];
                 Elem<T>::widen(rt[v], xt);
-                Elem<T>::widen(rd[v], xd);
+                if constexpr (RESID) Elem<T>::widen(rd[v], xd);
 #pragma unroll
                 for (int e = 0; e < EPV; ++e)
-                    if (start + (v0 + v) * EPV + e < hi) seg += W(xt[e], xd[e]);
+                    if (start + (v0 + v) * EPV + e < hi)
+                        seg += W.template w<RESID>(xt[e], RESID ? xd[e] : 0.f);
             }
         }
     } else {
@@ -332,14 +340,21 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
             for (int e = 0; e < kSub; ++e) {
                 const int j = max(lo, min(start + s0 + e, hi - 1));
                 xt[e] = Elem<T>::load(trow, j);
-                xd[e] = Elem<T>::load(drow, j);
+                xd[e] = RESID ? Elem<T>::load(drow, j) : 0.f;
             }
 #pragma unroll
             for (int e = 0; e < kSub; ++e)
-                if (start + s0 + e < hi) seg += W(xt[e], xd[e]);
+                if (start + s0 + e < hi) seg += W.template w<RESID>(xt[e], xd[e]);
         }
     }
     return seg;
+}
+
+template <typename T, bool VEC, int NSUB>
+__device__ inline double segment_sum_any(const T* trow, const T* drow, const Weigher& W, int lo,
+                                         int hi) {
+    return W.residual ? segment_sum<T, VEC, NSUB, true>(trow, drow, W, lo, hi)
+                      : segment_sum<T, VEC, NSUB, false>(trow, drow, W, lo, hi);
 }
 
 // Wait until this thread's global stores have completed.
@@ -422,7 +437,8 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
         drow = trow;
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
-            store_segment<NSUB>(segs, L, c, a.chunk2, segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi));
+            store_segment<NSUB>(segs, L, c, a.chunk2,
+                                segment_sum<T, VEC, NSUB, false>(trow, drow, W, lo, hi));
         }
         wait_stores();
         __syncthreads();
@@ -509,9 +525,8 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     decide<T>(a, b, ch == 0, &dc);
     Weigher W;
     W.mt = dc.mt;
-    W.inv_st = 1.0 / dc.st;
     W.md = dc.md;
-    W.inv_sd = 1.0 / dc.sd;
+    W.r = dc.st / dc.sd;
     W.sc = a.sc;
     W.residual = dc.s < k;
     const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + dc.s) * (size_t)a.V;
@@ -520,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
         : trow;
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    const double seg = segment_sum<T, VEC, NSUB>(trow, drow, W, lo, hi);
+    const double seg = segment_sum_any<T, VEC, NSUB>(trow, drow, W, lo, hi);
     const SegLayout L(a);
     store_segment<NSUB>(a.segs + (size_t)b * L.per_request(), L, ch, a.chunk2, seg);
     // Every thread's stores complete before the ticket is taken.
