@@ -309,8 +309,9 @@ def main():
             "logits_bytes": nbytes,
             "input_copies": copies,
             "seed": args.seed,
-            **({"k": case.k, "temperature": case.temperature}
-               if mode_of(case) != "tree" else {"N": case.N, "P": case.P, "L": case.L}),
+            **({"k": case.k} if mode_of(case) != "tree"
+               else {"N": case.N, "P": case.P, "L": case.L}),
+            **({"temperature": case.temperature} if mode_of(case) == "stochastic" else {}),
         },
         "hbm_gbps_whole_call": nbytes / (ms * 1e-3) / 1e9,
         "roofline": {
