@@ -60,6 +60,12 @@ def spec_verify_version() -> int:
     return _lib.load().spec_verify_version()
 
 
+def spec_verify_set_schedule(schedule: int) -> None:
+    """Process-wide stochastic schedule: ``_lib.SCHEDULE_AUTO``,
+    ``_lib.SCHEDULE_TWO_KERNELS`` or ``_lib.SCHEDULE_SELF_COMPUTE``."""
+    _lib.check("spec_verify_set_schedule", _lib.load().spec_verify_set_schedule(int(schedule)))
+
+
 def spec_verify_workspace_bytes(mode: int, B: int, rows_per_request: int, V: int,
                                 dtype: int) -> int:
     return int(_lib.load().spec_verify_workspace_bytes(mode, B, rows_per_request, V, dtype))

@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libspec_verify.so")
 F32, BF16 = 0, 1
 MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE = 0, 1, 2
 OK, INVALID_ARGUMENT, UNSUPPORTED_DTYPE, WORKSPACE_TOO_SMALL, LIMIT_EXCEEDED, HIP_ERROR = range(6)
+SCHEDULE_AUTO, SCHEDULE_TWO_KERNELS, SCHEDULE_SELF_COMPUTE = 0, 1, 2
 
 EXPORTED = (
     "spec_verify_version",
@@ -18,6 +19,7 @@ EXPORTED = (
     "spec_verify_workspace_bytes",
     "spec_verify_workspace_init",
     "spec_verify_profile_events",
+    "spec_verify_set_schedule",
     "spec_verify_stochastic",
     "spec_verify_greedy",
     "spec_verify_tree",
@@ -53,6 +55,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_workspace_init.restype = I
     lib.spec_verify_profile_events.argtypes = [P, I]
     lib.spec_verify_profile_events.restype = I
+    lib.spec_verify_set_schedule.argtypes = [I]
+    lib.spec_verify_set_schedule.restype = I
     lib.spec_verify_stochastic.argtypes = [P, P, I, P, P, ctypes.c_float, I, I, I, P, P, P, P,
                                            P, Z, P]
     lib.spec_verify_stochastic.restype = I

@@ -73,6 +73,14 @@ size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V,
     return g.bytes;
 }
 
+int spec_verify_set_schedule(int schedule) {
+    if (schedule != SPEC_VERIFY_SCHEDULE_AUTO && schedule != SPEC_VERIFY_SCHEDULE_TWO_KERNELS &&
+        schedule != SPEC_VERIFY_SCHEDULE_SELF_COMPUTE)
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    sv::g_stochastic_schedule = schedule;
+    return SPEC_VERIFY_OK;
+}
+
 int spec_verify_profile_events(void* const* events, int n_pairs) {
     if (n_pairs < 0 || (n_pairs > 0 && events == nullptr)) return SPEC_VERIFY_INVALID_ARGUMENT;
     g_events = n_pairs > 0 ? events : nullptr;

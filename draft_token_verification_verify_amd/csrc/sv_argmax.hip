@@ -52,6 +52,14 @@ struct ArgmaxOp : ArgmaxArgs {
         return static_cast<const T*>(target) + ((size_t)b * R + r) * (size_t)V;
     }
 
+    __device__ void publish(Partial16* dst, float f0, float f1, double d) const {
+        Partial16 p;
+        p.f0 = f0;
+        p.f1 = f1;
+        p.d = d;
+        *dst = p;
+    }
+
     __device__ void finish(float v, int i, float* f0, float* f1, double* d) const {
         wave_reduce_argmax(v, i);
         __shared__ float red_v[kWaves];

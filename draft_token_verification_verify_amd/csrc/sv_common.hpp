@@ -328,6 +328,13 @@ __device__ inline T load_coherent(const T* p) {
     return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait until this thread's global stores have completed.
+__device__ inline void wait_stores() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // Take an arrival ticket on `counter` after thread 0 has written this
 // workgroup's contribution (only thread 0 writes what other workgroups read).
 // Returns true in every thread of the last of `expected` arrivals; those

@@ -57,6 +57,11 @@ struct KernelEvents {
     hipEvent_t begin = nullptr, end = nullptr;
 };
 
+// Stochastic schedule: 0 one launch where rows are 16-byte aligned (else two
+// kernels), 1 two kernels, 2 one launch whose sampler items compute their
+// request's statistics themselves instead of waiting (for tests).
+extern int g_stochastic_schedule;
+
 hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
                           const KernelEvents& ev);
 hipError_t run_greedy(const GreedyCall& call, const Geometry& g, hipStream_t st,

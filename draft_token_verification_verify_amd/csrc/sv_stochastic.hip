@@ -53,7 +53,8 @@ struct CallArgs {
     int R, S, chunk;         // streaming geometry: rows per request, chunks per row
     int S2, chunk2;          // sampler geometry: chunks per stop row
     Scale sc;                // log2(e) / temperature
-    Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, d = sum (f1 unused)
+    Partial16* partials;     // [B, 2k+1, S]: f0 = chunk max, f1 = written flag, d = sum
+    int spin_limit;          // polls of unpublished partials before computing them here
     uint32_t* tickets;       // per request (padded): sampler arrivals
     double* segs;            // per request: stop-row mass per 64-token segment, run-major
     int32_t* out_tokens;     // [B, k+1]
@@ -79,6 +80,8 @@ struct StatsOp : CallArgs {
         return static_cast<const T*>(draft) + ((size_t)b * k + (r - k - 1)) * (size_t)V;
     }
 
+    __device__ void publish(Partial16* dst, float f0, float f1, double d) const;
+
     // Workgroup reduction of per-thread (max m, fp64 sum s against m) into the
     // tile's (M, S): every thread's sum is rescaled to the common M with an fp64
     // exponential, then summed in fixed order.
@@ -89,8 +92,11 @@ struct StatsOp : CallArgs {
         const double f = (m == -INFINITY) ? 0.0 : exp2_accurate(m, M, sc);
         const double Ssum = block_sum(s * f, red_d);
         *f0 = M;
-        *f1 = 0.f;
-        *d = Ssum;
+        *f1 = kPartialWritten;
+        // A chunk with a finite max sums to >= 1 (its largest logit counts 1);
+        // an all -inf chunk, whose weight in every merge is 0, stores 1.  So a
+        // published partial never reads back as the cleared (all-zero) state.
+        *d = (M == -INFINITY) ? 1.0 : Ssum;
     }
 
     __device__ void tile(int b, int r, int lo, int hi, const uint4* raw, int nvec, float* f0,
@@ -133,6 +139,57 @@ struct StatsOp : CallArgs {
     }
 };
 
+// Publish a statistics partial for readers in the same launch: two 8-byte
+// agent-coherent stores, each half carrying its own proof of publication
+// (f1 == written flag; d != 0).
+__device__ inline void publish_partial(Partial16* dst, float f0, float f1, double d) {
+    unsigned long long* q = reinterpret_cast<unsigned long long*>(dst);
+    store_coherent(q + 1, (unsigned long long)__double_as_longlong(d));
+    store_coherent(q, ((unsigned long long)__float_as_uint(f1) << 32) | __float_as_uint(f0));
+}
+
+// Statistics tile t of a 16-byte aligned problem with a runtime vector count:
+// the same element-to-thread mapping and the same operation order as
+// StatsOp::tile (masked slots add exactly 0 there), hence the same bits.  Used
+// by a sampler workgroup that computes partials itself instead of waiting.
+template <typename T>
+__device__ void stats_tile_runtime(const CallArgs& a, int t, float* f0, float* f1, double* d) {
+    constexpr int EPV = Elem<T>::kPerVec;
+    StatsOp<T, 1> op;
+    static_cast<CallArgs&>(op) = a;
+    const int U = a.chunk / (kThreads * EPV);
+    const int ch = t % a.S, rr = t / a.S;
+    const int r = rr % a.R, b = rr / a.R;
+    const int lo = ch * a.chunk, hi = min(a.V, lo + a.chunk);
+    const int nvec = (hi - lo) / EPV;
+    const uint4* base = reinterpret_cast<const uint4*>(op.row(b, r) + lo);
+    float m = -INFINITY;
+    for (int j = 0; j < U; ++j) {
+        const int v = (int)threadIdx.x + j * kThreads;
+        if (v < nvec) {
+            float x[EPV];
+            Elem<T>::widen(base[v], x);
+            for (int e = 0; e < EPV; ++e) m = fmaxf(m, x[e]);
+        }
+    }
+    const float ms = (m == -INFINITY) ? 0.f : m;
+    double s = 0.0;
+    for (int j = 0; j < U; ++j) {
+        const int v = (int)threadIdx.x + j * kThreads;
+        if (v < nvec) {
+            float x[EPV];
+            Elem<T>::widen(base[v], x);
+            for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[e] - ms, a.sc));
+        }
+    }
+    op.finish(m, s, f0, f1, d);
+}
+
+template <typename T, int U>
+__device__ void StatsOp<T, U>::publish(Partial16* dst, float f0, float f1, double d) const {
+    publish_partial(dst, f0, f1, d);
+}
+
 template <typename T, int U, bool VEC>
 __global__ __launch_bounds__(kThreads) void stats_kernel(CallArgs a) {
     StatsOp<T, U> op;
@@ -155,17 +212,69 @@ struct Decision {
 
 constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the merge
 
+// A partial as read back by a consumer: two 8-byte agent-coherent loads.
+struct PartialRead {
+    float f0;
+    bool ok;
+    double d;
+};
+__device__ inline PartialRead read_partial(const Partial16* p) {
+    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+    const unsigned long long h1 = load_coherent(q);
+    const unsigned long long h2 = load_coherent(q + 1);
+    PartialRead r;
+    r.f0 = __uint_as_float((unsigned)h1);
+    r.d = __longlong_as_double((long long)h2);
+    r.ok = __uint_as_float((unsigned)(h1 >> 32)) == kPartialWritten && h2 != 0ull;
+    return r;
+}
+
+// Make sure every partial of request b is published.  They come from an
+// earlier kernel (then the first check succeeds) or from statistics workgroups
+// of the same launch; after a.spin_limit polls this workgroup computes the
+// still-missing ones itself (same bits as their owners), so no wait depends on
+// another workgroup being scheduled.
+template <typename T>
+__device__ void await_partials(const CallArgs& a, int b) {
+    const int n = a.R * a.S;
+    Partial16* p = a.partials + (size_t)b * n;
+    for (int iter = 0;; ++iter) {
+        int ok = 1;
+        for (int t = threadIdx.x; t < n; t += kThreads) ok &= read_partial(p + t).ok;
+        if (__syncthreads_and(ok)) return;
+        if (iter >= a.spin_limit) break;
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __shared__ int sh_missing;
+    for (int t = 0; t < n; ++t) {
+        if (threadIdx.x == 0) sh_missing = !read_partial(p + t).ok;
+        __syncthreads();
+        const int missing = sh_missing;
+        __syncthreads();
+        if (missing) {
+            float f0, f1;
+            double d;
+            stats_tile_runtime<T>(a, b * n + t, &f0, &f1, &d);
+            if (threadIdx.x == 0) publish_partial(p + t, f0, f1, d);
+        }
+    }
+    wait_stores();  // this thread's own reads below see its stores
+    __syncthreads();
+}
+
 // Row statistics of request b: sh_m[r] = row max, sh_s[r] = sum of
 // 2^((x - max) * c) in fp64 (chunks merged in order).
+template <typename T>
 __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) {
     const int R = a.R, S = a.S, n = R * S;
     const Partial16* p = a.partials + (size_t)b * n;
+    await_partials<T>(a, b);
     if (n <= kMergeLds) {
         // Every thread takes a few partials: one fp64 exponential each.
         __shared__ float pm[kMergeLds];
         __shared__ double ps[kMergeLds];
         for (int t = threadIdx.x; t < n; t += kThreads) {
-            const Partial16 q = p[t];
+            const PartialRead q = read_partial(p + t);
             pm[t] = q.f0;
             ps[t] = q.d;
         }
@@ -190,10 +299,13 @@ __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) 
         for (int r = threadIdx.x; r < R; r += kThreads) {
             const Partial16* q = p + (size_t)r * S;
             float M = -INFINITY;
-            for (int ch = 0; ch < S; ++ch) M = fmaxf(M, q[ch].f0);
+            for (int ch = 0; ch < S; ++ch) M = fmaxf(M, read_partial(q + ch).f0);
             double acc = 0.0;
             if (M != -INFINITY)
-                for (int ch = 0; ch < S; ++ch) acc += q[ch].d * exp2_accurate(q[ch].f0, M, a.sc);
+                for (int ch = 0; ch < S; ++ch) {
+                    const PartialRead e = read_partial(q + ch);
+                    acc += e.d * exp2_accurate(e.f0, M, a.sc);
+                }
             sh_m[r] = M;
             sh_s[r] = acc;
         }
@@ -228,7 +340,7 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
         x = a.draft_tokens[(size_t)b * k + i];
         u = a.uniforms[(size_t)b * (k + 1) + i];
     }
-    merge_rows(a, b, sh_m, sh_s);
+    merge_rows<T>(a, b, sh_m, sh_s);
     if (i < k) {
         double P = 0.0, Q = 0.0;
         int acc = 0;
@@ -357,12 +469,6 @@ __device__ inline double segment_sum_any(const T* trow, const T* drow, const Wei
                       : segment_sum<T, VEC, NSUB, false>(trow, drow, W, lo, hi);
 }
 
-// Wait until this thread's global stores have completed.
-__device__ inline void wait_stores() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // The stop row's mass is kept per 64-token segment (segment f covers tokens
 // [64 f, 64 f + 64)).  A request's n segments are split into 256 runs of
@@ -515,11 +621,9 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
     clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
 }
 
+// One sampler work item: chunk ch of request b's stop row.
 template <typename T, bool VEC, int NSUB>
-__global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
-    const int tile = blockIdx.x;
-    const int b = tile / a.S2;
-    const int ch = tile % a.S2;
+__device__ void sample_item(const CallArgs& a, int b, int ch) {
     const int k = a.k;
     Decision dc;
     decide<T>(a, b, ch == 0, &dc);
@@ -543,6 +647,32 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
     __syncthreads();
     if (arrive_last(ticket_of(a.tickets, b), (uint32_t)a.S2, &last_flag))
         sample_final<T, VEC, NSUB>(a, b, dc.s, trow, drow, W);
+}
+
+template <typename T, bool VEC, int NSUB>
+__global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
+    sample_item<T, VEC, NSUB>(a, blockIdx.x / a.S2, blockIdx.x % a.S2);
+}
+
+// ---------------------------------------------------------------------------
+// One-launch schedule (16-byte aligned rows): the grid holds the statistics
+// tiles first, then the sampler items.  Workgroups are dispatched in index
+// order, so items start as statistics workgroups retire and sample the early
+// requests while the late requests are still streaming.  An item polls for its
+// request's partials and, past a bounded number of polls, computes the missing
+// ones itself (await_partials), so no wait depends on dispatch order.
+// ---------------------------------------------------------------------------
+template <typename T, int U, int NSUB>
+__global__ __launch_bounds__(kThreads) void onepass_kernel(CallArgs a) {
+    const int n_tiles = a.B * a.R * a.S;
+    if ((int)blockIdx.x < n_tiles) {
+        StatsOp<T, U> op;
+        static_cast<CallArgs&>(op) = a;
+        stream_tile_vec<T, U>(op);
+        return;
+    }
+    const int j = (int)blockIdx.x - n_tiles;
+    sample_item<T, true, NSUB>(a, j / a.S2, j % a.S2);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,6 +707,43 @@ static hipError_t launch_sample(const CallArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <typename T, int U>
+static hipError_t launch_onepass_u(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
+    const unsigned grid = (unsigned)((long long)a.B * a.R * a.S + (long long)a.B * a.S2);
+    switch (a.chunk2 / (kThreads * kSub)) {
+        case 4:
+            hipExtLaunchKernelGGL(onepass_kernel<T, U, 4>, dim3(grid), dim3(kThreads), 0, st,
+                                  ev.begin, ev.end, 0, a);
+            break;
+        case 2:
+            hipExtLaunchKernelGGL(onepass_kernel<T, U, 2>, dim3(grid), dim3(kThreads), 0, st,
+                                  ev.begin, ev.end, 0, a);
+            break;
+        default:
+            hipExtLaunchKernelGGL(onepass_kernel<T, U, 1>, dim3(grid), dim3(kThreads), 0, st,
+                                  ev.begin, ev.end, 0, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_onepass(const CallArgs& a, int U, hipStream_t st,
+                                 const KernelEvents& ev) {
+    switch (U) {
+        case 8: return launch_onepass_u<T, 8>(a, st, ev);
+        case 4: return launch_onepass_u<T, 4>(a, st, ev);
+        case 2: return launch_onepass_u<T, 2>(a, st, ev);
+        default: return launch_onepass_u<T, 1>(a, st, ev);
+    }
+}
+
+int g_stochastic_schedule = 0;
+
+// Polls of an unpublished partial before an item computes it itself: far above
+// any wait seen when workgroups are dispatched in order (a few microseconds).
+constexpr int kSpinLimit = 1 << 16;
+
 hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
                           const KernelEvents& ev) {
     char* ws = static_cast<char*>(call.workspace);
@@ -602,7 +769,11 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.p_at_draft = call.p_at_draft;
     a.q_at_draft = call.q_at_draft;
 
+    a.spin_limit = (g_stochastic_schedule == 2) ? 0 : kSpinLimit;
     hipError_t e;
+    if (call.vec && g_stochastic_schedule != 1)
+        return call.dtype == 1 ? launch_onepass<bf16_t>(a, g.U, st, ev)
+                               : launch_onepass<float>(a, g.U, st, ev);
     if (call.dtype == 1)
         e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st, ev)
                      : launch_stats<bf16_t, false>(a, g.U, st, ev);

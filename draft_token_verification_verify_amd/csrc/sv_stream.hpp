@@ -21,11 +21,14 @@ struct Partial16 {
 };
 static_assert(sizeof(Partial16) == 16, "Partial16 layout");
 
+// f1 of a published statistics partial (a cleared workspace reads 0).
+constexpr float kPartialWritten = 1.0f;
+
 // One workgroup per tile, rows 16-byte aligned (V a whole number of vectors).
 //   Op::row(b, r) -> const T* row start
 //   Op::tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d): reduce the tile held in
-//     raw[U] (this thread's vectors; slots >= nvec are padding); the returned
-//     values are published by thread 0.
+//     raw[U] (this thread's vectors; slots >= nvec are padding); thread 0 then
+//     calls Op::publish(&partials[t], f0, f1, d).
 template <typename T, int U, class Op>
 __device__ void stream_tile_vec(const Op& op) {
     constexpr int EPV = Elem<T>::kPerVec;
@@ -43,13 +46,7 @@ __device__ void stream_tile_vec(const Op& op) {
     float f0, f1;
     double d;
     op.tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d);
-    if (threadIdx.x == 0) {
-        Partial16 p;
-        p.f0 = f0;
-        p.f1 = f1;
-        p.d = d;
-        op.partials[t] = p;
-    }
+    if (threadIdx.x == 0) op.publish(op.partials + t, f0, f1, d);
 }
 
 // Same for rows that are not 16-byte aligned: scalar loads.
@@ -62,13 +59,7 @@ __device__ void stream_tile_scalar(const Op& op) {
     float f0, f1;
     double d;
     op.tile_scalar(b, r, lo, hi, &f0, &f1, &d);
-    if (threadIdx.x == 0) {
-        Partial16 p;
-        p.f0 = f0;
-        p.f1 = f1;
-        p.d = d;
-        op.partials[t] = p;
-    }
+    if (threadIdx.x == 0) op.publish(op.partials + t, f0, f1, d);
 }
 
 // Zero a request's partials once every reader has read them, so that the

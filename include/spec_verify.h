@@ -105,8 +105,33 @@ size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V,
 int spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Stochastic schedule (process-wide, not thread-safe; default AUTO).  All
+ * schedules give bit-identical results.
+ *
+ *   AUTO          rows 16-byte aligned (pointers and V * element size): one
+ *                 launch whose grid holds the statistics workgroups and then
+ *                 the sampling workgroups, which start as statistics
+ *                 workgroups retire and wait (bounded polling) for their
+ *                 request's statistics; otherwise TWO_KERNELS.
+ *   TWO_KERNELS   a statistics kernel, then a sampling kernel; no waits inside
+ *                 a kernel.
+ *   SELF_COMPUTE  like AUTO, but every sampling workgroup computes its
+ *                 request's statistics itself instead of waiting (slow; the
+ *                 fallback path of AUTO, exposed for testing).
+ *
+ * Returns INVALID_ARGUMENT for any other value.
+ */
+enum {
+    SPEC_VERIFY_SCHEDULE_AUTO = 0,
+    SPEC_VERIFY_SCHEDULE_TWO_KERNELS = 1,
+    SPEC_VERIFY_SCHEDULE_SELF_COMPUTE = 2
+};
+int spec_verify_set_schedule(int schedule);
+
+/*
  * Profiling hook.  After this call, every verification call launches its
- * streaming kernel (the one that reads every logits row) with events[2 * i] and
+ * streaming kernel (the one that reads every logits row; under the one-launch
+ * stochastic schedule, the whole call) with events[2 * i] and
  * events[2 * i + 1] attached as the kernel's start and stop events
  * (hipExtLaunchKernel: they take the kernel's own start and end timestamps),
  * with i advancing by one per call and wrapping at n_pairs.  The events are

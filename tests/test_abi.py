@@ -148,3 +148,10 @@ def test_tree_rejects(lib, kw, code):
 
 def test_workspace_init_rejects_null(lib):
     assert lib.spec_verify_workspace_init(None, 64, None) == _lib.INVALID_ARGUMENT
+
+
+def test_schedule_switch(lib):
+    for code in (_lib.SCHEDULE_TWO_KERNELS, _lib.SCHEDULE_SELF_COMPUTE, _lib.SCHEDULE_AUTO):
+        assert lib.spec_verify_set_schedule(code) == _lib.OK
+    assert lib.spec_verify_set_schedule(3) == _lib.INVALID_ARGUMENT
+    assert lib.spec_verify_set_schedule(-1) == _lib.INVALID_ARGUMENT

@@ -19,6 +19,18 @@ from tests.oracle_pins import CHI2_DF7_P001, chi2_stat, lib_softmax, sample_from
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(autouse=True, params=["auto", "two-kernels"])
+def schedule(request):
+    """Every case runs under the default one-launch schedule (two kernels where
+    rows are not 16-byte aligned) and under the two-kernel schedule."""
+    from draft_token_verification_verify_amd import _lib
+
+    sv.spec_verify_set_schedule(_lib.SCHEDULE_AUTO if request.param == "auto"
+                                else _lib.SCHEDULE_TWO_KERNELS)
+    yield request.param
+    sv.spec_verify_set_schedule(_lib.SCHEDULE_AUTO)
+
+
 def check(case, rows=None):
     gpu = H.run_stochastic(case)
     ref = H.oracle_stochastic(case, rows)
@@ -158,3 +170,42 @@ def test_emitted_tokens_distributed_as_p():
     assert chi2_stat(np.bincount(out[:, 0], minlength=V), p[0]) < CHI2_DF7_P001
     assert chi2_stat(np.bincount(out[s >= 1, 1], minlength=V), p[1]) < CHI2_DF7_P001
     assert chi2_stat(np.bincount(out[s >= 2, 2], minlength=V), p[2]) < CHI2_DF7_P001
+
+
+SCHEDULE_CASES = [
+    lambda: wl.c3(21),
+    lambda: wl.gaussian_stochastic(22, 5, 3, 40000, "bf16", target_sd=3.0, draft_noise_sd=1.0),
+    lambda: wl.gaussian_stochastic(23, 3, 0, 33000, "f32", target_sd=2.0, draft_noise_sd=1.0),
+    lambda: wl.gaussian_stochastic(24, 64, 5, 8, "f32", target_sd=1.0, draft_noise_sd=1.0),
+    lambda: wl.c4(25, B=6),
+]
+
+
+@pytest.mark.parametrize("make", SCHEDULE_CASES, ids=["c3", "bf16-V40000", "k0", "V8", "c4-B6"])
+def test_schedules_are_bit_identical(make, schedule):
+    """The one-launch schedule, the two-kernel schedule and the one-launch
+    schedule whose sampling workgroups compute the statistics themselves give
+    the same bits, and leave the workspace all zero."""
+    from draft_token_verification_verify_amd import _lib
+
+    if schedule != "auto":
+        pytest.skip("compares all schedules itself")
+    case = make()
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(0, case.B, case.k + 1, case.V,
+                                                    _lib.BF16 if case.dtype == "bf16" else _lib.F32),
+                     dtype=torch.uint8, device="cuda")
+    results = {}
+    try:
+        for name, code in [("auto", _lib.SCHEDULE_AUTO), ("two", _lib.SCHEDULE_TWO_KERNELS),
+                           ("self", _lib.SCHEDULE_SELF_COMPUTE)]:
+            sv.spec_verify_set_schedule(code)
+            results[name] = H.run_stochastic(case, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(torch.count_nonzero(ws)) == 0, f"workspace not zero after {name}"
+    finally:
+        sv.spec_verify_set_schedule(_lib.SCHEDULE_AUTO)
+    for name in ("two", "self"):
+        for key in results["auto"]:
+            np.testing.assert_array_equal(results[name][key], results["auto"][key],
+                                          err_msg=f"{case.name}: {name} vs auto, {key}")
+    H.compare_stochastic(results["auto"], H.oracle_stochastic(case), label=case.name)
