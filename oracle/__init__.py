@@ -53,6 +53,11 @@ def _open(path: str):
     lib.oracle_verify_stochastic.restype = i
     lib.oracle_verify_greedy.argtypes = [P, i, P, i, i, i, P, P, P]
     lib.oracle_verify_greedy.restype = i
+    lib.oracle_verify_stochastic_ragged.argtypes = [P, P, i, P, P, P, ctypes.c_double, i, i, i,
+                                                    P, P, P, P, P]
+    lib.oracle_verify_stochastic_ragged.restype = i
+    lib.oracle_verify_greedy_ragged.argtypes = [P, i, P, P, i, i, i, P, P, P]
+    lib.oracle_verify_greedy_ragged.restype = i
     lib.oracle_verify_tree.argtypes = [P, i, P, P, i, i, i, i, i, P, P, P, P]
     lib.oracle_verify_tree.restype = i
     return lib
@@ -89,11 +94,13 @@ def _ptr(a: np.ndarray | None):
 
 
 def stochastic(target_logits, draft_logits, draft_tokens, uniforms, temperature, *,
-               lib=None):
+               draft_lens=None, lib=None):
     """Oracle stochastic verify.
 
     Returns ``dict(out_tokens[B,k+1] int32, num_accepted[B] int32,
     p_at_draft[B,k] f64, q_at_draft[B,k] f64, margins[B,k+1] f64)``.
+    With ``draft_lens`` ([B] ints), request b uses only its first
+    ``draft_lens[b]`` drafts (clamped to [0, k]).
     """
     t, dt = _logits(target_logits)
     B, k1, V = t.shape
@@ -110,16 +117,23 @@ def stochastic(target_logits, draft_logits, draft_tokens, uniforms, temperature,
     pp = np.empty((B, k), np.float64)
     qq = np.empty((B, k), np.float64)
     mg = np.empty((B, k + 1), np.float64)
-    rc = (lib or _load()).oracle_verify_stochastic(
-        _ptr(t), _ptr(d), dt, _ptr(x), _ptr(u), float(temperature), B, k, V, _ptr(out),
-        _ptr(acc), _ptr(pp), _ptr(qq), _ptr(mg))
+    if draft_lens is None:
+        rc = (lib or _load()).oracle_verify_stochastic(
+            _ptr(t), _ptr(d), dt, _ptr(x), _ptr(u), float(temperature), B, k, V, _ptr(out),
+            _ptr(acc), _ptr(pp), _ptr(qq), _ptr(mg))
+    else:
+        ln = np.ascontiguousarray(draft_lens, dtype=np.int32).reshape(B)
+        rc = (lib or _load()).oracle_verify_stochastic_ragged(
+            _ptr(t), _ptr(d), dt, _ptr(x), _ptr(ln), _ptr(u), float(temperature), B, k, V,
+            _ptr(out), _ptr(acc), _ptr(pp), _ptr(qq), _ptr(mg))
     if rc != 0:
         raise ValueError(f"oracle_verify_stochastic failed with code {rc}")
     return dict(out_tokens=out, num_accepted=acc, p_at_draft=pp, q_at_draft=qq, margins=mg)
 
 
-def greedy(target_logits, draft_tokens, *, lib=None):
-    """Oracle greedy verify: ``dict(out_tokens, num_accepted, argmax[B,k+1])``."""
+def greedy(target_logits, draft_tokens, *, draft_lens=None, lib=None):
+    """Oracle greedy verify: ``dict(out_tokens, num_accepted, argmax[B,k+1])``; with
+    ``draft_lens``, request b uses only its first ``draft_lens[b]`` drafts."""
     t, dt = _logits(target_logits)
     B, k1, V = t.shape
     k = k1 - 1
@@ -127,8 +141,13 @@ def greedy(target_logits, draft_tokens, *, lib=None):
     out = np.empty((B, k + 1), np.int32)
     acc = np.empty((B,), np.int32)
     am = np.empty((B, k + 1), np.int32)
-    rc = (lib or _load()).oracle_verify_greedy(
-        _ptr(t), dt, _ptr(x), B, k, V, _ptr(out), _ptr(acc), _ptr(am))
+    if draft_lens is None:
+        rc = (lib or _load()).oracle_verify_greedy(
+            _ptr(t), dt, _ptr(x), B, k, V, _ptr(out), _ptr(acc), _ptr(am))
+    else:
+        ln = np.ascontiguousarray(draft_lens, dtype=np.int32).reshape(B)
+        rc = (lib or _load()).oracle_verify_greedy_ragged(
+            _ptr(t), dt, _ptr(x), _ptr(ln), B, k, V, _ptr(out), _ptr(acc), _ptr(am))
     if rc != 0:
         raise ValueError(f"oracle_verify_greedy failed with code {rc}")
     return dict(out_tokens=out, num_accepted=acc, argmax=am)

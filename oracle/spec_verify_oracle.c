@@ -272,6 +272,86 @@ int oracle_verify_stochastic(const void *target_logits, const void *draft_logits
     return ORACLE_OK;
 }
 
+/* Bytes of one logit of `dtype`. */
+static size_t elem_bytes(int dtype)
+{
+    return dtype == ORACLE_DTYPE_BF16 ? 2 : 4;
+}
+
+/* Draft length of request b under the ragged layout: draft_lens[b] clamped to
+ * [0, k] (k when draft_lens is NULL). */
+static int ragged_len(const int32_t *draft_lens, int b, int k)
+{
+    if (!draft_lens)
+        return k;
+    int kb = draft_lens[b];
+    return kb < 0 ? 0 : (kb > k ? k : kb);
+}
+
+/*
+ * Stochastic verification with per-request draft lengths ([TRTLLM] section on
+ * the acceptance pipeline, step 2: ragged verification, where each request is
+ * verified over its own window while buffers stay padded to the static
+ * maximum k).  Request b uses only its first k_b = draft_lens[b] drafts
+ * (clamped to [0, k]): it is verified exactly as a request of length k_b on
+ * its own -- target rows 0..k_b, draft rows 0..k_b-1, uniforms[b, 0..k_b-1]
+ * for the tests and uniforms[b, k_b] for the final token.  Layouts stay padded
+ * to k: out_tokens[b, k_b+1..k] = -1, p/q_at_draft[b, k_b..k-1] = 0 and
+ * margins[b, k_b+1..k] = +inf.
+ */
+int oracle_verify_stochastic_ragged(const void *target_logits, const void *draft_logits,
+                                    int dtype, const int32_t *draft_tokens,
+                                    const int32_t *draft_lens, const float *uniforms,
+                                    double temperature, int B, int k, int V,
+                                    int32_t *out_tokens, int32_t *num_accepted,
+                                    double *p_at_draft, double *q_at_draft, double *margins)
+{
+    if (B < 0 || k < 0 || V < 1)
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    const size_t eb = elem_bytes(dtype);
+    int32_t *out1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k + 1));
+    double *p1 = (double *)malloc(sizeof(double) * (size_t)(k + 1));
+    double *q1 = (double *)malloc(sizeof(double) * (size_t)(k + 1));
+    double *m1 = (double *)malloc(sizeof(double) * (size_t)(k + 1));
+    if (!out1 || !p1 || !q1 || !m1) {
+        free(out1);
+        free(p1);
+        free(q1);
+        free(m1);
+        return ORACLE_NO_MEMORY;
+    }
+    int rc = ORACLE_OK;
+    for (int b = 0; b < B && rc == ORACLE_OK; ++b) {
+        const int kb = ragged_len(draft_lens, b, k);
+        const char *t = (const char *)target_logits + eb * (size_t)b * (k + 1) * (size_t)V;
+        const char *d = draft_logits
+            ? (const char *)draft_logits + eb * (size_t)b * k * (size_t)V : NULL;
+        int32_t acc;
+        rc = oracle_verify_stochastic(t, d, dtype, draft_tokens + (size_t)b * k,
+                                      uniforms + (size_t)b * (k + 1), temperature, 1, kb, V,
+                                      out1, &acc, p1, q1, m1);
+        for (int i = 0; i <= k; ++i) {
+            out_tokens[(size_t)b * (k + 1) + i] = i <= kb ? out1[i] : -1;
+            if (margins)
+                margins[(size_t)b * (k + 1) + i] = i <= kb ? m1[i] : INFINITY;
+        }
+        for (int i = 0; i < k; ++i) {
+            if (p_at_draft)
+                p_at_draft[(size_t)b * k + i] = i < kb ? p1[i] : 0.0;
+            if (q_at_draft)
+                q_at_draft[(size_t)b * k + i] = i < kb ? q1[i] : 0.0;
+        }
+        num_accepted[b] = acc;
+    }
+    free(out1);
+    free(p1);
+    free(q1);
+    free(m1);
+    return rc;
+}
+
 /* Index of the largest raw logit of one row; the lowest index wins a tie. */
 static int32_t argmax_row(const void *logits, int dtype, size_t row_offset, int V)
 {
@@ -327,6 +407,48 @@ int oracle_verify_greedy(const void *target_logits, int dtype, const int32_t *dr
             free(arg);
     }
     return ORACLE_OK;
+}
+
+/*
+ * Greedy verification with per-request draft lengths (same reading as
+ * oracle_verify_stochastic_ragged): request b is verified as a request of
+ * length k_b = draft_lens[b] (clamped to [0, k]) on its own, target rows
+ * 0..k_b; out_tokens[b, k_b+1..k] = -1.  argmax_out[b, i] for i > k_b is -1.
+ */
+int oracle_verify_greedy_ragged(const void *target_logits, int dtype,
+                                const int32_t *draft_tokens, const int32_t *draft_lens, int B,
+                                int k, int V, int32_t *out_tokens, int32_t *num_accepted,
+                                int32_t *argmax_out)
+{
+    if (B < 0 || k < 0 || V < 1)
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    const size_t eb = elem_bytes(dtype);
+    int32_t *out1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k + 1));
+    int32_t *arg1 = (int32_t *)malloc(sizeof(int32_t) * (size_t)(k + 1));
+    if (!out1 || !arg1) {
+        free(out1);
+        free(arg1);
+        return ORACLE_NO_MEMORY;
+    }
+    int rc = ORACLE_OK;
+    for (int b = 0; b < B && rc == ORACLE_OK; ++b) {
+        const int kb = ragged_len(draft_lens, b, k);
+        const char *t = (const char *)target_logits + eb * (size_t)b * (k + 1) * (size_t)V;
+        int32_t acc;
+        rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb, V, out1, &acc,
+                                  arg1);
+        for (int i = 0; i <= k; ++i) {
+            out_tokens[(size_t)b * (k + 1) + i] = i <= kb ? out1[i] : -1;
+            if (argmax_out)
+                argmax_out[(size_t)b * (k + 1) + i] = i <= kb ? arg1[i] : -1;
+        }
+        num_accepted[b] = acc;
+    }
+    free(out1);
+    free(arg1);
+    return rc;
 }
 
 /*

@@ -454,6 +454,87 @@ def check_tree_unused_rows(lib):
     assert r["num_accepted"][0] == 2 and r["out_tokens"][0].tolist() == [2, 3, 4, -1]
 
 
+# ---- per-request draft lengths -----------------------------------------------------
+# Page "TensorRT-LLM source teardown (10)", acceptance-pipeline step 2: with
+# ragged verification each request is verified over its own window while the
+# buffers stay padded to the static maximum; padding must never count.
+
+def _ragged_case(rng, B, k, V, dtype):
+    t = rng.normal(0, 1.5, (B, k + 1, V)).astype(np.float32)
+    d = (t[:, :k] + rng.normal(0, 1.0, (B, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    # drafts often equal to the target's favourite token, so tests accept
+    fav = rng.random((B, k)) < 0.5
+    x[fav] = np.argmax(t[:, :k], axis=2)[fav]
+    u = rng.random((B, k + 1), dtype=np.float32)
+    if dtype == "bf16":
+        t, d = to_bf16_bits(t), to_bf16_bits(d)
+    return t, d, x, u
+
+
+def check_ragged_is_each_request_alone(lib):
+    """Request b with draft length k_b (clamped to [0, k]) gives what a request of
+    length k_b gives on its own: first k_b + 1 target rows, first k_b draft rows and
+    drafts, uniforms 0..k_b; the padded slots read -1 (tokens) and 0 (P, Q)."""
+    rng = np.random.default_rng(31)
+    B, k, V, T = 24, 4, 40, 0.9
+    for dtype in ("f32", "bf16"):
+        t, d, x, u = _ragged_case(rng, B, k, V, dtype)
+        lens = rng.integers(-2, k + 3, B).astype(np.int32)
+        r = oracle.stochastic(t, d, x, u, T, draft_lens=lens, lib=lib)
+        for b in range(B):
+            kb = int(min(max(lens[b], 0), k))
+            sl = slice(b, b + 1)
+            alone = oracle.stochastic(t[sl, :kb + 1], d[sl, :kb] if kb else None, x[sl, :kb],
+                                      u[sl, :kb + 1], T, lib=lib)
+            assert r["num_accepted"][b] == alone["num_accepted"][0]
+            assert np.array_equal(r["out_tokens"][b, :kb + 1], alone["out_tokens"][0])
+            assert np.all(r["out_tokens"][b, kb + 1:] == -1)
+            assert np.array_equal(r["p_at_draft"][b, :kb], alone["p_at_draft"][0])
+            assert np.all(r["p_at_draft"][b, kb:] == 0) and np.all(r["q_at_draft"][b, kb:] == 0)
+        # every draft length at k: the padded call is the plain call
+        full = oracle.stochastic(t, d, x, u, T, draft_lens=np.full(B, k, np.int32), lib=lib)
+        plain = oracle.stochastic(t, d, x, u, T, lib=lib)
+        for key in ("out_tokens", "num_accepted", "p_at_draft", "q_at_draft"):
+            assert np.array_equal(full[key], plain[key]), key
+
+
+def check_ragged_zero_length_samples_row_zero(lib):
+    """Draft length 0: no test; the token is the inverse-CDF draw of softmax(row 0 / T)
+    at uniforms[b, 0] (library softmax and searchsorted), then -1 padding."""
+    rng = np.random.default_rng(32)
+    B, k, V, T = 64, 3, 12, 0.7
+    t, d, x, u = _ragged_case(rng, B, k, V, "f32")
+    r = oracle.stochastic(t, d, x, u, T, draft_lens=np.zeros(B, np.int32), lib=lib)
+    p0 = lib_softmax(t[:, 0], T)
+    assert np.all(r["num_accepted"] == 0)
+    assert np.all(r["out_tokens"][:, 1:] == -1)
+    for b in range(B):
+        j, _ = lib_inverse_cdf(p0[b], float(u[b, 0]))
+        assert r["out_tokens"][b, 0] == j, b
+
+
+def check_greedy_ragged(lib):
+    """Greedy with draft length k_b: leading matches against np.argmax over rows
+    0..k_b-1 only, then the argmax of row s; -1 after it."""
+    rng = np.random.default_rng(33)
+    B, k, V = 40, 5, 30
+    t = np.round(rng.normal(0, 2, (B, k + 1, V))).astype(np.float32)
+    a = np.argmax(t, axis=2)
+    x = a[:, :k].astype(np.int32).copy()
+    x[rng.random((B, k)) < 0.15] = 0
+    lens = rng.integers(0, k + 1, B).astype(np.int32)
+    r = oracle.greedy(t, x, draft_lens=lens, lib=lib)
+    for b in range(B):
+        kb = int(lens[b])
+        s = 0
+        while s < kb and x[b, s] == a[b, s]:
+            s += 1
+        assert r["num_accepted"][b] == s
+        want = list(x[b, :s]) + [a[b, s]] + [-1] * (k - s)
+        assert list(r["out_tokens"][b]) == want, b
+
+
 ALL_CHECKS = [
     check_softmax_vs_library,
     check_identical_draft_accepts_all,
@@ -469,4 +550,7 @@ ALL_CHECKS = [
     check_tree_bruteforce,
     check_chain_tree_equals_greedy,
     check_tree_unused_rows,
+    check_ragged_is_each_request_alone,
+    check_ragged_zero_length_samples_row_zero,
+    check_greedy_ragged,
 ]

@@ -36,6 +36,14 @@ MUTANTS = {
     "tree highest tie": ("if (m > best_m) { /* strictly longer", "if (m >= best_m) { /* strictly longer"),
     "tree compares own row": ("if (tok[child] != a[row[m]])", "if (tok[child] != a[child])"),
     "tree emits last node token": ("out[best_m] = a[row[best_m]];", "out[best_m] = tok[row[best_m]];"),
+    "ragged drops the final token": (
+        "out_tokens[(size_t)b * (k + 1) + i] = i <= kb ? out1[i] : -1;\n            if (margins)",
+        "out_tokens[(size_t)b * (k + 1) + i] = i < kb ? out1[i] : -1;\n            if (margins)"),
+    "ragged ignores lengths": ("return kb < 0 ? 0 : (kb > k ? k : kb);", "return k;"),
+    "ragged final uniform at k": ("uniforms + (size_t)b * (k + 1), temperature, 1, kb, V,",
+                                  "uniforms + (size_t)b * (k + 1) + (k - kb), temperature, 1, kb, V,"),
+    "greedy ragged reads full rows": ("rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb, V, out1, &acc,",
+                                      "rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb < k ? kb + 1 : kb, V, out1, &acc,"),
 }
 
 
