@@ -108,15 +108,8 @@ def _workspace(ws, nbytes: int, device: torch.device) -> torch.Tensor:
     return ws
 
 
-def spec_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor | None,
-                           draft_tokens: torch.Tensor | None, uniforms: torch.Tensor,
-                           temperature: float, *, out_tokens=None, num_accepted=None,
-                           p_at_draft=None, q_at_draft=None, workspace=None, stream=None):
-    """Stochastic verification; returns ``(out_tokens[B,k+1], num_accepted[B])``.
-
-    ``p_at_draft`` / ``q_at_draft`` (float32 [B, k]), when given, receive the
-    target and draft probabilities of each draft token.
-    """
+def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
+                temperature, out_tokens, num_accepted, p_at_draft, q_at_draft, workspace, stream):
     device = target_logits.device
     dt = _dtype_code(target_logits)
     if target_logits.dim() != 3:
@@ -129,6 +122,8 @@ def spec_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tens
         _dev(draft_tokens, "draft_tokens", device, torch.int32, (B, k))
     else:
         draft_logits = draft_tokens = None
+    if draft_lens is not None:
+        _dev(draft_lens, "draft_lens", device, torch.int32, (B,))
     _dev(uniforms, "uniforms", device, torch.float32, (B, k + 1))
     if out_tokens is None:
         out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
@@ -141,17 +136,47 @@ def spec_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tens
             _dev(t, name, device, torch.float32, (B, k))
     nbytes = spec_verify_workspace_bytes(MODE_STOCHASTIC, B, k + 1, V, dt)
     ws = _workspace(workspace, nbytes, device)
-    st = _lib.load().spec_verify_stochastic(
-        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
-        float(temperature), B, k, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(p_at_draft),
-        _ptr(q_at_draft), _ptr(ws), ws.numel(), _stream(device, stream))
-    _lib.check("spec_verify_stochastic", st)
+    lib = _lib.load()
+    head = (_ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens))
+    tail = (_ptr(uniforms), float(temperature), B, k, V, _ptr(out_tokens), _ptr(num_accepted),
+            _ptr(p_at_draft), _ptr(q_at_draft), _ptr(ws), ws.numel(), _stream(device, stream))
+    if fn == "spec_verify_stochastic":
+        st = lib.spec_verify_stochastic(*head, *tail)
+    else:
+        st = lib.spec_verify_stochastic_ragged(*head, _ptr(draft_lens), *tail)
+    _lib.check(fn, st)
     return out_tokens, num_accepted
 
 
-def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor | None, *,
-                       out_tokens=None, num_accepted=None, workspace=None, stream=None):
-    """Greedy verification; returns ``(out_tokens[B,k+1], num_accepted[B])``."""
+def spec_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor | None,
+                           draft_tokens: torch.Tensor | None, uniforms: torch.Tensor,
+                           temperature: float, *, out_tokens=None, num_accepted=None,
+                           p_at_draft=None, q_at_draft=None, workspace=None, stream=None):
+    """Stochastic verification; returns ``(out_tokens[B,k+1], num_accepted[B])``.
+
+    ``p_at_draft`` / ``q_at_draft`` (float32 [B, k]), when given, receive the
+    target and draft probabilities of each draft token.
+    """
+    return _stochastic("spec_verify_stochastic", target_logits, draft_logits, draft_tokens, None,
+                       uniforms, temperature, out_tokens, num_accepted, p_at_draft, q_at_draft,
+                       workspace, stream)
+
+
+def spec_verify_stochastic_ragged(target_logits: torch.Tensor, draft_logits: torch.Tensor | None,
+                                  draft_tokens: torch.Tensor | None,
+                                  draft_lens: torch.Tensor | None, uniforms: torch.Tensor,
+                                  temperature: float, *, out_tokens=None, num_accepted=None,
+                                  p_at_draft=None, q_at_draft=None, workspace=None,
+                                  stream=None):
+    """Stochastic verification with a draft length per request (int32 [B] on the
+    device, clamped to [0, k]; None = k for all)."""
+    return _stochastic("spec_verify_stochastic_ragged", target_logits, draft_logits,
+                       draft_tokens, draft_lens, uniforms, temperature, out_tokens,
+                       num_accepted, p_at_draft, q_at_draft, workspace, stream)
+
+
+def _greedy(fn, target_logits, draft_tokens, draft_lens, out_tokens, num_accepted, workspace,
+            stream):
     device = target_logits.device
     dt = _dtype_code(target_logits)
     if target_logits.dim() != 3:
@@ -163,6 +188,8 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor |
         _dev(draft_tokens, "draft_tokens", device, torch.int32, (B, k))
     else:
         draft_tokens = None
+    if draft_lens is not None:
+        _dev(draft_lens, "draft_lens", device, torch.int32, (B,))
     if out_tokens is None:
         out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
     if num_accepted is None:
@@ -171,11 +198,31 @@ def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor |
     _dev(num_accepted, "num_accepted", device, torch.int32, (B,))
     nbytes = spec_verify_workspace_bytes(MODE_GREEDY, B, k + 1, V, dt)
     ws = _workspace(workspace, nbytes, device)
-    st = _lib.load().spec_verify_greedy(
-        _ptr(target_logits), dt, _ptr(draft_tokens), B, k, V, _ptr(out_tokens),
-        _ptr(num_accepted), _ptr(ws), ws.numel(), _stream(device, stream))
-    _lib.check("spec_verify_greedy", st)
+    lib = _lib.load()
+    tail = (B, k, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(ws), ws.numel(),
+            _stream(device, stream))
+    if fn == "spec_verify_greedy":
+        st = lib.spec_verify_greedy(_ptr(target_logits), dt, _ptr(draft_tokens), *tail)
+    else:
+        st = lib.spec_verify_greedy_ragged(_ptr(target_logits), dt, _ptr(draft_tokens),
+                                           _ptr(draft_lens), *tail)
+    _lib.check(fn, st)
     return out_tokens, num_accepted
+
+
+def spec_verify_greedy(target_logits: torch.Tensor, draft_tokens: torch.Tensor | None, *,
+                       out_tokens=None, num_accepted=None, workspace=None, stream=None):
+    """Greedy verification; returns ``(out_tokens[B,k+1], num_accepted[B])``."""
+    return _greedy("spec_verify_greedy", target_logits, draft_tokens, None, out_tokens,
+                   num_accepted, workspace, stream)
+
+
+def spec_verify_greedy_ragged(target_logits: torch.Tensor, draft_tokens: torch.Tensor | None,
+                              draft_lens: torch.Tensor | None, *, out_tokens=None,
+                              num_accepted=None, workspace=None, stream=None):
+    """Greedy verification with a draft length per request (int32 [B] on the device)."""
+    return _greedy("spec_verify_greedy_ragged", target_logits, draft_tokens, draft_lens,
+                   out_tokens, num_accepted, workspace, stream)
 
 
 def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,

@@ -21,7 +21,9 @@ EXPORTED = (
     "spec_verify_profile_events",
     "spec_verify_set_schedule",
     "spec_verify_stochastic",
+    "spec_verify_stochastic_ragged",
     "spec_verify_greedy",
+    "spec_verify_greedy_ragged",
     "spec_verify_tree",
 )
 
@@ -60,8 +62,13 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_stochastic.argtypes = [P, P, I, P, P, ctypes.c_float, I, I, I, P, P, P, P,
                                            P, Z, P]
     lib.spec_verify_stochastic.restype = I
+    lib.spec_verify_stochastic_ragged.argtypes = [P, P, I, P, P, P, ctypes.c_float, I, I, I, P,
+                                                  P, P, P, P, Z, P]
+    lib.spec_verify_stochastic_ragged.restype = I
     lib.spec_verify_greedy.argtypes = [P, I, P, I, I, I, P, P, P, Z, P]
     lib.spec_verify_greedy.restype = I
+    lib.spec_verify_greedy_ragged.argtypes = [P, I, P, P, I, I, I, P, P, P, Z, P]
+    lib.spec_verify_greedy_ragged.restype = I
     lib.spec_verify_tree.argtypes = [P, I, P, P, I, I, I, I, I, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.restype = I
     _lib = lib

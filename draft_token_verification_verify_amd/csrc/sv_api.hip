@@ -94,11 +94,12 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* st
     return finish(sv::run_fill_zero(workspace, workspace_bytes, (hipStream_t)stream));
 }
 
-int spec_verify_stochastic(const void* target_logits, const void* draft_logits, int dtype,
-                           const int32_t* draft_tokens, const float* uniforms,
-                           float temperature, int B, int k, int V, int32_t* out_tokens,
-                           int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+int spec_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,
+                                  int dtype, const int32_t* draft_tokens,
+                                  const int32_t* draft_lens, const float* uniforms,
+                                  float temperature, int B, int k, int V, int32_t* out_tokens,
+                                  int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
@@ -121,6 +122,7 @@ int spec_verify_stochastic(const void* target_logits, const void* draft_logits, 
     c.dtype = dtype;
     c.vec = vec_ok(target_logits, V, eb) && vec_ok(c.draft, V, eb);
     c.draft_tokens = draft_tokens;
+    c.draft_lens = draft_lens;
     c.uniforms = uniforms;
     c.temperature = temperature;
     c.B = B;
@@ -134,9 +136,21 @@ int spec_verify_stochastic(const void* target_logits, const void* draft_logits, 
     return finish(sv::run_stochastic(c, g, (hipStream_t)stream, next_events()));
 }
 
-int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draft_tokens, int B,
-                       int k, int V, int32_t* out_tokens, int32_t* num_accepted,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+int spec_verify_stochastic(const void* target_logits, const void* draft_logits, int dtype,
+                           const int32_t* draft_tokens, const float* uniforms,
+                           float temperature, int B, int k, int V, int32_t* out_tokens,
+                           int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    return spec_verify_stochastic_ragged(target_logits, draft_logits, dtype, draft_tokens,
+                                         nullptr, uniforms, temperature, B, k, V, out_tokens,
+                                         num_accepted, p_at_draft, q_at_draft, workspace,
+                                         workspace_bytes, stream);
+}
+
+int spec_verify_greedy_ragged(const void* target_logits, int dtype, const int32_t* draft_tokens,
+                              const int32_t* draft_lens, int B, int k, int V,
+                              int32_t* out_tokens, int32_t* num_accepted, void* workspace,
+                              size_t workspace_bytes, void* stream) {
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
@@ -154,6 +168,7 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
     c.dtype = dtype;
     c.vec = vec_ok(target_logits, V, eb);
     c.draft_tokens = draft_tokens;
+    c.draft_lens = draft_lens;
     c.B = B;
     c.k = k;
     c.V = V;
@@ -161,6 +176,14 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
     c.num_accepted = num_accepted;
     c.workspace = workspace;
     return finish(sv::run_greedy(c, g, (hipStream_t)stream, next_events()));
+}
+
+int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draft_tokens, int B,
+                       int k, int V, int32_t* out_tokens, int32_t* num_accepted,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return spec_verify_greedy_ragged(target_logits, dtype, draft_tokens, nullptr, B, k, V,
+                                     out_tokens, num_accepted, workspace, workspace_bytes,
+                                     stream);
 }
 
 int spec_verify_tree(const void* target_logits, int dtype, const int32_t* node_tokens,

@@ -32,6 +32,7 @@ struct ArgmaxArgs {
     Partial16* partials;  // [B, R, S]: f0 = chunk max, f1 = its lowest index (int bits)
     // greedy
     const int32_t* draft_tokens;  // [B, k]
+    const int32_t* lens;          // [B] draft length per request, or null (all k)
     int k;
     // tree
     const int32_t* node_tokens;  // [B, N+1]
@@ -50,6 +51,14 @@ template <typename T, int U, int MODE>
 struct ArgmaxOp : ArgmaxArgs {
     __device__ const T* row(int b, int r) const {
         return static_cast<const T*>(target) + ((size_t)b * R + r) * (size_t)V;
+    }
+
+    // Greedy draft length of request b: lens[b] clamped to [0, k], or k.
+    __device__ int kb_of(int b) const { return lens ? min(max(lens[b], 0), k) : k; }
+    // Greedy rows past a request's draft window are not read.
+    __device__ bool skip(int b, int r) const { return MODE == 1 && lens && r > kb_of(b); }
+    __device__ void publish_skipped(Partial16* dst) const {
+        publish(dst, -INFINITY, __int_as_float(INT_MAX), 0.0);
     }
 
     __device__ void publish(Partial16* dst, float f0, float f1, double d) const {
@@ -147,11 +156,12 @@ struct ArgmaxOp : ArgmaxArgs {
     __device__ void greedy_epilogue(int b) const {
         __shared__ int sh_a[kMaxK + 1];
         __shared__ int sh_s;
-        for (int r = threadIdx.x; r <= k; r += kThreads) sh_a[r] = row_argmax(b, r);
+        const int kb = kb_of(b);
+        for (int r = threadIdx.x; r <= kb; r += kThreads) sh_a[r] = row_argmax(b, r);
         __syncthreads();
         if (threadIdx.x == 0) {
             int s = 0;
-            while (s < k && draft_tokens[(size_t)b * k + s] == sh_a[s]) ++s;
+            while (s < kb && draft_tokens[(size_t)b * k + s] == sh_a[s]) ++s;
             sh_s = s;
             num_accepted[b] = s;
         }
@@ -313,6 +323,7 @@ hipError_t run_greedy(const GreedyCall& c, const Geometry& g, hipStream_t st,
                       const KernelEvents& ev) {
     ArgmaxArgs a = base_args(c.target, c.B, c.k + 1, c.V, g, c.workspace);
     a.draft_tokens = c.draft_tokens;
+    a.lens = c.draft_lens;
     a.k = c.k;
     a.out_tokens = c.out_tokens;
     a.num_accepted = c.num_accepted;

@@ -17,6 +17,7 @@ struct StochasticCall {
     int dtype;  // 0 f32, 1 bf16
     bool vec;   // rows are 16-byte aligned and V is a whole number of vectors
     const int32_t* draft_tokens;
+    const int32_t* draft_lens;  // [B] or null (every request uses k drafts)
     const float* uniforms;
     float temperature;
     int B, k, V;
@@ -32,6 +33,7 @@ struct GreedyCall {
     int dtype;
     bool vec;
     const int32_t* draft_tokens;
+    const int32_t* draft_lens;  // [B] or null
     int B, k, V;
     int32_t* out_tokens;
     int32_t* num_accepted;

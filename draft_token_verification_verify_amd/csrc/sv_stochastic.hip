@@ -48,6 +48,7 @@ struct CallArgs {
     const void* target;
     const void* draft;
     const int32_t* draft_tokens;
+    const int32_t* lens;     // [B] draft length per request, or null (all k)
     const float* uniforms;
     int B, k, V;
     int R, S, chunk;         // streaming geometry: rows per request, chunks per row
@@ -62,6 +63,22 @@ struct CallArgs {
     float* p_at_draft;       // [B, k] or null
     float* q_at_draft;       // [B, k] or null
 };
+
+// Draft length of request b: lens[b] clamped to [0, k] (per-request windows in
+// buffers padded to k; page "TensorRT-LLM source teardown (10)", acceptance
+// pipeline, step 2), or k.
+__device__ inline int draft_len(const CallArgs& a, int b) {
+    if (!a.lens) return a.k;
+    return min(max(a.lens[b], 0), a.k);
+}
+
+// Whether logits row r of request b (r = 0..k target, k+1.. draft) lies past
+// the request's draft window and is never read.
+__device__ inline bool row_unused(const CallArgs& a, int b, int r) {
+    if (!a.lens) return false;
+    const int kb = draft_len(a, b);
+    return (r <= a.k) ? (r > kb) : (r - a.k - 1 >= kb);
+}
 
 // p(x) = 2^((x - M) * c) / S in fp64; 0 when x or the whole row is -inf.
 __device__ inline double prob_of(float x, float M, double S, const Scale& k) {
@@ -81,6 +98,12 @@ struct StatsOp : CallArgs {
     }
 
     __device__ void publish(Partial16* dst, float f0, float f1, double d) const;
+    // Rows past a request's draft window are not read; their partial is the
+    // one of an all -inf chunk.
+    __device__ bool skip(int b, int r) const { return row_unused(*this, b, r); }
+    __device__ void publish_skipped(Partial16* dst) const {
+        publish(dst, -INFINITY, kPartialWritten, 1.0);
+    }
 
     // Workgroup reduction of per-thread (max m, fp64 sum s against m) into the
     // tile's (M, S): every thread's sum is rescaled to the common M with an fp64
@@ -160,6 +183,12 @@ __device__ void stats_tile_runtime(const CallArgs& a, int t, float* f0, float* f
     const int U = a.chunk / (kThreads * EPV);
     const int ch = t % a.S, rr = t / a.S;
     const int r = rr % a.R, b = rr / a.R;
+    if (op.skip(b, r)) {
+        *f0 = -INFINITY;
+        *f1 = kPartialWritten;
+        *d = 1.0;
+        return;
+    }
     const int lo = ch * a.chunk, hi = min(a.V, lo + a.chunk);
     const int nvec = (hi - lo) / EPV;
     const uint4* base = reinterpret_cast<const uint4*>(op.row(b, r) + lo);
@@ -205,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void stats_kernel(CallArgs a) {
 // The request's decision, computed by every sampler workgroup of the request
 // from the streaming partials (fixed chunk order, fp64).
 struct Decision {
-    int s;
+    int s, kb;  // stop row, draft length
     float mt, md;
     double st, sd;
 };
@@ -320,9 +349,10 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
     const int k = a.k;
+    const int kb = draft_len(a, b);
     // Wave 1 gathers the tested logits target[b, i, x_i] and draft[b, i, x_i]
     // while wave 0 merges the partials.
-    if (threadIdx.x >= 64 && threadIdx.x < 64 + k) {
+    if (threadIdx.x >= 64 && threadIdx.x < 64 + kb) {
         const int i = threadIdx.x - 64;
         const int32_t x = a.draft_tokens[(size_t)b * k + i];
         float gt = -INFINITY, gd = -INFINITY;
@@ -336,15 +366,15 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     const int i = threadIdx.x;  // test i runs in thread i (k <= 64)
     int32_t x = 0;
     float u = 0.f;
-    if (i < k) {
+    if (i < kb) {
         x = a.draft_tokens[(size_t)b * k + i];
         u = a.uniforms[(size_t)b * (k + 1) + i];
     }
     merge_rows<T>(a, b, sh_m, sh_s);
-    if (i < k) {
+    if (i < k) {  // past the window (i >= kb): no test, P = Q = 0 reported
         double P = 0.0, Q = 0.0;
         int acc = 0;
-        if (x >= 0 && x < a.V) {
+        if (i < kb && x >= 0 && x < a.V) {
             P = prob_of(sh_g[i], sh_m[i], sh_s[i], a.sc);
             Q = prob_of(sh_g[k + 1 + i], sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
             acc = (P >= Q) || ((double)u * Q < P);  // strict u < min(1, P/Q), no division
@@ -357,8 +387,8 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-        int s = k;
-        for (int j = 0; j < k; ++j)
+        int s = kb;
+        for (int j = 0; j < kb; ++j)
             if (!sh_acc[j]) { s = j; break; }
         sh_stop = s;
         if (write_outputs) a.num_accepted[b] = s;
@@ -372,10 +402,11 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
             // out_tokens[b, s] is written by the final draw.
         }
     out->s = s;
+    out->kb = kb;
     out->mt = sh_m[s];
     out->st = sh_s[s];
-    out->md = (s < k) ? sh_m[k + 1 + s] : 0.f;
-    out->sd = (s < k) ? sh_s[k + 1 + s] : 1.0;
+    out->md = (s < kb) ? sh_m[k + 1 + s] : 0.f;
+    out->sd = (s < kb) ? sh_s[k + 1 + s] : 1.0;
     __syncthreads();
 }
 
@@ -509,8 +540,8 @@ __device__ inline void store_segment(double* req_segs, const SegLayout& L, int c
 // exceeds u_k * Z; where rounding leaves every running mass at or below it, the
 // last entry with positive weight.
 template <typename T, bool VEC, int NSUB>
-__device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow, const T* drow,
-                             Weigher W) {
+__device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const T* trow,
+                             const T* drow, Weigher W) {
     __shared__ double sh_wave[kWaves];
     __shared__ int sh_first[kWaves], sh_last[kWaves], sh_seg;
     __shared__ double sh_run0;
@@ -521,7 +552,7 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, const T* trow,
     const int first = tid * G;
     const int len = max(0, min(G, n - first));   // this thread's run: segments [first, first + len)
     double* segs = a.segs + (size_t)b * L.per_request();
-    const double u = (double)a.uniforms[(size_t)b * (k + 1) + k];
+    const double u = (double)a.uniforms[(size_t)b * (k + 1) + kb];  // the final draw's uniform
 
     double v[kRegSegs];
     double grp, incl, Z;
@@ -632,7 +663,7 @@ __device__ void sample_item(const CallArgs& a, int b, int ch) {
     W.md = dc.md;
     W.r = dc.st / dc.sd;
     W.sc = a.sc;
-    W.residual = dc.s < k;
+    W.residual = dc.s < dc.kb;
     const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + dc.s) * (size_t)a.V;
     const T* drow = W.residual
         ? static_cast<const T*>(a.draft) + ((size_t)b * k + dc.s) * (size_t)a.V
@@ -646,7 +677,7 @@ __device__ void sample_item(const CallArgs& a, int b, int ch) {
     wait_stores();
     __syncthreads();
     if (arrive_last(ticket_of(a.tickets, b), (uint32_t)a.S2, &last_flag))
-        sample_final<T, VEC, NSUB>(a, b, dc.s, trow, drow, W);
+        sample_final<T, VEC, NSUB>(a, b, dc.s, dc.kb, trow, drow, W);
 }
 
 template <typename T, bool VEC, int NSUB>
@@ -751,6 +782,7 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.target = call.target;
     a.draft = call.draft;
     a.draft_tokens = call.draft_tokens;
+    a.lens = call.draft_lens;
     a.uniforms = call.uniforms;
     a.B = call.B;
     a.k = call.k;

@@ -26,6 +26,8 @@ constexpr float kPartialWritten = 1.0f;
 
 // One workgroup per tile, rows 16-byte aligned (V a whole number of vectors).
 //   Op::row(b, r) -> const T* row start
+//   Op::skip(b, r) -> true for a row that is not read (its partial is
+//     Op::publish_skipped's)
 //   Op::tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d): reduce the tile held in
 //     raw[U] (this thread's vectors; slots >= nvec are padding); thread 0 then
 //     calls Op::publish(&partials[t], f0, f1, d).
@@ -35,6 +37,10 @@ __device__ void stream_tile_vec(const Op& op) {
     const int t = blockIdx.x;
     const int ch = t % op.S, rr = t / op.S;
     const int r = rr % op.R, b = rr / op.R;
+    if (op.skip(b, r)) {  // row outside the request's window: nothing to read
+        if (threadIdx.x == 0) op.publish_skipped(op.partials + t);
+        return;
+    }
     const int lo = ch * op.chunk, hi = min(op.V, lo + op.chunk);
     const int nvec = (hi - lo) / EPV;
     const uint4* base = reinterpret_cast<const uint4*>(op.row(b, r) + lo);
@@ -55,6 +61,10 @@ __device__ void stream_tile_scalar(const Op& op) {
     const int t = blockIdx.x;
     const int ch = t % op.S, rr = t / op.S;
     const int r = rr % op.R, b = rr / op.R;
+    if (op.skip(b, r)) {
+        if (threadIdx.x == 0) op.publish_skipped(op.partials + t);
+        return;
+    }
     const int lo = ch * op.chunk, hi = min(op.V, lo + op.chunk);
     float f0, f1;
     double d;

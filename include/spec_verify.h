@@ -171,9 +171,9 @@ int spec_verify_profile_events(void *const *events, int n_pairs);
  *   p_at_draft, q_at_draft [B, k] float32 or NULL: P and Q of every draft
  *                 position (0 for an out-of-range draft id).
  *
- * The call launches two kernels: a single-pass streaming kernel that reads every
- * logits row once and decides s, and a sampler that reads only each request's
- * stop row(s).
+ * Work: one streaming pass that reads every logits row once (softmax
+ * statistics), then a sampler that reads only each request's stop row(s); in
+ * one launch or two kernels (see spec_verify_set_schedule).
  */
 int spec_verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
                            const int32_t *draft_tokens, const float *uniforms,
@@ -181,6 +181,30 @@ int spec_verify_stochastic(const void *target_logits, const void *draft_logits, 
                            int32_t *out_tokens, int32_t *num_accepted,
                            float *p_at_draft, float *q_at_draft,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stochastic verification with a draft length per request (page "TensorRT-LLM
+ * source teardown (10)", acceptance pipeline, step 2: ragged verification,
+ * every request verified over its own window while buffers stay padded to the
+ * static maximum k; padding never counts).
+ *
+ *   draft_lens [B] int32, device: request b uses its first
+ *              k_b = clamp(draft_lens[b], 0, k) drafts (NULL: k_b = k for all).
+ *
+ * Request b gives exactly what spec_verify_stochastic gives for that request
+ * alone with k = k_b: target rows 0..k_b, draft rows and tokens 0..k_b-1,
+ * uniforms[b, i] for test i < k_b and uniforms[b, k_b] for the final token.
+ * Rows past the window are not read.  The other arguments and layouts are those
+ * of spec_verify_stochastic (padded to k): out_tokens[b, k_b+1..k] = -1,
+ * p_at_draft / q_at_draft [b, k_b..k-1] = 0, num_accepted[b] <= k_b.
+ */
+int spec_verify_stochastic_ragged(const void *target_logits, const void *draft_logits,
+                                  int dtype, const int32_t *draft_tokens,
+                                  const int32_t *draft_lens, const float *uniforms,
+                                  float temperature, int B, int k, int V,
+                                  int32_t *out_tokens, int32_t *num_accepted,
+                                  float *p_at_draft, float *q_at_draft,
+                                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Greedy verification of B linear drafts of length k.
@@ -195,6 +219,18 @@ int spec_verify_stochastic(const void *target_logits, const void *draft_logits, 
 int spec_verify_greedy(const void *target_logits, int dtype, const int32_t *draft_tokens,
                        int B, int k, int V, int32_t *out_tokens, int32_t *num_accepted,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Greedy verification with a draft length per request (same reading as
+ * spec_verify_stochastic_ragged): request b compares its first
+ * k_b = clamp(draft_lens[b], 0, k) drafts with a_0..a_{k_b-1} and emits
+ * draft[0..s-1], a_s, then -1 up to position k; rows past k_b are not read.
+ * draft_lens [B] int32, device (NULL: k_b = k).
+ */
+int spec_verify_greedy_ragged(const void *target_logits, int dtype, const int32_t *draft_tokens,
+                              const int32_t *draft_lens, int B, int k, int V,
+                              int32_t *out_tokens, int32_t *num_accepted, void *workspace,
+                              size_t workspace_bytes, void *stream);
 
 /*
  * Tree (EAGLE-style) greedy verification.

@@ -18,7 +18,9 @@ PROB_ATOL = 1e-30
 GUARD = 1e-6
 
 
-def run_stochastic(case, *, workspace=None):
+def run_stochastic(case, *, workspace=None, draft_lens=None):
+    """Run the case through the binding (the ragged entry point when
+    ``draft_lens`` is given)."""
     dev = torch.device("cuda", 0)
     t = to_dev(case.target, case.dtype)
     d = to_dev(case.draft, case.dtype) if case.k > 0 else None
@@ -26,17 +28,25 @@ def run_stochastic(case, *, workspace=None):
     u = to_dev(case.uniforms.astype(np.float32))
     p = torch.empty((case.B, case.k), dtype=torch.float32, device=dev)
     q = torch.empty((case.B, case.k), dtype=torch.float32, device=dev)
-    out, acc = sv.spec_verify_stochastic(t, d, x, u, case.temperature, p_at_draft=p,
-                                         q_at_draft=q, workspace=workspace)
+    if draft_lens is None:
+        out, acc = sv.spec_verify_stochastic(t, d, x, u, case.temperature, p_at_draft=p,
+                                             q_at_draft=q, workspace=workspace)
+    else:
+        ln = to_dev(np.asarray(draft_lens, dtype=np.int32))
+        out, acc = sv.spec_verify_stochastic_ragged(t, d, x, ln, u, case.temperature,
+                                                    p_at_draft=p, q_at_draft=q,
+                                                    workspace=workspace)
     torch.cuda.synchronize()
     return dict(out_tokens=out.cpu().numpy(), num_accepted=acc.cpu().numpy(),
                 p_at_draft=p.cpu().numpy(), q_at_draft=q.cpu().numpy())
 
 
-def oracle_stochastic(case, rows=None):
+def oracle_stochastic(case, rows=None, draft_lens=None):
     sel = slice(None) if rows is None else rows
+    lens = None if draft_lens is None else np.asarray(draft_lens, dtype=np.int32)[sel]
     return oracle.stochastic(case.target[sel], case.draft[sel] if case.k > 0 else None,
-                             case.draft_tokens[sel], case.uniforms[sel], case.temperature)
+                             case.draft_tokens[sel], case.uniforms[sel], case.temperature,
+                             draft_lens=lens)
 
 
 def compare_stochastic(gpu, ref, rows=None, label=""):
@@ -65,10 +75,14 @@ def compare_stochastic(gpu, ref, rows=None, label=""):
     return int(amb.sum()), int((amb & ~same).sum())
 
 
-def run_greedy(case, *, workspace=None):
+def run_greedy(case, *, workspace=None, draft_lens=None):
     t = to_dev(case.target, case.dtype)
     x = to_dev(case.draft_tokens.astype(np.int32)) if case.k > 0 else None
-    out, acc = sv.spec_verify_greedy(t, x, workspace=workspace)
+    if draft_lens is None:
+        out, acc = sv.spec_verify_greedy(t, x, workspace=workspace)
+    else:
+        ln = to_dev(np.asarray(draft_lens, dtype=np.int32))
+        out, acc = sv.spec_verify_greedy_ragged(t, x, ln, workspace=workspace)
     torch.cuda.synchronize()
     return dict(out_tokens=out.cpu().numpy(), num_accepted=acc.cpu().numpy())
 

@@ -155,3 +155,19 @@ def test_schedule_switch(lib):
         assert lib.spec_verify_set_schedule(code) == _lib.OK
     assert lib.spec_verify_set_schedule(3) == _lib.INVALID_ARGUMENT
     assert lib.spec_verify_set_schedule(-1) == _lib.INVALID_ARGUMENT
+
+
+def test_ragged_entry_points_validate_like_the_dense_ones(lib):
+    # same host checks: unsupported dtype, bad sizes, too-small workspace
+    st = lib.spec_verify_stochastic_ragged
+    assert st(FAKE, FAKE, 9, FAKE, FAKE, FAKE, 1.0, 2, 3, 100, FAKE, FAKE, None, None, FAKE,
+              1 << 30, None) == _lib.UNSUPPORTED_DTYPE
+    assert st(FAKE, FAKE, _lib.BF16, FAKE, FAKE, FAKE, 0.0, 2, 3, 100, FAKE, FAKE, None, None,
+              FAKE, 1 << 30, None) == _lib.INVALID_ARGUMENT
+    assert st(FAKE, FAKE, _lib.BF16, FAKE, FAKE, FAKE, 1.0, 2, 3, 100, FAKE, FAKE, None, None,
+              FAKE, 8, None) == _lib.WORKSPACE_TOO_SMALL
+    gr = lib.spec_verify_greedy_ragged
+    assert gr(FAKE, _lib.F32, FAKE, FAKE, 0, 3, 100, FAKE, FAKE, FAKE, 1 << 30,
+              None) == _lib.INVALID_ARGUMENT
+    assert gr(FAKE, _lib.F32, FAKE, FAKE, 2, 100, 100, FAKE, FAKE, FAKE, 1 << 30,
+              None) == _lib.LIMIT_EXCEEDED
