@@ -58,6 +58,10 @@ def _open(path: str):
     lib.oracle_verify_stochastic_ragged.restype = i
     lib.oracle_verify_greedy_ragged.argtypes = [P, i, P, P, i, i, i, P, P, P]
     lib.oracle_verify_greedy_ragged.restype = i
+    lib.oracle_philox4x64_10.argtypes = [P, P, P]
+    lib.oracle_philox4x64_10.restype = None
+    lib.oracle_philox_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i, i, P]
+    lib.oracle_philox_uniforms.restype = None
     lib.oracle_verify_tree.argtypes = [P, i, P, P, i, i, i, i, i, P, P, P, P]
     lib.oracle_verify_tree.restype = i
     return lib
@@ -151,6 +155,24 @@ def greedy(target_logits, draft_tokens, *, draft_lens=None, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_verify_greedy failed with code {rc}")
     return dict(out_tokens=out, num_accepted=acc, argmax=am)
+
+
+def philox4x64_10(counter, key, *, lib=None) -> np.ndarray:
+    """One Philox4x64-10 block: four uint64 words for a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(counter, dtype=np.uint64).reshape(4)
+    k = np.ascontiguousarray(key, dtype=np.uint64).reshape(2)
+    out = np.empty(4, np.uint64)
+    (lib or _load()).oracle_philox4x64_10(_ptr(c), _ptr(k), _ptr(out))
+    return out
+
+
+def philox_uniforms(seed: int, offset: int, B: int, n: int, *, lib=None) -> np.ndarray:
+    """uniforms[B, n] float32 of request b, draw i: counter (offset, b, i // 4, 0),
+    key (seed, 0), word i % 4, (word >> 40) * 2^-24."""
+    out = np.empty((B, n), np.float32)
+    (lib or _load()).oracle_philox_uniforms(ctypes.c_uint64(seed), ctypes.c_uint64(offset), B,
+                                            n, _ptr(out))
+    return out
 
 
 def tree(target_logits, node_tokens, paths, *, lib=None):

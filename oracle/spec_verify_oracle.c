@@ -352,6 +352,63 @@ int oracle_verify_stochastic_ragged(const void *target_logits, const void *draft
     return rc;
 }
 
+/*
+ * Counter-based uniforms.  [TRTLLM] "Rejection sampling" draws its uniforms
+ * from Philox with a per-call (seed, offset) instead of taking them as an
+ * input.  Generator: Philox4x64-10 as published by Salmon, Moraes, Dror and
+ * Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011): ten rounds of
+ * two 64x64->128-bit multiplications by fixed odd constants, the high halves
+ * XORed with the other two counter words and the key, the key advanced by two
+ * Weyl constants between rounds.
+ * Reading (the pages fix no layout): the uniform of request b, draw i comes
+ * from the block at counter (offset, b, i / 4, 0) with key (seed, 0), word
+ * i % 4, as (word >> 40) * 2^-24 (24 random bits: exact in float32, in
+ * [0, 1)).  Draws i = 0..k-1 drive the tests, draw k (k_b with ragged lengths)
+ * the final token, exactly like the uniforms[b, i] input of the other calls.
+ */
+static void philox_round(uint64_t ctr[4], const uint64_t key[2])
+{
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    unsigned __int128 p0 = (unsigned __int128)M0 * ctr[0];
+    unsigned __int128 p1 = (unsigned __int128)M1 * ctr[2];
+    uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+    uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+    uint64_t c1 = ctr[1], c3 = ctr[3];
+    ctr[0] = hi1 ^ c1 ^ key[0];
+    ctr[1] = lo1;
+    ctr[2] = hi0 ^ c3 ^ key[1];
+    ctr[3] = lo0;
+}
+
+void oracle_philox4x64_10(const uint64_t counter[4], const uint64_t key[2], uint64_t out[4])
+{
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c[4] = {counter[0], counter[1], counter[2], counter[3]};
+    uint64_t k[2] = {key[0], key[1]};
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k[0] += W0;
+            k[1] += W1;
+        }
+        philox_round(c, k);
+    }
+    for (int i = 0; i < 4; ++i)
+        out[i] = c[i];
+}
+
+/* uniforms[b, i] for b < B, i < n under the layout above. */
+void oracle_philox_uniforms(uint64_t seed, uint64_t offset, int B, int n, float *uniforms)
+{
+    const uint64_t key[2] = {seed, 0};
+    for (int b = 0; b < B; ++b)
+        for (int i = 0; i < n; ++i) {
+            const uint64_t ctr[4] = {offset, (uint64_t)b, (uint64_t)(i / 4), 0};
+            uint64_t block[4];
+            oracle_philox4x64_10(ctr, key, block);
+            uniforms[(size_t)b * n + i] = (float)((double)(block[i % 4] >> 40) * 0x1p-24);
+        }
+}
+
 /* Index of the largest raw logit of one row; the lowest index wins a tie. */
 static int32_t argmax_row(const void *logits, int dtype, size_t row_offset, int V)
 {

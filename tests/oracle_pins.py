@@ -535,6 +535,50 @@ def check_greedy_ragged(lib):
         assert list(r["out_tokens"][b]) == want, b
 
 
+# ---- counter-based uniforms ------------------------------------------------------
+# Page "TensorRT-LLM source teardown (10)", "Rejection sampling": uniforms come
+# from Philox with a per-call (seed, offset).  The generator is Philox4x64-10;
+# NumPy's Philox bit generator is the same published generator and serves as
+# the library pin.
+
+def numpy_philox_block(counter, key) -> np.ndarray:
+    """Philox4x64-10 block at `counter` by NumPy.  NumPy's Philox advances its
+    256-bit little-endian counter before producing a block, so it is started one
+    below."""
+    n = sum(int(v) << (64 * i) for i, v in enumerate(counter)) - 1
+    n %= 1 << 256
+    prev = np.array([(n >> (64 * i)) & ((1 << 64) - 1) for i in range(4)], dtype=np.uint64)
+    bg = np.random.Philox(key=np.asarray(key, dtype=np.uint64), counter=prev)
+    return bg.random_raw(4)
+
+
+def check_philox_matches_numpy(lib):
+    """oracle Philox4x64-10 blocks equal NumPy's on random and edge counters/keys."""
+    rng = np.random.default_rng(41)
+    cases = [([0, 0, 0, 0], [0, 0]), ([0, 1, 0, 0], [1, 0]),
+             ([2**64 - 1, 2**64 - 1, 3, 0], [2**64 - 1, 2**64 - 1])]
+    for _ in range(20):
+        cases.append((rng.integers(0, 2**64 - 1, 4, dtype=np.uint64, endpoint=True),
+                      rng.integers(0, 2**64 - 1, 2, dtype=np.uint64, endpoint=True)))
+    for c, k in cases:
+        got = oracle.philox4x64_10(np.array(c, np.uint64), np.array(k, np.uint64), lib=lib)
+        assert np.array_equal(got, numpy_philox_block(c, k)), (c, k)
+
+
+def check_philox_uniform_layout(lib):
+    """uniforms[b, i] = top 24 bits of word i % 4 of the block at counter
+    (offset, b, i // 4, 0), key (seed, 0), times 2^-24; in [0, 1), mean 1/2."""
+    seed, offset, B, n = 0x1234_5678_9ABC_DEF0, 77, 5, 11
+    u = oracle.philox_uniforms(seed, offset, B, n, lib=lib)
+    for b in range(B):
+        for i in range(n):
+            w = numpy_philox_block([offset, b, i // 4, 0], [seed, 0])[i % 4]
+            assert u[b, i] == np.float32(float(int(w) >> 40) * 2.0**-24), (b, i)
+    big = oracle.philox_uniforms(9, 3, 2000, 50, lib=lib)
+    assert big.min() >= 0.0 and big.max() < 1.0
+    assert abs(float(big.mean()) - 0.5) < 5 * np.sqrt(1 / 12 / big.size)
+
+
 ALL_CHECKS = [
     check_softmax_vs_library,
     check_identical_draft_accepts_all,
@@ -553,4 +597,6 @@ ALL_CHECKS = [
     check_ragged_is_each_request_alone,
     check_ragged_zero_length_samples_row_zero,
     check_greedy_ragged,
+    check_philox_matches_numpy,
+    check_philox_uniform_layout,
 ]

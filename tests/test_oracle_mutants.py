@@ -44,6 +44,11 @@ MUTANTS = {
                                   "uniforms + (size_t)b * (k + 1) + (k - kb), temperature, 1, kb, V,"),
     "greedy ragged reads full rows": ("rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb, V, out1, &acc,",
                                       "rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb < k ? kb + 1 : kb, V, out1, &acc,"),
+    "philox wrong multiplier": ("M1 = 0xCA5A826395121157ull", "M1 = 0xCA5A826395121155ull"),
+    "philox key not advanced": ("            k[0] += W0;\n", ""),
+    "philox words swapped": ("    ctr[1] = lo1;\n", "    ctr[1] = lo0;\n"),
+    "philox nine rounds": ("for (int round = 0; round < 10; ++round)", "for (int round = 0; round < 9; ++round)"),
+    "philox uniform low bits": ("(block[i % 4] >> 40)", "(block[i % 4] & 0xFFFFFF)"),
 }
 
 
