@@ -109,7 +109,8 @@ def _workspace(ws, nbytes: int, device: torch.device) -> torch.Tensor:
 
 
 def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
-                temperature, out_tokens, num_accepted, p_at_draft, q_at_draft, workspace, stream):
+                temperature, out_tokens, num_accepted, p_at_draft, q_at_draft, workspace, stream,
+                seed=0, offset=0):
     device = target_logits.device
     dt = _dtype_code(target_logits)
     if target_logits.dim() != 3:
@@ -124,7 +125,8 @@ def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, unifo
         draft_logits = draft_tokens = None
     if draft_lens is not None:
         _dev(draft_lens, "draft_lens", device, torch.int32, (B,))
-    _dev(uniforms, "uniforms", device, torch.float32, (B, k + 1))
+    if fn != "spec_verify_stochastic_philox":
+        _dev(uniforms, "uniforms", device, torch.float32, (B, k + 1))
     if out_tokens is None:
         out_tokens = torch.empty((B, k + 1), dtype=torch.int32, device=device)
     if num_accepted is None:
@@ -142,8 +144,11 @@ def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, unifo
             _ptr(p_at_draft), _ptr(q_at_draft), _ptr(ws), ws.numel(), _stream(device, stream))
     if fn == "spec_verify_stochastic":
         st = lib.spec_verify_stochastic(*head, *tail)
-    else:
+    elif fn == "spec_verify_stochastic_ragged":
         st = lib.spec_verify_stochastic_ragged(*head, _ptr(draft_lens), *tail)
+    else:
+        st = lib.spec_verify_stochastic_philox(*head, _ptr(draft_lens), int(seed) & (2**64 - 1),
+                                               int(offset) & (2**64 - 1), *tail[1:])
     _lib.check(fn, st)
     return out_tokens, num_accepted
 
@@ -173,6 +178,21 @@ def spec_verify_stochastic_ragged(target_logits: torch.Tensor, draft_logits: tor
     return _stochastic("spec_verify_stochastic_ragged", target_logits, draft_logits,
                        draft_tokens, draft_lens, uniforms, temperature, out_tokens,
                        num_accepted, p_at_draft, q_at_draft, workspace, stream)
+
+
+def spec_verify_stochastic_philox(target_logits: torch.Tensor,
+                                  draft_logits: torch.Tensor | None,
+                                  draft_tokens: torch.Tensor | None,
+                                  draft_lens: torch.Tensor | None, seed: int, offset: int,
+                                  temperature: float, *, out_tokens=None, num_accepted=None,
+                                  p_at_draft=None, q_at_draft=None, workspace=None,
+                                  stream=None):
+    """Stochastic verification whose uniforms are Philox4x64-10 draws from
+    ``(seed, offset)`` (draw i of request b: counter (offset, b, i // 4, 0), key
+    (seed, 0), word i % 4, top 24 bits / 2^24)."""
+    return _stochastic("spec_verify_stochastic_philox", target_logits, draft_logits,
+                       draft_tokens, draft_lens, None, temperature, out_tokens, num_accepted,
+                       p_at_draft, q_at_draft, workspace, stream, seed=seed, offset=offset)
 
 
 def _greedy(fn, target_logits, draft_tokens, draft_lens, out_tokens, num_accepted, workspace,

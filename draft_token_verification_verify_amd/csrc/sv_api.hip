@@ -94,20 +94,22 @@ int spec_verify_workspace_init(void* workspace, size_t workspace_bytes, void* st
     return finish(sv::run_fill_zero(workspace, workspace_bytes, (hipStream_t)stream));
 }
 
-int spec_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,
-                                  int dtype, const int32_t* draft_tokens,
-                                  const int32_t* draft_lens, const float* uniforms,
-                                  float temperature, int B, int k, int V, int32_t* out_tokens,
-                                  int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
-                                  void* workspace, size_t workspace_bytes, void* stream) {
+static int stochastic_impl(const void* target_logits, const void* draft_logits, int dtype,
+                           const int32_t* draft_tokens, const int32_t* draft_lens,
+                           const float* uniforms, bool counter_uniforms, uint64_t seed,
+                           uint64_t offset, float temperature, int B, int k, int V,
+                           int32_t* out_tokens, int32_t* num_accepted, float* p_at_draft,
+                           float* q_at_draft, void* workspace, size_t workspace_bytes,
+                           void* stream) {
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!(temperature >= SPEC_VERIFY_MIN_TEMPERATURE) ||
         !(temperature <= SPEC_VERIFY_MAX_TEMPERATURE))
         return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (!target_logits || !uniforms || !out_tokens || !num_accepted || !workspace)
+    if (!target_logits || !out_tokens || !num_accepted || !workspace)
         return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!counter_uniforms && !uniforms) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
     sv::Geometry g;
@@ -123,7 +125,9 @@ int spec_verify_stochastic_ragged(const void* target_logits, const void* draft_l
     c.vec = vec_ok(target_logits, V, eb) && vec_ok(c.draft, V, eb);
     c.draft_tokens = draft_tokens;
     c.draft_lens = draft_lens;
-    c.uniforms = uniforms;
+    c.uniforms = counter_uniforms ? nullptr : uniforms;
+    c.seed = seed;
+    c.offset = offset;
     c.temperature = temperature;
     c.B = B;
     c.k = k;
@@ -136,15 +140,36 @@ int spec_verify_stochastic_ragged(const void* target_logits, const void* draft_l
     return finish(sv::run_stochastic(c, g, (hipStream_t)stream, next_events()));
 }
 
+int spec_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,
+                                  int dtype, const int32_t* draft_tokens,
+                                  const int32_t* draft_lens, const float* uniforms,
+                                  float temperature, int B, int k, int V, int32_t* out_tokens,
+                                  int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    return stochastic_impl(target_logits, draft_logits, dtype, draft_tokens, draft_lens,
+                           uniforms, false, 0, 0, temperature, B, k, V, out_tokens, num_accepted,
+                           p_at_draft, q_at_draft, workspace, workspace_bytes, stream);
+}
+
 int spec_verify_stochastic(const void* target_logits, const void* draft_logits, int dtype,
                            const int32_t* draft_tokens, const float* uniforms,
                            float temperature, int B, int k, int V, int32_t* out_tokens,
                            int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
                            void* workspace, size_t workspace_bytes, void* stream) {
-    return spec_verify_stochastic_ragged(target_logits, draft_logits, dtype, draft_tokens,
-                                         nullptr, uniforms, temperature, B, k, V, out_tokens,
-                                         num_accepted, p_at_draft, q_at_draft, workspace,
-                                         workspace_bytes, stream);
+    return stochastic_impl(target_logits, draft_logits, dtype, draft_tokens, nullptr, uniforms,
+                           false, 0, 0, temperature, B, k, V, out_tokens, num_accepted,
+                           p_at_draft, q_at_draft, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_stochastic_philox(const void* target_logits, const void* draft_logits, int dtype,
+                                  const int32_t* draft_tokens, const int32_t* draft_lens,
+                                  uint64_t seed, uint64_t offset, float temperature, int B, int k,
+                                  int V, int32_t* out_tokens, int32_t* num_accepted,
+                                  float* p_at_draft, float* q_at_draft, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+    return stochastic_impl(target_logits, draft_logits, dtype, draft_tokens, draft_lens, nullptr,
+                           true, seed, offset, temperature, B, k, V, out_tokens, num_accepted,
+                           p_at_draft, q_at_draft, workspace, workspace_bytes, stream);
 }
 
 int spec_verify_greedy_ragged(const void* target_logits, int dtype, const int32_t* draft_tokens,

@@ -18,7 +18,8 @@ struct StochasticCall {
     bool vec;   // rows are 16-byte aligned and V is a whole number of vectors
     const int32_t* draft_tokens;
     const int32_t* draft_lens;  // [B] or null (every request uses k drafts)
-    const float* uniforms;
+    const float* uniforms;      // [B, k+1], or null: Philox draws from (seed, offset)
+    unsigned long long seed, offset;
     float temperature;
     int B, k, V;
     int32_t* out_tokens;

@@ -49,7 +49,8 @@ struct CallArgs {
     const void* draft;
     const int32_t* draft_tokens;
     const int32_t* lens;     // [B] draft length per request, or null (all k)
-    const float* uniforms;
+    const float* uniforms;   // [B, k+1], or null: counter-based draws from (seed, offset)
+    unsigned long long seed, offset;
     int B, k, V;
     int R, S, chunk;         // streaming geometry: rows per request, chunks per row
     int S2, chunk2;          // sampler geometry: chunks per stop row
@@ -78,6 +79,46 @@ __device__ inline bool row_unused(const CallArgs& a, int b, int r) {
     if (!a.lens) return false;
     const int kb = draft_len(a, b);
     return (r <= a.k) ? (r > kb) : (r - a.k - 1 >= kb);
+}
+
+// Counter-based uniforms (page "TensorRT-LLM source teardown (10)", "Rejection
+// sampling": a per-call seed and offset instead of an input tensor).
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy
+// as 1, 2, 3", SC 2011): ten rounds, each multiplying counter words 0 and 2 by
+// two odd 64-bit constants (128-bit products), XORing the high halves with the
+// other two words and the key, and keeping the low halves; the key advances by
+// two Weyl constants between rounds.  Draw i of request b is word i % 4 of the
+// block at counter (offset, b, i / 4, 0) with key (seed, 0), as its top 24
+// bits times 2^-24: exact in float32, in [0, 1).
+__device__ inline float philox_uniform(unsigned long long seed, unsigned long long offset, int b,
+                                       int i) {
+    unsigned long long c0 = offset, c1 = (unsigned long long)b, c2 = (unsigned long long)(i / 4),
+                       c3 = 0ull;
+    unsigned long long k0 = seed, k1 = 0ull;
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        if (round > 0) {
+            k0 += 0x9E3779B97F4A7C15ull;
+            k1 += 0xBB67AE8584CAA73Bull;
+        }
+        const unsigned long long m0 = 0xD2E7470EE14C6C93ull, m1 = 0xCA5A826395121157ull;
+        const unsigned long long hi0 = __umul64hi(m0, c0), lo0 = m0 * c0;
+        const unsigned long long hi1 = __umul64hi(m1, c2), lo1 = m1 * c2;
+        const unsigned long long n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    const int w = i % 4;
+    const unsigned long long word = w == 0 ? c0 : w == 1 ? c1 : w == 2 ? c2 : c3;
+    return (float)(word >> 40) * 0x1p-24f;
+}
+
+// Draw i of request b: the input tensor's uniforms[b, i], or the counter-based one.
+__device__ inline float uniform_at(const CallArgs& a, int b, int i) {
+    if (a.uniforms) return a.uniforms[(size_t)b * (a.k + 1) + i];
+    return philox_uniform(a.seed, a.offset, b, i);
 }
 
 // p(x) = 2^((x - M) * c) / S in fp64; 0 when x or the whole row is -inf.
@@ -368,7 +409,7 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     float u = 0.f;
     if (i < kb) {
         x = a.draft_tokens[(size_t)b * k + i];
-        u = a.uniforms[(size_t)b * (k + 1) + i];
+        u = uniform_at(a, b, i);
     }
     merge_rows<T>(a, b, sh_m, sh_s);
     if (i < k) {  // past the window (i >= kb): no test, P = Q = 0 reported
@@ -552,7 +593,7 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const 
     const int first = tid * G;
     const int len = max(0, min(G, n - first));   // this thread's run: segments [first, first + len)
     double* segs = a.segs + (size_t)b * L.per_request();
-    const double u = (double)a.uniforms[(size_t)b * (k + 1) + kb];  // the final draw's uniform
+    const double u = (double)uniform_at(a, b, kb);  // the final draw's uniform
 
     double v[kRegSegs];
     double grp, incl, Z;
@@ -784,6 +825,8 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.draft_tokens = call.draft_tokens;
     a.lens = call.draft_lens;
     a.uniforms = call.uniforms;
+    a.seed = call.seed;
+    a.offset = call.offset;
     a.B = call.B;
     a.k = call.k;
     a.V = call.V;

@@ -207,6 +207,23 @@ int spec_verify_stochastic_ragged(const void *target_logits, const void *draft_l
                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * Stochastic verification with counter-based uniforms instead of an input
+ * tensor (page "TensorRT-LLM source teardown (10)", "Rejection sampling": a
+ * per-call seed and offset).  Draw i of request b (tests i < k_b, final token
+ * k_b) is word i % 4 of the Philox4x64-10 block (Salmon et al., SC 2011) at
+ * counter (offset, b, i / 4, 0) with key (seed, 0), as its top 24 bits times
+ * 2^-24.  Otherwise identical to spec_verify_stochastic_ragged (draft_lens may
+ * be NULL); a caller advances `offset` between calls to get fresh draws.
+ */
+int spec_verify_stochastic_philox(const void *target_logits, const void *draft_logits,
+                                  int dtype, const int32_t *draft_tokens,
+                                  const int32_t *draft_lens, uint64_t seed, uint64_t offset,
+                                  float temperature, int B, int k, int V,
+                                  int32_t *out_tokens, int32_t *num_accepted,
+                                  float *p_at_draft, float *q_at_draft,
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * Greedy verification of B linear drafts of length k.
  *
  *   target_logits [B, k+1, V] dtype; draft_tokens [B, k] int32 (NULL if k == 0).
