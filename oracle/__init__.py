@@ -58,6 +58,10 @@ def _open(path: str):
     lib.oracle_verify_stochastic_ragged.restype = i
     lib.oracle_verify_greedy_ragged.argtypes = [P, i, P, P, i, i, i, P, P, P]
     lib.oracle_verify_greedy_ragged.restype = i
+    lib.oracle_verify_stochastic_filtered.argtypes = [P, P, i, P, P, ctypes.c_double, i,
+                                                      ctypes.c_double, ctypes.c_double, i, i, i,
+                                                      P, P, P, P, P, P]
+    lib.oracle_verify_stochastic_filtered.restype = i
     lib.oracle_philox4x64_10.argtypes = [P, P, P]
     lib.oracle_philox4x64_10.restype = None
     lib.oracle_philox_uniforms.argtypes = [ctypes.c_uint64, ctypes.c_uint64, i, i, P]
@@ -98,14 +102,17 @@ def _ptr(a: np.ndarray | None):
 
 
 def stochastic(target_logits, draft_logits, draft_tokens, uniforms, temperature, *,
-               draft_lens=None, lib=None):
+               draft_lens=None, top_k=0, top_p=1.0, min_p=0.0, lib=None):
     """Oracle stochastic verify.
 
     Returns ``dict(out_tokens[B,k+1] int32, num_accepted[B] int32,
     p_at_draft[B,k] f64, q_at_draft[B,k] f64, margins[B,k+1] f64)``.
     With ``draft_lens`` ([B] ints), request b uses only its first
-    ``draft_lens[b]`` drafts (clamped to [0, k]).
+    ``draft_lens[b]`` drafts (clamped to [0, k]).  With ``top_k``, ``top_p`` or
+    ``min_p`` set, every row is filtered first and the result also holds
+    ``filter_margins[B]``.
     """
+    filtered = top_k != 0 or top_p != 1.0 or min_p != 0.0
     t, dt = _logits(target_logits)
     B, k1, V = t.shape
     k = k1 - 1
@@ -121,7 +128,14 @@ def stochastic(target_logits, draft_logits, draft_tokens, uniforms, temperature,
     pp = np.empty((B, k), np.float64)
     qq = np.empty((B, k), np.float64)
     mg = np.empty((B, k + 1), np.float64)
-    if draft_lens is None:
+    fm = np.full((B,), np.inf, np.float64)
+    if filtered:
+        assert draft_lens is None, "filtering with ragged lengths is not modelled"
+        rc = (lib or _load()).oracle_verify_stochastic_filtered(
+            _ptr(t), _ptr(d), dt, _ptr(x), _ptr(u), float(temperature), int(top_k),
+            float(top_p), float(min_p), B, k, V, _ptr(out), _ptr(acc), _ptr(pp), _ptr(qq),
+            _ptr(mg), _ptr(fm))
+    elif draft_lens is None:
         rc = (lib or _load()).oracle_verify_stochastic(
             _ptr(t), _ptr(d), dt, _ptr(x), _ptr(u), float(temperature), B, k, V, _ptr(out),
             _ptr(acc), _ptr(pp), _ptr(qq), _ptr(mg))
@@ -132,7 +146,8 @@ def stochastic(target_logits, draft_logits, draft_tokens, uniforms, temperature,
             _ptr(out), _ptr(acc), _ptr(pp), _ptr(qq), _ptr(mg))
     if rc != 0:
         raise ValueError(f"oracle_verify_stochastic failed with code {rc}")
-    return dict(out_tokens=out, num_accepted=acc, p_at_draft=pp, q_at_draft=qq, margins=mg)
+    return dict(out_tokens=out, num_accepted=acc, p_at_draft=pp, q_at_draft=qq, margins=mg,
+                filter_margins=fm)
 
 
 def greedy(target_logits, draft_tokens, *, draft_lens=None, lib=None):
@@ -196,10 +211,15 @@ def tree(target_logits, node_tokens, paths, *, lib=None):
     return dict(out_tokens=out, num_accepted=acc, best_path=best, accepted_nodes=nodes)
 
 
-def ambiguous_requests(margins: np.ndarray, band: float = 1e-6) -> np.ndarray:
-    """Boolean [B]: some decision actually taken lies within ``band`` of its boundary.
+def ambiguous_requests(margins: np.ndarray, band: float = 1e-6, filter_margins=None,
+                       filter_band: float = 1e-9) -> np.ndarray:
+    """Boolean [B]: some decision actually taken lies within ``band`` of its boundary,
+    or (filtered calls) a filter threshold lies within ``filter_band`` of flipping.
 
     The decisions taken by request b are tests 0..min(s, k-1) and the final
     sample; untaken tests carry +inf margins, so the row minimum suffices.
     """
-    return np.min(margins, axis=1) < band
+    amb = np.min(margins, axis=1) < band
+    if filter_margins is not None:
+        amb |= np.asarray(filter_margins) < filter_band
+    return amb

@@ -141,6 +141,106 @@ static int32_t inverse_cdf(const double *w, int V, double u, double *margin)
 }
 
 /*
+ * Symmetric filtering of a row's distribution ([TRTLLM] "Rejection sampling":
+ * the sampling filters -- temperature, top-k, top-p, min_p -- must be applied
+ * to the target and the draft side identically).  The pages name the filters
+ * but do not define them; readings (standard definitions, all thresholds on
+ * the raw logit x, which orders tokens exactly as p does):
+ *   top-k (0 < top_k < V): keep x >= the top_k-th largest logit, counting
+ *         repeated values (every token tied with it is kept);
+ *   top-p (0 < top_p < 1): among the top-k survivors, in descending logit
+ *         order, keep the smallest run of distinct logit values whose mass
+ *         reaches top_p times the survivors' mass (ties kept);
+ *   min_p (0 < min_p <= 1): keep p >= min_p * max p, i.e.
+ *         x >= max x + T * ln(min_p);
+ * applied in this order; the kept tokens' probabilities are renormalised and
+ * every other token gets probability 0.
+ */
+struct oracle_filter {
+    int top_k;
+    double top_p;
+    double min_p;
+};
+
+static int cmp_desc(const void *a, const void *b)
+{
+    double x = *(const double *)a, y = *(const double *)b;
+    return (x < y) - (x > y);
+}
+
+/* probs[] (the row's softmax) is filtered in place.  *margin receives how far
+ * the top-p decision was from flipping (distance of the target mass to the
+ * nearer cumulative edge, relative to the survivors' mass) and how close any
+ * logit lies to the min_p threshold (absolute, in logit units); +inf when
+ * neither filter is active. */
+static void filter_row(const void *logits, int dtype, size_t row_offset, int V,
+                       double temperature, const struct oracle_filter *f, double *probs,
+                       double *scratch, double *margin)
+{
+    *margin = INFINITY;
+    double thr = -INFINITY;
+    double xmax = -INFINITY;
+    for (int j = 0; j < V; ++j) {
+        double x = logit_at(logits, dtype, row_offset + (size_t)j);
+        scratch[j] = x;
+        if (x > xmax)
+            xmax = x;
+    }
+    qsort(scratch, (size_t)V, sizeof(double), cmp_desc);
+    if (f->top_k > 0 && f->top_k < V)
+        thr = scratch[f->top_k - 1];
+    if (f->top_p > 0.0 && f->top_p < 1.0) {
+        double mass1 = 0.0;
+        for (int j = 0; j < V; ++j)
+            if (logit_at(logits, dtype, row_offset + (size_t)j) >= thr)
+                mass1 += probs[j];
+        double target = f->top_p * mass1;
+        /* walk the distinct survivor values in descending order */
+        double cum = 0.0;
+        int g = 0;
+        while (g < V && scratch[g] >= thr) {
+            double value = scratch[g];
+            double group = 0.0;
+            for (int j = 0; j < V; ++j)
+                if (logit_at(logits, dtype, row_offset + (size_t)j) == value)
+                    group += probs[j];
+            double before = cum;
+            cum += group;
+            if (cum >= target) {
+                double lo = target - before, hi = cum - target;
+                double m = (lo < hi ? lo : hi) / mass1;
+                if (m < *margin)
+                    *margin = m;
+                thr = value;
+                break;
+            }
+            while (g < V && scratch[g] == value)
+                ++g;
+        }
+    }
+    if (f->min_p > 0.0) {
+        double tmin = xmax + temperature * log(f->min_p);
+        for (int j = 0; j < V; ++j) {
+            double d = fabs(logit_at(logits, dtype, row_offset + (size_t)j) - tmin);
+            if (d < *margin)
+                *margin = d;
+        }
+        if (tmin > thr)
+            thr = tmin;
+    }
+    if (thr == -INFINITY)
+        return;
+    double total = 0.0;
+    for (int j = 0; j < V; ++j) {
+        if (logit_at(logits, dtype, row_offset + (size_t)j) < thr)
+            probs[j] = 0.0;
+        total += probs[j];
+    }
+    for (int j = 0; j < V; ++j)
+        probs[j] /= total;
+}
+
+/*
  * Stochastic verification of B linear drafts of length k.
  *
  *   target_logits [B, k+1, V]  (dtype)   draft_logits [B, k, V] (dtype)
@@ -161,11 +261,52 @@ static int32_t inverse_cdf(const double *w, int V, double u, double *margin)
  *   2. rejected at row s: sample from max(0, p_s - q_s), normalised;
  *      all k accepted: sample the bonus token from p_k ([BOOK] FAQ 2).
  */
+static int verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
+                             const int32_t *draft_tokens, const float *uniforms,
+                             double temperature, int B, int k, int V,
+                             int32_t *out_tokens, int32_t *num_accepted,
+                             double *p_at_draft, double *q_at_draft, double *margins,
+                             const struct oracle_filter *filter, double *filter_margins);
+
 int oracle_verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
                              const int32_t *draft_tokens, const float *uniforms,
                              double temperature, int B, int k, int V,
                              int32_t *out_tokens, int32_t *num_accepted,
                              double *p_at_draft, double *q_at_draft, double *margins)
+{
+    return verify_stochastic(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                             temperature, B, k, V, out_tokens, num_accepted, p_at_draft,
+                             q_at_draft, margins, NULL, NULL);
+}
+
+/*
+ * Stochastic verification with every target and draft row filtered
+ * (filter_row) before the tests and the final draw.  top_k = 0, top_p = 1 and
+ * min_p = 0 switch the respective filter off.  filter_margins [B] (may be
+ * NULL): the smallest filter margin over the request's rows.
+ */
+int oracle_verify_stochastic_filtered(const void *target_logits, const void *draft_logits,
+                                      int dtype, const int32_t *draft_tokens,
+                                      const float *uniforms, double temperature, int top_k,
+                                      double top_p, double min_p, int B, int k, int V,
+                                      int32_t *out_tokens, int32_t *num_accepted,
+                                      double *p_at_draft, double *q_at_draft, double *margins,
+                                      double *filter_margins)
+{
+    if (top_k < 0 || !(top_p > 0.0) || top_p > 1.0 || !(min_p >= 0.0) || min_p > 1.0)
+        return ORACLE_BAD_ARGUMENT;
+    struct oracle_filter f = {top_k, top_p, min_p};
+    return verify_stochastic(target_logits, draft_logits, dtype, draft_tokens, uniforms,
+                             temperature, B, k, V, out_tokens, num_accepted, p_at_draft,
+                             q_at_draft, margins, &f, filter_margins);
+}
+
+static int verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
+                             const int32_t *draft_tokens, const float *uniforms,
+                             double temperature, int B, int k, int V,
+                             int32_t *out_tokens, int32_t *num_accepted,
+                             double *p_at_draft, double *q_at_draft, double *margins,
+                             const struct oracle_filter *filter, double *filter_margins)
 {
     if (B < 0 || k < 0 || V < 1 || !(temperature > 0.0) || isinf(temperature))
         return ORACLE_BAD_ARGUMENT;
@@ -174,18 +315,33 @@ int oracle_verify_stochastic(const void *target_logits, const void *draft_logits
     double *p = (double *)malloc(sizeof(double) * (size_t)V);
     double *q = (double *)malloc(sizeof(double) * (size_t)V);
     double *w = (double *)malloc(sizeof(double) * (size_t)V);
-    if (!p || !q || !w) {
+    double *scratch = (double *)malloc(sizeof(double) * (size_t)V);
+    if (!p || !q || !w || !scratch) {
         free(p);
         free(q);
         free(w);
+        free(scratch);
         return ORACLE_NO_MEMORY;
     }
+    double fmargin;
+/* One row's distribution: softmax, then the filter when there is one. */
+#define ROW_DIST(logits, offset, out)                                                   \
+    do {                                                                                \
+        softmax_row((logits), dtype, (offset), V, temperature, (out));                  \
+        if (filter) {                                                                   \
+            filter_row((logits), dtype, (offset), V, temperature, filter, (out), scratch, \
+                       &fmargin);                                                       \
+            if (fmargin < request_fmargin)                                              \
+                request_fmargin = fmargin;                                              \
+        }                                                                               \
+    } while (0)
 
     for (int b = 0; b < B; ++b) {
         const int32_t *x = draft_tokens + (size_t)b * k;
         const float *u = uniforms + (size_t)b * (k + 1);
         int32_t *out = out_tokens + (size_t)b * (k + 1);
         double *margin = margins ? margins + (size_t)b * (k + 1) : NULL;
+        double request_fmargin = INFINITY;
         if (margin)
             for (int i = 0; i <= k; ++i)
                 margin[i] = INFINITY;
@@ -195,8 +351,8 @@ int oracle_verify_stochastic(const void *target_logits, const void *draft_logits
         for (int i = 0; i < k; ++i) {
             size_t t_row = ((size_t)b * (k + 1) + i) * (size_t)V;
             size_t d_row = ((size_t)b * k + i) * (size_t)V;
-            softmax_row(target_logits, dtype, t_row, V, temperature, p);
-            softmax_row(draft_logits, dtype, d_row, V, temperature, q);
+            ROW_DIST(target_logits, t_row, p);
+            ROW_DIST(draft_logits, d_row, q);
             int in_range = x[i] >= 0 && x[i] < V;
             double P = in_range ? p[x[i]] : 0.0;
             double Q = in_range ? q[x[i]] : 0.0;
@@ -228,21 +384,19 @@ int oracle_verify_stochastic(const void *target_logits, const void *draft_logits
             size_t d_row = ((size_t)b * k + i) * (size_t)V;
             int in_range = x[i] >= 0 && x[i] < V;
             if (p_at_draft) {
-                softmax_row(target_logits, dtype, t_row, V, temperature, p);
+                ROW_DIST(target_logits, t_row, p);
                 p_at_draft[(size_t)b * k + i] = in_range ? p[x[i]] : 0.0;
             }
             if (q_at_draft) {
-                softmax_row(draft_logits, dtype, d_row, V, temperature, q);
+                ROW_DIST(draft_logits, d_row, q);
                 q_at_draft[(size_t)b * k + i] = in_range ? q[x[i]] : 0.0;
             }
         }
 
         /* Step 2: the one final token. */
-        softmax_row(target_logits, dtype, ((size_t)b * (k + 1) + s) * (size_t)V, V,
-                    temperature, p);
+        ROW_DIST(target_logits, ((size_t)b * (k + 1) + s) * (size_t)V, p);
         if (s < k) {
-            softmax_row(draft_logits, dtype, ((size_t)b * k + s) * (size_t)V, V,
-                        temperature, q);
+            ROW_DIST(draft_logits, ((size_t)b * k + s) * (size_t)V, q);
             double Z = 0.0;
             for (int j = 0; j < V; ++j) {
                 double d = p[j] - q[j];
@@ -265,10 +419,14 @@ int oracle_verify_stochastic(const void *target_logits, const void *draft_logits
         for (int i = s + 1; i <= k; ++i)
             out[i] = -1;
         num_accepted[b] = s;
+        if (filter_margins)
+            filter_margins[b] = request_fmargin;
     }
+#undef ROW_DIST
     free(p);
     free(q);
     free(w);
+    free(scratch);
     return ORACLE_OK;
 }
 

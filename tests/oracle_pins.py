@@ -579,6 +579,122 @@ def check_philox_uniform_layout(lib):
     assert abs(float(big.mean()) - 0.5) < 5 * np.sqrt(1 / 12 / big.size)
 
 
+# ---- symmetric filtering ------------------------------------------------------------
+# Page "TensorRT-LLM source teardown (10)", "Rejection sampling": temperature,
+# top-k, top-p and min_p must filter target and draft identically.  Readings:
+# thresholds on the logit; top-k keeps ties of the k-th value; top-p keeps the
+# smallest run of the top-k survivors (descending) whose renormalised mass
+# reaches top_p; min_p keeps p >= min_p * max p; in that order.
+
+def _one_row_case(logits_t, logits_d, token):
+    t = np.array([[logits_t, logits_t]], np.float32)  # k = 1: row 0 tested, row 1 bonus
+    d = np.array([[logits_d]], np.float32)
+    x = np.array([[token]], np.int32)
+    u = np.array([[0.5, 0.5]], np.float32)
+    return t, d, x, u
+
+
+def check_filter_off_is_plain(lib):
+    """top_k in {0, V, V+3}, top_p = 1, min_p = 0 give the unfiltered results."""
+    rng = np.random.default_rng(51)
+    B, k, V = 16, 3, 20
+    t = rng.normal(0, 1.5, (B, k + 1, V)).astype(np.float32)
+    d = (t[:, :k] + rng.normal(0, 1, (B, k, V))).astype(np.float32)
+    x = rng.integers(0, V, (B, k)).astype(np.int32)
+    u = rng.random((B, k + 1), dtype=np.float32)
+    plain = oracle.stochastic(t, d, x, u, 0.9, lib=lib)
+    for tk in (V, V + 3):
+        r = oracle.stochastic(t, d, x, u, 0.9, top_k=tk, lib=lib)
+        for key in ("out_tokens", "num_accepted", "p_at_draft", "q_at_draft"):
+            assert np.array_equal(r[key], plain[key]), (tk, key)
+
+
+def check_top_k_closed_form(lib):
+    """top-k: P = p(x) / sum of the k largest p (torch.topk), 0 outside them; the
+    k-th value's ties are all kept."""
+    rng = np.random.default_rng(52)
+    V = 12
+    logits = rng.normal(0, 2, V).astype(np.float32)
+    p = lib_softmax(logits)
+    for kk in (1, 3, 7):
+        top = torch.topk(torch.from_numpy(p), kk).indices.numpy()
+        for token in range(V):
+            t, d, x, u = _one_row_case(logits, logits, token)
+            r = oracle.stochastic(t, d, x, u, 1.0, top_k=kk, lib=lib)
+            want = p[token] / p[top].sum() if token in top else 0.0
+            assert abs(r["p_at_draft"][0, 0] - want) < 1e-12, (kk, token)
+    tied = np.array([2, 1, 1, 0], np.float32)
+    t, d, x, u = _one_row_case(tied, tied, 2)
+    r = oracle.stochastic(t, d, x, u, 1.0, top_k=2, lib=lib)
+    e = np.exp([2.0, 1.0, 1.0])
+    assert abs(r["p_at_draft"][0, 0] - e[1] / e.sum()) < 1e-12
+
+
+def check_top_p_closed_form(lib):
+    """top-p on p = (.5, .3, .2): 0.45 keeps {0}; 0.75 keeps {0, 1}; 0.85 keeps all.
+    top-k = 3 then top-p = 0.75 on p = (.4, .3, .2, .1) renormalises first and keeps
+    {0, 1} (without renormalising it would keep {0, 1, 2})."""
+    base = np.log(np.array([0.5, 0.3, 0.2])).astype(np.float32)
+    p = lib_softmax(base)
+    for top_p, kept in ((0.45, [0]), (0.75, [0, 1]), (0.85, [0, 1, 2])):
+        for token in range(3):
+            t, d, x, u = _one_row_case(base, base, token)
+            r = oracle.stochastic(t, d, x, u, 1.0, top_p=top_p, lib=lib)
+            want = p[token] / p[kept].sum() if token in kept else 0.0
+            assert abs(r["p_at_draft"][0, 0] - want) < 1e-9, (top_p, token)
+    four = np.log(np.array([0.4, 0.3, 0.2, 0.1])).astype(np.float32)
+    p4 = lib_softmax(four)
+    for token in range(4):
+        t, d, x, u = _one_row_case(four, four, token)
+        r = oracle.stochastic(t, d, x, u, 1.0, top_k=3, top_p=0.75, lib=lib)
+        want = p4[token] / p4[:2].sum() if token < 2 else 0.0
+        assert abs(r["p_at_draft"][0, 0] - want) < 1e-9, token
+
+
+def check_min_p_closed_form(lib):
+    """min_p = 0.5 on p = (.5, .3, .2) keeps p >= .25: {0, 1}; at temperature 2 the
+    threshold is on p = softmax(x / 2)."""
+    base = np.log(np.array([0.5, 0.3, 0.2])).astype(np.float32)
+    for T in (1.0, 2.0):
+        p = lib_softmax(base, T)
+        kept = p >= 0.5 * p.max()
+        for token in range(3):
+            t, d, x, u = _one_row_case(base, base, token)
+            r = oracle.stochastic(t, d, x, u, T, min_p=0.5, lib=lib)
+            want = p[token] / p[kept].sum() if kept[token] else 0.0
+            assert abs(r["p_at_draft"][0, 0] - want) < 1e-9, (T, token)
+
+
+def check_filtered_output_distribution(lib, trials: int = 400_000):
+    """Chi-squared: with both sides filtered (top-k 5, top-p 0.9) and x ~ q', the first
+    emitted token is distributed as p', the filtered target (p' from a sort of the
+    library softmax)."""
+    rng = np.random.default_rng(53)
+    V = 8
+    tl = rng.normal(0, 1.2, (2, V)).astype(np.float32)
+    dl = (tl[:1] + rng.normal(0, 1.0, (1, V))).astype(np.float32)
+
+    def filtered(logits):
+        p = lib_softmax(logits)
+        order = np.argsort(-logits, kind="stable")
+        keep = np.zeros(V, bool)
+        keep[order[:5]] = True
+        p5 = np.where(keep, p, 0.0) / p[keep].sum()
+        cum = np.cumsum(p5[order])
+        cut = order[: int(np.searchsorted(cum, 0.9)) + 1]
+        out = np.zeros(V)
+        out[cut] = p[cut]
+        return out / out.sum()
+
+    pf, qf = filtered(tl[0]), filtered(dl[0])
+    x = sample_from(rng, qf, trials).reshape(trials, 1)
+    u = rng.random((trials, 2), dtype=np.float32)
+    t = np.broadcast_to(tl, (trials, 2, V)).copy()
+    d = np.broadcast_to(dl, (trials, 1, V)).copy()
+    r = oracle.stochastic(t, d, x, u, 1.0, top_k=5, top_p=0.9, lib=lib)
+    assert chi2_stat(np.bincount(r["out_tokens"][:, 0], minlength=V), pf) < CHI2_DF7_P001
+
+
 ALL_CHECKS = [
     check_softmax_vs_library,
     check_identical_draft_accepts_all,
@@ -599,4 +715,9 @@ ALL_CHECKS = [
     check_greedy_ragged,
     check_philox_matches_numpy,
     check_philox_uniform_layout,
+    check_filter_off_is_plain,
+    check_top_k_closed_form,
+    check_top_p_closed_form,
+    check_min_p_closed_form,
+    check_filtered_output_distribution,
 ]

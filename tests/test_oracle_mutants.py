@@ -21,10 +21,10 @@ MUTANTS = {
     "residual unclamped": ("w[j] = d > 0.0 ? d : 0.0;", "w[j] = d;"),
     "residual ignores draft": ("if (s < k) {", "if (0) {"),
     "bonus from row k-1": (
-        "softmax_row(target_logits, dtype, ((size_t)b * (k + 1) + s) * (size_t)V, V,",
-        "softmax_row(target_logits, dtype, ((size_t)b * (k + 1) + (s == k && s > 0 ? s - 1 : s)) * (size_t)V, V,"),
-    "target row shifted": ("size_t t_row = ((size_t)b * (k + 1) + i) * (size_t)V;\n            size_t d_row = ((size_t)b * k + i) * (size_t)V;\n            softmax_row",
-                           "size_t t_row = ((size_t)b * (k + 1) + i + 1) * (size_t)V;\n            size_t d_row = ((size_t)b * k + i) * (size_t)V;\n            softmax_row"),
+        "ROW_DIST(target_logits, ((size_t)b * (k + 1) + s) * (size_t)V, p);",
+        "ROW_DIST(target_logits, ((size_t)b * (k + 1) + (s == k && s > 0 ? s - 1 : s)) * (size_t)V, p);"),
+    "target row shifted": ("size_t t_row = ((size_t)b * (k + 1) + i) * (size_t)V;\n            size_t d_row = ((size_t)b * k + i) * (size_t)V;\n            ROW_DIST",
+                           "size_t t_row = ((size_t)b * (k + 1) + i + 1) * (size_t)V;\n            size_t d_row = ((size_t)b * k + i) * (size_t)V;\n            ROW_DIST"),
     "final sample uses u[s]": ("inverse_cdf(w, V, (double)u[k], &final_margin);",
                                "inverse_cdf(w, V, (double)u[s], &final_margin);"),
     "cdf non-strict": ("if (above > target) {", "if (above >= target) {"),
@@ -44,6 +44,11 @@ MUTANTS = {
                                   "uniforms + (size_t)b * (k + 1) + (k - kb), temperature, 1, kb, V,"),
     "greedy ragged reads full rows": ("rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb, V, out1, &acc,",
                                       "rc = oracle_verify_greedy(t, dtype, draft_tokens + (size_t)b * k, 1, kb < k ? kb + 1 : kb, V, out1, &acc,"),
+    "top-k off by one": ("thr = scratch[f->top_k - 1];", "thr = scratch[f->top_k];"),
+    "top-p not renormalised": ("double target = f->top_p * mass1;", "double target = f->top_p;"),
+    "top-p one group late": ("            if (cum >= target) {\n                double lo", "            if (cum > target + 0.05) {\n                double lo"),
+    "min_p sign": ("double tmin = xmax + temperature * log(f->min_p);", "double tmin = xmax - temperature * log(f->min_p);"),
+    "filter target only": ("        if (filter) {                                                                   \\", "        if (filter && (logits) == target_logits) {                                      \\"),
     "philox wrong multiplier": ("M1 = 0xCA5A826395121157ull", "M1 = 0xCA5A826395121155ull"),
     "philox key not advanced": ("            k[0] += W0;\n", ""),
     "philox words swapped": ("    ctr[1] = lo1;\n", "    ctr[1] = lo0;\n"),
