@@ -19,7 +19,9 @@ from . import _lib
 from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_TREE, SpecVerifyError)
 
 __all__ = [
-    "spec_verify_stochastic", "spec_verify_greedy", "spec_verify_tree",
+    "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
+    "spec_verify_stochastic_filtered", "spec_verify_greedy", "spec_verify_greedy_ragged",
+    "spec_verify_tree", "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
     "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE",
 ]
@@ -110,7 +112,7 @@ def _workspace(ws, nbytes: int, device: torch.device) -> torch.Tensor:
 
 def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, uniforms,
                 temperature, out_tokens, num_accepted, p_at_draft, q_at_draft, workspace, stream,
-                seed=0, offset=0):
+                seed=0, offset=0, top_k=0, top_p=1.0, min_p=0.0):
     device = target_logits.device
     dt = _dtype_code(target_logits)
     if target_logits.dim() != 3:
@@ -146,6 +148,9 @@ def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, unifo
         st = lib.spec_verify_stochastic(*head, *tail)
     elif fn == "spec_verify_stochastic_ragged":
         st = lib.spec_verify_stochastic_ragged(*head, _ptr(draft_lens), *tail)
+    elif fn == "spec_verify_stochastic_filtered":
+        st = lib.spec_verify_stochastic_filtered(*head, *tail[:2], int(top_k), float(top_p),
+                                                 float(min_p), *tail[2:])
     else:
         st = lib.spec_verify_stochastic_philox(*head, _ptr(draft_lens), int(seed) & (2**64 - 1),
                                                int(offset) & (2**64 - 1), *tail[1:])
@@ -193,6 +198,22 @@ def spec_verify_stochastic_philox(target_logits: torch.Tensor,
     return _stochastic("spec_verify_stochastic_philox", target_logits, draft_logits,
                        draft_tokens, draft_lens, None, temperature, out_tokens, num_accepted,
                        p_at_draft, q_at_draft, workspace, stream, seed=seed, offset=offset)
+
+
+def spec_verify_stochastic_filtered(target_logits: torch.Tensor,
+                                    draft_logits: torch.Tensor | None,
+                                    draft_tokens: torch.Tensor | None, uniforms: torch.Tensor,
+                                    temperature: float, top_k: int = 0, top_p: float = 1.0,
+                                    min_p: float = 0.0, *, out_tokens=None, num_accepted=None,
+                                    p_at_draft=None, q_at_draft=None, workspace=None,
+                                    stream=None):
+    """Stochastic verification with top-k / top-p / min-p applied alike to every
+    target and draft row (0 / 1.0 / 0.0 switch a filter off; top_p and min_p
+    are passed as float32)."""
+    return _stochastic("spec_verify_stochastic_filtered", target_logits, draft_logits,
+                       draft_tokens, None, uniforms, temperature, out_tokens, num_accepted,
+                       p_at_draft, q_at_draft, workspace, stream, top_k=top_k, top_p=top_p,
+                       min_p=min_p)
 
 
 def _greedy(fn, target_logits, draft_tokens, draft_lens, out_tokens, num_accepted, workspace,

@@ -23,6 +23,7 @@ EXPORTED = (
     "spec_verify_stochastic",
     "spec_verify_stochastic_ragged",
     "spec_verify_stochastic_philox",
+    "spec_verify_stochastic_filtered",
     "spec_verify_greedy",
     "spec_verify_greedy_ragged",
     "spec_verify_tree",
@@ -70,6 +71,10 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_stochastic_philox.argtypes = [P, P, I, P, P, U64, U64, ctypes.c_float, I, I,
                                                   I, P, P, P, P, P, Z, P]
     lib.spec_verify_stochastic_philox.restype = I
+    F = ctypes.c_float
+    lib.spec_verify_stochastic_filtered.argtypes = [P, P, I, P, P, F, I, F, F, I, I, I, P, P, P,
+                                                    P, P, Z, P]
+    lib.spec_verify_stochastic_filtered.restype = I
     lib.spec_verify_greedy.argtypes = [P, I, P, I, I, I, P, P, P, Z, P]
     lib.spec_verify_greedy.restype = I
     lib.spec_verify_greedy_ragged.argtypes = [P, I, P, P, I, I, I, P, P, P, Z, P]

@@ -100,7 +100,7 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
                            uint64_t offset, float temperature, int B, int k, int V,
                            int32_t* out_tokens, int32_t* num_accepted, float* p_at_draft,
                            float* q_at_draft, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           void* stream, const sv::FilterCall* filter = nullptr) {
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
@@ -112,6 +112,7 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     if (!counter_uniforms && !uniforms) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (filter && V > SPEC_VERIFY_MAX_FILTER_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
     sv::Geometry g;
     if (!sv::make_geometry(0, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
     if ((long long)B * g.R * g.S > 0x7fffffffLL || (long long)B * g.S2 > 0x7fffffffLL)
@@ -137,7 +138,29 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     c.p_at_draft = p_at_draft;
     c.q_at_draft = q_at_draft;
     c.workspace = workspace;
+    if (filter)
+        return finish(sv::run_stochastic_filtered(c, *filter, g, (hipStream_t)stream, next_events()));
     return finish(sv::run_stochastic(c, g, (hipStream_t)stream, next_events()));
+}
+
+int spec_verify_stochastic_filtered(const void* target_logits, const void* draft_logits,
+                                    int dtype, const int32_t* draft_tokens,
+                                    const float* uniforms, float temperature, int top_k,
+                                    float top_p, float min_p, int B, int k, int V,
+                                    int32_t* out_tokens, int32_t* num_accepted,
+                                    float* p_at_draft, float* q_at_draft, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (top_k < 0 || !(top_p > 0.0f) || !(top_p <= 1.0f) || !(min_p >= 0.0f) || !(min_p <= 1.0f))
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    sv::FilterCall f;
+    f.top_k = top_k;
+    f.top_p = top_p;
+    f.min_p = min_p;
+    const bool on = (top_k > 0 && top_k < V) || top_p < 1.0f || min_p > 0.0f;
+    return stochastic_impl(target_logits, draft_logits, dtype, draft_tokens, nullptr, uniforms,
+                           false, 0, 0, temperature, B, k, V, out_tokens, num_accepted,
+                           p_at_draft, q_at_draft, workspace, workspace_bytes, stream,
+                           on ? &f : nullptr);
 }
 
 int spec_verify_stochastic_ragged(const void* target_logits, const void* draft_logits,

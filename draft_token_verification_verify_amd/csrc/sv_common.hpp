@@ -53,7 +53,7 @@ struct Geometry {
     int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8
     int S2;          // stop-row chunks per request (stochastic sampler)
     int chunk2;      // elements per stop-row chunk
-    size_t off_tickets, off_partials, off_segs, bytes;
+    size_t off_tickets, off_partials, off_segs, off_rowf, bytes;
 };
 
 // log2(e) / temperature, the factor that turns a logit difference into a
@@ -106,6 +106,8 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     const long long nseg = (long long)g->S2 * (g->chunk2 / 64);
     off = align_up(off + sizeof(double) * (size_t)B * (size_t)((nseg + kThreads - 1) / kThreads) *
                              kThreads, 256);
+    g->off_rowf = off;  // per-row sampling filter of the filtered call (stochastic only)
+    off = align_up(off + (mode == 0 ? 16 * (size_t)rows : 0), 256);
     g->bytes = off;
     return true;
 }

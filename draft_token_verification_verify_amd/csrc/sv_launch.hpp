@@ -29,6 +29,13 @@ struct StochasticCall {
     void* workspace;
 };
 
+// Sampling filters of the filtered stochastic call (top_k 0 / top_p 1 /
+// min_p 0: off).
+struct FilterCall {
+    int top_k;
+    float top_p, min_p;
+};
+
 struct GreedyCall {
     const void* target;
     int dtype;
@@ -67,6 +74,12 @@ extern int g_stochastic_schedule;
 
 hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
                           const KernelEvents& ev);
+// Filtered call: statistics, then the per-row filter selection, then the
+// sampler with every row's filter applied.
+hipError_t run_stochastic_filtered(const StochasticCall& call, const FilterCall& f,
+                                   const Geometry& g, hipStream_t st, const KernelEvents& ev);
+hipError_t run_filter(const StochasticCall& call, const FilterCall& f, const Geometry& g,
+                      hipStream_t st);
 hipError_t run_greedy(const GreedyCall& call, const Geometry& g, hipStream_t st,
                       const KernelEvents& ev);
 hipError_t run_tree(const TreeCall& call, const Geometry& g, hipStream_t st,

@@ -63,6 +63,7 @@ struct CallArgs {
     int32_t* num_accepted;   // [B]
     float* p_at_draft;       // [B, k] or null
     float* q_at_draft;       // [B, k] or null
+    RowFilter* rowf;         // [B, 2k+1] sampling filter per row (filtered call), else null
 };
 
 // Draft length of request b: lens[b] clamped to [0, k] (per-request windows in
@@ -278,26 +279,10 @@ struct Decision {
     int s, kb;  // stop row, draft length
     float mt, md;
     double st, sd;
+    float taut, taud;  // filter thresholds of the stop rows (-inf: unfiltered)
 };
 
 constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the merge
-
-// A partial as read back by a consumer: two 8-byte agent-coherent loads.
-struct PartialRead {
-    float f0;
-    bool ok;
-    double d;
-};
-__device__ inline PartialRead read_partial(const Partial16* p) {
-    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
-    const unsigned long long h1 = load_coherent(q);
-    const unsigned long long h2 = load_coherent(q + 1);
-    PartialRead r;
-    r.f0 = __uint_as_float((unsigned)h1);
-    r.d = __longlong_as_double((long long)h2);
-    r.ok = __uint_as_float((unsigned)(h1 >> 32)) == kPartialWritten && h2 != 0ull;
-    return r;
-}
 
 // Make sure every partial of request b is published.  They come from an
 // earlier kernel (then the first check succeeds) or from statistics workgroups
@@ -383,9 +368,9 @@ __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) 
     __syncthreads();
 }
 
-template <typename T>
+template <typename T, bool FILT>
 __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
-    __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1];
+    __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1], sh_tau[2 * kMaxK + 1];
     __shared__ double sh_s[2 * kMaxK + 1];
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
@@ -411,13 +396,26 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
         x = a.draft_tokens[(size_t)b * k + i];
         u = uniform_at(a, b, i);
     }
-    merge_rows<T>(a, b, sh_m, sh_s);
+    if constexpr (FILT) {
+        // Filtered rows: maximum, kept mass and threshold from the selection kernel.
+        for (int r = threadIdx.x; r < a.R; r += kThreads) {
+            const RowFilter f = a.rowf[(size_t)b * a.R + r];
+            sh_m[r] = f.m;
+            sh_s[r] = f.s;
+            sh_tau[r] = f.tau;
+        }
+        __syncthreads();
+    } else {
+        merge_rows<T>(a, b, sh_m, sh_s);
+    }
     if (i < k) {  // past the window (i >= kb): no test, P = Q = 0 reported
         double P = 0.0, Q = 0.0;
         int acc = 0;
         if (i < kb && x >= 0 && x < a.V) {
-            P = prob_of(sh_g[i], sh_m[i], sh_s[i], a.sc);
-            Q = prob_of(sh_g[k + 1 + i], sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
+            const float gt = sh_g[i], gd = sh_g[k + 1 + i];
+            // A token below its row's filter threshold has probability 0.
+            if (!FILT || gt >= sh_tau[i]) P = prob_of(gt, sh_m[i], sh_s[i], a.sc);
+            if (!FILT || gd >= sh_tau[k + 1 + i]) Q = prob_of(gd, sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
             acc = (P >= Q) || ((double)u * Q < P);  // strict u < min(1, P/Q), no division
         }
         sh_acc[i] = acc;
@@ -448,6 +446,8 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
     out->st = sh_s[s];
     out->md = (s < kb) ? sh_m[k + 1 + s] : 0.f;
     out->sd = (s < kb) ? sh_s[k + 1 + s] : 1.0;
+    out->taut = FILT ? sh_tau[s] : -INFINITY;
+    out->taud = (FILT && s < kb) ? sh_tau[k + 1 + s] : -INFINITY;
     __syncthreads();
 }
 
@@ -457,25 +457,29 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
 // stopped on a rejection, else S_t * p = e_t.  Here e = 2^((x - row max) * c).
 // Tokens within 2^-8 of their row's maximum (the few that carry most of the
 // mass) take the fp64 exponential; the others the fp32 one, whose error is
-// then negligible against the total.
+// then negligible against the total.  Filtered rows (FILT) weigh a token below
+// the row's threshold as 0.
 struct Weigher {
     float mt, md;
     double r;
     Scale sc;
     bool residual;
+    float taut, taud;
     __device__ inline double e_of(float x, float m) const {
         const float a = scaled(x - m, sc);
         if (a > -8.f) return exp2_accurate(x, m, sc);
         return (double)fast_exp2(a);
     }
-    template <bool RESID>
+    template <bool RESID, bool FILT>
     __device__ inline double w(float xt, float xd) const {
-        const double et = e_of(xt, mt);
+        const double et = (!FILT || xt >= taut) ? e_of(xt, mt) : 0.0;
         if constexpr (!RESID) return et;
-        return fmax(fma(-r, e_of(xd, md), et), 0.0);
+        const double ed = (!FILT || xd >= taud) ? e_of(xd, md) : 0.0;
+        return fmax(fma(-r, ed, et), 0.0);
     }
-    __device__ inline double operator()(float xt, float xd) const {
-        return residual ? w<true>(xt, xd) : w<false>(xt, xd);
+    template <bool FILT>
+    __device__ inline double weigh(float xt, float xd) const {
+        return residual ? w<true, FILT>(xt, xd) : w<false, FILT>(xt, xd);
     }
 };
 
@@ -487,7 +491,7 @@ constexpr int kSub = 16;  // tokens per sampler sub-step
 // masked); the draft row is read only for a residual.  The per-token bound test
 // stays a branch even in full chunks: it keeps the compiler from interleaving
 // all of the segment's tokens, whose registers would cost occupancy.
-template <typename T, bool VEC, int NSUB, bool RESID>
+template <typename T, bool VEC, int NSUB, bool RESID, bool FILT>
 __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, int lo, int hi) {
     constexpr int SEG = NSUB * kSub;
     const int start = lo + (int)threadIdx.x * SEG;
@@ -513,7 +517,7 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
 #pragma unroll
                 for (int e = 0; e < EPV; ++e)
                     if (start + (v0 + v) * EPV + e < hi)
-                        seg += W.template w<RESID>(xt[e], RESID ? xd[e] : 0.f);
+                        seg += W.template w<RESID, FILT>(xt[e], RESID ? xd[e] : 0.f);
             }
         }
     } else {
@@ -528,17 +532,17 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
             }
 #pragma unroll
             for (int e = 0; e < kSub; ++e)
-                if (start + s0 + e < hi) seg += W.template w<RESID>(xt[e], xd[e]);
+                if (start + s0 + e < hi) seg += W.template w<RESID, FILT>(xt[e], xd[e]);
         }
     }
     return seg;
 }
 
-template <typename T, bool VEC, int NSUB>
+template <typename T, bool VEC, int NSUB, bool FILT>
 __device__ inline double segment_sum_any(const T* trow, const T* drow, const Weigher& W, int lo,
                                          int hi) {
-    return W.residual ? segment_sum<T, VEC, NSUB, true>(trow, drow, W, lo, hi)
-                      : segment_sum<T, VEC, NSUB, false>(trow, drow, W, lo, hi);
+    return W.residual ? segment_sum<T, VEC, NSUB, true, FILT>(trow, drow, W, lo, hi)
+                      : segment_sum<T, VEC, NSUB, false, FILT>(trow, drow, W, lo, hi);
 }
 
 
@@ -580,7 +584,7 @@ __device__ inline void store_segment(double* req_segs, const SegLayout& L, int c
 // Each level takes the first entry with positive weight whose running mass
 // exceeds u_k * Z; where rounding leaves every running mass at or below it, the
 // last entry with positive weight.
-template <typename T, bool VEC, int NSUB>
+template <typename T, bool VEC, int NSUB, bool FILT>
 __device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const T* trow,
                              const T* drow, Weigher W) {
     __shared__ double sh_wave[kWaves];
@@ -616,7 +620,7 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const 
         for (int c = 0; c < a.S2; ++c) {
             const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
             store_segment<NSUB>(segs, L, c, a.chunk2,
-                                segment_sum<T, VEC, NSUB, false>(trow, drow, W, lo, hi));
+                                segment_sum<T, VEC, NSUB, false, FILT>(trow, drow, W, lo, hi));
         }
         wait_stores();
         __syncthreads();
@@ -675,7 +679,7 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const 
         const int base_tok = sh_seg * kStoredSeg;
         const int j = base_tok + lane;
         double w = 0.0;
-        if (j < a.V) w = W(Elem<T>::load(trow, j), Elem<T>::load(drow, j));
+        if (j < a.V) w = W.template weigh<FILT>(Elem<T>::load(trow, j), Elem<T>::load(drow, j));
         const double run = sh_run0 + wave_inclusive_scan(w);
         const unsigned long long hit = __ballot(over && w > 0.0 && run > tau);
         const unsigned long long pos = __ballot(w > 0.0);
@@ -691,39 +695,44 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const 
     // taking its ticket).
     for (int g = 0; g < G; ++g) segs[(size_t)g * kThreads + tid] = 0.0;
     clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
+    if constexpr (FILT)
+        for (int r = tid; r < a.R; r += kThreads)
+            *reinterpret_cast<uint4*>(a.rowf + (size_t)b * a.R + r) = make_uint4(0, 0, 0, 0);
 }
 
 // One sampler work item: chunk ch of request b's stop row.
-template <typename T, bool VEC, int NSUB>
+template <typename T, bool VEC, int NSUB, bool FILT>
 __device__ void sample_item(const CallArgs& a, int b, int ch) {
     const int k = a.k;
     Decision dc;
-    decide<T>(a, b, ch == 0, &dc);
+    decide<T, FILT>(a, b, ch == 0, &dc);
     Weigher W;
     W.mt = dc.mt;
     W.md = dc.md;
     W.r = dc.st / dc.sd;
     W.sc = a.sc;
     W.residual = dc.s < dc.kb;
+    W.taut = dc.taut;
+    W.taud = dc.taud;
     const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (k + 1) + dc.s) * (size_t)a.V;
     const T* drow = W.residual
         ? static_cast<const T*>(a.draft) + ((size_t)b * k + dc.s) * (size_t)a.V
         : trow;
     __shared__ int last_flag;
     const int lo = ch * a.chunk2, hi = min(a.V, lo + a.chunk2);
-    const double seg = segment_sum_any<T, VEC, NSUB>(trow, drow, W, lo, hi);
+    const double seg = segment_sum_any<T, VEC, NSUB, FILT>(trow, drow, W, lo, hi);
     const SegLayout L(a);
     store_segment<NSUB>(a.segs + (size_t)b * L.per_request(), L, ch, a.chunk2, seg);
     // Every thread's stores complete before the ticket is taken.
     wait_stores();
     __syncthreads();
     if (arrive_last(ticket_of(a.tickets, b), (uint32_t)a.S2, &last_flag))
-        sample_final<T, VEC, NSUB>(a, b, dc.s, dc.kb, trow, drow, W);
+        sample_final<T, VEC, NSUB, FILT>(a, b, dc.s, dc.kb, trow, drow, W);
 }
 
-template <typename T, bool VEC, int NSUB>
+template <typename T, bool VEC, int NSUB, bool FILT>
 __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
-    sample_item<T, VEC, NSUB>(a, blockIdx.x / a.S2, blockIdx.x % a.S2);
+    sample_item<T, VEC, NSUB, FILT>(a, blockIdx.x / a.S2, blockIdx.x % a.S2);
 }
 
 // ---------------------------------------------------------------------------
@@ -744,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void onepass_kernel(CallArgs a) {
         return;
     }
     const int j = (int)blockIdx.x - n_tiles;
-    sample_item<T, true, NSUB>(a, j / a.S2, j % a.S2);
+    sample_item<T, true, NSUB, false>(a, j / a.S2, j % a.S2);
 }
 
 // ---------------------------------------------------------------------------
@@ -768,13 +777,13 @@ static hipError_t launch_stats(const CallArgs& a, int U, hipStream_t st, const K
     }
 }
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, bool FILT = false>
 static hipError_t launch_sample(const CallArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
     switch (a.chunk2 / (kThreads * kSub)) {
-        case 4: sample_kernel<T, VEC, 4><<<grid, block, 0, st>>>(a); break;
-        case 2: sample_kernel<T, VEC, 2><<<grid, block, 0, st>>>(a); break;
-        default: sample_kernel<T, VEC, 1><<<grid, block, 0, st>>>(a); break;
+        case 4: sample_kernel<T, VEC, 4, FILT><<<grid, block, 0, st>>>(a); break;
+        case 2: sample_kernel<T, VEC, 2, FILT><<<grid, block, 0, st>>>(a); break;
+        default: sample_kernel<T, VEC, 1, FILT><<<grid, block, 0, st>>>(a); break;
     }
     return hipGetLastError();
 }
@@ -816,8 +825,7 @@ int g_stochastic_schedule = 0;
 // any wait seen when workgroups are dispatched in order (a few microseconds).
 constexpr int kSpinLimit = 1 << 16;
 
-hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
-                          const KernelEvents& ev) {
+static CallArgs make_args(const StochasticCall& call, const Geometry& g) {
     char* ws = static_cast<char*>(call.workspace);
     CallArgs a;
     a.target = call.target;
@@ -843,8 +851,14 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     a.num_accepted = call.num_accepted;
     a.p_at_draft = call.p_at_draft;
     a.q_at_draft = call.q_at_draft;
-
+    a.rowf = nullptr;
     a.spin_limit = (g_stochastic_schedule == 2) ? 0 : kSpinLimit;
+    return a;
+}
+
+hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
+                          const KernelEvents& ev) {
+    const CallArgs a = make_args(call, g);
     hipError_t e;
     if (call.vec && g_stochastic_schedule != 1)
         return call.dtype == 1 ? launch_onepass<bf16_t>(a, g.U, st, ev)
@@ -859,6 +873,26 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
     if (call.dtype == 1)
         return call.vec ? launch_sample<bf16_t, true>(a, st) : launch_sample<bf16_t, false>(a, st);
     return call.vec ? launch_sample<float, true>(a, st) : launch_sample<float, false>(a, st);
+}
+
+hipError_t run_stochastic_filtered(const StochasticCall& call, const FilterCall& f,
+                                   const Geometry& g, hipStream_t st, const KernelEvents& ev) {
+    CallArgs a = make_args(call, g);
+    a.rowf = reinterpret_cast<RowFilter*>(static_cast<char*>(call.workspace) + g.off_rowf);
+    hipError_t e;
+    if (call.dtype == 1)
+        e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st, ev)
+                     : launch_stats<bf16_t, false>(a, g.U, st, ev);
+    else
+        e = call.vec ? launch_stats<float, true>(a, g.U, st, ev)
+                     : launch_stats<float, false>(a, g.U, st, ev);
+    if (e != hipSuccess) return e;
+    e = run_filter(call, f, g, st);
+    if (e != hipSuccess) return e;
+    if (call.dtype == 1)
+        return call.vec ? launch_sample<bf16_t, true, true>(a, st)
+                        : launch_sample<bf16_t, false, true>(a, st);
+    return call.vec ? launch_sample<float, true, true>(a, st) : launch_sample<float, false, true>(a, st);
 }
 
 }  // namespace sv

@@ -24,6 +24,34 @@ static_assert(sizeof(Partial16) == 16, "Partial16 layout");
 // f1 of a published statistics partial (a cleared workspace reads 0).
 constexpr float kPartialWritten = 1.0f;
 
+// A partial as read back by a consumer: two 8-byte agent-coherent loads.
+struct PartialRead {
+    float f0;
+    bool ok;
+    double d;
+};
+__device__ inline PartialRead read_partial(const Partial16* p) {
+    const unsigned long long* q = reinterpret_cast<const unsigned long long*>(p);
+    const unsigned long long h1 = load_coherent(q);
+    const unsigned long long h2 = load_coherent(q + 1);
+    PartialRead r;
+    r.f0 = __uint_as_float((unsigned)h1);
+    r.d = __longlong_as_double((long long)h2);
+    r.ok = __uint_as_float((unsigned)(h1 >> 32)) == kPartialWritten && h2 != 0ull;
+    return r;
+}
+
+// Sampling filter of one logits row, as the filtered stochastic call passes it
+// from its selection kernel to the sampler: the row keeps the tokens whose
+// logit is >= tau (every token when tau = -inf), m is the row maximum and s the
+// kept mass, the sum of 2^((x - m) * c) over the kept tokens.
+struct RowFilter {
+    float tau;
+    float m;
+    double s;
+};
+static_assert(sizeof(RowFilter) == 16, "RowFilter layout");
+
 // One workgroup per tile, rows 16-byte aligned (V a whole number of vectors).
 //   Op::row(b, r) -> const T* row start
 //   Op::skip(b, r) -> true for a row that is not read (its partial is

@@ -73,6 +73,7 @@ enum spec_verify_status {
 #define SPEC_VERIFY_MAX_PATH_LEN 64   /* L */
 #define SPEC_VERIFY_MAX_PATH_TABLE 16384 /* P * L */
 #define SPEC_VERIFY_MAX_VOCAB (1 << 30)
+#define SPEC_VERIFY_MAX_FILTER_VOCAB (1 << 22) /* V of a filtered call with a filter on */
 #define SPEC_VERIFY_MIN_TEMPERATURE 1e-20f /* keeps log2(e)/T finite in fp32 */
 #define SPEC_VERIFY_MAX_TEMPERATURE 1e20f
 
@@ -222,6 +223,45 @@ int spec_verify_stochastic_philox(const void *target_logits, const void *draft_l
                                   int32_t *out_tokens, int32_t *num_accepted,
                                   float *p_at_draft, float *q_at_draft,
                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stochastic verification with sampling filters applied to every target and
+ * every draft row alike (page "TensorRT-LLM source teardown (10)", "Rejection
+ * sampling": both sides must be filtered identically -- temperature, top-k,
+ * top-p, min-p -- or the acceptance test is wrong; page "Inside vLLM: Anatomy
+ * of a High-Throughput LLM Inference System" sets top_p in its example).  The
+ * pages name the filters without defining them; a row keeps the tokens whose
+ * logit x is >= tau = the largest of
+ *   top-k: the top_k-th largest logit of the row, counting repeated values
+ *          (off when top_k == 0 or top_k >= V);
+ *   top-p: the smallest logit value v such that the tokens x >= v among the
+ *          top-k survivors hold at least top_p of the survivors' mass (every
+ *          token tied with v kept; off when top_p == 1);
+ *   min-p: max x + temperature * ln(min_p), i.e. p >= min_p * max p (off when
+ *          min_p == 0);
+ * and the kept tokens' probabilities are renormalised; every other token has
+ * probability 0 in the tests (p_at_draft / q_at_draft report the filtered
+ * values) and in the final draw.
+ *
+ *   top_k  >= 0;  top_p in (0, 1];  min_p in [0, 1].
+ *
+ * Other arguments, layouts and outputs as spec_verify_stochastic; every request
+ * uses k drafts.  With every filter off this is spec_verify_stochastic.  With a
+ * filter on, V <= SPEC_VERIFY_MAX_FILTER_VOCAB (else LIMIT_EXCEEDED), and the
+ * call runs a per-row selection pass over the logits between the statistics
+ * and the sampler.  The masses that decide top-p come from fast weights
+ * (~1.5e-7 relative) when the boundary is more than 1e-6 (relative) from the
+ * nearest edge between distinct logit values, otherwise from fp64 weights
+ * (~1e-12 relative): only a boundary closer than that to an edge can come out
+ * differently from exact arithmetic.
+ */
+int spec_verify_stochastic_filtered(const void *target_logits, const void *draft_logits,
+                                    int dtype, const int32_t *draft_tokens,
+                                    const float *uniforms, float temperature, int top_k,
+                                    float top_p, float min_p, int B, int k, int V,
+                                    int32_t *out_tokens, int32_t *num_accepted,
+                                    float *p_at_draft, float *q_at_draft,
+                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Greedy verification of B linear drafts of length k.

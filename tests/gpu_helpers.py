@@ -49,12 +49,18 @@ def oracle_stochastic(case, rows=None, draft_lens=None):
                              draft_lens=lens)
 
 
-def compare_stochastic(gpu, ref, rows=None, label=""):
-    """Assert parity; return (n_ambiguous, n_disagreeing_ambiguous)."""
+def compare_stochastic(gpu, ref, rows=None, label="", filter_band=None):
+    """Assert parity; return (n_ambiguous, n_disagreeing_ambiguous).  With
+    ``filter_band``, a request whose filter decisions lie within it of flipping
+    counts as ambiguous too."""
     sel = slice(None) if rows is None else rows
     g_out, g_acc = gpu["out_tokens"][sel], gpu["num_accepted"][sel]
     g_p, g_q = gpu["p_at_draft"][sel], gpu["q_at_draft"][sel]
-    amb = oracle.ambiguous_requests(ref["margins"], GUARD)
+    if filter_band is None:
+        amb = oracle.ambiguous_requests(ref["margins"], GUARD)
+    else:
+        amb = oracle.ambiguous_requests(ref["margins"], GUARD, ref["filter_margins"],
+                                        filter_band)
     same = (g_acc == ref["num_accepted"]) & np.all(g_out == ref["out_tokens"], axis=1)
     bad = np.nonzero(~same & ~amb)[0]
     assert bad.size == 0, (

@@ -101,6 +101,39 @@ def test_stochastic_k0_needs_no_draft_pointers_but_checks_workspace(lib):
     assert stoch(lib, k=0, d=None, x=None, wsb=8) == _lib.WORKSPACE_TOO_SMALL
 
 
+def filtered(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dtype=_lib.BF16, x=FAKE, u=FAKE, T=1.0, top_k=10, top_p=0.9,
+             min_p=0.05, B=2, k=3, V=100, out=FAKE, acc=FAKE, p=None, q=None, ws=FAKE,
+             wsb=1 << 30, stream=None)
+    a.update(kw)
+    return lib.spec_verify_stochastic_filtered(
+        a["t"], a["d"], a["dtype"], a["x"], a["u"], a["T"], a["top_k"], a["top_p"], a["min_p"],
+        a["B"], a["k"], a["V"], a["out"], a["acc"], a["p"], a["q"], a["ws"], a["wsb"],
+        a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(top_k=-1), _lib.INVALID_ARGUMENT),
+    (dict(top_p=0.0), _lib.INVALID_ARGUMENT),
+    (dict(top_p=-0.5), _lib.INVALID_ARGUMENT),
+    (dict(top_p=1.5), _lib.INVALID_ARGUMENT),
+    (dict(top_p=math.nan), _lib.INVALID_ARGUMENT),
+    (dict(min_p=-0.1), _lib.INVALID_ARGUMENT),
+    (dict(min_p=1.01), _lib.INVALID_ARGUMENT),
+    (dict(min_p=math.nan), _lib.INVALID_ARGUMENT),
+    (dict(T=0.0), _lib.INVALID_ARGUMENT),
+    (dict(u=None), _lib.INVALID_ARGUMENT),
+    (dict(dtype=7), _lib.UNSUPPORTED_DTYPE),
+    (dict(k=65), _lib.LIMIT_EXCEEDED),
+    (dict(V=(1 << 22) + 1), _lib.LIMIT_EXCEEDED),
+    (dict(wsb=16), _lib.WORKSPACE_TOO_SMALL),
+    # every filter off: the plain call's checks (no vocabulary limit of the filters)
+    (dict(top_k=0, top_p=1.0, min_p=0.0, V=(1 << 22) + 1, wsb=16), _lib.WORKSPACE_TOO_SMALL),
+])
+def test_filtered_rejects(lib, kw, code):
+    assert filtered(lib, **kw) == code
+
+
 def greedy(lib, **kw):
     a = dict(t=FAKE, dtype=_lib.F32, x=FAKE, B=2, k=3, V=100, out=FAKE, acc=FAKE, ws=FAKE,
              wsb=1 << 30, stream=None)
