@@ -46,6 +46,12 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--top-k", type=int, default=0,
+                    help="stochastic workloads: top-k filter of every row (0: off)")
+    ap.add_argument("--top-p", type=float, default=1.0,
+                    help="stochastic workloads: top-p filter of every row (1: off)")
+    ap.add_argument("--min-p", type=float, default=0.0,
+                    help="stochastic workloads: min-p filter of every row (0: off)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     return ap.parse_args()
@@ -104,8 +110,9 @@ def device_inputs(case, copies: int):
     return sets
 
 
-def make_step(case, sets):
-    """Return step(i) running one verification call on input copy i % len(sets)."""
+def make_step(case, sets, filt=None):
+    """Return step(i) running one verification call on input copy i % len(sets)
+    (the filtered stochastic call when ``filt`` = (top_k, top_p, min_p))."""
     import torch
 
     import draft_token_verification_verify_amd as sv
@@ -119,9 +126,15 @@ def make_step(case, sets):
 
         def step(i):
             s = sets[i % len(sets)]
-            sv.spec_verify_stochastic(s["target"], s.get("draft"), s.get("draft_tokens"),
-                                      s["uniforms"], case.temperature, out_tokens=out,
-                                      num_accepted=acc, workspace=ws)
+            if filt is None:
+                sv.spec_verify_stochastic(s["target"], s.get("draft"), s.get("draft_tokens"),
+                                          s["uniforms"], case.temperature, out_tokens=out,
+                                          num_accepted=acc, workspace=ws)
+            else:
+                sv.spec_verify_stochastic_filtered(s["target"], s.get("draft"),
+                                                   s.get("draft_tokens"), s["uniforms"],
+                                                   case.temperature, *filt, out_tokens=out,
+                                                   num_accepted=acc, workspace=ws)
         return step, out, acc
     if mode == "greedy":
         out = torch.empty((case.B, case.k + 1), dtype=torch.int32, device=dev)
@@ -211,11 +224,15 @@ def load_traffic(workload: str, src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, seconds: float):
+def cpu_baseline(case, seconds: float, filt=None):
     """The oracle (single-threaded fp64 C) on whole requests of the same workload
     until about `seconds` of CPU time has been spent."""
+    import numpy as np
+
     import oracle
 
+    fkw = {} if filt is None else dict(top_k=filt[0], top_p=float(np.float32(filt[1])),
+                                       min_p=float(np.float32(filt[2])))
     mode = mode_of(case)
     done = 0
     t0 = time.perf_counter()
@@ -224,7 +241,7 @@ def cpu_baseline(case, seconds: float):
         sl = slice(b, b + 1)
         if mode == "stochastic":
             oracle.stochastic(case.target[sl], case.draft[sl] if case.k > 0 else None,
-                              case.draft_tokens[sl], case.uniforms[sl], case.temperature)
+                              case.draft_tokens[sl], case.uniforms[sl], case.temperature, **fkw)
         elif mode == "greedy":
             oracle.greedy(case.target[sl], case.draft_tokens[sl])
         else:
@@ -235,7 +252,8 @@ def cpu_baseline(case, seconds: float):
             break
     rows_per_req = case.rows // case.B
     return dict(value=done * rows_per_req / el, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{done} requests of {case.name} (seed {case.meta.get('seed')}), "
+                sample=f"{done} requests of {case.name} (seed {case.meta.get('seed')})"
+                       f"{'' if filt is None else ' with filters ' + str(fkw)}, "
                        f"one request per call, {el:.1f} s on one host thread")
 
 
@@ -273,7 +291,11 @@ def main():
     nbytes = streaming_bytes(case)
     copies = args.copies or max(1, math.ceil((1 << 30) / nbytes))
     sets = device_inputs(case, copies)
-    step, out, acc = make_step(case, sets)
+    filt = None
+    if mode_of(case) == "stochastic" and (0 < args.top_k < case.V or args.top_p < 1.0
+                                          or args.min_p > 0.0):
+        filt = (args.top_k, args.top_p, args.min_p)
+    step, out, acc = make_step(case, sets, filt)
     print(f"bench: {copies} input copies, {args.warmup} warmup + {args.steps} timed steps",
           file=sys.stderr, flush=True)
 
@@ -282,7 +304,11 @@ def main():
 
     ms = time_steps(step, args.steps, args.warmup)
     one_launch_ms = None
-    if mode_of(case) == "stochastic":
+    if filt is not None:
+        # Statistics kernel, per-row filter selection, sampler; the events sit
+        # on the statistics kernel.
+        kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
+    elif mode_of(case) == "stochastic":
         # The default schedule runs statistics and sampling in one launch; the
         # streaming roofline is taken on the statistics kernel of the
         # two-kernel schedule (same workload, same bytes), and the one-launch
@@ -301,7 +327,9 @@ def main():
     achieved = nbytes / (k_avg * 1e-3) / 1e9
     n_acc = acc.cpu().numpy()
     src_hash = source_hash()
-    traffic = load_traffic(args.workload, src_hash)
+    traffic = load_traffic(args.workload, src_hash) if filt is None else None
+    wname = case.name if filt is None else (
+        f"{case.name}-topk{args.top_k}-topp{args.top_p:g}-minp{args.min_p:g}")
 
     line = {
         "metric": METRIC,
@@ -317,7 +345,7 @@ def main():
         "dtype": "bf16" if case.dtype == "bf16" else "f32",
         "data": "synthetic",
         "config": {
-            "workload": case.name,
+            "workload": wname,
             "mode": mode_of(case),
             "B": case.B,
             "rows_per_step": rows,
@@ -328,11 +356,14 @@ def main():
             **({"k": case.k} if mode_of(case) != "tree"
                else {"N": case.N, "P": case.P, "L": case.L}),
             **({"temperature": case.temperature} if mode_of(case) == "stochastic" else {}),
+            **({} if filt is None else {"top_k": args.top_k, "top_p": args.top_p,
+                                        "min_p": args.min_p}),
         },
         "hbm_gbps_whole_call": nbytes / (ms * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("statistics kernel (two-kernel schedule)" if mode_of(case) == "stochastic"
+            "kernel": ("statistics kernel (filtered call)" if filt is not None else
+                       "statistics kernel (two-kernel schedule)" if mode_of(case) == "stochastic"
                        else "argmax kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
@@ -355,7 +386,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, filt)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -46,9 +46,22 @@ constexpr int kBins = 2048;          // weight bins, 1/16 octave each
 constexpr int kBinsPerOctave = 16;
 constexpr int kDigitBits = 8;        // radix digit of the narrowing passes
 constexpr int kDigits = 1 << kDigitBits;
-constexpr int kCand = 8192;          // logits gathered into LDS for the exact selection
+constexpr int kCand = 12288;         // LDS logit buffer
+constexpr int kSortCap = 8192;       // general path: a bin is sorted in LDS up to this size
+                                     // (a power of two <= kCand: the sort pads to one)
+constexpr int kTop = 10240;          // fast path: the top of a row gathered into LDS
+constexpr int kSub = kCand - kTop;   // fast path: one weight bin of it, to be sorted
+static_assert((kSortCap & (kSortCap - 1)) == 0 && kSortCap <= kCand, "sorted buffer");
+static_assert((kSub & (kSub - 1)) == 0, "sorted sub-buffer");
+constexpr int kFirstLim = 128;       // fast path: first gather reaches 8 octaves down
 constexpr int kMassBits = 41;       // fixed-point mass: 2^41 units per octave-top weight
 constexpr double kCertify = 1e-6;    // top-p margin (relative) the fast weights may decide
+// Relative error bound of a row's mass from the streaming statistics (fp32
+// exponentials, exponents rounded once in fp32; |exponent| weighted by mass is
+// at most ~22 octaves for V <= 2^22), with a factor 3 to spare; a top-p edge
+// decided against that mass must be this far from the target, and the gather
+// overshoots the target by twice as much.
+constexpr double kRowMassErr = 1e-5;
 
 struct FilterArgs {
     const void* target;
@@ -98,6 +111,21 @@ __device__ inline int bin_of(float x, float m, float bin_scale) {
     return t < (float)(kBins - 1) ? (int)t : kBins - 1;
 }
 
+// The smallest logit whose bin is below lim (bins are monotone in x, so
+// bin_of(x) < lim exactly when x >= it): a binary search over the
+// order-preserving keys between -inf and the maximum.
+__device__ inline float lowest_in_bins(int lim, float m, float bin_scale) {
+    if (lim >= kBins) return -INFINITY;
+    if (lim <= 0) return INFINITY;
+    uint32_t lo = key_of<float>(-INFINITY), hi = key_of<float>(m);
+    while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if (bin_of(value_of_key<float>(mid), m, bin_scale) < lim) hi = mid;
+        else lo = mid + 1;
+    }
+    return value_of_key<float>(lo);
+}
+
 // Weights of bin b lie in (2^-(o+1), 2^-o], o its octave (the last bin shares
 // octave 127).  Masses are kept in units of 2^-(o + 41) per bin: a weight is
 // then at most 2^41 units and is rounded to within 2^-42 of itself, and a bin's
@@ -126,31 +154,28 @@ __device__ inline unsigned long long qweight(float x, float m, double c64, int b
 }
 
 // Every element of a row, in a fixed per-thread order (so per-thread sums are
-// the same on every run).
-template <typename T, bool VEC, class F>
+// the same on every run).  Each thread keeps BATCH 16-byte loads in flight (a
+// light per-element body affords 16: a whole 128K-token bf16 row in one round
+// trip per thread).
+template <typename T, bool VEC, int BATCH = 4, class F>
 __device__ inline void for_each_logit(const T* row, int V, F&& f) {
     if constexpr (VEC) {
         constexpr int EPV = Elem<T>::kPerVec;
         const int nvec = V / EPV;
         const uint4* p = reinterpret_cast<const uint4*>(row);
-        int v = threadIdx.x;
-        for (; v + 3 * kSelThreads < nvec; v += 4 * kSelThreads) {
-            uint4 raw[4];
+        for (int v0 = threadIdx.x; v0 < nvec; v0 += BATCH * kSelThreads) {
+            uint4 raw[BATCH];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) raw[j] = p[v + j * kSelThreads];
+            for (int j = 0; j < BATCH; ++j) raw[j] = p[min(v0 + j * kSelThreads, nvec - 1)];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                float x[EPV];
-                Elem<T>::widen(raw[j], x);
+            for (int j = 0; j < BATCH; ++j) {
+                if (v0 + j * kSelThreads < nvec) {
+                    float x[EPV];
+                    Elem<T>::widen(raw[j], x);
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) f(x[e]);
+                    for (int e = 0; e < EPV; ++e) f(x[e]);
+                }
             }
-        }
-        for (; v < nvec; v += kSelThreads) {
-            float x[EPV];
-            Elem<T>::widen(p[v], x);
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) f(x[e]);
         }
     } else {
         for (int j = threadIdx.x; j < V; j += kSelThreads) f(Elem<T>::load(row, j));
@@ -168,7 +193,15 @@ struct SelLds {
     } mass;
     uint32_t dcnt[kDigits];           // digit histogram of a narrowing pass
     unsigned long long dmass[kDigits];
-    float cand[kCand];                // gathered logits
+    union {
+        float cand[kCand];            // general path: one bin's gathered logits
+        struct {
+            float top[kTop];          // fast path: every logit of the top weight bins
+            float sub[kSub];          // fast path: one bin of those, sorted
+        } f;
+    } buf;
+    double bscan[6];
+    int n_sub;
     unsigned long long red_u[kSelWaves];
     double red_d[kSelWaves];
     float red_f[kSelWaves];
@@ -185,6 +218,25 @@ __device__ inline unsigned long long wave_inclusive_scan_u64(unsigned long long 
         if (lane >= d) v += o;
     }
     return v;
+}
+
+// Append v to buf (capacity cap) at *count when take is set: one LDS atomic per
+// wave, each taking lane at the next free slot in lane order (the order within
+// buf is not fixed; every reader sorts or sums order-free).  Inactive lanes
+// take no part: the leader is the first active lane that takes.
+// Returns this lane's slot (-1 when it does not take; >= cap when full).
+__device__ inline int wave_append(bool take, float v, float* buf, int cap, int* count) {
+    const unsigned long long mask = __ballot(take);
+    if (!mask) return -1;
+    const int lane = threadIdx.x & 63;
+    const int leader = __ffsll((long long)mask) - 1;
+    int base = 0;
+    if (lane == leader) base = atomicAdd(count, __popcll(mask));
+    base = __shfl(base, leader);
+    if (!take) return -1;
+    const int i = base + __popcll(mask & ((1ull << lane) - 1));
+    if (i < cap) buf[i] = v;
+    return i;
 }
 
 // Exclusive prefix over the workgroup in thread order; *total = the sum.
@@ -251,8 +303,10 @@ __device__ inline double sel_sum_f64(double v, SelLds& L) {
 
 __device__ inline int sel_min_int(int v, SelLds& L) {
     if (threadIdx.x == 0) L.red_i = 0x7fffffff;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d));
     __syncthreads();
-    atomicMin(&L.red_i, v);
+    if ((threadIdx.x & 63) == 0) atomicMin(&L.red_i, v);
     __syncthreads();
     const int r = L.red_i;
     __syncthreads();
@@ -310,7 +364,67 @@ __device__ inline int first_bin_count(const uint32_t* incl, int nb, uint32_t r, 
     return (int)sel_sum_u64(below, L);
 }
 
-// Descending bitonic sort of cand[0, n) (n <= kCand), padded with -inf.
+// Running totals over weight bins [0, nb) of the counts and the fixed-point
+// masses (bin units folded in, fp64 in a fixed order): the first bin whose
+// running count reaches r (by_count) or whose running mass reaches target, nb
+// when none does, with the totals before and through it and over all nb bins.
+struct BinScan {
+    int bin;
+    unsigned long long cnt_ex, cnt_total;
+    double mass_ex, mass_in, mass_total;
+};
+
+__device__ inline BinScan scan_find(SelLds& L, int nb, bool by_count, unsigned long long r,
+                                    double target) {
+    // One wave walks the bins 64 at a time (lane l: bin 64 j + l), carrying the
+    // running totals; the other waves wait.
+    if (threadIdx.x < 64) {
+        const int lane = threadIdx.x;
+        unsigned long long carry_c = 0;
+        double carry_m = 0.0;
+        int hit = -1;
+        for (int j = 0; j < nb; j += 64) {
+            const int b = j + lane;
+            const unsigned long long c = b < nb ? L.cnt[b] : 0ull;
+            const double mq = b < nb ? (double)L.mass.q[b] * unit_of(b) : 0.0;
+            const unsigned long long cin = carry_c + wave_inclusive_scan_u64(c);
+            const double min_ = carry_m + wave_inclusive_scan(mq);
+            if (hit < 0) {
+                const unsigned long long found =
+                    __ballot(b < nb && (by_count ? cin >= r : min_ >= target));
+                if (found) {
+                    hit = j + __ffsll((long long)found) - 1;
+                    if (b == hit) {
+                        L.bscan[0] = (double)(cin - c);
+                        L.bscan[1] = min_ - mq;
+                        L.bscan[2] = min_;
+                    }
+                }
+            }
+            carry_c = __shfl(cin, 63);
+            carry_m = __shfl(min_, 63);
+        }
+        if (lane == 0) {
+            L.red_i = hit < 0 ? nb : hit;
+            L.bscan[3] = (double)carry_c;  // totals over the nb bins
+            L.bscan[4] = carry_m;
+        }
+    }
+    __syncthreads();
+    BinScan out;
+    out.bin = L.red_i;
+    out.cnt_total = (unsigned long long)L.bscan[3];
+    out.mass_total = L.bscan[4];
+    const bool hit = out.bin < nb;
+    out.cnt_ex = hit ? (unsigned long long)L.bscan[0] : out.cnt_total;
+    out.mass_ex = hit ? L.bscan[1] : out.mass_total;
+    out.mass_in = hit ? L.bscan[2] : out.mass_total;
+    __syncthreads();
+    return out;
+}
+
+// Descending bitonic sort of cand[0, n), padded with -inf up to the next power
+// of two (which must fit in the buffer).
 __device__ inline void sort_desc(float* cand, int n) {
     int npad = 2;
     while (npad < n) npad <<= 1;
@@ -346,7 +460,7 @@ struct SelectOut {
 //              from the running mass at the two edges of v's group (0 when
 //              none was found).
 template <typename T, bool VEC>
-__device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, int bin,
+__device__ __attribute__((always_inline)) SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, int bin,
                                    float floor_v, uint32_t n_set, bool rank_mode, uint32_t r,
                                    double base, double target, bool acc, SelLds& L) {
     constexpr int KB = KeyBits<T>::value;
@@ -360,7 +474,7 @@ __device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, i
         return done == 0 || (key_of<T>(x) >> (KB - done)) == prefix;
     };
     // Narrow by key digits until the candidates fit in LDS.
-    while (n > (uint32_t)kCand && done < KB) {
+    while (n > (uint32_t)kSortCap && done < KB) {
         const int w = min(kDigitBits, KB - done);
         const int shift = KB - done - w;
         const uint32_t mask = (1u << w) - 1;
@@ -400,7 +514,7 @@ __device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, i
         __syncthreads();
     }
     SelectOut out;
-    if (n > (uint32_t)kCand) {  // one key left: every candidate has the same value
+    if (n > (uint32_t)kSortCap) {  // one key left: every candidate has the same value
         out.tau = value_of_key<T>(prefix);
         const double before = base + (double)mass_above * unit;
         const double after =
@@ -414,15 +528,15 @@ __device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, i
     for_each_logit<T, VEC>(row, a.V, [&](float x) {
         if (in_set(x)) {
             const int i = atomicAdd(&L.n_gathered, 1);
-            if (i < kCand) L.cand[i] = x;
+            if (i < kSortCap) L.buf.cand[i] = x;
         }
     });
     __syncthreads();
-    const int ng = min(L.n_gathered, kCand);
+    const int ng = min(L.n_gathered, kSortCap);
     __syncthreads();
-    sort_desc(L.cand, ng);
+    sort_desc(L.buf.cand, ng);
     if (rank_mode) {
-        out.tau = L.cand[max(min((int)r, ng), 1) - 1];
+        out.tau = L.buf.cand[max(min((int)r, ng), 1) - 1];
         out.margin = 0.0;
         __syncthreads();
         return out;
@@ -434,7 +548,7 @@ __device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, i
     const int lo = threadIdx.x * per;
     unsigned long long own = 0;
     for (int i = 0; i < per; ++i)
-        if (lo + i < ng) own += qweight(L.cand[lo + i], m, a.c64, bin, acc);
+        if (lo + i < ng) own += qweight(L.buf.cand[lo + i], m, a.c64, bin, acc);
     unsigned long long total;
     unsigned long long run = mass_above + sel_exclusive_scan(own, L, &total);
     int hit = 0x7fffffff;
@@ -442,8 +556,8 @@ __device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, i
     for (int i = 0; i < per; ++i) {
         const int j = lo + i;
         if (j < ng) {
-            run += qweight(L.cand[j], m, a.c64, bin, acc);
-            const bool group_end = (j == ng - 1) || (L.cand[j + 1] != L.cand[j]);
+            run += qweight(L.buf.cand[j], m, a.c64, bin, acc);
+            const bool group_end = (j == ng - 1) || (L.buf.cand[j + 1] != L.buf.cand[j]);
             if (group_end && base + (double)run * unit >= target && j < hit) {
                 hit = j;
                 run_hit = run;
@@ -454,23 +568,317 @@ __device__ SelectOut select_in_bin(const T* row, const FilterArgs& a, float m, i
     if (hit == h && h < ng) L.bcast = run_hit;
     __syncthreads();
     if (h >= ng) {
-        out.tau = L.cand[max(ng - 1, 0)];
+        out.tau = L.buf.cand[max(ng - 1, 0)];
         out.margin = 0.0;
         __syncthreads();
         return out;
     }
-    out.tau = L.cand[h];
+    out.tau = L.buf.cand[h];
     const unsigned long long end = L.bcast;
     unsigned long long eq = 0;
-    for (int j = threadIdx.x; j < ng; j += kSelThreads) eq += L.cand[j] == out.tau;
+    for (int j = threadIdx.x; j < ng; j += kSelThreads) eq += L.buf.cand[j] == out.tau;
     eq = sel_sum_u64(eq, L);
     const unsigned long long start = end - eq * qweight(out.tau, m, a.c64, bin, acc);
     out.margin = fmin(base + (double)end * unit - target, target - (base + (double)start * unit));
     return out;
 }
 
+// ---------------------------------------------------------------------------
+// Fast path: the top of the row.
+// ---------------------------------------------------------------------------
+
+// Copy the logits of weight bin `bin` that are >= floor_v from the gathered
+// top of the row into sub[] and sort them (descending).  False when the bin is
+// too large for sub[].
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kSelThreads) void filter_kernel(FilterArgs a) {
+__device__ inline bool gather_bin(SelLds& L, const T* x, bool complete, int ntop, float m,
+                                  const FilterArgs& a, int bin, float floor_v) {
+    if (L.cnt[bin] > (uint32_t)kSub) return false;
+    if (threadIdx.x == 0) L.n_sub = 0;
+    __syncthreads();
+    if (complete) {  // every logit of the bin is in top[]
+        for (int i0 = 0; i0 < ntop; i0 += kSelThreads) {
+            const int i = i0 + threadIdx.x;
+            const float v = i < ntop ? L.buf.f.top[i] : -INFINITY;
+            wave_append(i < ntop && bin_of(v, m, a.bin_scale) == bin && v >= floor_v, v,
+                        L.buf.f.sub, kSub, &L.n_sub);
+        }
+    } else {  // top[] overflowed: one pass over the row for the bin's logits
+        const float x_lo = lowest_in_bins(bin + 1, m, a.bin_scale);
+        const float x_hi = lowest_in_bins(bin, m, a.bin_scale);
+        const float lo = fmaxf(x_lo, floor_v);
+        for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
+            wave_append(v >= lo && v < x_hi, v, L.buf.f.sub, kSub, &L.n_sub);
+        });
+    }
+    __syncthreads();
+    sort_desc(L.buf.f.sub, L.n_sub);
+    return true;
+}
+
+struct Walk {
+    bool found;
+    float tau;
+    double margin, mass;  // mass: base + the mass of sub's entries >= tau
+};
+
+// Top-p inside one sorted bin: the first group end (last entry of a run of
+// equal values) of sub[0, ns) whose running mass base + ... reaches target,
+// with fp64 weights (fixed point, order-free sums).
+__device__ inline Walk walk_sub(SelLds& L, int ns, float m, const FilterArgs& a, int bin,
+                                double base, double target) {
+    const double unit = unit_of(bin);
+    const float* v = L.buf.f.sub;
+    const int per = (ns + kSelThreads - 1) / kSelThreads;
+    const int lo = threadIdx.x * per;
+    unsigned long long own = 0;
+    for (int i = 0; i < per; ++i)
+        if (lo + i < ns) own += qweight(v[lo + i], m, a.c64, bin, true);
+    unsigned long long total;
+    unsigned long long run = sel_exclusive_scan(own, L, &total);
+    int hit = 0x7fffffff;
+    unsigned long long run_hit = 0;
+    for (int i = 0; i < per; ++i) {
+        const int j = lo + i;
+        if (j < ns) {
+            run += qweight(v[j], m, a.c64, bin, true);
+            const bool group_end = (j == ns - 1) || (v[j + 1] != v[j]);
+            if (group_end && base + (double)run * unit >= target && j < hit) {
+                hit = j;
+                run_hit = run;
+            }
+        }
+    }
+    const int h = sel_min_int(hit, L);
+    if (hit == h && h < ns) L.bcast = run_hit;
+    __syncthreads();
+    Walk w;
+    w.found = h < ns;
+    w.tau = w.found ? v[h] : -INFINITY;
+    w.margin = 0.0;
+    w.mass = 0.0;
+    if (w.found) {
+        const unsigned long long end = L.bcast;
+        unsigned long long eq = 0;
+        for (int j = threadIdx.x; j < ns; j += kSelThreads) eq += v[j] == w.tau;
+        eq = sel_sum_u64(eq, L);
+        const unsigned long long start = end - eq * qweight(w.tau, m, a.c64, bin, true);
+        w.mass = base + (double)end * unit;
+        w.margin = fmin(w.mass - target, target - (base + (double)start * unit));
+    }
+    __syncthreads();
+    return w;
+}
+
+// Gather every logit of the top weight bins -- 8 octaves below the maximum,
+// then 16, 32, ... until the boundaries of the filters that are on lie inside
+// -- with per-bin counts and fp64 masses, and read the thresholds and the kept
+// mass off that set: top-k from the sorted boundary bin, top-p by a walk over
+// its boundary bin (against the top-k set's mass, or against the row's mass
+// from the streaming statistics when top-k is off, where a decision closer
+// than kRowMassErr is left to the general path).  Returns false, having
+// decided nothing, when the set outgrows LDS or a decision is left open.
+template <typename T, bool VEC>
+__device__ __attribute__((always_inline)) bool fast_filter(const T* x, const FilterArgs& a, float m, double s_row, float tau_m,
+                            float* tau_out, double* s_out, SelLds& L) {
+    const bool topk = a.top_k > 0 && a.top_k < a.V;
+    const bool topp = a.top_p < 1.0;
+    for (int i = threadIdx.x; i < kBins; i += kSelThreads) {
+        L.cnt[i] = 0;
+        L.mass.q[i] = 0;
+    }
+    if (threadIdx.x == 0) L.n_gathered = 0;
+    __syncthreads();
+    // Top-p alone usually reaches further down than 8 octaves: start at 16.
+    int lim_prev = 0, lim = (topp && !topk) ? 2 * kFirstLim : kFirstLim;
+    bool complete = true;  // top[] holds every logit of the bins below lim
+    BinScan sc;
+    for (;;) {
+        const int n0 = min(L.n_gathered, kTop);
+        // bins [lim_prev, lim) are the logits in [x_lo, x_hi)
+        const float x_lo = lowest_in_bins(lim, m, a.bin_scale);
+        const float x_hi = lowest_in_bins(lim_prev, m, a.bin_scale);
+        for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
+            const int i = wave_append(v >= x_lo && v < x_hi, v, L.buf.f.top, kTop, &L.n_gathered);
+            if (i >= kTop) {  // no room: count and weigh it here
+                const int bn = bin_of(v, m, a.bin_scale);
+                atomicAdd(&L.cnt[bn], 1u);
+                atomicAdd(&L.mass.q[bn], qweight(v, m, a.c64, bn, true));
+            }
+        });
+        __syncthreads();
+        const int n1 = min(L.n_gathered, kTop);
+        complete = complete && L.n_gathered <= kTop;
+        __syncthreads();
+        // Counts and fp64 masses of the newly gathered logits, from LDS.
+        for (int i = n0 + threadIdx.x; i < n1; i += kSelThreads) {
+            const float v = L.buf.f.top[i];
+            const int bn = bin_of(v, m, a.bin_scale);
+            atomicAdd(&L.cnt[bn], 1u);
+            atomicAdd(&L.mass.q[bn], qweight(v, m, a.c64, bn, true));
+        }
+        __syncthreads();
+        sc = topk ? scan_find(L, lim, true, (unsigned long long)a.top_k, 0.0)
+                  : scan_find(L, lim, false, 0ull, a.top_p * s_row * (1.0 + 2.0 * kRowMassErr));
+        if (sc.bin < lim || lim == kBins) break;
+        lim_prev = lim;
+        lim = min(2 * lim, kBins);
+    }
+    const bool whole_row = lim == kBins;  // then the gathered masses are the row's
+    const int ntop = min(L.n_gathered, kTop);
+
+    float tau_k = -INFINITY, tau_p = -INFINITY;
+    double s_k = 0.0, s_p = 0.0;
+    int bk = lim, nk = 0;
+    if (topk) {
+        bk = sc.bin;
+        const int r = (int)(a.top_k - sc.cnt_ex);
+        if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bk, -INFINITY)) return false;
+        const int ns = L.n_sub;
+        tau_k = L.buf.f.sub[max(min(r, ns), 1) - 1];
+        unsigned long long c = 0, q = 0;
+        for (int i = threadIdx.x; i < ns; i += kSelThreads)
+            if (L.buf.f.sub[i] >= tau_k) {
+                ++c;
+                q += qweight(L.buf.f.sub[i], m, a.c64, bk, true);
+            }
+        nk = (int)sel_sum_u64(c, L);
+        s_k = sc.mass_ex + (double)sel_sum_u64(q, L) * unit_of(bk);
+    }
+    if (topp) {
+        const double mass1 = topk ? s_k : whole_row ? sc.mass_total : s_row;
+        const bool exact = topk || whole_row;
+        const double target = a.top_p * mass1;
+        // Bins before bk lie wholly in the top-k set; bin bk's part >= tau_k
+        // holds the rest of its mass, which reaches the target.
+        const BinScan sp = scan_find(L, topk ? bk : lim, false, 0ull, target);
+        const int bp = sp.bin;
+        if (!topk && bp == lim) return false;
+        int ns;
+        if (topk && bp == bk) {
+            ns = nk;  // sub holds bin bk sorted: its first nk entries are >= tau_k
+        } else {
+            if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bp, -INFINITY)) return false;
+            ns = L.n_sub;
+        }
+        Walk w = walk_sub(L, ns, m, a, bp, sp.mass_ex, target);
+        if (!w.found) return false;
+        // Too close to call against the statistics' mass: the row's mass
+        // again, as the gathered bins' fp64 mass plus the rest of the row,
+        // first with the fast weights (within ~2e-7 of that rest), then, if
+        // still too close, with fp64 weights (then the decision is final).
+        if (!exact && w.margin <= kRowMassErr * mass1) {
+            const float x_lo = lowest_in_bins(lim, m, a.bin_scale);
+            int in_sub = bp;  // the bin held (sorted) in sub[]
+            for (int tier = 0; tier < 2; ++tier) {
+                const bool acc64 = tier == 1;
+                double acc = 0.0;
+                for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
+                    if (v < x_lo) acc += weight_of(v, m, a.c64, acc64);
+                });
+                const double rest = sel_sum_f64(acc, L);
+                const double mass1b = sc.mass_total + rest;
+                const double target_b = a.top_p * mass1b;
+                const BinScan sq = scan_find(L, lim, false, 0ull, target_b);
+                if (sq.bin == lim) return false;
+                if (sq.bin != in_sub) {
+                    if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, sq.bin, -INFINITY))
+                        return false;
+                    ns = L.n_sub;
+                    in_sub = sq.bin;
+                }
+                w = walk_sub(L, ns, m, a, sq.bin, sq.mass_ex, target_b);
+                if (!w.found) return false;
+                if (acc64 || w.margin > 1e-6 * rest + 1e-11 * mass1b) break;
+            }
+        }
+        tau_p = w.tau;
+        s_p = w.mass;
+    }
+    const float tau = fmaxf(tau_m, fmaxf(tau_k, tau_p));
+    double s;
+    if (topp && tau == tau_p) {
+        s = s_p;
+    } else if (topk && tau == tau_k) {
+        s = s_k;
+    } else {
+        // min-p above the others: every kept logit lies in the gathered bins
+        // (at or before the bin of a threshold below tau).
+        const int bt = bin_of(tau, m, a.bin_scale);
+        const BinScan st = scan_find(L, bt, true, ~0ull, 0.0);
+        if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bt, tau)) return false;
+        unsigned long long q = 0;
+        for (int i = threadIdx.x; i < L.n_sub; i += kSelThreads)
+            q += qweight(L.buf.f.sub[i], m, a.c64, bt, true);
+        s = st.mass_total + (double)sel_sum_u64(q, L) * unit_of(bt);
+    }
+    *tau_out = tau;
+    *s_out = s;
+    return true;
+}
+
+// General path: top-k and top-p from a histogram of the whole row (counts; for
+// top-p, masses with the fast weights, repeated with fp64 weights when the
+// fast ones land within kCertify of a group edge) and the boundary bin
+// gathered, narrowed by key digits where it is larger than LDS.  Returns tau.
+template <typename T, bool VEC>
+__device__ __attribute__((always_inline)) float general_thresholds(const T* x, const FilterArgs& a, float m, float tau_m,
+                                    SelLds& L) {
+    float tau_k = -INFINITY, tau_p = -INFINITY;
+    if (a.top_k > 0 && a.top_k < a.V) {
+        for (int i = threadIdx.x; i < kBins; i += kSelThreads) L.cnt[i] = 0;
+        __syncthreads();
+        for_each_logit<T, VEC>(x, a.V, [&](float v) {
+            atomicAdd(&L.cnt[bin_of(v, m, a.bin_scale)], 1u);
+        });
+        __syncthreads();
+        scan_bins(L, false);
+        const int bk = min(first_bin_count(L.cnt, kBins, (uint32_t)a.top_k, L), kBins - 1);
+        const uint32_t ex = bk ? L.cnt[bk - 1] : 0u;
+        tau_k = select_in_bin<T, VEC>(x, a, m, bk, -INFINITY, L.cnt[bk] - ex, true,
+                                      (uint32_t)a.top_k - ex, 0.0, 0.0, false, L).tau;
+    }
+    if (a.top_p < 1.0) {
+        // Over the top-k survivors: a pass with the fast weights, and a
+        // second one with fp64 weights only when the first lands within
+        // kCertify of a group edge (the fast masses are within ~1.5e-7
+        // relative, so a wider margin decides the same way).
+        for (int acc = 0; acc < 2; ++acc) {
+            for (int i = threadIdx.x; i < kBins; i += kSelThreads) {
+                L.cnt[i] = 0;
+                L.mass.q[i] = 0;
+            }
+            __syncthreads();
+            for_each_logit<T, VEC>(x, a.V, [&](float v) {
+                if (v >= tau_k) {
+                    const int bn = bin_of(v, m, a.bin_scale);
+                    atomicAdd(&L.cnt[bn], 1u);
+                    atomicAdd(&L.mass.q[bn], qweight(v, m, a.c64, bn, acc != 0));
+                }
+            });
+            __syncthreads();
+            scan_bins(L, true);
+            const double mass1 = L.mass.cum[kBins - 1];
+            const double target = a.top_p * mass1;
+            unsigned long long below = 0;
+            for (int i = threadIdx.x; i < kBins; i += kSelThreads)
+                below += L.mass.cum[i] < target;
+            int bp = (int)sel_sum_u64(below, L);
+            if (bp == kBins) bp = first_bin_count(L.cnt, kBins, L.cnt[kBins - 1], L);
+            bp = min(bp, kBins - 1);
+            const double base = bp ? L.mass.cum[bp - 1] : 0.0;
+            const uint32_t n_set = L.cnt[bp] - (bp ? L.cnt[bp - 1] : 0u);
+            const SelectOut o = select_in_bin<T, VEC>(x, a, m, bp, tau_k, n_set, false, 0u,
+                                                      base, target, acc != 0, L);
+            tau_p = o.tau;
+            if (o.margin > kCertify * mass1) break;
+        }
+    }
+    return fmaxf(tau_m, fmaxf(tau_k, tau_p));
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
     __shared__ SelLds L;
     const int row = blockIdx.x, b = row / a.R, r = row % a.R;
     const T* x = filter_row<T>(a, b, r);
@@ -485,63 +893,29 @@ __global__ __launch_bounds__(kSelThreads) void filter_kernel(FilterArgs a) {
     if (m != -INFINITY) {
         // min-p: the smallest float >= m + T ln(min_p) (x >= it exactly when
         // x >= the real threshold).
-        if (a.min_p > 0.0) tau = __double2float_ru((double)m + a.temperature * log(a.min_p));
-        float tau_k = -INFINITY, tau_p = -INFINITY;
-        if (a.top_k > 0 && a.top_k < a.V) {
-            for (int i = threadIdx.x; i < kBins; i += kSelThreads) L.cnt[i] = 0;
-            __syncthreads();
-            for_each_logit<T, VEC>(x, a.V, [&](float v) {
-                atomicAdd(&L.cnt[bin_of(v, m, a.bin_scale)], 1u);
-            });
-            __syncthreads();
-            scan_bins(L, false);
-            const int bk = min(first_bin_count(L.cnt, kBins, (uint32_t)a.top_k, L), kBins - 1);
-            const uint32_t ex = bk ? L.cnt[bk - 1] : 0u;
-            tau_k = select_in_bin<T, VEC>(x, a, m, bk, -INFINITY, L.cnt[bk] - ex, true,
-                                          (uint32_t)a.top_k - ex, 0.0, 0.0, false, L).tau;
-        }
-        if (a.top_p < 1.0) {
-            // Over the top-k survivors: a pass with the fast weights, and a
-            // second one with fp64 weights only when the first lands within
-            // kCertify of a group edge (the fast masses are within ~1.5e-7
-            // relative, so a wider margin decides the same way).
-            for (int acc = 0; acc < 2; ++acc) {
-                for (int i = threadIdx.x; i < kBins; i += kSelThreads) {
-                    L.cnt[i] = 0;
-                    L.mass.q[i] = 0;
-                }
-                __syncthreads();
-                for_each_logit<T, VEC>(x, a.V, [&](float v) {
-                    if (v >= tau_k) {
-                        const int bn = bin_of(v, m, a.bin_scale);
-                        atomicAdd(&L.cnt[bn], 1u);
-                        atomicAdd(&L.mass.q[bn], qweight(v, m, a.c64, bn, acc != 0));
-                    }
-                });
-                __syncthreads();
-                scan_bins(L, true);
-                const double mass1 = L.mass.cum[kBins - 1];
-                const double target = a.top_p * mass1;
-                unsigned long long below = 0;
-                for (int i = threadIdx.x; i < kBins; i += kSelThreads)
-                    below += L.mass.cum[i] < target;
-                int bp = (int)sel_sum_u64(below, L);
-                if (bp == kBins) bp = first_bin_count(L.cnt, kBins, L.cnt[kBins - 1], L);
-                bp = min(bp, kBins - 1);
-                const double base = bp ? L.mass.cum[bp - 1] : 0.0;
-                const uint32_t n_set = L.cnt[bp] - (bp ? L.cnt[bp - 1] : 0u);
-                const SelectOut o = select_in_bin<T, VEC>(x, a, m, bp, tau_k, n_set, false, 0u,
-                                                          base, target, acc != 0, L);
-                tau_p = o.tau;
-                if (o.margin > kCertify * mass1) break;
+        const float tau_m =
+            a.min_p > 0.0 ? __double2float_ru((double)m + a.temperature * log(a.min_p)) : -INFINITY;
+        const bool topk = a.top_k > 0 && a.top_k < a.V;
+        const bool topp = a.top_p < 1.0;
+        bool decided = false;
+        if (topk || topp) {
+            // The row's mass from the statistics partials (fp64, fixed order).
+            double sp = 0.0;
+            for (int ch = threadIdx.x; ch < a.S; ch += kSelThreads) {
+                const PartialRead q = read_partial(a.partials + (size_t)row * a.S + ch);
+                if (q.f0 != -INFINITY) sp += q.d * exp2_f64(((double)q.f0 - (double)m) * a.c64);
             }
+            const double s_row = sel_sum_f64(sp, L);
+            decided = fast_filter<T, VEC>(x, a, m, s_row, tau_m, &tau, &s, L);
         }
-        tau = fmaxf(tau, fmaxf(tau_k, tau_p));
-        double acc = 0.0;
-        for_each_logit<T, VEC>(x, a.V, [&](float v) {
-            if (v >= tau) acc += weight_of(v, m, a.c64, false);
-        });
-        s = sel_sum_f64(acc, L);
+        if (!decided) {
+            tau = general_thresholds<T, VEC>(x, a, m, tau_m, L);
+            double acc = 0.0;
+            for_each_logit<T, VEC>(x, a.V, [&](float v) {
+                if (v >= tau) acc += weight_of(v, m, a.c64, false);
+            });
+            s = sel_sum_f64(acc, L);
+        }
     }
     if (threadIdx.x == 0) {
         RowFilter f;
