@@ -68,6 +68,9 @@ def _open(path: str):
     lib.oracle_philox_uniforms.restype = None
     lib.oracle_verify_tree.argtypes = [P, i, P, P, i, i, i, i, i, P, P, P, P]
     lib.oracle_verify_tree.restype = i
+    lib.oracle_verify_tree_stochastic.argtypes = [P, P, i, P, P, P, ctypes.c_double, i, i, i, i,
+                                                  i, P, P, P, P]
+    lib.oracle_verify_tree_stochastic.restype = i
     return lib
 
 
@@ -209,6 +212,44 @@ def tree(target_logits, node_tokens, paths, *, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_verify_tree failed with code {rc}")
     return dict(out_tokens=out, num_accepted=acc, best_path=best, accepted_nodes=nodes)
+
+
+def tree_stochastic(target_logits, draft_logits, node_tokens, paths, uniforms, temperature, *,
+                    lib=None):
+    """Oracle stochastic tree verify (multi-candidate speculative sampling over
+    each accepted node's children): ``dict(out_tokens[B,L], num_accepted[B],
+    accepted_nodes[B,L], margins[B,N+1])``; ``uniforms[b, c-1]`` drives node c's
+    test, ``uniforms[b, N]`` the final draw."""
+    t, dt = _logits(target_logits)
+    B, N1, V = t.shape
+    N = N1 - 1
+    d, dd = _logits(draft_logits)
+    assert dd == dt and d.shape == t.shape
+    nt = np.ascontiguousarray(node_tokens, dtype=np.int32).reshape(B, N1)
+    pa = np.ascontiguousarray(paths, dtype=np.int32)
+    assert pa.ndim == 3 and pa.shape[0] == B
+    P, L = pa.shape[1], pa.shape[2]
+    u = np.ascontiguousarray(uniforms, dtype=np.float32).reshape(B, N1)
+    out = np.empty((B, L), np.int32)
+    acc = np.empty((B,), np.int32)
+    nodes = np.empty((B, L), np.int32)
+    mg = np.empty((B, N1), np.float64)
+    rc = (lib or _load()).oracle_verify_tree_stochastic(
+        _ptr(t), _ptr(d), dt, _ptr(nt), _ptr(pa), _ptr(u), float(temperature), B, N, P, L, V,
+        _ptr(out), _ptr(acc), _ptr(nodes), _ptr(mg))
+    if rc != 0:
+        raise ValueError(f"oracle_verify_tree_stochastic failed with code {rc}")
+    return dict(out_tokens=out, num_accepted=acc, accepted_nodes=nodes, margins=mg)
+
+
+def gather_rows(src, accepted_nodes, num_accepted, dst):
+    """Oracle accepted-row gather: ``dst[b, j] = src[b, accepted_nodes[b, j]]`` for
+    ``j < num_accepted[b]``; other rows of ``dst`` are left as they are."""
+    out = np.array(dst, copy=True)
+    for b in range(src.shape[0]):
+        for j in range(int(num_accepted[b])):
+            out[b, j] = src[b, accepted_nodes[b, j]]
+    return out
 
 
 def ambiguous_requests(margins: np.ndarray, band: float = 1e-6, filter_margins=None,

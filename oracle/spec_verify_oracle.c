@@ -748,3 +748,167 @@ int oracle_verify_tree(const void *target_logits, int dtype, const int32_t *node
     free(a);
     return ORACLE_OK;
 }
+
+/*
+ * Stochastic tree verification.
+ *
+ * The pages verify a draft tree against the target's rows in one pass by
+ * "rejection sampling" ([EAGLE] "Target-model verification: tree attention and
+ * batched parallelism"; the paths tensor [batch, max_decoding_tokens,
+ * max_path_len] of "Eagle-2 multi-level tree drafting") without stating the
+ * rule for several candidate children.  Reading: the linear rule of verify_stochastic
+ * applied to the children of each accepted node in turn, in the form of
+ * multi-candidate speculative sampling (SpecInfer, Miao et al., ASPLOS 2024):
+ *
+ *   target_logits [B, N+1, V]: row n is the target distribution after node n
+ *                 (node 0 is the root, the last committed token).
+ *   draft_logits  [B, N+1, V]: row n is the draft distribution that node n's
+ *                 children were drawn from (rows of leaves are not read).
+ *   node_tokens [B, N+1]: node n's token ([b, 0] ignored).
+ *   paths [B, P, L]: node indices root-first, -1 padded; node paths[t] is a
+ *                 child of node paths[t-1] (the first row that names a node
+ *                 fixes its parent); rows whose first entry is not in [0, N]
+ *                 are unused, and an entry outside [0, N] ends a row.
+ *   uniforms [B, N+1]: uniforms[b, c-1] drives the test of node c (c >= 1);
+ *                 uniforms[b, N] drives the final draw.
+ *
+ *   n = 0; p = softmax(target row n / T); q = softmax(draft row n / T).
+ *   For each child c of n, in ascending node order: with x = token of c,
+ *   P = p(x), Q = q(x): accept when P >= Q or u * Q < P, and reject an x
+ *   outside [0, V) (as verify_stochastic does).  On acceptance: n = c and start again one level down.
+ *   On rejection: p = max(0, p - q) renormalised (left as it is if that mass is
+ *   0), and the next child is tried against it.  When no child of n is
+ *   accepted (or n has none), the final token is drawn from p by inverse CDF
+ *   with uniforms[b, N].
+ *
+ *   out_tokens [B, L]: the accepted nodes' tokens, the final token, then -1.
+ *   num_accepted [B]: accepted nodes.  accepted_nodes [B, L]: their indices,
+ *   then -1.  margins [B, N+1] (may be NULL): for each test taken, |u - t|
+ *   with t = min(1, P/Q) (as verify_stochastic; +inf for an id outside the
+ *   vocabulary and for tests not taken), and the final draw's margin
+ *   (inverse_cdf) at index N.
+ *
+ * A tree that is a single chain 0 -> 1 -> ... -> k is verify_stochastic with
+ * k drafts (draft row i of the linear call = row i here).
+ */
+int oracle_verify_tree_stochastic(const void *target_logits, const void *draft_logits, int dtype,
+                                  const int32_t *node_tokens, const int32_t *paths,
+                                  const float *uniforms, double temperature, int B, int N, int P,
+                                  int L, int V, int32_t *out_tokens, int32_t *num_accepted,
+                                  int32_t *accepted_nodes, double *margins)
+{
+    if (B < 0 || N < 0 || P < 0 || L < 1 || V < 1 || !(temperature > 0.0) || isinf(temperature))
+        return ORACLE_BAD_ARGUMENT;
+    if (dtype != ORACLE_DTYPE_F32 && dtype != ORACLE_DTYPE_BF16)
+        return ORACLE_BAD_ARGUMENT;
+    double *p = (double *)malloc(sizeof(double) * (size_t)V);
+    double *q = (double *)malloc(sizeof(double) * (size_t)V);
+    double *w = (double *)malloc(sizeof(double) * (size_t)V);
+    int32_t *parent = (int32_t *)malloc(sizeof(int32_t) * (size_t)(N + 1));
+    if (!p || !q || !w || !parent) {
+        free(p);
+        free(q);
+        free(w);
+        free(parent);
+        return ORACLE_NO_MEMORY;
+    }
+    for (int b = 0; b < B; ++b) {
+        const int32_t *tok = node_tokens + (size_t)b * (N + 1);
+        const float *u = uniforms + (size_t)b * (N + 1);
+        double *margin = margins ? margins + (size_t)b * (N + 1) : NULL;
+        if (margin)
+            for (int i = 0; i <= N; ++i)
+                margin[i] = INFINITY;
+        for (int n = 0; n <= N; ++n)
+            parent[n] = -1;
+        for (int r = 0; r < P; ++r) {
+            const int32_t *row = paths + ((size_t)b * P + r) * (size_t)L;
+            if (row[0] < 0 || row[0] > N)
+                continue;
+            for (int t = 1; t < L; ++t) {
+                int32_t c = row[t];
+                if (c < 0 || c > N)
+                    break;
+                if (c != 0 && parent[c] < 0)
+                    parent[c] = row[t - 1];
+            }
+        }
+
+        int32_t *out = out_tokens + (size_t)b * L;
+        int32_t *nodes = accepted_nodes ? accepted_nodes + (size_t)b * L : NULL;
+        for (int t = 0; t < L; ++t) {
+            out[t] = -1;
+            if (nodes)
+                nodes[t] = -1;
+        }
+        int n = 0, depth = 0;
+        for (;;) {
+            softmax_row(target_logits, dtype, ((size_t)b * (N + 1) + n) * (size_t)V, V,
+                        temperature, p);
+            int has_child = 0;
+            for (int c = 1; c <= N; ++c)
+                if (parent[c] == n)
+                    has_child = 1;
+            if (has_child)
+                softmax_row(draft_logits, dtype, ((size_t)b * (N + 1) + n) * (size_t)V, V,
+                            temperature, q);
+            int next = -1, rejected = 0;
+            for (int c = 1; c <= N && next < 0 && depth + 1 < L; ++c) {
+                if (parent[c] != n)
+                    continue;
+                int32_t x = tok[c];
+                int in_range = x >= 0 && x < V;
+                double P_ = in_range ? p[x] : 0.0;
+                double Q_ = in_range ? q[x] : 0.0;
+                int accepted;
+                if (!in_range)
+                    accepted = 0; /* an id outside the vocabulary is rejected */
+                else if (P_ >= Q_)
+                    accepted = 1;
+                else
+                    accepted = (double)u[c - 1] < P_ / Q_;
+                if (margin) {
+                    double threshold = (P_ >= Q_) ? 1.0 : P_ / Q_;
+                    margin[c - 1] = in_range ? fabs((double)u[c - 1] - threshold) : INFINITY;
+                }
+                if (accepted) {
+                    next = c;
+                    break;
+                }
+                /* w: the residual, kept unnormalised for the final draw (as
+                 * verify_stochastic draws from it); p: its normalised form for
+                 * the next sibling's test. */
+                double Z = 0.0;
+                for (int j = 0; j < V; ++j) {
+                    const double excess = p[j] - q[j];
+                    w[j] = excess > 0.0 ? excess : 0.0;
+                    Z += w[j];
+                }
+                if (Z > 0.0)
+                    for (int j = 0; j < V; ++j)
+                        p[j] = w[j] / Z;
+                else
+                    memcpy(w, p, sizeof(double) * (size_t)V);
+                rejected = 1;
+            }
+            if (next < 0) {
+                double final_margin;
+                out[depth] = inverse_cdf(rejected ? w : p, V, (double)u[N], &final_margin);
+                if (margin)
+                    margin[N] = final_margin;
+                break;
+            }
+            out[depth] = tok[next];
+            if (nodes)
+                nodes[depth] = next;
+            ++depth;
+            n = next;
+        }
+        num_accepted[b] = depth;
+    }
+    free(p);
+    free(q);
+    free(w);
+    free(parent);
+    return ORACLE_OK;
+}

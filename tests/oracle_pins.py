@@ -695,6 +695,133 @@ def check_filtered_output_distribution(lib, trials: int = 400_000):
     assert chi2_stat(np.bincount(r["out_tokens"][:, 0], minlength=V), pf) < CHI2_DF7_P001
 
 
+# ---- stochastic tree ----------------------------------------------------------
+
+def _chain_paths(B, k, P=3):
+    paths = np.full((B, P, k + 1), -1, np.int32)
+    paths[:, 1, :] = np.arange(k + 1)
+    return paths
+
+
+def check_tree_stochastic_chain_is_linear(lib):
+    """A single-chain tree is the linear stochastic verification on the same rows
+    (same tokens, accept counts and margins), f32 and bf16."""
+    rng = np.random.default_rng(61)
+    for dtype, V, k, T in (("f32", 40, 4, 1.0), ("bf16", 300, 3, 0.8), ("f32", 7, 6, 1.3)):
+        B = 64
+        t32 = rng.normal(0, 2, (B, k + 1, V)).astype(np.float32)
+        d32 = (t32 + rng.normal(0, 1, (B, k + 1, V))).astype(np.float32)
+        t = to_bf16_bits(t32) if dtype == "bf16" else t32
+        d = to_bf16_bits(d32) if dtype == "bf16" else d32
+        qf = lib_softmax(bf16_bits_to_f64(d) if dtype == "bf16" else d, T)
+        x = np.stack([[sample_from(rng, qf[b, i], 1)[0] for i in range(k)] for b in range(B)])
+        x = x.astype(np.int32)
+        x[rng.random((B, k)) < 0.05] = V  # a few ids outside the vocabulary
+        u = rng.random((B, k + 1), dtype=np.float32)
+        tok = np.concatenate([np.zeros((B, 1), np.int32), x], axis=1)
+        r = oracle.tree_stochastic(t, d, tok, _chain_paths(B, k), u, T, lib=lib)
+        g = oracle.stochastic(t, d[:, :k], x, u, T, lib=lib)
+        np.testing.assert_array_equal(r["num_accepted"], g["num_accepted"])
+        np.testing.assert_array_equal(r["out_tokens"], g["out_tokens"])
+        np.testing.assert_array_equal(r["margins"], g["margins"])
+        for b in range(B):
+            s = int(r["num_accepted"][b])
+            assert r["accepted_nodes"][b, :s].tolist() == list(range(1, s + 1))
+            assert np.all(r["accepted_nodes"][b, s:] == -1)
+
+
+def check_tree_stochastic_sibling_residual(lib):
+    """Root with two children: the first child is rejected (u above P/Q), the
+    second is tested against normalise(max(0, p - q)) (closed form from the library
+    softmax), on both sides of its threshold."""
+    V = 4
+    tl = np.log(np.array([[0.4, 0.1, 0.3, 0.2]] + [[0.25] * V] * 2)).astype(np.float32)
+    dl = np.log(np.array([[0.1, 0.5, 0.25, 0.15]] + [[0.25] * V] * 2)).astype(np.float32)
+    p = lib_softmax(tl[0])
+    q = lib_softmax(dl[0])
+    x1, x2 = 1, 2
+    assert p[x1] < q[x1]
+    res = np.maximum(p - q, 0.0)
+    res /= res.sum()
+    assert res[x2] < q[x2] and res[x2] > 0
+    thr = res[x2] / q[x2]
+    paths = np.array([[[0, 1], [0, 2]]], np.int32)
+    tok = np.array([[0, x1, x2]], np.int32)
+    for u2, want in ((thr * 0.999, 1), (min(thr * 1.001, 0.999), 0)):
+        u = np.array([[0.999, u2, 0.25]], np.float32)
+        r = oracle.tree_stochastic(tl[None], dl[None], tok, paths, u, 1.0, lib=lib)
+        if want:
+            assert r["num_accepted"][0] == 1 and r["accepted_nodes"][0, 0] == 2
+            assert r["out_tokens"][0, 0] == x2
+        else:
+            # both rejected: the final draw is from the second residual
+            assert r["num_accepted"][0] == 0
+            res2 = np.maximum(res - q, 0.0)
+            j, _ = lib_inverse_cdf(res2, 0.25)
+            assert r["out_tokens"][0, 0] == j
+
+
+def check_tree_stochastic_output_distribution(lib, trials: int = 300_000):
+    """Chi-squared: three children drawn independently from q at the root; the
+    first emitted token (an accepted child's, or the final draw) is distributed as
+    p (the property the rule is built for)."""
+    rng = np.random.default_rng(67)
+    V, m = 8, 3
+    tl = rng.normal(0, 1.2, (m + 1, V)).astype(np.float32)
+    dl = (tl + rng.normal(0, 1.0, (m + 1, V))).astype(np.float32)
+    p = lib_softmax(tl[0])
+    q = lib_softmax(dl[0])
+    tok = np.zeros((trials, m + 1), np.int32)
+    tok[:, 1:] = sample_from(rng, q, trials * m).reshape(trials, m)
+    paths = np.full((trials, m, 2), -1, np.int32)
+    for c in range(1, m + 1):
+        paths[:, c - 1] = [0, c]
+    u = rng.random((trials, m + 1), dtype=np.float32)
+    t = np.broadcast_to(tl, (trials, m + 1, V)).copy()
+    d = np.broadcast_to(dl, (trials, m + 1, V)).copy()
+    r = oracle.tree_stochastic(t, d, tok, paths, u, 1.0, lib=lib)
+    assert chi2_stat(np.bincount(r["out_tokens"][:, 0], minlength=V), p) < CHI2_DF7_P001
+
+
+def check_tree_stochastic_identical_draft(lib):
+    """q = p at every node: the first child of each node is always accepted and the
+    walk follows first children to a leaf."""
+    rng = np.random.default_rng(71)
+    B, V = 32, 30
+    N = 6  # 0 -> {1, 2}, 1 -> {3, 4}, 3 -> {5}, 2 -> {6}
+    parent = [-1, 0, 0, 1, 1, 3, 2]
+    t = rng.normal(0, 2, (B, N + 1, V)).astype(np.float32)
+    tok = rng.integers(0, V, (B, N + 1)).astype(np.int32)
+    paths = np.full((B, 3, 4), -1, np.int32)
+    paths[:, 0] = [0, 1, 3, 5]
+    paths[:, 1] = [0, 1, 4, -1]
+    paths[:, 2] = [0, 2, 6, -1]
+    u = rng.random((B, N + 1), dtype=np.float32)
+    r = oracle.tree_stochastic(t, t.copy(), tok, paths, u, 1.0, lib=lib)
+    assert np.all(r["num_accepted"] == 3)
+    assert np.all(r["accepted_nodes"][:, :3] == [1, 3, 5])
+    np.testing.assert_array_equal(r["out_tokens"][:, :3], tok[:, [1, 3, 5]])
+    for b in range(B):  # the final draw is from the leaf's target row
+        j, _ = lib_inverse_cdf(lib_softmax(t[b, 5]), float(u[b, N]))
+        assert r["out_tokens"][b, 3] == j
+    assert parent[5] == 3
+
+
+def check_gather_rows_example(lib):
+    """Accepted-row gather on a hand-built case: request 0 keeps nodes 3 and 1 in
+    that order, request 1 none, request 2 node 2; other rows stay untouched."""
+    src = np.arange(3 * 4 * 2, dtype=np.int32).reshape(3, 4, 2)  # row (b, n) = [8b+2n, 8b+2n+1]
+    nodes = np.array([[3, 1, -1], [-1, -1, -1], [2, -1, -1]], np.int32)
+    acc = np.array([2, 0, 1], np.int32)
+    dst = np.full((3, 3, 2), -7, np.int32)
+    out = oracle.gather_rows(src, nodes, acc, dst)
+    want = np.full((3, 3, 2), -7, np.int32)
+    want[0, 0] = [6, 7]
+    want[0, 1] = [2, 3]
+    want[2, 0] = [20, 21]
+    np.testing.assert_array_equal(out, want)
+
+
 ALL_CHECKS = [
     check_softmax_vs_library,
     check_identical_draft_accepts_all,
@@ -720,4 +847,9 @@ ALL_CHECKS = [
     check_top_p_closed_form,
     check_min_p_closed_form,
     check_filtered_output_distribution,
+    check_tree_stochastic_chain_is_linear,
+    check_tree_stochastic_sibling_residual,
+    check_tree_stochastic_output_distribution,
+    check_tree_stochastic_identical_draft,
+    check_gather_rows_example,
 ]

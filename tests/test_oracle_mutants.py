@@ -49,6 +49,17 @@ MUTANTS = {
     "top-p one group late": ("            if (cum >= target) {\n                double lo", "            if (cum > target + 0.05) {\n                double lo"),
     "min_p sign": ("double tmin = xmax + temperature * log(f->min_p);", "double tmin = xmax - temperature * log(f->min_p);"),
     "filter target only": ("        if (filter) {                                                                   \\", "        if (filter && (logits) == target_logits) {                                      \\"),
+    "tree residual not carried to siblings": ("                        p[j] = w[j] / Z;\n",
+                                              "                        p[j] = p[j];\n"),
+    "tree test uniform index": ("accepted = (double)u[c - 1] < P_ / Q_;",
+                                "accepted = (double)u[c] < P_ / Q_;"),
+    "tree accepts out-of-range ids": ("accepted = 0; /* an id outside the vocabulary is rejected */",
+                                      "accepted = 1; /* an id outside the vocabulary is rejected */"),
+    "tree siblings last first": ("for (int c = 1; c <= N && next < 0 && depth + 1 < L; ++c) {",
+                                 "for (int c = N; c >= 1 && next < 0 && depth + 1 < L; --c) {"),
+    "tree draft row of the child": (
+        "softmax_row(draft_logits, dtype, ((size_t)b * (N + 1) + n) * (size_t)V, V,",
+        "softmax_row(draft_logits, dtype, ((size_t)b * (N + 1) + (n < N ? n + 1 : n)) * (size_t)V, V,"),
     "philox wrong multiplier": ("M1 = 0xCA5A826395121157ull", "M1 = 0xCA5A826395121155ull"),
     "philox key not advanced": ("            k[0] += W0;\n", ""),
     "philox words swapped": ("    ctr[1] = lo1;\n", "    ctr[1] = lo0;\n"),
