@@ -21,7 +21,8 @@ from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_TREE, SpecVerif
 __all__ = [
     "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
     "spec_verify_stochastic_filtered", "spec_verify_greedy", "spec_verify_greedy_ragged",
-    "spec_verify_tree", "spec_verify_set_schedule",
+    "spec_verify_tree", "spec_verify_tree_stochastic", "spec_verify_gather_rows",
+    "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
     "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE",
 ]
@@ -296,3 +297,61 @@ def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,
         _stream(device, stream))
     _lib.check("spec_verify_tree", st)
     return tuple(outs)
+
+
+def spec_verify_tree_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor,
+                                node_tokens: torch.Tensor, paths: torch.Tensor,
+                                uniforms: torch.Tensor, temperature: float, *, out_tokens=None,
+                                num_accepted=None, accepted_nodes=None, stream=None):
+    """Stochastic tree verification (each accepted node's children tested in
+    ascending order against the residual of their rejected siblings); returns
+    ``(out_tokens[B,L], num_accepted[B], accepted_nodes[B,L])``.  ``uniforms``
+    is float32 [B, N+1]: entry c-1 drives node c's test, entry N the final draw."""
+    device = target_logits.device
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3 or paths.dim() != 3:
+        raise ValueError("target_logits must be [B, N+1, V] and paths [B, P, L]")
+    B, N1, V = target_logits.shape
+    _, P, L = paths.shape
+    _dev(target_logits, "target_logits", device)
+    _dev(draft_logits, "draft_logits", device, target_logits.dtype, (B, N1, V))
+    _dev(node_tokens, "node_tokens", device, torch.int32, (B, N1))
+    _dev(paths, "paths", device, torch.int32, (B, P, L))
+    _dev(uniforms, "uniforms", device, torch.float32, (B, N1))
+    outs = []
+    for name, t, shape in (("out_tokens", out_tokens, (B, L)),
+                           ("num_accepted", num_accepted, (B,)),
+                           ("accepted_nodes", accepted_nodes, (B, L))):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.int32, device=device)
+        outs.append(_dev(t, name, device, torch.int32, shape))
+    st = _lib.load().spec_verify_tree_stochastic(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(node_tokens), _ptr(paths),
+        _ptr(uniforms), float(temperature), B, N1 - 1, P, L, V, _ptr(outs[0]), _ptr(outs[1]),
+        _ptr(outs[2]), _stream(device, stream))
+    _lib.check("spec_verify_tree_stochastic", st)
+    return tuple(outs)
+
+
+def spec_verify_gather_rows(src: torch.Tensor, accepted_nodes: torch.Tensor,
+                            num_accepted: torch.Tensor, dst: torch.Tensor, *, stream=None):
+    """``dst[b, j] = src[b, accepted_nodes[b, j]]`` for ``j < num_accepted[b]`` (rows of
+    any dtype and trailing shape, contiguous); other slots of ``dst`` are left
+    as they are.  Returns ``dst``."""
+    device = src.device
+    if src.dim() < 2 or dst.dim() != src.dim() or dst.shape[2:] != src.shape[2:]:
+        raise ValueError("src must be [B, N1, ...] and dst [B, L, ...] with the same row shape")
+    if dst.dtype != src.dtype:
+        raise TypeError("src and dst must have the same dtype")
+    B, N1 = src.shape[:2]
+    L = dst.shape[1]
+    _dev(src, "src", device)
+    _dev(dst, "dst", device, shape=(B, L) + tuple(src.shape[2:]))
+    _dev(accepted_nodes, "accepted_nodes", device, torch.int32, (B, L))
+    _dev(num_accepted, "num_accepted", device, torch.int32, (B,))
+    row_bytes = src[0, 0].numel() * src.element_size() if src.numel() else 0
+    st = _lib.load().spec_verify_gather_rows(_ptr(src), _ptr(dst), row_bytes,
+                                             _ptr(accepted_nodes), _ptr(num_accepted), B, N1, L,
+                                             _stream(device, stream))
+    _lib.check("spec_verify_gather_rows", st)
+    return dst

@@ -27,6 +27,8 @@ EXPORTED = (
     "spec_verify_greedy",
     "spec_verify_greedy_ragged",
     "spec_verify_tree",
+    "spec_verify_tree_stochastic",
+    "spec_verify_gather_rows",
 )
 
 _lib = None
@@ -81,6 +83,11 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_greedy_ragged.restype = I
     lib.spec_verify_tree.argtypes = [P, I, P, P, I, I, I, I, I, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.restype = I
+    lib.spec_verify_tree_stochastic.argtypes = [P, P, I, P, P, P, ctypes.c_float, I, I, I, I, I,
+                                                P, P, P, P]
+    lib.spec_verify_tree_stochastic.restype = I
+    lib.spec_verify_gather_rows.argtypes = [P, P, Z, P, P, I, I, I, P]
+    lib.spec_verify_gather_rows.restype = I
     _lib = lib
     return lib
 

@@ -273,4 +273,62 @@ int spec_verify_tree(const void* target_logits, int dtype, const int32_t* node_t
     return finish(sv::run_tree(c, g, (hipStream_t)stream, next_events()));
 }
 
+int spec_verify_tree_stochastic(const void* target_logits, const void* draft_logits, int dtype,
+                                const int32_t* node_tokens, const int32_t* paths,
+                                const float* uniforms, float temperature, int B, int N, int P,
+                                int L, int V, int32_t* out_tokens, int32_t* num_accepted,
+                                int32_t* accepted_nodes, void* stream) {
+    const int eb = elem_bytes_of(dtype);
+    if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
+    if (B < 1 || N < 0 || P < 0 || L < 1 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!(temperature >= SPEC_VERIFY_MIN_TEMPERATURE) ||
+        !(temperature <= SPEC_VERIFY_MAX_TEMPERATURE))
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!target_logits || !draft_logits || !node_tokens || !uniforms || !out_tokens ||
+        !num_accepted)
+        return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (P > 0 && !paths) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (N + 1 > SPEC_VERIFY_MAX_TREE_ROWS || P > SPEC_VERIFY_MAX_PATHS ||
+        L > SPEC_VERIFY_MAX_PATH_LEN || (long long)P * L > SPEC_VERIFY_MAX_PATH_TABLE ||
+        V > SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB)
+        return SPEC_VERIFY_LIMIT_EXCEEDED;
+    sv::TreeStochCall c;
+    c.target = target_logits;
+    c.draft = draft_logits;
+    c.dtype = dtype;
+    c.vec = vec_ok(target_logits, V, eb) && vec_ok(draft_logits, V, eb);
+    c.node_tokens = node_tokens;
+    c.paths = paths;
+    c.uniforms = uniforms;
+    c.temperature = temperature;
+    c.B = B;
+    c.N = N;
+    c.P = P;
+    c.L = L;
+    c.V = V;
+    c.out_tokens = out_tokens;
+    c.num_accepted = num_accepted;
+    c.accepted_nodes = accepted_nodes;
+    return finish(sv::run_tree_stochastic(c, (hipStream_t)stream));
+}
+
+int spec_verify_gather_rows(const void* src, void* dst, size_t row_bytes,
+                            const int32_t* accepted_nodes, const int32_t* num_accepted, int B,
+                            int N1, int L, void* stream) {
+    if (B < 1 || N1 < 1 || L < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!src || !dst || !accepted_nodes || !num_accepted) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if ((long long)B * L > 0x7fffffffLL) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (row_bytes == 0) return SPEC_VERIFY_OK;
+    sv::GatherCall c;
+    c.src = src;
+    c.dst = dst;
+    c.row_bytes = row_bytes;
+    c.accepted_nodes = accepted_nodes;
+    c.num_accepted = num_accepted;
+    c.B = B;
+    c.N1 = N1;
+    c.L = L;
+    return finish(sv::run_gather_rows(c, (hipStream_t)stream));
+}
+
 }  // extern "C"

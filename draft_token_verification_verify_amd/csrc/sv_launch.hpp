@@ -62,6 +62,32 @@ struct TreeCall {
     void* workspace;
 };
 
+// Stochastic tree verification (no workspace).
+struct TreeStochCall {
+    const void* target;
+    const void* draft;
+    int dtype;
+    bool vec;
+    const int32_t* node_tokens;
+    const int32_t* paths;
+    const float* uniforms;
+    float temperature;
+    int B, N, P, L, V;
+    int32_t* out_tokens;
+    int32_t* num_accepted;
+    int32_t* accepted_nodes;
+};
+
+// Accepted-row gather.
+struct GatherCall {
+    const void* src;
+    void* dst;
+    size_t row_bytes;
+    const int32_t* accepted_nodes;
+    const int32_t* num_accepted;
+    int B, N1, L;
+};
+
 // Optional events recorded around the streaming kernel (both null = none).
 struct KernelEvents {
     hipEvent_t begin = nullptr, end = nullptr;
@@ -85,5 +111,7 @@ hipError_t run_greedy(const GreedyCall& call, const Geometry& g, hipStream_t st,
 hipError_t run_tree(const TreeCall& call, const Geometry& g, hipStream_t st,
                     const KernelEvents& ev);
 hipError_t run_fill_zero(void* ptr, size_t bytes, hipStream_t st);
+hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st);
+hipError_t run_gather_rows(const GatherCall& c, hipStream_t st);
 
 }  // namespace sv

@@ -1,0 +1,486 @@
+// sv_tree_stochastic.hip -- stochastic verification of a draft tree, and the
+// gather of the accepted rows (KV relocation).
+//
+// Tree rule (page "05 - TensorRT-LLM speculative decoding and auto-deploy",
+// "Target-model verification: tree attention and batched parallelism": the
+// target scores every tree node in one pass and "rejection sampling" decides
+// what is kept; the paths table of "Eagle-2 multi-level tree drafting").  The
+// page gives no rule for several candidate children; the one used is the
+// linear rule applied to the children of each accepted node in turn
+// (multi-candidate speculative sampling, SpecInfer, Miao et al., ASPLOS 2024):
+// at node n with target distribution p (row n) and draft distribution q (the
+// draft row that n's children were drawn from), children are tested in
+// ascending node order -- accept child x when p(x) >= q(x) or u q(x) < p(x) --
+// and every rejection replaces p by max(0, p - q) renormalised before the next
+// child is tried.  An accepted child becomes the next n; when none is
+// accepted, one token is drawn from the last residual (or from row n itself
+// if nothing was rejected there) by inverse CDF.  A single-chain tree is the
+// linear call.
+//
+// One workgroup of 1024 threads per request walks its tree.  The parent of
+// every node comes from the paths table (the first row that names a node
+// fixes its parent).  Each visited node costs one pass over its target and
+// draft rows for their softmax statistics, one pass per rejected child for the
+// residual's mass, and the final draw one pass for the weights' running total
+// by tiles plus one tile for the token.  Every sum runs in a fixed order, so
+// results do not change between runs.
+#include "sv_common.hpp"
+#include "sv_launch.hpp"
+
+namespace sv {
+
+constexpr int kTsThreads = 1024;
+constexpr int kTsWaves = kTsThreads / 64;
+constexpr int kMaxTreeNodes = 1024;            // N + 1
+constexpr int kMaxRejections = kMaxTreeNodes;  // a node has at most N children
+constexpr int kTsPer = 8;                      // logits per thread per tile
+constexpr int kTsTile = kTsThreads * kTsPer;   // logits per tile
+constexpr int kTsTiles = 64;                   // tiles per row: V <= 524288
+
+struct TreeStochArgs {
+    const void* target;
+    const void* draft;
+    const int32_t* node_tokens;  // [B, N+1]
+    const int32_t* paths;        // [B, P, L]
+    const float* uniforms;       // [B, N+1]
+    int B, N, P, L, V;
+    Scale sc;
+    int32_t* out_tokens;      // [B, L]
+    int32_t* num_accepted;    // [B]
+    int32_t* accepted_nodes;  // [B, L] or null
+};
+
+struct TsLds {
+    int first[kMaxTreeNodes];   // first occurrence (row * L + t) of each node in paths
+    int parent[kMaxTreeNodes];
+    double z[kMaxRejections];   // residual masses at the current node
+    double red_d[kTsWaves];
+    float red_f[kTsWaves];
+    double tile_sum[kTsTiles];
+    int red_i;
+    int pick_tile;
+    double pick_base;
+};
+
+// Weight 2^((x - m) c) of a logit in fp64: the fp64 exponential within 2^-8
+// of the row maximum (most of the mass), fp32 below.
+__device__ inline double ts_weight(float x, float m, const Scale& sc) {
+    if (x == -INFINITY) return 0.0;
+    const float a = scaled(x - m, sc);
+    if (a > -8.f) return exp2_accurate(x, m, sc);
+    return (double)fast_exp2(a);
+}
+
+__device__ inline float ts_block_max(float v, TsLds& L) {
+    v = wave_max(v);
+    if ((threadIdx.x & 63) == 0) L.red_f[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = L.red_f[0];
+#pragma unroll
+    for (int w = 1; w < kTsWaves; ++w) r = fmaxf(r, L.red_f[w]);
+    __syncthreads();
+    return r;
+}
+
+__device__ inline double ts_block_sum(double v, TsLds& L) {
+    v = wave_reduce_sum(v);
+    if ((threadIdx.x & 63) == 0) L.red_d[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = L.red_d[0];
+#pragma unroll
+    for (int w = 1; w < kTsWaves; ++w) r += L.red_d[w];
+    __syncthreads();
+    return r;
+}
+
+// Workgroup minimum of an int (one LDS atomic per wave).
+__device__ inline int ts_block_min(int v, TsLds& L) {
+    if (threadIdx.x == 0) L.red_i = 0x7fffffff;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) atomicMin(&L.red_i, v);
+    __syncthreads();
+    const int r = L.red_i;
+    __syncthreads();
+    return r;
+}
+
+// Exclusive prefix in thread order (fixed order); *total = the sum.
+__device__ inline double ts_block_scan(double v, TsLds& L, double* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const double inc = wave_inclusive_scan(v);
+    if (lane == 63) L.red_d[wave] = inc;
+    __syncthreads();
+    double before = 0.0, all = 0.0;
+#pragma unroll
+    for (int w = 0; w < kTsWaves; ++w) {
+        const double t = L.red_d[w];
+        if (w < wave) before += t;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + (inc - v);
+}
+
+// The row is read in tiles of kTsThreads * 8 logits; thread t takes the 8
+// consecutive logits at tile * 8192 + 8 t (one 16-byte load for bf16 rows
+// when aligned).  Tile-major, thread-minor order is ascending vocabulary order.
+
+template <typename T, bool VEC>
+__device__ inline void ts_load8(const T* row, int V, int tile, float* x) {
+    const int j0 = tile * kTsTile + (int)threadIdx.x * kTsPer;
+    if constexpr (VEC) {
+        if (j0 + kTsPer <= V) {
+            if constexpr (sizeof(T) == 2) {
+                Elem<T>::widen(load16(row + j0), x);
+            } else {
+                float a[4], b[4];
+                Elem<T>::widen(load16(row + j0), a);
+                Elem<T>::widen(load16(row + j0 + 4), b);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    x[e] = a[e];
+                    x[4 + e] = b[e];
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < kTsPer; ++e) x[e] = (j0 + e < V) ? Elem<T>::load(row, j0 + e) : -INFINITY;
+}
+
+// Softmax statistics of a row: maximum m and s = sum of 2^((x - m) c).
+struct RowStats {
+    float m;
+    double s;
+};
+
+template <typename T, bool VEC>
+__device__ RowStats ts_row_stats(const T* row, int V, const Scale& sc, TsLds& L) {
+    const int tiles = (V + kTsTile - 1) / kTsTile;
+    float mt = -INFINITY;
+    for (int k = 0; k < tiles; ++k) {
+        float x[kTsPer];
+        ts_load8<T, VEC>(row, V, k, x);
+#pragma unroll
+        for (int e = 0; e < kTsPer; ++e) mt = fmaxf(mt, x[e]);
+    }
+    const float ms = (mt == -INFINITY) ? 0.f : mt;
+    double st = 0.0;
+    for (int k = 0; k < tiles; ++k) {
+        float x[kTsPer];
+        ts_load8<T, VEC>(row, V, k, x);
+#pragma unroll
+        for (int e = 0; e < kTsPer; ++e) st += (double)fast_exp2(scaled(x[e] - ms, sc));
+    }
+    RowStats r;
+    r.m = ts_block_max(mt, L);
+    const double f = (mt == -INFINITY || r.m == -INFINITY) ? 0.0 : exp2_accurate(mt, r.m, sc);
+    r.s = ts_block_sum(st * f, L);
+    return r;
+}
+
+// The current distribution at token x: p after nrej rejections,
+// p_i = max(0, p_{i-1} - q) / z_i (p_{i-1} kept where z_i == 0), and q.
+struct Dist {
+    float mt, md;
+    double st, sd;
+    Scale sc;
+    int nrej;
+    const double* z;
+    __device__ inline double p0(float xt) const {
+        return (mt == -INFINITY || !(st > 0.0)) ? 0.0 : ts_weight(xt, mt, sc) / st;
+    }
+    __device__ inline double q(float xd) const {
+        return (md == -INFINITY || !(sd > 0.0)) ? 0.0 : ts_weight(xd, md, sc) / sd;
+    }
+    // p after the first `upto` rejections, given p0 and q at a token.
+    __device__ inline double chain(double p, double qv, int upto) const {
+        for (int i = 0; i < upto; ++i) {
+            const double zi = z[i];
+            if (zi > 0.0) p = fmax(p - qv, 0.0) / zi;
+        }
+        return p;
+    }
+};
+
+// Sum over the row of w(v) = max(0, p_nrej(v) - q(v)) (residual) or p_nrej(v),
+// tile by tile, each tile's sum stored in L.tile_sum (fixed order); returns
+// the total.
+template <typename T, bool VEC>
+__device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist& D, bool residual,
+                                 TsLds& L) {
+    const int tiles = (V + kTsTile - 1) / kTsTile;
+    double total = 0.0;
+    for (int k = 0; k < tiles; ++k) {
+        float xt[kTsPer], xd[kTsPer];
+        ts_load8<T, VEC>(trow, V, k, xt);
+        if (residual) ts_load8<T, VEC>(drow, V, k, xd);
+        double own = 0.0;
+#pragma unroll
+        for (int e = 0; e < kTsPer; ++e) {
+            const double qv = residual ? D.q(xd[e]) : 0.0;
+            const double p = D.chain(D.p0(xt[e]), qv, D.nrej);
+            own += residual ? fmax(p - qv, 0.0) : p;
+        }
+        const double s = ts_block_sum(own, L);
+        if (threadIdx.x == 0) L.tile_sum[k] = s;
+        total += s;
+    }
+    __syncthreads();
+    return total;
+}
+
+// Inverse CDF over the weights of the last ts_weight_pass: the smallest token
+// whose running weight exceeds u * Z (Z = that pass's total), else the last
+// token with positive weight.
+template <typename T, bool VEC>
+__device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool residual, double Z,
+                       double u, TsLds& L) {
+    const int tiles = (V + kTsTile - 1) / kTsTile;
+    const double target = u * Z;
+    if (threadIdx.x == 0) {
+        double run = 0.0;
+        int pick = -1, last = -1;
+        double pick_base = 0.0, last_base = 0.0;
+        for (int k = 0; k < tiles; ++k) {
+            const double w = L.tile_sum[k];
+            if (w > 0.0) {
+                last = k;
+                last_base = run;
+                if (pick < 0 && run + w > target) {
+                    pick = k;
+                    pick_base = run;
+                }
+            }
+            run += w;
+        }
+        if (pick < 0) {
+            pick = max(last, 0);
+            pick_base = last_base;
+        }
+        L.pick_tile = pick;
+        L.pick_base = pick_base;
+    }
+    __syncthreads();
+    const int k = L.pick_tile;
+    const double base = L.pick_base;
+    float xt[kTsPer], xd[kTsPer];
+    ts_load8<T, VEC>(trow, V, k, xt);
+    if (residual) ts_load8<T, VEC>(drow, V, k, xd);
+    double w[kTsPer], own = 0.0;
+#pragma unroll
+    for (int e = 0; e < kTsPer; ++e) {
+        const double qv = residual ? D.q(xd[e]) : 0.0;
+        const double p = D.chain(D.p0(xt[e]), qv, D.nrej);
+        w[e] = residual ? fmax(p - qv, 0.0) : p;
+        own += w[e];
+    }
+    double tile_total;
+    double run = base + ts_block_scan(own, L, &tile_total);
+    const int j0 = k * kTsTile + (int)threadIdx.x * kTsPer;
+    int hit = 0x7fffffff, lastpos = -1;
+#pragma unroll
+    for (int e = 0; e < kTsPer; ++e) {
+        if (w[e] > 0.0) {
+            lastpos = j0 + e;
+            if (run + w[e] > target && hit == 0x7fffffff) hit = j0 + e;
+        }
+        run += w[e];
+    }
+    int tok = ts_block_min(hit, L);
+    if (tok == 0x7fffffff)  // rounding left every running weight at or below u * Z
+        tok = max(-ts_block_min(-lastpos, L), 0);
+    return tok;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochArgs a) {
+    __shared__ TsLds L;
+    const int b = blockIdx.x, N = a.N, V = a.V, Lp = a.L;
+    const int32_t* tok = a.node_tokens + (size_t)b * (N + 1);
+    const float* u = a.uniforms + (size_t)b * (N + 1);
+    const int32_t* paths = a.paths + (size_t)b * a.P * Lp;
+
+    // Parents: the first occurrence (row-major) of a node in a usable row.
+    for (int n = threadIdx.x; n <= N; n += kTsThreads) {
+        L.first[n] = 0x7fffffff;
+        L.parent[n] = -1;
+    }
+    __syncthreads();
+    for (int r = threadIdx.x; r < a.P; r += kTsThreads) {
+        const int32_t* row = paths + (size_t)r * Lp;
+        if (row[0] < 0 || row[0] > N) continue;
+        for (int t = 1; t < Lp; ++t) {
+            const int32_t c = row[t];
+            if (c < 0 || c > N) break;
+            if (c != 0) atomicMin(&L.first[c], r * Lp + t);
+        }
+    }
+    __syncthreads();
+    for (int c = 1 + (int)threadIdx.x; c <= N; c += kTsThreads) {
+        const int f = L.first[c];
+        if (f != 0x7fffffff) L.parent[c] = paths[f - 1];  // the entry before it in its row
+    }
+    __syncthreads();
+
+    int32_t* out = a.out_tokens + (size_t)b * Lp;
+    int32_t* nodes = a.accepted_nodes ? a.accepted_nodes + (size_t)b * Lp : nullptr;
+    for (int t = threadIdx.x; t < Lp; t += kTsThreads) {
+        out[t] = -1;
+        if (nodes) nodes[t] = -1;
+    }
+
+    int n = 0, depth = 0;
+    for (;;) {
+        const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (N + 1) + n) * (size_t)V;
+        const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * (N + 1) + n) * (size_t)V;
+        // Does n have a child (tested only while depth + 1 < L)?
+        int has = 0;
+        for (int c = 1 + (int)threadIdx.x; c <= N; c += kTsThreads) has |= L.parent[c] == n;
+        const bool test = __syncthreads_or(has) && depth + 1 < Lp;
+        Dist D;
+        D.sc = a.sc;
+        D.nrej = 0;
+        D.z = L.z;
+        const RowStats st = ts_row_stats<T, VEC>(trow, V, a.sc, L);
+        D.mt = st.m;
+        D.st = st.s;
+        D.md = -INFINITY;
+        D.sd = 1.0;
+        if (test) {
+            const RowStats sd = ts_row_stats<T, VEC>(drow, V, a.sc, L);
+            D.md = sd.m;
+            D.sd = sd.s;
+        }
+        int next = -1;
+        double Zlast = 0.0;
+        if (test) {
+            for (int c = 1; c <= N; ++c) {
+                if (L.parent[c] != n) continue;  // uniform: LDS, same for every thread
+                const int32_t x = tok[c];
+                bool accepted = false;
+                if (x >= 0 && x < V) {
+                    const double qv = D.q(Elem<T>::load(drow, x));
+                    const double pv = D.chain(D.p0(Elem<T>::load(trow, x)), qv, D.nrej);
+                    accepted = (pv >= qv) || ((double)u[c - 1] * qv < pv);
+                }
+                if (accepted) {
+                    next = c;
+                    break;
+                }
+                // Rejected: the residual's mass, then the next sibling against it.
+                Zlast = ts_weight_pass<T, VEC>(trow, drow, V, D, true, L);
+                if (threadIdx.x == 0) L.z[D.nrej] = Zlast;
+                __syncthreads();
+                ++D.nrej;
+            }
+        }
+        if (next < 0) {
+            // Final draw: the last residual max(0, p - q) as it stands (its mass
+            // Zlast; p itself where that mass is 0), else row n's p.
+            const bool residual = D.nrej > 0 && Zlast > 0.0;
+            Dist F = D;
+            if (residual) F.nrej = D.nrej - 1;  // w = max(0, p_{nrej-1} - q)
+            // (For a residual, the last rejection's pass left exactly these
+            // weights' tile sums in L.tile_sum.)
+            const double Z = residual ? Zlast
+                                      : ts_weight_pass<T, VEC>(trow, drow, V, F, false, L);
+            const int token = ts_draw<T, VEC>(trow, drow, V, F, residual, Z, (double)u[N], L);
+            if (threadIdx.x == 0) {
+                out[depth] = token;
+                a.num_accepted[b] = depth;
+            }
+            return;
+        }
+        if (threadIdx.x == 0) {
+            out[depth] = tok[next];
+            if (nodes) nodes[depth] = next;
+        }
+        ++depth;
+        n = next;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Accepted-row gather: dst[b, j] = src[b, accepted_nodes[b, j]] for
+// j < num_accepted[b] (page "TensorRT-LLM source teardown (10)", KV rewind,
+// step 4: the accepted draft rows moved to their logical, contiguous places).
+// One workgroup per (request, slot); 16-byte copies when rows allow.
+// ---------------------------------------------------------------------------
+struct GatherArgs {
+    const char* src;
+    char* dst;
+    size_t row_bytes;
+    const int32_t* nodes;
+    const int32_t* num_accepted;
+    int B, N1, L;
+    bool vec;
+};
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs g) {
+    const int b = blockIdx.x / g.L, j = blockIdx.x % g.L;
+    const int na = g.num_accepted[b];
+    if (j >= na || j < 0) return;
+    const int n = g.nodes[(size_t)b * g.L + j];
+    if (n < 0 || n >= g.N1) return;  // not a node of the source: leave the slot
+    const char* s = g.src + ((size_t)b * g.N1 + n) * g.row_bytes;
+    char* d = g.dst + ((size_t)b * g.L + j) * g.row_bytes;
+    if (g.vec) {
+        const size_t nv = g.row_bytes / 16;
+        const uint4* s4 = reinterpret_cast<const uint4*>(s);
+        uint4* d4 = reinterpret_cast<uint4*>(d);
+        for (size_t i = threadIdx.x; i < nv; i += 256) d4[i] = s4[i];
+    } else {
+        for (size_t i = threadIdx.x; i < g.row_bytes; i += 256) d[i] = s[i];
+    }
+}
+
+hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st) {
+    TreeStochArgs a;
+    a.target = c.target;
+    a.draft = c.draft;
+    a.node_tokens = c.node_tokens;
+    a.paths = c.paths;
+    a.uniforms = c.uniforms;
+    a.B = c.B;
+    a.N = c.N;
+    a.P = c.P;
+    a.L = c.L;
+    a.V = c.V;
+    a.sc = make_scale(c.temperature);
+    a.out_tokens = c.out_tokens;
+    a.num_accepted = c.num_accepted;
+    a.accepted_nodes = c.accepted_nodes;
+    const dim3 grid((unsigned)c.B), block(kTsThreads);
+    if (c.dtype == 1) {
+        if (c.vec) tree_stochastic_kernel<bf16_t, true><<<grid, block, 0, st>>>(a);
+        else tree_stochastic_kernel<bf16_t, false><<<grid, block, 0, st>>>(a);
+    } else {
+        if (c.vec) tree_stochastic_kernel<float, true><<<grid, block, 0, st>>>(a);
+        else tree_stochastic_kernel<float, false><<<grid, block, 0, st>>>(a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t run_gather_rows(const GatherCall& c, hipStream_t st) {
+    GatherArgs g;
+    g.src = static_cast<const char*>(c.src);
+    g.dst = static_cast<char*>(c.dst);
+    g.row_bytes = c.row_bytes;
+    g.nodes = c.accepted_nodes;
+    g.num_accepted = c.num_accepted;
+    g.B = c.B;
+    g.N1 = c.N1;
+    g.L = c.L;
+    g.vec = (c.row_bytes % 16 == 0) && (reinterpret_cast<uintptr_t>(c.src) % 16 == 0) &&
+            (reinterpret_cast<uintptr_t>(c.dst) % 16 == 0);
+    gather_rows_kernel<<<dim3((unsigned)((long long)c.B * c.L)), dim3(256), 0, st>>>(g);
+    return hipGetLastError();
+}
+
+}  // namespace sv

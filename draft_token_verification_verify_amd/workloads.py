@@ -37,7 +37,8 @@ import numpy as np
 __all__ = [
     "StochasticCase", "GreedyCase", "TreeCase",
     "gaussian_stochastic", "zipf_stochastic", "gaussian_greedy", "random_tree_case",
-    "c1", "c2_greedy", "c2_stochastic", "c3", "c4", "c5",
+    "c1", "c2_greedy", "c2_stochastic", "c3", "c4", "c5", "stochastic_tree_case",
+    "StochasticTreeCase",
     "bf16_bits", "bits_to_float", "to_device",
 ]
 
@@ -324,6 +325,63 @@ def random_tree_case(seed: int, B: int, N: int, depth: int, V: int, dtype: str, 
             else:
                 tokens[b, n] = int(rng.integers(0, V))
     return TreeCase(name, B, N, P, L, V, dtype, target, tokens, paths, parents, dict(seed=seed))
+
+
+@dataclass
+class StochasticTreeCase:
+    name: str
+    B: int
+    N: int
+    P: int
+    L: int
+    V: int
+    dtype: str
+    temperature: float
+    target: np.ndarray         # [B, N+1, V]
+    draft: np.ndarray          # [B, N+1, V]: row n, the distribution n's children come from
+    node_tokens: np.ndarray    # [B, N+1] int32
+    paths: np.ndarray          # [B, P, L] int32, -1 padded
+    uniforms: np.ndarray       # [B, N+1] float32
+    parents: np.ndarray        # [B, N+1] int32; generator bookkeeping
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def rows(self) -> int:
+        return self.B * (self.N + 1)
+
+    @property
+    def logits_bytes(self) -> int:
+        return self.target.nbytes + self.draft.nbytes
+
+
+def stochastic_tree_case(seed: int, B: int, N: int, depth: int, V: int, dtype: str, *,
+                         P: int | None = None, max_children: int = 10, target_sd: float = 3.0,
+                         draft_noise_sd: float = 1.0, temperature: float = 1.0,
+                         name: str = "stree") -> StochasticTreeCase:
+    """Random trees as random_tree_case; target ~ N(0, target_sd); draft = target +
+    N(0, draft_noise_sd); every node's token drawn from softmax(draft row of its
+    parent / T) (Gumbel-max), independently of its siblings."""
+    rng = np.random.default_rng(seed)
+    P = N if P is None else P
+    L = depth + 1
+    t32 = rng.normal(0.0, target_sd, size=(B, N + 1, V)).astype(np.float32)
+    d32 = (t32 + rng.normal(0.0, draft_noise_sd, size=(B, N + 1, V))).astype(np.float32)
+    target = _finish(t32, dtype)
+    draft = _finish(d32, dtype)
+    del t32, d32
+    dfl = _as_float(draft, dtype)
+    parents = np.empty((B, N + 1), np.int32)
+    paths = np.empty((B, P, L), np.int32)
+    tokens = np.zeros((B, N + 1), np.int32)
+    for b in range(B):
+        par = _random_tree(rng, N, depth, max_children)
+        parents[b] = par
+        paths[b] = _paths_of(par, P, L)
+        z = dfl[b, par[1:]].astype(np.float64) / temperature  # [N, V]: the parents' rows
+        tokens[b, 1:] = np.argmax(z + rng.gumbel(size=z.shape), axis=1).astype(np.int32)
+    u = rng.random((B, N + 1), dtype=np.float32)
+    return StochasticTreeCase(name, B, N, P, L, V, dtype, _f32(temperature), target, draft,
+                              tokens, paths, u, parents, dict(seed=seed))
 
 
 # ---- the five named workloads -------------------------------------------------

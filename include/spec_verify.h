@@ -74,6 +74,7 @@ enum spec_verify_status {
 #define SPEC_VERIFY_MAX_PATH_TABLE 16384 /* P * L */
 #define SPEC_VERIFY_MAX_VOCAB (1 << 30)
 #define SPEC_VERIFY_MAX_FILTER_VOCAB (1 << 22) /* V of a filtered call with a filter on */
+#define SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB (1 << 19) /* V of spec_verify_tree_stochastic */
 #define SPEC_VERIFY_MIN_TEMPERATURE 1e-20f /* keeps log2(e)/T finite in fp32 */
 #define SPEC_VERIFY_MAX_TEMPERATURE 1e20f
 
@@ -315,6 +316,70 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *node_t
                      int32_t *out_tokens, int32_t *num_accepted, int32_t *best_path,
                      int32_t *accepted_nodes, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/*
+ * Stochastic verification of a draft tree.  The page "05 - TensorRT-LLM
+ * speculative decoding and auto-deploy" ("Target-model verification: tree
+ * attention and batched parallelism") checks every tree node against the
+ * target in one pass by "rejection sampling", with the tree given as the paths
+ * table of "Eagle-2 multi-level tree drafting", and states no rule for several
+ * candidate children.  The rule used: starting at the root, the children of
+ * the current node are tested in ascending node order as the linear call tests
+ * one draft (accept child c when p(x) >= q(x) or u q(x) < p(x), x its token, p
+ * the current target distribution, q the draft row the children were drawn
+ * from); each rejection replaces p by max(0, p - q) renormalised; an accepted
+ * child becomes the current node (one level down, at most L - 1 levels);
+ * when no child is accepted, one token is drawn from the last residual
+ * max(0, p - q) (from p when nothing was rejected at that node, or when the
+ * residual has no mass) by inverse CDF, as in the linear call.  With children
+ * drawn independently from q this emits tokens distributed as the target's
+ * (multi-candidate speculative sampling, SpecInfer, Miao et al., ASPLOS 2024);
+ * a single-chain tree gives exactly spec_verify_stochastic.
+ *
+ *   target_logits [B, N+1, V] dtype: row n, the target distribution after
+ *                  node n (node 0 = the root, the last committed token).
+ *   draft_logits  [B, N+1, V] dtype: row n, the draft distribution node n's
+ *                  children were drawn from (rows of leaves are not read).
+ *   node_tokens   [B, N+1] int32: node n's token ([b, 0] ignored).
+ *   paths         [B, P, L] int32: node indices root-first, -1 padded; node
+ *                  paths[t] is a child of paths[t-1], the first row (then the
+ *                  first position) that names a node fixing its parent; a row
+ *                  whose first entry is not in [0, N] is unused and an entry
+ *                  outside [0, N] ends a row.
+ *   uniforms      [B, N+1] fp32 in [0, 1): uniforms[b, c-1] drives node c's
+ *                  test, uniforms[b, N] the final draw.
+ *   out_tokens     [B, L] int32: the accepted nodes' tokens, the final token,
+ *                  then -1.
+ *   num_accepted   [B] int32: accepted nodes (tree depth reached).
+ *   accepted_nodes [B, L] int32 or NULL: their node indices, then -1.
+ *
+ * Limits: N + 1 <= SPEC_VERIFY_MAX_TREE_ROWS, P <= SPEC_VERIFY_MAX_PATHS,
+ * L <= SPEC_VERIFY_MAX_PATH_LEN, P * L <= SPEC_VERIFY_MAX_PATH_TABLE,
+ * V <= SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB.  No workspace.  Draft ids outside
+ * [0, V) are rejected.  One workgroup per request walks its tree: each visited
+ * node reads its two rows once for their statistics, once more per rejected
+ * child, and once for the final draw.
+ */
+int spec_verify_tree_stochastic(const void *target_logits, const void *draft_logits, int dtype,
+                                const int32_t *node_tokens, const int32_t *paths,
+                                const float *uniforms, float temperature, int B, int N, int P,
+                                int L, int V, int32_t *out_tokens, int32_t *num_accepted,
+                                int32_t *accepted_nodes, void *stream);
+
+/*
+ * Gather of the accepted rows (page "TensorRT-LLM source teardown (10)", KV
+ * rewind, fourth step: the accepted draft tokens' KV rows, scattered when the
+ * draft was a tree, are moved to contiguous logical positions):
+ *   dst[b, j, :] = src[b, accepted_nodes[b, j], :] for j < num_accepted[b].
+ *   src [B, N1, row_bytes] bytes, device; dst [B, L, row_bytes] bytes, device
+ *   (must not overlap src); accepted_nodes [B, L] and num_accepted [B] int32,
+ *   device (the outputs of spec_verify_tree or spec_verify_tree_stochastic).
+ * Slots j >= num_accepted[b], and slots whose node is outside [0, N1), are
+ * left as they are.  16-byte copies when row_bytes and both pointers allow.
+ */
+int spec_verify_gather_rows(const void *src, void *dst, size_t row_bytes,
+                            const int32_t *accepted_nodes, const int32_t *num_accepted, int B,
+                            int N1, int L, void *stream);
 
 #ifdef __cplusplus
 }

@@ -134,6 +134,49 @@ def test_filtered_rejects(lib, kw, code):
     assert filtered(lib, **kw) == code
 
 
+def tree_stoch(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dtype=_lib.BF16, nt=FAKE, paths=FAKE, u=FAKE, T=1.0, B=2, N=5, P=3,
+             L=4, V=100, out=FAKE, acc=FAKE, nodes=None, stream=None)
+    a.update(kw)
+    return lib.spec_verify_tree_stochastic(a["t"], a["d"], a["dtype"], a["nt"], a["paths"],
+                                           a["u"], a["T"], a["B"], a["N"], a["P"], a["L"],
+                                           a["V"], a["out"], a["acc"], a["nodes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=3), _lib.UNSUPPORTED_DTYPE),
+    (dict(B=0), _lib.INVALID_ARGUMENT),
+    (dict(N=-1), _lib.INVALID_ARGUMENT),
+    (dict(L=0), _lib.INVALID_ARGUMENT),
+    (dict(T=0.0), _lib.INVALID_ARGUMENT),
+    (dict(T=math.nan), _lib.INVALID_ARGUMENT),
+    (dict(d=None), _lib.INVALID_ARGUMENT),
+    (dict(u=None), _lib.INVALID_ARGUMENT),
+    (dict(paths=None), _lib.INVALID_ARGUMENT),
+    (dict(N=1024), _lib.LIMIT_EXCEEDED),
+    (dict(L=65), _lib.LIMIT_EXCEEDED),
+    (dict(P=1000, L=20), _lib.LIMIT_EXCEEDED),
+    (dict(V=(1 << 19) + 1), _lib.LIMIT_EXCEEDED),
+])
+def test_tree_stochastic_rejects(lib, kw, code):
+    assert tree_stoch(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), _lib.INVALID_ARGUMENT),
+    (dict(N1=0), _lib.INVALID_ARGUMENT),
+    (dict(L=0), _lib.INVALID_ARGUMENT),
+    (dict(src=None), _lib.INVALID_ARGUMENT),
+    (dict(nodes=None), _lib.INVALID_ARGUMENT),
+    (dict(rb=0), _lib.OK),  # nothing to copy: nothing launched
+])
+def test_gather_rows_rejects(lib, kw, code):
+    a = dict(src=FAKE, dst=FAKE, rb=64, nodes=FAKE, acc=FAKE, B=2, N1=5, L=4)
+    a.update(kw)
+    assert lib.spec_verify_gather_rows(a["src"], a["dst"], a["rb"], a["nodes"], a["acc"], a["B"],
+                                       a["N1"], a["L"], None) == code
+
+
 def greedy(lib, **kw):
     a = dict(t=FAKE, dtype=_lib.F32, x=FAKE, B=2, k=3, V=100, out=FAKE, acc=FAKE, ws=FAKE,
              wsb=1 << 30, stream=None)
