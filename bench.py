@@ -40,7 +40,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="c3",
-                    choices=["c1", "c2-greedy", "c2-stochastic", "c3", "c4", "c5"])
+                    choices=["c1", "c2-greedy", "c2-stochastic", "c3", "c4", "c5", "c5-stochastic"])
     ap.add_argument("--copies", type=int, default=0,
                     help="input copies to rotate over (0: enough for >= 1 GiB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -72,6 +72,9 @@ def make_case(name: str, seed: int):
     return {
         "c1": wl.c1, "c2-greedy": wl.c2_greedy, "c2-stochastic": wl.c2_stochastic,
         "c3": wl.c3, "c4": wl.c4, "c5": wl.c5,
+        "c5-stochastic": lambda s: wl.stochastic_tree_case(
+            s, 32, 60, 6, 128256, "bf16", target_sd=3.0, draft_noise_sd=1.0,
+            name="c5-stochastic-tree-B32-N60-depth6-V128256-bf16"),
     }[name](seed)
 
 
@@ -82,6 +85,8 @@ def mode_of(case) -> str:
         return "stochastic"
     if isinstance(case, wl.GreedyCase):
         return "greedy"
+    if isinstance(case, wl.StochasticTreeCase):
+        return "tree-stochastic"
     return "tree"
 
 
@@ -100,6 +105,11 @@ def device_inputs(case, copies: int):
         base["uniforms"] = to_dev(case.uniforms.astype(np.float32))
     elif mode == "greedy":
         base["draft_tokens"] = to_dev(case.draft_tokens.astype(np.int32))
+    elif mode == "tree-stochastic":
+        base["draft"] = to_dev(case.draft, case.dtype)
+        base["node_tokens"] = to_dev(case.node_tokens.astype(np.int32))
+        base["paths"] = to_dev(case.paths.astype(np.int32))
+        base["uniforms"] = to_dev(case.uniforms.astype(np.float32))
     else:
         base["node_tokens"] = to_dev(case.node_tokens.astype(np.int32))
         base["paths"] = to_dev(case.paths.astype(np.int32))
@@ -144,6 +154,18 @@ def make_step(case, sets, filt=None):
             s = sets[i % len(sets)]
             sv.spec_verify_greedy(s["target"], s["draft_tokens"], out_tokens=out,
                                   num_accepted=acc, workspace=ws)
+        return step, out, acc
+    if mode == "tree-stochastic":
+        out = torch.empty((case.B, case.L), dtype=torch.int32, device=dev)
+        acc = torch.empty((case.B,), dtype=torch.int32, device=dev)
+        nodes = torch.empty((case.B, case.L), dtype=torch.int32, device=dev)
+
+        def step(i):
+            s = sets[i % len(sets)]
+            sv.spec_verify_tree_stochastic(s["target"], s["draft"], s["node_tokens"], s["paths"],
+                                           s["uniforms"], case.temperature, out_tokens=out,
+                                           num_accepted=acc, accepted_nodes=nodes)
+        step.nodes = nodes
         return step, out, acc
     out = torch.empty((case.B, case.L), dtype=torch.int32, device=dev)
     acc = torch.empty((case.B,), dtype=torch.int32, device=dev)
@@ -208,7 +230,29 @@ def streaming_bytes(case) -> int:
     """Algorithmic bytes of the streaming kernel: one read of every logits row."""
     if mode_of(case) == "stochastic":
         return case.target.nbytes + (case.draft.nbytes if case.k > 0 else 0)
+    if mode_of(case) == "tree-stochastic":
+        return case.target.nbytes + case.draft.nbytes
     return case.target.nbytes
+
+
+def tree_walk_bytes(case, nodes, acc) -> int:
+    """Algorithmic bytes of a stochastic tree walk: one read of the target row of
+    every visited node (the root and the accepted nodes) and of the draft row of
+    every visited node whose children were tested."""
+    import numpy as np
+
+    row = case.V * (2 if case.dtype == "bf16" else 4)
+    total = 0
+    for b in range(case.B):
+        has_child = np.zeros(case.N + 1, bool)
+        par = case.parents[b]
+        has_child[par[par >= 0]] = True
+        visited = [0] + [int(n) for n in nodes[b, :int(acc[b])]]
+        for depth, n in enumerate(visited):
+            total += row
+            if has_child[n] and depth + 1 < case.L:
+                total += row
+    return total
 
 
 def load_traffic(workload: str, src_hash: str):
@@ -244,6 +288,9 @@ def cpu_baseline(case, seconds: float, filt=None):
                               case.draft_tokens[sl], case.uniforms[sl], case.temperature, **fkw)
         elif mode == "greedy":
             oracle.greedy(case.target[sl], case.draft_tokens[sl])
+        elif mode == "tree-stochastic":
+            oracle.tree_stochastic(case.target[sl], case.draft[sl], case.node_tokens[sl],
+                                   case.paths[sl], case.uniforms[sl], case.temperature)
         else:
             oracle.tree(case.target[sl], case.node_tokens[sl], case.paths[sl])
         done += 1
@@ -290,6 +337,8 @@ def main():
           file=sys.stderr, flush=True)
     nbytes = streaming_bytes(case)
     copies = args.copies or max(1, math.ceil((1 << 30) / nbytes))
+    if mode_of(case) == "tree-stochastic" and not args.copies:
+        copies = 8  # a walk reads a few rows per request: rotate far beyond the MALL
     sets = device_inputs(case, copies)
     filt = None
     if mode_of(case) == "stochastic" and (0 < args.top_k < case.V or args.top_p < 1.0
@@ -322,6 +371,9 @@ def main():
     else:
         kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
     k_avg = float(np.mean(kernel_ms))
+    if mode_of(case) == "tree-stochastic":
+        # the walk reads only the visited rows: the same outputs on every copy
+        nbytes = tree_walk_bytes(case, step.nodes.cpu().numpy(), acc.cpu().numpy())
     rows = case.rows
     value = rows / (ms * 1e-3)
     achieved = nbytes / (k_avg * 1e-3) / 1e9
@@ -353,9 +405,10 @@ def main():
             "logits_bytes": nbytes,
             "input_copies": copies,
             "seed": args.seed,
-            **({"k": case.k} if mode_of(case) != "tree"
+            **({"k": case.k} if mode_of(case) in ("stochastic", "greedy")
                else {"N": case.N, "P": case.P, "L": case.L}),
-            **({"temperature": case.temperature} if mode_of(case) == "stochastic" else {}),
+            **({"temperature": case.temperature}
+               if mode_of(case) in ("stochastic", "tree-stochastic") else {}),
             **({} if filt is None else {"top_k": args.top_k, "top_p": args.top_p,
                                         "min_p": args.min_p}),
         },
@@ -364,7 +417,8 @@ def main():
             "bound": "hbm",
             "kernel": ("statistics kernel (filtered call)" if filt is not None else
                        "statistics kernel (two-kernel schedule)" if mode_of(case) == "stochastic"
-                       else "argmax kernel"),
+                       else "tree walk kernel (one workgroup per request)"
+                       if mode_of(case) == "tree-stochastic" else "argmax kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -309,7 +309,7 @@ int spec_verify_tree_stochastic(const void* target_logits, const void* draft_log
     c.out_tokens = out_tokens;
     c.num_accepted = num_accepted;
     c.accepted_nodes = accepted_nodes;
-    return finish(sv::run_tree_stochastic(c, (hipStream_t)stream));
+    return finish(sv::run_tree_stochastic(c, (hipStream_t)stream, next_events()));
 }
 
 int spec_verify_gather_rows(const void* src, void* dst, size_t row_bytes,

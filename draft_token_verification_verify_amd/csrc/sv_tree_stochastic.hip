@@ -33,9 +33,9 @@ constexpr int kTsThreads = 1024;
 constexpr int kTsWaves = kTsThreads / 64;
 constexpr int kMaxTreeNodes = 1024;            // N + 1
 constexpr int kMaxRejections = kMaxTreeNodes;  // a node has at most N children
-constexpr int kTsPer = 8;                      // logits per thread per tile
+constexpr int kTsPer = 16;                     // logits per thread per tile
 constexpr int kTsTile = kTsThreads * kTsPer;   // logits per tile
-constexpr int kTsTiles = 64;                   // tiles per row: V <= 524288
+constexpr int kTsTiles = 32;                   // tiles per row: V <= 524288
 
 struct TreeStochArgs {
     const void* target;
@@ -53,7 +53,7 @@ struct TreeStochArgs {
 struct TsLds {
     int first[kMaxTreeNodes];   // first occurrence (row * L + t) of each node in paths
     int parent[kMaxTreeNodes];
-    double z[kMaxRejections];   // residual masses at the current node
+    double inv_z[kMaxRejections];  // reciprocal residual masses at the current node
     double red_d[kTsWaves];
     float red_f[kTsWaves];
     double tile_sum[kTsTiles];
@@ -124,27 +124,21 @@ __device__ inline double ts_block_scan(double v, TsLds& L, double* total) {
     return before + (inc - v);
 }
 
-// The row is read in tiles of kTsThreads * 8 logits; thread t takes the 8
-// consecutive logits at tile * 8192 + 8 t (one 16-byte load for bf16 rows
-// when aligned).  Tile-major, thread-minor order is ascending vocabulary order.
-
+// The row is read in tiles of kTsThreads * 16 logits; thread t takes the 16
+// consecutive logits at tile * 16384 + 16 t (all of its 16-byte loads issued
+// together when the row is aligned).  Tile-major, thread-minor order is
+// ascending vocabulary order.
 template <typename T, bool VEC>
-__device__ inline void ts_load8(const T* row, int V, int tile, float* x) {
+__device__ inline void ts_load(const T* row, int V, int tile, float* x) {
     const int j0 = tile * kTsTile + (int)threadIdx.x * kTsPer;
     if constexpr (VEC) {
+        constexpr int EPV = Elem<T>::kPerVec;
         if (j0 + kTsPer <= V) {
-            if constexpr (sizeof(T) == 2) {
-                Elem<T>::widen(load16(row + j0), x);
-            } else {
-                float a[4], b[4];
-                Elem<T>::widen(load16(row + j0), a);
-                Elem<T>::widen(load16(row + j0 + 4), b);
+            uint4 raw[kTsPer / EPV];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    x[e] = a[e];
-                    x[4 + e] = b[e];
-                }
-            }
+            for (int v = 0; v < kTsPer / EPV; ++v) raw[v] = load16(row + j0 + v * EPV);
+#pragma unroll
+            for (int v = 0; v < kTsPer / EPV; ++v) Elem<T>::widen(raw[v], x + v * EPV);
             return;
         }
     }
@@ -152,56 +146,81 @@ __device__ inline void ts_load8(const T* row, int V, int tile, float* x) {
     for (int e = 0; e < kTsPer; ++e) x[e] = (j0 + e < V) ? Elem<T>::load(row, j0 + e) : -INFINITY;
 }
 
-// Softmax statistics of a row: maximum m and s = sum of 2^((x - m) c).
+// Softmax statistics of a row: maximum m and s = sum of 2^((x - m) c), in one
+// pass: each thread sums against its running maximum, rescaling its sum (fp64
+// exponential) when the maximum grows; threads are then merged in fixed order.
 struct RowStats {
     float m;
     double s;
 };
 
+struct RunStats {
+    float m = -INFINITY;
+    double s = 0.0;
+    // The 16 logits of one tile: the running maximum first (one rescale at
+    // most), then their terms against it.
+    __device__ inline void add_tile(const float* x, const Scale& sc) {
+        float tm = m;
+#pragma unroll
+        for (int e = 0; e < kTsPer; ++e) tm = fmaxf(tm, x[e]);
+        if (tm > m) {
+            if (m != -INFINITY) s *= exp2_accurate(m, tm, sc);
+            m = tm;
+        }
+        const float ms = (m == -INFINITY) ? 0.f : m;
+#pragma unroll
+        for (int e = 0; e < kTsPer; ++e) s += (double)fast_exp2(scaled(x[e] - ms, sc));
+    }
+};
+
+__device__ inline RowStats ts_merge(const RunStats& r, const Scale& sc, TsLds& L) {
+    RowStats out;
+    out.m = ts_block_max(r.m, L);
+    const double f = (r.m == -INFINITY || out.m == -INFINITY) ? 0.0 : exp2_accurate(r.m, out.m, sc);
+    out.s = ts_block_sum(r.m == -INFINITY ? 0.0 : r.s * f, L);
+    return out;
+}
+
+// Statistics of the target row and, when `both`, of the draft row, in one pass.
 template <typename T, bool VEC>
-__device__ RowStats ts_row_stats(const T* row, int V, const Scale& sc, TsLds& L) {
+__device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, const Scale& sc,
+                             TsLds& L, RowStats* st, RowStats* sd) {
     const int tiles = (V + kTsTile - 1) / kTsTile;
-    float mt = -INFINITY;
+    RunStats rt, rd;
     for (int k = 0; k < tiles; ++k) {
-        float x[kTsPer];
-        ts_load8<T, VEC>(row, V, k, x);
-#pragma unroll
-        for (int e = 0; e < kTsPer; ++e) mt = fmaxf(mt, x[e]);
+        float xt[kTsPer], xd[kTsPer];
+        ts_load<T, VEC>(trow, V, k, xt);
+        if (both) ts_load<T, VEC>(drow, V, k, xd);
+        rt.add_tile(xt, sc);
+        if (both) rd.add_tile(xd, sc);
     }
-    const float ms = (mt == -INFINITY) ? 0.f : mt;
-    double st = 0.0;
-    for (int k = 0; k < tiles; ++k) {
-        float x[kTsPer];
-        ts_load8<T, VEC>(row, V, k, x);
-#pragma unroll
-        for (int e = 0; e < kTsPer; ++e) st += (double)fast_exp2(scaled(x[e] - ms, sc));
-    }
-    RowStats r;
-    r.m = ts_block_max(mt, L);
-    const double f = (mt == -INFINITY || r.m == -INFINITY) ? 0.0 : exp2_accurate(mt, r.m, sc);
-    r.s = ts_block_sum(st * f, L);
-    return r;
+    *st = ts_merge(rt, sc, L);
+    if (both) *sd = ts_merge(rd, sc, L);
 }
 
 // The current distribution at token x: p after nrej rejections,
 // p_i = max(0, p_{i-1} - q) / z_i (p_{i-1} kept where z_i == 0), and q.
+// Divisions by the row masses and the residual masses are multiplications by
+// their reciprocals (within an ulp of the quotient).
 struct Dist {
     float mt, md;
-    double st, sd;
+    double inv_st, inv_sd;  // 1 / row mass (0 for a row without mass)
     Scale sc;
     int nrej;
-    const double* z;
-    __device__ inline double p0(float xt) const {
-        return (mt == -INFINITY || !(st > 0.0)) ? 0.0 : ts_weight(xt, mt, sc) / st;
+    const double* inv_z;    // 1 / residual mass after each rejection (0: mass was 0)
+    __device__ inline void set(float m_t, double s_t, float m_d, double s_d) {
+        mt = m_t;
+        md = m_d;
+        inv_st = (m_t == -INFINITY || !(s_t > 0.0)) ? 0.0 : 1.0 / s_t;
+        inv_sd = (m_d == -INFINITY || !(s_d > 0.0)) ? 0.0 : 1.0 / s_d;
     }
-    __device__ inline double q(float xd) const {
-        return (md == -INFINITY || !(sd > 0.0)) ? 0.0 : ts_weight(xd, md, sc) / sd;
-    }
+    __device__ inline double p0(float xt) const { return ts_weight(xt, mt, sc) * inv_st; }
+    __device__ inline double q(float xd) const { return ts_weight(xd, md, sc) * inv_sd; }
     // p after the first `upto` rejections, given p0 and q at a token.
     __device__ inline double chain(double p, double qv, int upto) const {
         for (int i = 0; i < upto; ++i) {
-            const double zi = z[i];
-            if (zi > 0.0) p = fmax(p - qv, 0.0) / zi;
+            const double iz = inv_z[i];
+            if (iz > 0.0) p = fmax(p - qv, 0.0) * iz;
         }
         return p;
     }
@@ -217,8 +236,8 @@ __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist
     double total = 0.0;
     for (int k = 0; k < tiles; ++k) {
         float xt[kTsPer], xd[kTsPer];
-        ts_load8<T, VEC>(trow, V, k, xt);
-        if (residual) ts_load8<T, VEC>(drow, V, k, xd);
+        ts_load<T, VEC>(trow, V, k, xt);
+        if (residual) ts_load<T, VEC>(drow, V, k, xd);
         double own = 0.0;
 #pragma unroll
         for (int e = 0; e < kTsPer; ++e) {
@@ -269,27 +288,26 @@ __device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool 
     const int k = L.pick_tile;
     const double base = L.pick_base;
     float xt[kTsPer], xd[kTsPer];
-    ts_load8<T, VEC>(trow, V, k, xt);
-    if (residual) ts_load8<T, VEC>(drow, V, k, xd);
-    double w[kTsPer], own = 0.0;
-#pragma unroll
-    for (int e = 0; e < kTsPer; ++e) {
+    ts_load<T, VEC>(trow, V, k, xt);
+    if (residual) ts_load<T, VEC>(drow, V, k, xd);
+    auto weight = [&](int e) {
         const double qv = residual ? D.q(xd[e]) : 0.0;
         const double p = D.chain(D.p0(xt[e]), qv, D.nrej);
-        w[e] = residual ? fmax(p - qv, 0.0) : p;
-        own += w[e];
-    }
+        return residual ? fmax(p - qv, 0.0) : p;
+    };
+    double own = 0.0;
+    for (int e = 0; e < kTsPer; ++e) own += weight(e);
     double tile_total;
     double run = base + ts_block_scan(own, L, &tile_total);
     const int j0 = k * kTsTile + (int)threadIdx.x * kTsPer;
     int hit = 0x7fffffff, lastpos = -1;
-#pragma unroll
-    for (int e = 0; e < kTsPer; ++e) {
-        if (w[e] > 0.0) {
+    for (int e = 0; e < kTsPer; ++e) {  // the same weights, in the same order
+        const double w = weight(e);
+        if (w > 0.0) {
             lastpos = j0 + e;
-            if (run + w[e] > target && hit == 0x7fffffff) hit = j0 + e;
+            if (run + w > target && hit == 0x7fffffff) hit = j0 + e;
         }
-        run += w[e];
+        run += w;
     }
     int tok = ts_block_min(hit, L);
     if (tok == 0x7fffffff)  // rounding left every running weight at or below u * Z
@@ -345,17 +363,10 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
         Dist D;
         D.sc = a.sc;
         D.nrej = 0;
-        D.z = L.z;
-        const RowStats st = ts_row_stats<T, VEC>(trow, V, a.sc, L);
-        D.mt = st.m;
-        D.st = st.s;
-        D.md = -INFINITY;
-        D.sd = 1.0;
-        if (test) {
-            const RowStats sd = ts_row_stats<T, VEC>(drow, V, a.sc, L);
-            D.md = sd.m;
-            D.sd = sd.s;
-        }
+        D.inv_z = L.inv_z;
+        RowStats st, sd;
+        ts_row_stats<T, VEC>(trow, drow, test, V, a.sc, L, &st, &sd);
+        D.set(st.m, st.s, test ? sd.m : -INFINITY, test ? sd.s : 0.0);
         int next = -1;
         double Zlast = 0.0;
         if (test) {
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
                 }
                 // Rejected: the residual's mass, then the next sibling against it.
                 Zlast = ts_weight_pass<T, VEC>(trow, drow, V, D, true, L);
-                if (threadIdx.x == 0) L.z[D.nrej] = Zlast;
+                if (threadIdx.x == 0) L.inv_z[D.nrej] = Zlast > 0.0 ? 1.0 / Zlast : 0.0;
                 __syncthreads();
                 ++D.nrej;
             }
@@ -440,7 +451,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs g) {
     }
 }
 
-hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st) {
+hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st, const KernelEvents& ev) {
     TreeStochArgs a;
     a.target = c.target;
     a.draft = c.draft;
@@ -457,12 +468,21 @@ hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st) {
     a.num_accepted = c.num_accepted;
     a.accepted_nodes = c.accepted_nodes;
     const dim3 grid((unsigned)c.B), block(kTsThreads);
+    // The events (when set) take the kernel's own start and end timestamps.
     if (c.dtype == 1) {
-        if (c.vec) tree_stochastic_kernel<bf16_t, true><<<grid, block, 0, st>>>(a);
-        else tree_stochastic_kernel<bf16_t, false><<<grid, block, 0, st>>>(a);
+        if (c.vec)
+            hipExtLaunchKernelGGL(tree_stochastic_kernel<bf16_t, true>, grid, block, 0, st,
+                                  ev.begin, ev.end, 0, a);
+        else
+            hipExtLaunchKernelGGL(tree_stochastic_kernel<bf16_t, false>, grid, block, 0, st,
+                                  ev.begin, ev.end, 0, a);
     } else {
-        if (c.vec) tree_stochastic_kernel<float, true><<<grid, block, 0, st>>>(a);
-        else tree_stochastic_kernel<float, false><<<grid, block, 0, st>>>(a);
+        if (c.vec)
+            hipExtLaunchKernelGGL(tree_stochastic_kernel<float, true>, grid, block, 0, st,
+                                  ev.begin, ev.end, 0, a);
+        else
+            hipExtLaunchKernelGGL(tree_stochastic_kernel<float, false>, grid, block, 0, st,
+                                  ev.begin, ev.end, 0, a);
     }
     return hipGetLastError();
 }
