@@ -462,9 +462,16 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
 struct Weigher {
     float mt, md;
     double r;
+    float r32;     // r rounded to fp32
+    float ad_big;  // draft exponent above which r e_d may pass 2^-8: -8 - log2(r)
     Scale sc;
     bool residual;
     float taut, taud;
+    __device__ inline void set_ratio(double ratio) {
+        r = ratio;
+        r32 = (float)ratio;
+        ad_big = -8.f - log2f(r32);
+    }
     __device__ inline double e_of(float x, float m) const {
         const float a = scaled(x - m, sc);
         if (a > -8.f) return exp2_accurate(x, m, sc);
@@ -481,6 +488,30 @@ struct Weigher {
     __device__ inline double weigh(float xt, float xd) const {
         return residual ? w<true, FILT>(xt, xd) : w<false, FILT>(xt, xd);
     }
+    // Add one token's weight to a segment sum: a token whose terms may pass
+    // 2^-8 (of the target row's maximum weight) as w() gives it, in fp64;
+    // every other token entirely in fp32 (its exponentials are the fp32 ones
+    // of w() already), summed apart and added to the fp64 sum once.
+    template <bool RESID, bool FILT>
+    __device__ inline void add(float xt, float xd, double& big, float& small) const {
+        const bool kt = !FILT || xt >= taut;
+        const float at = scaled(xt - mt, sc);
+        if constexpr (!RESID) {
+            if (!kt) return;
+            if (at > -8.f) big += exp2_accurate(xt, mt, sc);
+            else small += fast_exp2(at);
+        } else {
+            const bool kd = !FILT || xd >= taud;
+            const float ad = scaled(xd - md, sc);
+            if ((kt && at > -8.f) || (kd && ad > ad_big)) {
+                big += w<true, FILT>(xt, xd);
+            } else {
+                const float et = kt ? fast_exp2(at) : 0.f;
+                const float ed = kd ? fast_exp2(ad) : 0.f;
+                small += fmaxf(fmaf(-r32, ed, et), 0.f);
+            }
+        }
+    }
 };
 
 constexpr int kSub = 16;  // tokens per sampler sub-step
@@ -496,6 +527,7 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
     constexpr int SEG = NSUB * kSub;
     const int start = lo + (int)threadIdx.x * SEG;
     double seg = 0.0;
+    float small = 0.f;
     if constexpr (VEC) {
         constexpr int EPV = Elem<T>::kPerVec;
         constexpr int NV = SEG / EPV;                  // vectors per row in the segment
@@ -517,7 +549,7 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
 #pragma unroll
                 for (int e = 0; e < EPV; ++e)
                     if (start + (v0 + v) * EPV + e < hi)
-                        seg += W.template w<RESID, FILT>(xt[e], RESID ? xd[e] : 0.f);
+                        W.template add<RESID, FILT>(xt[e], RESID ? xd[e] : 0.f, seg, small);
             }
         }
     } else {
@@ -532,10 +564,10 @@ __device__ double segment_sum(const T* trow, const T* drow, const Weigher& W, in
             }
 #pragma unroll
             for (int e = 0; e < kSub; ++e)
-                if (start + s0 + e < hi) seg += W.template w<RESID, FILT>(xt[e], xd[e]);
+                if (start + s0 + e < hi) W.template add<RESID, FILT>(xt[e], xd[e], seg, small);
         }
     }
-    return seg;
+    return seg + (double)small;
 }
 
 template <typename T, bool VEC, int NSUB, bool FILT>
@@ -709,7 +741,7 @@ __device__ void sample_item(const CallArgs& a, int b, int ch) {
     Weigher W;
     W.mt = dc.mt;
     W.md = dc.md;
-    W.r = dc.st / dc.sd;
+    W.set_ratio(dc.st / dc.sd);
     W.sc = a.sc;
     W.residual = dc.s < dc.kb;
     W.taut = dc.taut;
