@@ -182,12 +182,17 @@ struct StatsOp : CallArgs {
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int e = 0; e < EPV; ++e) m = fmaxf(m, x[j][e]);
+        // The terms of each 16-byte vector are summed in fp32, the vectors' sums
+        // in fp64.
         const float ms = (m == -INFINITY) ? 0.f : m;
         double s = 0.0;
 #pragma unroll
-        for (int j = 0; j < U; ++j)
+        for (int j = 0; j < U; ++j) {
+            float g = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[j][e] - ms, sc));
+            for (int e = 0; e < EPV; ++e) g += fast_exp2(scaled(x[j][e] - ms, sc));
+            s += (double)g;
+        }
         finish(m, s, f0, f1, d);
     }
 
@@ -250,7 +255,9 @@ __device__ void stats_tile_runtime(const CallArgs& a, int t, float* f0, float* f
         if (v < nvec) {
             float x[EPV];
             Elem<T>::widen(base[v], x);
-            for (int e = 0; e < EPV; ++e) s += (double)fast_exp2(scaled(x[e] - ms, a.sc));
+            float g = 0.f;
+            for (int e = 0; e < EPV; ++e) g += fast_exp2(scaled(x[e] - ms, a.sc));
+            s += (double)g;
         }
     }
     op.finish(m, s, f0, f1, d);
