@@ -321,8 +321,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build measures one GPU only; run it with --gpus 1 "
-              "(sharding across GPUs is described in DESIGN.md, not run)", file=sys.stderr)
+        print("bench.py measures one GPU: run it with --gpus 1 (requests would shard across "
+              "GPUs with no exchange; no multi-GPU run is made here)", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -355,7 +355,8 @@ def main():
     one_launch_ms = None
     if filt is not None:
         # Statistics kernel, per-row filter selection, sampler; the events sit
-        # on the statistics kernel.
+        # on the selection kernel, the call's longest (its algorithmic read is
+        # one pass over every row, like the statistics kernel's).
         kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
     elif mode_of(case) == "stochastic":
         # The default schedule runs statistics and sampling in one launch; the
@@ -415,7 +416,7 @@ def main():
         "hbm_gbps_whole_call": nbytes / (ms * 1e-3) / 1e9,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("statistics kernel (filtered call)" if filt is not None else
+            "kernel": ("filter selection kernel (filtered call)" if filt is not None else
                        "statistics kernel (two-kernel schedule)" if mode_of(case) == "stochastic"
                        else "tree walk kernel (one workgroup per request)"
                        if mode_of(case) == "tree-stochastic" else "argmax kernel"),

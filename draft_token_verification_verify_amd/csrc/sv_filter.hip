@@ -927,13 +927,15 @@ __global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
 }
 
 template <typename T, bool VEC>
-static hipError_t launch_filter(const FilterArgs& a, hipStream_t st) {
-    filter_kernel<T, VEC><<<dim3((unsigned)(a.B * a.R)), dim3(kSelThreads), 0, st>>>(a);
+static hipError_t launch_filter(const FilterArgs& a, hipStream_t st, const KernelEvents& ev) {
+    // The events (when set) take the kernel's own start and end timestamps.
+    hipExtLaunchKernelGGL(filter_kernel<T, VEC>, dim3((unsigned)(a.B * a.R)), dim3(kSelThreads),
+                          0, st, ev.begin, ev.end, 0, a);
     return hipGetLastError();
 }
 
 hipError_t run_filter(const StochasticCall& call, const FilterCall& f, const Geometry& g,
-                      hipStream_t st) {
+                      hipStream_t st, const KernelEvents& ev) {
     char* ws = static_cast<char*>(call.workspace);
     FilterArgs a;
     a.target = call.target;
@@ -952,8 +954,9 @@ hipError_t run_filter(const StochasticCall& call, const FilterCall& f, const Geo
     a.partials = reinterpret_cast<const Partial16*>(ws + g.off_partials);
     a.rowf = reinterpret_cast<RowFilter*>(ws + g.off_rowf);
     if (call.dtype == 1)
-        return call.vec ? launch_filter<bf16_t, true>(a, st) : launch_filter<bf16_t, false>(a, st);
-    return call.vec ? launch_filter<float, true>(a, st) : launch_filter<float, false>(a, st);
+        return call.vec ? launch_filter<bf16_t, true>(a, st, ev)
+                        : launch_filter<bf16_t, false>(a, st, ev);
+    return call.vec ? launch_filter<float, true>(a, st, ev) : launch_filter<float, false>(a, st, ev);
 }
 
 }  // namespace sv

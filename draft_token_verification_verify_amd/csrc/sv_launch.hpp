@@ -105,7 +105,7 @@ hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStre
 hipError_t run_stochastic_filtered(const StochasticCall& call, const FilterCall& f,
                                    const Geometry& g, hipStream_t st, const KernelEvents& ev);
 hipError_t run_filter(const StochasticCall& call, const FilterCall& f, const Geometry& g,
-                      hipStream_t st);
+                      hipStream_t st, const KernelEvents& ev);
 hipError_t run_greedy(const GreedyCall& call, const Geometry& g, hipStream_t st,
                       const KernelEvents& ev);
 hipError_t run_tree(const TreeCall& call, const Geometry& g, hipStream_t st,

@@ -919,14 +919,15 @@ hipError_t run_stochastic_filtered(const StochasticCall& call, const FilterCall&
     CallArgs a = make_args(call, g);
     a.rowf = reinterpret_cast<RowFilter*>(static_cast<char*>(call.workspace) + g.off_rowf);
     hipError_t e;
+    const KernelEvents none;  // the events, when set, go to the selection kernel
     if (call.dtype == 1)
-        e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st, ev)
-                     : launch_stats<bf16_t, false>(a, g.U, st, ev);
+        e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st, none)
+                     : launch_stats<bf16_t, false>(a, g.U, st, none);
     else
-        e = call.vec ? launch_stats<float, true>(a, g.U, st, ev)
-                     : launch_stats<float, false>(a, g.U, st, ev);
+        e = call.vec ? launch_stats<float, true>(a, g.U, st, none)
+                     : launch_stats<float, false>(a, g.U, st, none);
     if (e != hipSuccess) return e;
-    e = run_filter(call, f, g, st);
+    e = run_filter(call, f, g, st, ev);
     if (e != hipSuccess) return e;
     if (call.dtype == 1)
         return call.vec ? launch_sample<bf16_t, true, true>(a, st)

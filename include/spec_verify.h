@@ -133,8 +133,9 @@ int spec_verify_set_schedule(int schedule);
 /*
  * Profiling hook.  After this call, every verification call launches its
  * streaming kernel (the one that reads every logits row; under the one-launch
- * stochastic schedule, the whole call; for the filtered call, its statistics
- * kernel; for spec_verify_tree_stochastic, its one kernel) with events[2 * i] and
+ * stochastic schedule, the whole call; for the filtered call, its per-row
+ * selection kernel; for spec_verify_tree_stochastic, its one kernel) with
+ * events[2 * i] and
  * events[2 * i + 1] attached as the kernel's start and stop events
  * (hipExtLaunchKernel: they take the kernel's own start and end timestamps),
  * with i advancing by one per call and wrapping at n_pairs.  The events are
