@@ -149,14 +149,29 @@ __device__ inline double weight_of(float x, float m, double c64, bool acc) {
     return ldexp((double)fast_exp2((float)(a - n)), (int)n);
 }
 
+// Weight of a logit at least 8 octaves below the maximum (a <= -8), with no
+// call: the fast form of weight_of (acc false), or (acc) the fp64 exponential
+// inlined, for loops over the tail of a row.
+__device__ __attribute__((always_inline)) inline double tail_weight(float x, float m, double c64,
+                                                                    bool acc) {
+    if (x == -INFINITY) return 0.0;
+    const double a = ((double)x - (double)m) * c64;
+    if (a < -1100.0) return 0.0;
+    if (acc) return exp2(a);
+    const double n = floor(a);
+    return ldexp((double)fast_exp2((float)(a - n)), (int)n);
+}
+
 __device__ inline unsigned long long qweight(float x, float m, double c64, int bin, bool acc) {
     return (unsigned long long)(ldexp(weight_of(x, m, c64, acc), octave_of(bin) + kMassBits) + 0.5);
 }
 
 // Every element of a row, in a fixed per-thread order (so per-thread sums are
-// the same on every run).  Each thread keeps BATCH 16-byte loads in flight (a
-// light per-element body affords 16: a whole 128K-token bf16 row in one round
-// trip per thread).
+// the same on every run).  Each thread keeps BATCH 16-byte loads in flight.
+// Only one vector's elements are unrolled: the batch is walked by a loop that
+// shifts the loaded vectors down one register slot per step, so the loop body
+// holds EPV copies of f, not BATCH * EPV (the kernel's loops are otherwise
+// larger than the instruction cache that two compute units share).
 template <typename T, bool VEC, int BATCH = 4, class F>
 __device__ inline void for_each_logit(const T* row, int V, F&& f) {
     if constexpr (VEC) {
@@ -167,14 +182,16 @@ __device__ inline void for_each_logit(const T* row, int V, F&& f) {
             uint4 raw[BATCH];
 #pragma unroll
             for (int j = 0; j < BATCH; ++j) raw[j] = p[min(v0 + j * kSelThreads, nvec - 1)];
-#pragma unroll
+#pragma unroll 1
             for (int j = 0; j < BATCH; ++j) {
                 if (v0 + j * kSelThreads < nvec) {
                     float x[EPV];
-                    Elem<T>::widen(raw[j], x);
+                    Elem<T>::widen(raw[0], x);
 #pragma unroll
                     for (int e = 0; e < EPV; ++e) f(x[e]);
                 }
+#pragma unroll
+                for (int t = 0; t + 1 < BATCH; ++t) raw[t] = raw[t + 1];
             }
         }
     } else {
@@ -209,6 +226,25 @@ struct SelLds {
     int red_i;
     int n_gathered;
 };
+
+// The first active lane's value.  For values that every lane of the
+// workgroup holds alike (read back from LDS after a barrier): the compiler then
+// keeps them in scalar registers instead of vector registers that the long
+// per-logit loops need.
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline uint32_t uniform(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_readfirstlane((int)v);
+}
+__device__ inline float uniform(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ inline unsigned long long uniform(unsigned long long v) {
+    const uint32_t lo = uniform((uint32_t)v), hi = uniform((uint32_t)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ inline double uniform(double v) {
+    return __longlong_as_double((long long)uniform((unsigned long long)__double_as_longlong(v)));
+}
 
 __device__ inline unsigned long long wave_inclusive_scan_u64(unsigned long long v) {
     const int lane = threadIdx.x & 63;
@@ -254,7 +290,7 @@ __device__ inline unsigned long long sel_exclusive_scan(unsigned long long v, Se
         all += t;
     }
     __syncthreads();
-    *total = all;
+    *total = uniform(all);
     return before + inc - v;
 }
 
@@ -286,7 +322,7 @@ __device__ inline float sel_max(float v, SelLds& L) {
 #pragma unroll
     for (int w = 1; w < kSelWaves; ++w) r = fmaxf(r, L.red_f[w]);
     __syncthreads();
-    return r;
+    return uniform(r);
 }
 
 // fp64 sum in a fixed order (same bits on every run).
@@ -298,7 +334,7 @@ __device__ inline double sel_sum_f64(double v, SelLds& L) {
 #pragma unroll
     for (int w = 1; w < kSelWaves; ++w) r += L.red_d[w];
     __syncthreads();
-    return r;
+    return uniform(r);
 }
 
 __device__ inline int sel_min_int(int v, SelLds& L) {
@@ -308,7 +344,7 @@ __device__ inline int sel_min_int(int v, SelLds& L) {
     __syncthreads();
     if ((threadIdx.x & 63) == 0) atomicMin(&L.red_i, v);
     __syncthreads();
-    const int r = L.red_i;
+    const int r = uniform(L.red_i);
     __syncthreads();
     return r;
 }
@@ -412,13 +448,13 @@ __device__ inline BinScan scan_find(SelLds& L, int nb, bool by_count, unsigned l
     }
     __syncthreads();
     BinScan out;
-    out.bin = L.red_i;
-    out.cnt_total = (unsigned long long)L.bscan[3];
-    out.mass_total = L.bscan[4];
+    out.bin = uniform(L.red_i);
+    out.cnt_total = (unsigned long long)uniform(L.bscan[3]);
+    out.mass_total = uniform(L.bscan[4]);
     const bool hit = out.bin < nb;
-    out.cnt_ex = hit ? (unsigned long long)L.bscan[0] : out.cnt_total;
-    out.mass_ex = hit ? L.bscan[1] : out.mass_total;
-    out.mass_in = hit ? L.bscan[2] : out.mass_total;
+    out.cnt_ex = hit ? (unsigned long long)uniform(L.bscan[0]) : out.cnt_total;
+    out.mass_ex = hit ? uniform(L.bscan[1]) : out.mass_total;
+    out.mass_in = hit ? uniform(L.bscan[2]) : out.mass_total;
     __syncthreads();
     return out;
 }
@@ -593,7 +629,9 @@ __device__ __attribute__((always_inline)) SelectOut select_in_bin(const T* row, 
 template <typename T, bool VEC>
 __device__ inline bool gather_bin(SelLds& L, const T* x, bool complete, int ntop, float m,
                                   const FilterArgs& a, int bin, float floor_v) {
-    if (L.cnt[bin] > (uint32_t)kSub) return false;
+    const bool fits = L.cnt[bin] <= (uint32_t)kSub;
+    __syncthreads();  // every wave has read the count before anyone may rewrite it
+    if (!uniform((int)fits)) return false;
     if (threadIdx.x == 0) L.n_sub = 0;
     __syncthreads();
     if (complete) {  // every logit of the bin is in top[]
@@ -612,7 +650,7 @@ __device__ inline bool gather_bin(SelLds& L, const T* x, bool complete, int ntop
         });
     }
     __syncthreads();
-    sort_desc(L.buf.f.sub, L.n_sub);
+    sort_desc(L.buf.f.sub, uniform(L.n_sub));
     return true;
 }
 
@@ -654,11 +692,11 @@ __device__ inline Walk walk_sub(SelLds& L, int ns, float m, const FilterArgs& a,
     __syncthreads();
     Walk w;
     w.found = h < ns;
-    w.tau = w.found ? v[h] : -INFINITY;
+    w.tau = w.found ? uniform(v[h]) : -INFINITY;
     w.margin = 0.0;
     w.mass = 0.0;
     if (w.found) {
-        const unsigned long long end = L.bcast;
+        const unsigned long long end = uniform(L.bcast);
         unsigned long long eq = 0;
         for (int j = threadIdx.x; j < ns; j += kSelThreads) eq += v[j] == w.tau;
         eq = sel_sum_u64(eq, L);
@@ -694,7 +732,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
     bool complete = true;  // top[] holds every logit of the bins below lim
     BinScan sc;
     for (;;) {
-        const int n0 = min(L.n_gathered, kTop);
+        const int n0 = min(uniform(L.n_gathered), kTop);
         // bins [lim_prev, lim) are the logits in [x_lo, x_hi)
         const float x_lo = lowest_in_bins(lim, m, a.bin_scale);
         const float x_hi = lowest_in_bins(lim_prev, m, a.bin_scale);
@@ -707,8 +745,9 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
             }
         });
         __syncthreads();
-        const int n1 = min(L.n_gathered, kTop);
-        complete = complete && L.n_gathered <= kTop;
+        const int ngat = uniform(L.n_gathered);
+        const int n1 = min(ngat, kTop);
+        complete = complete && ngat <= kTop;
         __syncthreads();
         // Counts and fp64 masses of the newly gathered logits, from LDS.
         for (int i = n0 + threadIdx.x; i < n1; i += kSelThreads) {
@@ -725,7 +764,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
         lim = min(2 * lim, kBins);
     }
     const bool whole_row = lim == kBins;  // then the gathered masses are the row's
-    const int ntop = min(L.n_gathered, kTop);
+    const int ntop = min(uniform(L.n_gathered), kTop);
 
     float tau_k = -INFINITY, tau_p = -INFINITY;
     double s_k = 0.0, s_p = 0.0;
@@ -734,8 +773,8 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
         bk = sc.bin;
         const int r = (int)(a.top_k - sc.cnt_ex);
         if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bk, -INFINITY)) return false;
-        const int ns = L.n_sub;
-        tau_k = L.buf.f.sub[max(min(r, ns), 1) - 1];
+        const int ns = uniform(L.n_sub);
+        tau_k = uniform(L.buf.f.sub[max(min(r, ns), 1) - 1]);
         unsigned long long c = 0, q = 0;
         for (int i = threadIdx.x; i < ns; i += kSelThreads)
             if (L.buf.f.sub[i] >= tau_k) {
@@ -759,7 +798,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
             ns = nk;  // sub holds bin bk sorted: its first nk entries are >= tau_k
         } else {
             if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bp, -INFINITY)) return false;
-            ns = L.n_sub;
+            ns = uniform(L.n_sub);
         }
         Walk w = walk_sub(L, ns, m, a, bp, sp.mass_ex, target);
         if (!w.found) return false;
@@ -773,9 +812,15 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
             for (int tier = 0; tier < 2; ++tier) {
                 const bool acc64 = tier == 1;
                 double acc = 0.0;
-                for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
-                    if (v < x_lo) acc += weight_of(v, m, a.c64, acc64);
-                });
+                // x < x_lo lies at least lim / 16 >= 8 octaves down.
+                if (acc64)
+                    for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
+                        if (v < x_lo) acc += tail_weight(v, m, a.c64, true);
+                    });
+                else
+                    for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
+                        if (v < x_lo) acc += tail_weight(v, m, a.c64, false);
+                    });
                 const double rest = sel_sum_f64(acc, L);
                 const double mass1b = sc.mass_total + rest;
                 const double target_b = a.top_p * mass1b;
@@ -784,7 +829,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
                 if (sq.bin != in_sub) {
                     if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, sq.bin, -INFINITY))
                         return false;
-                    ns = L.n_sub;
+                    ns = uniform(L.n_sub);
                     in_sub = sq.bin;
                 }
                 w = walk_sub(L, ns, m, a, sq.bin, sq.mass_ex, target_b);
@@ -808,7 +853,8 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
         const BinScan st = scan_find(L, bt, true, ~0ull, 0.0);
         if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bt, tau)) return false;
         unsigned long long q = 0;
-        for (int i = threadIdx.x; i < L.n_sub; i += kSelThreads)
+        const int nb_sub = uniform(L.n_sub);
+        for (int i = threadIdx.x; i < nb_sub; i += kSelThreads)
             q += qweight(L.buf.f.sub[i], m, a.c64, bt, true);
         s = st.mass_total + (double)sel_sum_u64(q, L) * unit_of(bt);
     }
@@ -825,6 +871,7 @@ template <typename T, bool VEC>
 __device__ __attribute__((always_inline)) float general_thresholds(const T* x, const FilterArgs& a, float m, float tau_m,
                                     SelLds& L) {
     float tau_k = -INFINITY, tau_p = -INFINITY;
+    __syncthreads();  // the fast path's last reads of the bins are done
     if (a.top_k > 0 && a.top_k < a.V) {
         for (int i = threadIdx.x; i < kBins; i += kSelThreads) L.cnt[i] = 0;
         __syncthreads();
