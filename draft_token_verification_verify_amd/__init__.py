@@ -16,7 +16,8 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_TREE, SpecVerifyError)
+from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_STOCHASTIC_FILTERED, MODE_TREE,
+                   SpecVerifyError)
 
 __all__ = [
     "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
@@ -24,7 +25,7 @@ __all__ = [
     "spec_verify_tree", "spec_verify_tree_stochastic", "spec_verify_gather_rows",
     "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
-    "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE",
+    "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE", "MODE_STOCHASTIC_FILTERED",
 ]
 
 
@@ -139,7 +140,11 @@ def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, unifo
     for name, t in (("p_at_draft", p_at_draft), ("q_at_draft", q_at_draft)):
         if t is not None:
             _dev(t, name, device, torch.float32, (B, k))
+    filtered = fn == "spec_verify_stochastic_filtered"
     nbytes = spec_verify_workspace_bytes(MODE_STOCHASTIC, B, k + 1, V, dt)
+    if filtered and (workspace is None or isinstance(workspace, Workspace)):
+        # room for the filter candidates (a caller's own tensor may be either size)
+        nbytes = spec_verify_workspace_bytes(MODE_STOCHASTIC_FILTERED, B, k + 1, V, dt)
     ws = _workspace(workspace, nbytes, device)
     lib = _lib.load()
     head = (_ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens))

@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(HERE, "libspec_verify.so")
 
 # Stable enums, same values as include/spec_verify.h.
 F32, BF16 = 0, 1
-MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE = 0, 1, 2
+MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE, MODE_STOCHASTIC_FILTERED = 0, 1, 2, 3
 OK, INVALID_ARGUMENT, UNSUPPORTED_DTYPE, WORKSPACE_TOO_SMALL, LIMIT_EXCEEDED, HIP_ERROR = range(6)
 SCHEDULE_AUTO, SCHEDULE_TWO_KERNELS, SCHEDULE_SELF_COMPUTE = 0, 1, 2
 

@@ -65,7 +65,7 @@ const char* spec_verify_status_string(int status) {
 
 size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype) {
     const int eb = elem_bytes_of(dtype);
-    if (eb == 0 || mode < 0 || mode > 2 || V > SPEC_VERIFY_MAX_VOCAB) return 0;
+    if (eb == 0 || mode < 0 || mode > 3 || V > SPEC_VERIFY_MAX_VOCAB) return 0;
     if (mode != 2 && rows_per_request - 1 > SPEC_VERIFY_MAX_K) return 0;
     if (mode == 2 && rows_per_request > SPEC_VERIFY_MAX_TREE_ROWS) return 0;
     sv::Geometry g;
@@ -118,6 +118,10 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     if ((long long)B * g.R * g.S > 0x7fffffffLL || (long long)B * g.S2 > 0x7fffffffLL)
         return SPEC_VERIFY_LIMIT_EXCEEDED;
     if (workspace_bytes < g.bytes) return SPEC_VERIFY_WORKSPACE_TOO_SMALL;
+    if (filter) {  // room for the filter candidates: the same layout plus their buffer
+        sv::Geometry g3;
+        if (sv::make_geometry(3, B, k + 1, V, eb, &g3) && workspace_bytes >= g3.bytes) g = g3;
+    }
 
     sv::StochasticCall c;
     c.target = target_logits;

@@ -53,8 +53,33 @@ struct Geometry {
     int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8
     int S2;          // stop-row chunks per request (stochastic sampler)
     int chunk2;      // elements per stop-row chunk
-    size_t off_tickets, off_partials, off_segs, off_rowf, bytes;
+    int cand_cap;    // filter candidate slots per row (mode 3), else 0: S segments of cand_seg
+    int cand_seg;    // slots per streaming chunk (a power of two)
+    size_t off_tickets, off_partials, off_segs, off_rowf, off_ccount, off_tails, off_cand, bytes;
 };
+
+// Sampling filters: weight bins of 1/16 octave below a row's maximum m,
+// bin = floor((m - x) * 16 log2(e) / T), the last bin taking everything 128
+// octaves down.  Monotone in x (a larger x never gets a larger bin), so every
+// bin is an interval of logits, and a smaller m never gives a larger bin.
+constexpr int kFilterBins = 2048;
+constexpr int kFilterBinsPerOctave = 16;
+// The filtered call's candidate gather keeps every logit of a row whose bin is
+// below kCandBins (16 octaves), in up to kCandCap slots per row.
+constexpr int kCandBins = 256;
+constexpr int kCandCap = 16384;
+constexpr int kCandMaxChunks = 256;  // rows of more streaming chunks keep no candidates
+
+// Bins per unit of logit, 16 log2(e) / T, rounded to fp32 once: one value for
+// every kernel that bins.
+inline float filter_bin_scale(float temperature) {
+    return (float)(1.4426950408889634074 / (double)temperature * kFilterBinsPerOctave);
+}
+
+__host__ __device__ inline int filter_bin_of(float x, float m, float bin_scale) {
+    const float t = fmaxf((m - x) * bin_scale, 0.f);
+    return t < (float)(kFilterBins - 1) ? (int)t : kFilterBins - 1;
+}
 
 // log2(e) / temperature, the factor that turns a logit difference into a
 // base-2 exponent.  The fp32 pair (hi, lo) carries it to ~2^-48 relative, so an
@@ -67,12 +92,16 @@ struct Scale {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// mode: 0 stochastic, 1 greedy, 2 tree; rows_per_request: k+1 or N+1.
+// mode: 0 stochastic, 1 greedy, 2 tree, 3 stochastic with filter candidates
+// (mode 0's layout plus a candidate buffer at the end); rows_per_request: k+1
+// or N+1.
 inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem_bytes,
                           Geometry* g) {
     if (B < 1 || rows_per_request < 1 || V < 1 || (elem_bytes != 2 && elem_bytes != 4))
         return false;
     const int epv = 16 / elem_bytes;  // elements per 16-byte vector
+    bool cand = mode == 3;
+    if (cand) mode = 0;
     g->R = (mode == 0) ? 2 * rows_per_request - 1 : rows_per_request;
     const long long rows = (long long)B * g->R;
     // Largest per-thread vector count whose tile count still fills the chip
@@ -108,6 +137,21 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
                              kThreads, 256);
     g->off_rowf = off;  // per-row sampling filter of the filtered call (stochastic only)
     off = align_up(off + (mode == 0 ? 16 * (size_t)rows : 0), 256);
+    // Candidates: per row up to kCandCap slots (fewer for a short vocabulary),
+    // split into one power-of-two segment per streaming chunk.
+    cand = cand && g->S <= kCandMaxChunks;
+    const long long vpad = ((long long)V + 63) / 64 * 64;
+    const long long per_row = vpad < kCandCap ? vpad : kCandCap;
+    int seg = 1;
+    while ((long long)seg * 2 * g->S <= per_row) seg *= 2;
+    g->cand_seg = cand ? seg : 0;
+    g->cand_cap = cand ? seg * g->S : 0;
+    g->off_ccount = off;  // candidates found per chunk
+    off = align_up(off + (cand ? sizeof(uint32_t) * (size_t)rows * (size_t)g->S : 0), 256);
+    g->off_tails = off;   // mass of the other logits per chunk
+    off = align_up(off + (cand ? sizeof(double) * (size_t)rows * (size_t)g->S : 0), 256);
+    g->off_cand = off;    // candidate logits, cand_cap per row
+    off = align_up(off + sizeof(float) * (size_t)rows * (size_t)g->cand_cap, 256);
     g->bytes = off;
     return true;
 }

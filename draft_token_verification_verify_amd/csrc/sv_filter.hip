@@ -15,6 +15,11 @@
 // applied in that order.  A row keeps the tokens with x >= tau, tau the largest
 // of the three thresholds, and its kept mass is renormalised.
 //
+// With a workspace sized for it and top-k or top-p on, a gather kernel first
+// collects, in one parallel pass after the statistics, every logit less than
+// 16 octaves of weight below its row's maximum and (top-p alone) the fp64 mass
+// of the others; the selection below then reads those instead of its row.
+//
 // One workgroup of 1024 threads per logits row:
 //   1. The row maximum m, from the streaming kernel's statistics partials.
 //   2. With top-k or top-p on: a histogram of the row over bins of 1/16 octave
@@ -42,8 +47,8 @@ namespace sv {
 
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kBins = 2048;          // weight bins, 1/16 octave each
-constexpr int kBinsPerOctave = 16;
+constexpr int kBins = kFilterBins;   // weight bins, 1/16 octave each
+constexpr int kBinsPerOctave = kFilterBinsPerOctave;
 constexpr int kDigitBits = 8;        // radix digit of the narrowing passes
 constexpr int kDigits = 1 << kDigitBits;
 constexpr int kCand = 12288;         // LDS logit buffer
@@ -54,6 +59,7 @@ constexpr int kSub = kCand - kTop;   // fast path: one weight bin of it, to be s
 static_assert((kSortCap & (kSortCap - 1)) == 0 && kSortCap <= kCand, "sorted buffer");
 static_assert((kSub & (kSub - 1)) == 0, "sorted sub-buffer");
 constexpr int kFirstLim = 128;       // fast path: first gather reaches 8 octaves down
+static_assert(kCandMaxChunks <= kBins, "tail masses are staged in the bin arrays");
 constexpr int kMassBits = 41;       // fixed-point mass: 2^41 units per octave-top weight
 constexpr double kCertify = 1e-6;    // top-p margin (relative) the fast weights may decide
 // Relative error bound of a row's mass from the streaming statistics (fp32
@@ -75,6 +81,10 @@ struct FilterArgs {
     double top_p, min_p;
     const Partial16* partials;  // [B, R, S] statistics partials (f0 = chunk max)
     RowFilter* rowf;            // [B, R] output
+    float* cand;                // [B, R, S, seg] candidates of the gather kernel, or null
+    uint32_t* ccount;           // [B, R, S] candidates found per chunk
+    double* tails;              // [B, R, S] mass of the other logits, per chunk (top-p alone)
+    int seg;                    // slots per chunk (a power of two)
 };
 
 template <typename T>
@@ -107,8 +117,7 @@ __device__ inline float value_of_key(uint32_t key) {
 // Weight bin of x below the row maximum m: monotone (a larger x never gets a
 // larger bin), so every bin is an interval of logits.
 __device__ inline int bin_of(float x, float m, float bin_scale) {
-    const float t = fmaxf((m - x) * bin_scale, 0.f);
-    return t < (float)(kBins - 1) ? (int)t : kBins - 1;
+    return filter_bin_of(x, m, bin_scale);
 }
 
 // The smallest logit whose bin is below lim (bins are monotone in x, so
@@ -118,6 +127,20 @@ __device__ inline float lowest_in_bins(int lim, float m, float bin_scale) {
     if (lim >= kBins) return -INFINITY;
     if (lim <= 0) return INFINITY;
     uint32_t lo = key_of<float>(-INFINITY), hi = key_of<float>(m);
+    auto below = [&](uint32_t q) { return bin_of(value_of_key<float>(q), m, bin_scale) < lim; };
+    // First single steps over the keys from m - lim / bin_scale, which lands
+    // within a few keys of the answer (the answer is unique, so the steps and
+    // the search agree); the binary search when they do not get there.
+    const float guess = m - (float)lim / bin_scale;
+    uint32_t q = guess >= -INFINITY ? min(max(key_of<float>(guess), lo), hi) : lo;
+    for (int step = 0; step < 16; ++step) {
+        if (!below(q)) {
+            ++q;  // q < hi: below(hi) holds
+        } else {
+            if (q == lo || !below(q - 1)) return value_of_key<float>(q);
+            --q;
+        }
+    }
     while (lo < hi) {
         const uint32_t mid = lo + (hi - lo) / 2;
         if (bin_of(value_of_key<float>(mid), m, bin_scale) < lim) hi = mid;
@@ -200,6 +223,134 @@ __device__ inline void for_each_logit(const T* row, int V, F&& f) {
 }
 
 // ---------------------------------------------------------------------------
+// Candidate gather (when the workspace has room for it): one 256-thread
+// workgroup per statistics chunk, after the statistics, so every chunk knows
+// its row's maximum m.  The logits of the chunk whose bin is below kCandBins
+// go to the row's candidate buffer (one atomic per workgroup claims their
+// slots; a row whose candidates outgrow the buffer keeps counting, and its
+// filter then reads the row itself); the weights of the others are summed into
+// the chunk's tail mass.  The selection then reads a few thousand candidates
+// per row instead of the row, and has the mass below its first gather without
+// another pass.
+// ---------------------------------------------------------------------------
+struct CandArgs {
+    const void* target;
+    const void* draft;
+    int k, V, R;
+    int S, chunk;       // streaming chunks per row, elements per chunk
+    double c64;
+    float bin_scale;
+    const Partial16* partials;
+    float* cand;        // [B, R, S, seg]: one segment per chunk
+    uint32_t* ccount;   // [B, R, S]: candidates found per chunk (may exceed seg)
+    double* tails;      // [B, R, S]: mass of the other logits per chunk
+    int seg;
+};
+
+// 2^a in fp64 for a in [-1100, 0]: 2^n 2^(j/64) 2^r with n = floor(a), j the
+// next six bits, r in [0, 1/64); 2^(j/64) from `tab` (64 entries, each the
+// library's fp64 exponential), 2^r by its Taylor polynomial to degree 5
+// (truncation below (ln2 / 64)^6 / 720 < 2e-15 relative).  Within a few fp64
+// ulp; about a third of the library call's instructions.
+__device__ inline double exp2_tab64(double a, const double* tab) {
+    const double n = floor(a);
+    const double t = (a - n) * 64.0;  // exact: a - n in [0, 1), times a power of two
+    const double jd = floor(t);
+    const double r = (t - jd) * (1.0 / 64.0);
+    const double l = 0.69314718055994530942;
+    double p = l * l * l * l * l / 120.0;
+    p = fma(p, r, l * l * l * l / 24.0);
+    p = fma(p, r, l * l * l / 6.0);
+    p = fma(p, r, l * l / 2.0);
+    p = fma(p, r, l);
+    p = fma(p, r, 1.0);
+    return ldexp(tab[(int)jd] * p, (int)n);
+}
+
+// TAIL: also sum the chunk's tail mass, with fp64 weights (the selection uses
+// it for top-p without top-k only, and then decides against it as against the
+// whole row's mass).
+template <typename T, int U, bool TAIL>
+__global__ __launch_bounds__(kThreads) void cand_kernel(CandArgs a) {
+    constexpr int EPV = Elem<T>::kPerVec;
+    __shared__ float red_f[kWaves];
+    __shared__ double red_d[kWaves];
+    __shared__ int wsum[kWaves];
+    __shared__ double tab[64];
+    if (TAIL && threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    const int t = blockIdx.x, ch = t % a.S, row = t / a.S;
+    const int b = row / a.R, r = row % a.R;
+    // The tile's loads go out first; the row maximum and the floor are worked
+    // out while they are in flight.
+    const T* rowp = (r <= a.k)
+        ? static_cast<const T*>(a.target) + ((size_t)b * (a.k + 1) + r) * (size_t)a.V
+        : static_cast<const T*>(a.draft) + ((size_t)b * a.k + (r - a.k - 1)) * (size_t)a.V;
+    const int lo = ch * a.chunk, hi = min(a.V, lo + a.chunk);
+    const int nvec = (hi - lo) / EPV;
+    const uint4* base = reinterpret_cast<const uint4*>(rowp + lo);
+    uint4 raw[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
+    float mloc = -INFINITY;
+    for (int i = threadIdx.x; i < a.S; i += kThreads)
+        mloc = fmaxf(mloc, read_partial(a.partials + (size_t)row * a.S + i).f0);
+    const float m = block_max(mloc, red_f);
+    if (m == -INFINITY) return;  // nothing to keep; the tail stays 0
+    const float x_lo = lowest_in_bins(kCandBins, m, a.bin_scale);
+    int n = 0;
+    double tail = 0.0;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        float x[EPV];
+        Elem<T>::widen(raw[j], x);
+        const bool ok = (int)threadIdx.x + j * kThreads < nvec;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const bool c = ok && x[e] >= x_lo;
+            n += c ? 1 : 0;
+            if (TAIL && ok && !c && x[e] != -INFINITY) {
+                const double w = ((double)x[e] - (double)m) * a.c64;
+                if (w > -1100.0) tail += exp2_tab64(w, tab);
+            }
+        }
+    }
+    if (TAIL) {
+        const double tsum = block_sum(tail, red_d);
+        if (threadIdx.x == 0 && tsum != 0.0) a.tails[t] = tsum;
+    }
+    // Exclusive prefix of the candidate counts over the workgroup; the slots.
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, total = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        before += w < wave ? wsum[w] : 0;
+        total += wsum[w];
+    }
+    if (total == 0) return;  // the same on every thread
+    if (threadIdx.x == 0) a.ccount[t] = (uint32_t)total;
+    if (total > a.seg) return;  // overflow: the row's filter reads the row itself
+    int pos = before + incl - n;
+    float* dst = a.cand + (size_t)t * a.seg;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        float x[EPV];
+        Elem<T>::widen(raw[j], x);
+        const bool ok = (int)threadIdx.x + j * kThreads < nvec;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e)
+            if (ok && x[e] >= x_lo) dst[pos++] = x[e];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Workgroup-wide steps (1024 threads).
 // ---------------------------------------------------------------------------
 struct SelLds {
@@ -218,6 +369,7 @@ struct SelLds {
         } f;
     } buf;
     double bscan[6];
+    uint32_t tcnt[kCandMaxChunks];    // candidates per chunk of this row
     int n_sub;
     unsigned long long red_u[kSelWaves];
     double red_d[kSelWaves];
@@ -718,7 +870,8 @@ __device__ inline Walk walk_sub(SelLds& L, int ns, float m, const FilterArgs& a,
 // decided nothing, when the set outgrows LDS or a decision is left open.
 template <typename T, bool VEC>
 __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const FilterArgs& a, float m, double s_row, float tau_m,
-                            float* tau_out, double* s_out, SelLds& L) {
+                            const float* cand, double rest_cand, float* tau_out,
+                            double* s_out, SelLds& L) {
     const bool topk = a.top_k > 0 && a.top_k < a.V;
     const bool topp = a.top_p < 1.0;
     for (int i = threadIdx.x; i < kBins; i += kSelThreads) {
@@ -731,22 +884,42 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
     int lim_prev = 0, lim = (topp && !topk) ? 2 * kFirstLim : kFirstLim;
     bool complete = true;  // top[] holds every logit of the bins below lim
     BinScan sc;
+    int n_have = 0;  // entries of top[] already counted (read after a barrier, never during a pass)
     for (;;) {
-        const int n0 = min(uniform(L.n_gathered), kTop);
+        const int n0 = n_have;
         // bins [lim_prev, lim) are the logits in [x_lo, x_hi)
         const float x_lo = lowest_in_bins(lim, m, a.bin_scale);
         const float x_hi = lowest_in_bins(lim_prev, m, a.bin_scale);
-        for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
-            const int i = wave_append(v >= x_lo && v < x_hi, v, L.buf.f.top, kTop, &L.n_gathered);
+        auto put = [&](bool take, float v) {
+            const int i = wave_append(take, v, L.buf.f.top, kTop, &L.n_gathered);
             if (i >= kTop) {  // no room: count and weigh it here
                 const int bn = bin_of(v, m, a.bin_scale);
                 atomicAdd(&L.cnt[bn], 1u);
                 atomicAdd(&L.mass.q[bn], qweight(v, m, a.c64, bn, true));
             }
-        });
+        };
+        if (cand && lim <= kCandBins) {
+            // Every logit of bins < kCandBins is among the row's candidates:
+            // chunk c's in slots [c seg, c seg + tcnt[c]).
+            const int nslots = a.S * a.seg;
+            for (int i0 = 0; i0 < nslots; i0 += 4 * kSelThreads) {
+                float v[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = i0 + j * kSelThreads + (int)threadIdx.x;
+                    const bool ok = i < nslots && (uint32_t)(i & (a.seg - 1)) < L.tcnt[i / a.seg];
+                    v[j] = ok ? cand[i] : -INFINITY;
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) put(v[j] >= x_lo && v[j] < x_hi, v[j]);
+            }
+        } else {
+            for_each_logit<T, VEC, 4>(x, a.V, [&](float v) { put(v >= x_lo && v < x_hi, v); });
+        }
         __syncthreads();
         const int ngat = uniform(L.n_gathered);
         const int n1 = min(ngat, kTop);
+        n_have = n1;
         complete = complete && ngat <= kTop;
         __syncthreads();
         // Counts and fp64 masses of the newly gathered logits, from LDS.
@@ -785,8 +958,16 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
         s_k = sc.mass_ex + (double)sel_sum_u64(q, L) * unit_of(bk);
     }
     if (topp) {
-        const double mass1 = topk ? s_k : whole_row ? sc.mass_total : s_row;
-        const bool exact = topk || whole_row;
+        // With the gather kernel's candidates (and top-k off), the first
+        // gather reaches exactly kCandBins bins down and the mass of the rest
+        // of the row comes with them, from fp64 weights: the row's mass is
+        // then known as well as from a whole-row gather.
+        const bool with_tail = !topk && cand && lim == kCandBins;
+        const double mass1 = topk        ? s_k
+                             : whole_row ? sc.mass_total
+                             : with_tail ? sc.mass_total + rest_cand
+                                         : s_row;
+        const bool exact = topk || whole_row || with_tail;
         const double target = a.top_p * mass1;
         // Bins before bk lie wholly in the top-k set; bin bk's part >= tau_k
         // holds the rest of its mass, which reaches the target.
@@ -929,6 +1110,23 @@ __global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
     __shared__ SelLds L;
     const int row = blockIdx.x, b = row / a.R, r = row % a.R;
     const T* x = filter_row<T>(a, b, r);
+    // The gather kernel's candidates of this row (per-chunk counts staged in
+    // LDS), usable when every chunk's fit its segment, and the mass of the
+    // rest of the row (fixed order).
+    float* cand = a.cand ? a.cand + (size_t)row * a.S * a.seg : nullptr;
+    int over = 0;
+    if (cand)
+        for (int ch = threadIdx.x; ch < a.S; ch += kSelThreads) {
+            const uint32_t c = a.ccount[(size_t)row * a.S + ch];
+            L.tcnt[ch] = c;
+            L.mass.cum[ch] = a.tails[(size_t)row * a.S + ch];  // free until the selection
+            over |= c > (uint32_t)a.seg;
+        }
+    over = __syncthreads_or(over);
+    const float* usable = (cand && !over) ? cand : nullptr;
+    double rest_cand = 0.0;
+    if (cand)
+        for (int ch = 0; ch < a.S; ++ch) rest_cand += L.mass.cum[ch];
 
     float mloc = -INFINITY;
     for (int ch = threadIdx.x; ch < a.S; ch += kSelThreads)
@@ -953,7 +1151,7 @@ __global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
                 if (q.f0 != -INFINITY) sp += q.d * exp2_f64(((double)q.f0 - (double)m) * a.c64);
             }
             const double s_row = sel_sum_f64(sp, L);
-            decided = fast_filter<T, VEC>(x, a, m, s_row, tau_m, &tau, &s, L);
+            decided = fast_filter<T, VEC>(x, a, m, s_row, tau_m, usable, rest_cand, &tau, &s, L);
         }
         if (!decided) {
             tau = general_thresholds<T, VEC>(x, a, m, tau_m, L);
@@ -971,6 +1169,18 @@ __global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
         f.s = s;
         a.rowf[row] = f;
     }
+    if (cand) {  // leave the workspace zero: the candidates written, the counts, the tails
+        __syncthreads();
+        const int nslots = a.S * a.seg;
+        for (int i = threadIdx.x; i < nslots; i += kSelThreads) {
+            const uint32_t c = L.tcnt[i / a.seg];
+            if (c <= (uint32_t)a.seg && (uint32_t)(i & (a.seg - 1)) < c) cand[i] = 0.f;
+        }
+        for (int ch = threadIdx.x; ch < a.S; ch += kSelThreads) {
+            a.tails[(size_t)row * a.S + ch] = 0.0;
+            a.ccount[(size_t)row * a.S + ch] = 0u;
+        }
+    }
 }
 
 template <typename T, bool VEC>
@@ -978,6 +1188,17 @@ static hipError_t launch_filter(const FilterArgs& a, hipStream_t st, const Kerne
     // The events (when set) take the kernel's own start and end timestamps.
     hipExtLaunchKernelGGL(filter_kernel<T, VEC>, dim3((unsigned)(a.B * a.R)), dim3(kSelThreads),
                           0, st, ev.begin, ev.end, 0, a);
+    return hipGetLastError();
+}
+
+template <typename T, bool TAIL>
+static hipError_t launch_cand(const CandArgs& c, int U, unsigned n_tiles, hipStream_t st) {
+    switch (U) {
+        case 8: cand_kernel<T, 8, TAIL><<<n_tiles, kThreads, 0, st>>>(c); break;
+        case 4: cand_kernel<T, 4, TAIL><<<n_tiles, kThreads, 0, st>>>(c); break;
+        case 2: cand_kernel<T, 2, TAIL><<<n_tiles, kThreads, 0, st>>>(c); break;
+        default: cand_kernel<T, 1, TAIL><<<n_tiles, kThreads, 0, st>>>(c); break;
+    }
     return hipGetLastError();
 }
 
@@ -993,13 +1214,50 @@ hipError_t run_filter(const StochasticCall& call, const FilterCall& f, const Geo
     a.R = g.R;
     a.S = g.S;
     a.c64 = 1.4426950408889634074 / (double)call.temperature;
-    a.bin_scale = (float)(a.c64 * kBinsPerOctave);
+    a.bin_scale = filter_bin_scale(call.temperature);
     a.temperature = (double)call.temperature;
     a.top_k = f.top_k;
     a.top_p = (double)f.top_p;
     a.min_p = (double)f.min_p;
     a.partials = reinterpret_cast<const Partial16*>(ws + g.off_partials);
     a.rowf = reinterpret_cast<RowFilter*>(ws + g.off_rowf);
+    // Candidates when the workspace has room (mode 3 layout), the rows are
+    // 16-byte aligned and top-k or top-p is on (min-p alone needs one pass over
+    // each row for its kept mass either way).
+    const bool topk_on = f.top_k > 0 && f.top_k < call.V, topp_on = f.top_p < 1.0f;
+    const bool cand = g.cand_seg > 0 && call.vec && (topk_on || topp_on);
+    a.cand = cand ? reinterpret_cast<float*>(ws + g.off_cand) : nullptr;
+    a.ccount = cand ? reinterpret_cast<uint32_t*>(ws + g.off_ccount) : nullptr;
+    a.tails = cand ? reinterpret_cast<double*>(ws + g.off_tails) : nullptr;
+    a.seg = cand ? g.cand_seg : 0;
+    if (cand) {
+        CandArgs c;
+        c.target = call.target;
+        c.draft = call.draft;
+        c.k = call.k;
+        c.V = call.V;
+        c.R = g.R;
+        c.S = g.S;
+        c.chunk = g.chunk;
+        c.c64 = a.c64;
+        c.bin_scale = a.bin_scale;
+        c.partials = a.partials;
+        c.cand = a.cand;
+        c.ccount = a.ccount;
+        c.tails = a.tails;
+        c.seg = a.seg;
+        const unsigned n_tiles = (unsigned)((long long)call.B * g.R * g.S);
+        // The tail masses serve top-p without top-k only (its first gather
+        // reaches exactly kCandBins bins down).
+        const bool tail = topp_on && !topk_on;
+        const hipError_t e =
+            call.dtype == 1
+                ? (tail ? launch_cand<bf16_t, true>(c, g.U, n_tiles, st)
+                        : launch_cand<bf16_t, false>(c, g.U, n_tiles, st))
+                : (tail ? launch_cand<float, true>(c, g.U, n_tiles, st)
+                        : launch_cand<float, false>(c, g.U, n_tiles, st));
+        if (e != hipSuccess) return e;
+    }
     if (call.dtype == 1)
         return call.vec ? launch_filter<bf16_t, true>(a, st, ev)
                         : launch_filter<bf16_t, false>(a, st, ev);

@@ -54,7 +54,15 @@ enum spec_verify_dtype {
 enum spec_verify_mode {
     SPEC_VERIFY_MODE_STOCHASTIC = 0,
     SPEC_VERIFY_MODE_GREEDY = 1,
-    SPEC_VERIFY_MODE_TREE = 2
+    SPEC_VERIFY_MODE_TREE = 2,
+    /* Sizing only: the stochastic workspace plus a buffer in which the
+     * filtered call (with top-k or top-p on) collects, per logits row, the
+     * logits within 16 octaves of weight of the row's maximum (up to 16384
+     * slots of 4 bytes per row) and the mass of the others, in one parallel
+     * pass, so that its per-row selection reads those instead of the row.
+     * spec_verify_stochastic_filtered accepts a workspace of either size and
+     * gives the same bits with both; this one is faster. */
+    SPEC_VERIFY_MODE_STOCHASTIC_FILTERED = 3
 };
 
 enum spec_verify_status {

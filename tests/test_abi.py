@@ -51,7 +51,17 @@ def test_workspace_sizing(lib):
     assert ws(_lib.MODE_GREEDY, 8, 5, 32000, _lib.BF16) > 0
     assert ws(_lib.MODE_TREE, 32, 61, 128256, _lib.BF16) > 0
     assert ws(_lib.MODE_STOCHASTIC, 1, 1, 1, _lib.F32) > 0  # k = 0, V = 1
-    assert ws(3, 1, 2, 10, _lib.F32) == 0           # unknown mode
+    assert ws(4, 1, 2, 10, _lib.F32) == 0           # unknown mode
+    # the filtered call's size: the stochastic one plus, per logits row
+    # (B (2k + 1) rows), 16384 candidate slots of 4 bytes and, per 16384-element
+    # chunk (8 at V = 128256), a count and an fp64 tail mass; fewer slots for a
+    # short vocabulary
+    base = ws(_lib.MODE_STOCHASTIC, 64, 4, 128256, _lib.BF16)
+    filt = ws(_lib.MODE_STOCHASTIC_FILTERED, 64, 4, 128256, _lib.BF16)
+    per_row = 16384 * 4 + 8 * (4 + 8)
+    assert base + 64 * 7 * per_row <= filt <= base + 64 * 7 * per_row + 1024
+    small = ws(_lib.MODE_STOCHASTIC_FILTERED, 2, 3, 100, _lib.F32)
+    assert ws(_lib.MODE_STOCHASTIC, 2, 3, 100, _lib.F32) + 2 * 5 * 128 * 4 <= small
     assert ws(_lib.MODE_STOCHASTIC, 1, 2, 10, 7) == 0  # unknown dtype
     assert ws(_lib.MODE_STOCHASTIC, 0, 2, 10, _lib.F32) == 0
     assert ws(_lib.MODE_STOCHASTIC, 1, 66, 10, _lib.F32) == 0  # k = 65

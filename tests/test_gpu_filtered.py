@@ -172,14 +172,49 @@ def test_masked_tokens_and_top_k_beyond_the_finite_ones():
         check(case, top_k, top_p, min_p, f"masked-k{top_k}")
 
 
-def test_workspace_is_zero_after_filtered_calls():
+@pytest.mark.parametrize("mode", [_lib.MODE_STOCHASTIC, _lib.MODE_STOCHASTIC_FILTERED])
+def test_workspace_is_zero_after_filtered_calls(mode):
     case = wl.gaussian_stochastic(5, 8, 3, 6000, "bf16", target_sd=2.0, draft_noise_sd=1.0)
     dev = torch.device("cuda", 0)
-    ws = torch.zeros(sv.spec_verify_workspace_bytes(0, case.B, case.k + 1, case.V, _lib.BF16),
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(mode, case.B, case.k + 1, case.V, _lib.BF16),
                      dtype=torch.uint8, device=dev)
-    for top_k, top_p, min_p in ((5, 1.0, 0.0), (0, 0.9, 0.05), (30, 0.7, 0.0)):
+    for top_k, top_p, min_p in ((5, 1.0, 0.0), (0, 0.9, 0.05), (30, 0.7, 0.0), (0, 1.0, 0.1)):
         run_filtered(case, top_k, top_p, min_p, workspace=ws)
         assert int(torch.count_nonzero(ws)) == 0
+
+
+def _workspace(case, mode):
+    dt = _lib.BF16 if case.dtype == "bf16" else _lib.F32
+    return torch.zeros(sv.spec_verify_workspace_bytes(mode, case.B, case.k + 1, case.V, dt),
+                       dtype=torch.uint8, device=torch.device("cuda", 0))
+
+
+@pytest.mark.parametrize("sname,make", SHAPES, ids=[s[0] for s in SHAPES])
+def test_candidates_and_row_passes_give_the_same_bits(sname, make):
+    """A workspace with room for the statistics' candidates and one without
+    (the filter then reads every row itself) give identical outputs: the
+    thresholds and kept masses come from order-free fixed-point sums."""
+    case = make(4)
+    small, large = _workspace(case, _lib.MODE_STOCHASTIC), _workspace(
+        case, _lib.MODE_STOCHASTIC_FILTERED)
+    for _, top_k, top_p, min_p in FILTERS:
+        a = run_filtered(case, top_k, top_p, min_p, workspace=small)
+        b = run_filtered(case, top_k, top_p, min_p, workspace=large)
+        for key in a:
+            np.testing.assert_array_equal(a[key], b[key], err_msg=f"{key} {top_k} {top_p} {min_p}")
+
+
+def test_row_passes_parity():
+    """The filter that reads every row (workspace without candidate room)
+    against the oracle."""
+    case = wl.c3(6, B=6)
+    ws = _workspace(case, _lib.MODE_STOCHASTIC)
+    for _, top_k, top_p, min_p in FILTERS:
+        gpu = run_filtered(case, top_k, top_p, min_p, workspace=ws)
+        ref = oracle_filtered(case, top_k, top_p, min_p)
+        exact = min_p == 1.0 and top_p == 1.0 and not 0 < top_k < case.V
+        H.compare_stochastic(gpu, ref, label=f"rows/{top_k}/{top_p}/{min_p}",
+                             filter_band=None if exact else FILTER_GUARD)
 
 
 def test_repeat_calls_are_bit_identical():
