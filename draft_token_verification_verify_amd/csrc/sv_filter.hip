@@ -253,10 +253,10 @@ struct CandArgs {
 // (truncation below (ln2 / 64)^6 / 720 < 2e-15 relative).  Within a few fp64
 // ulp; about a third of the library call's instructions.
 __device__ inline double exp2_tab64(double a, const double* tab) {
-    const double n = floor(a);
-    const double t = (a - n) * 64.0;  // exact: a - n in [0, 1), times a power of two
-    const double jd = floor(t);
-    const double r = (t - jd) * (1.0 / 64.0);
+    const double t = a * 64.0;         // exact (a power of two)
+    const double kd = floor(t);
+    const int k = (int)kd;             // a in [-1100, 0]: k fits easily
+    const double r = (t - kd) * (1.0 / 64.0);  // exact, in [0, 1/64)
     const double l = 0.69314718055994530942;
     double p = l * l * l * l * l / 120.0;
     p = fma(p, r, l * l * l * l / 24.0);
@@ -264,7 +264,7 @@ __device__ inline double exp2_tab64(double a, const double* tab) {
     p = fma(p, r, l * l / 2.0);
     p = fma(p, r, l);
     p = fma(p, r, 1.0);
-    return ldexp(tab[(int)jd] * p, (int)n);
+    return ldexp(tab[k & 63] * p, k >> 6);  // k = 64 n + j, j in [0, 64)
 }
 
 // TAIL: also sum the chunk's tail mass, with fp64 weights (the selection uses
