@@ -60,6 +60,7 @@ static_assert((kSortCap & (kSortCap - 1)) == 0 && kSortCap <= kCand, "sorted buf
 static_assert((kSub & (kSub - 1)) == 0, "sorted sub-buffer");
 constexpr int kFirstLim = 128;       // fast path: first gather reaches 8 octaves down
 static_assert(kCandMaxChunks <= kBins, "tail masses are staged in the bin arrays");
+static_assert(kCandMaxChunks <= 4 * 64, "one wave turns the chunk counts into a prefix");
 constexpr int kMassBits = 41;       // fixed-point mass: 2^41 units per octave-top weight
 constexpr double kCertify = 1e-6;    // top-p margin (relative) the fast weights may decide
 // Relative error bound of a row's mass from the streaming statistics (fp32
@@ -159,6 +160,26 @@ __device__ inline double unit_of(int bin) { return ldexp(1.0, -(octave_of(bin) +
 // fp64 2^a, out of line: it sits on a rare branch of the per-logit loops.
 __device__ __noinline__ double exp2_f64(double a) { return exp2(a); }
 
+// 2^a in fp64 for a in [-1100, 0]: 2^n 2^(j/64) 2^r with n = floor(a), j the
+// next six bits, r in [0, 1/64); 2^(j/64) from `tab` (64 entries, each the
+// library's fp64 exponential), 2^r by its Taylor polynomial to degree 5
+// (truncation below (ln2 / 64)^6 / 720 < 2e-15 relative).  Within a few fp64
+// ulp; about a third of the library call's instructions.
+__device__ inline double exp2_tab64(double a, const double* tab) {
+    const double t = a * 64.0;         // exact (a power of two)
+    const double kd = floor(t);
+    const int k = (int)kd;             // a in [-1100, 0]: k fits easily
+    const double r = (t - kd) * (1.0 / 64.0);  // exact, in [0, 1/64)
+    const double l = 0.69314718055994530942;
+    double p = l * l * l * l * l / 120.0;
+    p = fma(p, r, l * l * l * l / 24.0);
+    p = fma(p, r, l * l * l / 6.0);
+    p = fma(p, r, l * l / 2.0);
+    p = fma(p, r, l);
+    p = fma(p, r, 1.0);
+    return ldexp(tab[k & 63] * p, k >> 6);  // k = 64 n + j, j in [0, 64)
+}
+
 // 2^((x - m) c) for x <= m, fp64.  Accurate (acc): the fp64 exponential for
 // every logit.  Otherwise the fp64 exponential above 2^-8 and below it 2^n
 // times the fp32 exponential of the fractional part, n = floor of the fp64
@@ -246,26 +267,6 @@ struct CandArgs {
     double* tails;      // [B, R, S]: mass of the other logits per chunk
     int seg;
 };
-
-// 2^a in fp64 for a in [-1100, 0]: 2^n 2^(j/64) 2^r with n = floor(a), j the
-// next six bits, r in [0, 1/64); 2^(j/64) from `tab` (64 entries, each the
-// library's fp64 exponential), 2^r by its Taylor polynomial to degree 5
-// (truncation below (ln2 / 64)^6 / 720 < 2e-15 relative).  Within a few fp64
-// ulp; about a third of the library call's instructions.
-__device__ inline double exp2_tab64(double a, const double* tab) {
-    const double t = a * 64.0;         // exact (a power of two)
-    const double kd = floor(t);
-    const int k = (int)kd;             // a in [-1100, 0]: k fits easily
-    const double r = (t - kd) * (1.0 / 64.0);  // exact, in [0, 1/64)
-    const double l = 0.69314718055994530942;
-    double p = l * l * l * l * l / 120.0;
-    p = fma(p, r, l * l * l * l / 24.0);
-    p = fma(p, r, l * l * l / 6.0);
-    p = fma(p, r, l * l / 2.0);
-    p = fma(p, r, l);
-    p = fma(p, r, 1.0);
-    return ldexp(tab[k & 63] * p, k >> 6);  // k = 64 n + j, j in [0, 64)
-}
 
 // TAIL: also sum the chunk's tail mass, with fp64 weights (the selection uses
 // it for top-p without top-k only, and then decides against it as against the
@@ -369,7 +370,7 @@ struct SelLds {
         } f;
     } buf;
     double bscan[6];
-    uint32_t tcnt[kCandMaxChunks];    // candidates per chunk of this row
+    uint32_t tcnt[kCandMaxChunks];    // candidates per chunk of this row, then their inclusive prefix
     int n_sub;
     unsigned long long red_u[kSelWaves];
     double red_d[kSelWaves];
@@ -614,6 +615,45 @@ __device__ inline BinScan scan_find(SelLds& L, int nb, bool by_count, unsigned l
 // Descending bitonic sort of cand[0, n), padded with -inf up to the next power
 // of two (which must fit in the buffer).
 __device__ inline void sort_desc(float* cand, int n) {
+    if (n <= 64) {
+        // One wave, in registers: bitonic network over lanes by shuffles
+        // (lane pairs i < j = i ^ stride keep the larger value at i in
+        // descending blocks, at j in ascending ones).
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            float v = lane < n ? cand[lane] : -INFINITY;
+#pragma unroll
+            for (int size = 2; size <= 64; size <<= 1)
+#pragma unroll
+                for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                    const float o = __shfl_xor(v, stride);
+                    const bool keep_max = ((lane & stride) == 0) == ((lane & size) == 0);
+                    v = keep_max ? fmaxf(v, o) : fminf(v, o);
+                }
+            if (lane < n) cand[lane] = v;
+        }
+        __syncthreads();
+        return;
+    }
+    if (n <= 512) {
+        // Rank sort: entry t goes to the number of entries above it, or equal
+        // to it at a smaller index (n broadcast LDS reads per thread, no
+        // network of barriers).
+        const int t = threadIdx.x;
+        float v = 0.f;
+        int rank = 0;
+        if (t < n) {
+            v = cand[t];
+            for (int j = 0; j < n; ++j) {
+                const float u = cand[j];
+                rank += (u > v || (u == v && j < t)) ? 1 : 0;
+            }
+        }
+        __syncthreads();
+        if (t < n) cand[rank] = v;
+        __syncthreads();
+        return;
+    }
     int npad = 2;
     while (npad < n) npad <<= 1;
     for (int i = n + threadIdx.x; i < npad; i += kSelThreads) cand[i] = -INFINITY;
@@ -775,12 +815,42 @@ __device__ __attribute__((always_inline)) SelectOut select_in_bin(const T* row, 
 // Fast path: the top of the row.
 // ---------------------------------------------------------------------------
 
+// Every candidate of the row (from the gather kernel): chunk c's in slots
+// [c seg, c seg + its count) of `cand`; candidate g (in chunk order) lies in
+// the first chunk whose inclusive count prefix L.tcnt exceeds g.  Four loads
+// per thread in flight.
+template <class F>
+__device__ inline void for_each_candidate(const float* cand, int S, int seg, const SelLds& L,
+                                          F&& f) {
+    const int total = (int)L.tcnt[S - 1];
+    for (int g0 = 0; g0 < total; g0 += 4 * kSelThreads) {
+        float v[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int g = g0 + j * kSelThreads + (int)threadIdx.x;
+            v[j] = -INFINITY;
+            if (g < total) {
+                int lo = 0, hi = S - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi) >> 1;
+                    if ((int)L.tcnt[mid] > g) hi = mid;
+                    else lo = mid + 1;
+                }
+                v[j] = cand[lo * seg + g - (lo ? (int)L.tcnt[lo - 1] : 0)];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f(v[j]);  // -inf for the slots past the end
+    }
+}
+
 // Copy the logits of weight bin `bin` that are >= floor_v from the gathered
 // top of the row into sub[] and sort them (descending).  False when the bin is
 // too large for sub[].
 template <typename T, bool VEC>
 __device__ inline bool gather_bin(SelLds& L, const T* x, bool complete, int ntop, float m,
-                                  const FilterArgs& a, int bin, float floor_v) {
+                                  const FilterArgs& a, int bin, float floor_v,
+                                  const float* cand) {
     const bool fits = L.cnt[bin] <= (uint32_t)kSub;
     __syncthreads();  // every wave has read the count before anyone may rewrite it
     if (!uniform((int)fits)) return false;
@@ -793,13 +863,13 @@ __device__ inline bool gather_bin(SelLds& L, const T* x, bool complete, int ntop
             wave_append(i < ntop && bin_of(v, m, a.bin_scale) == bin && v >= floor_v, v,
                         L.buf.f.sub, kSub, &L.n_sub);
         }
-    } else {  // top[] overflowed: one pass over the row for the bin's logits
+    } else {  // top[] overflowed: one pass over the candidates or the row for the bin's logits
         const float x_lo = lowest_in_bins(bin + 1, m, a.bin_scale);
         const float x_hi = lowest_in_bins(bin, m, a.bin_scale);
         const float lo = fmaxf(x_lo, floor_v);
-        for_each_logit<T, VEC, 4>(x, a.V, [&](float v) {
-            wave_append(v >= lo && v < x_hi, v, L.buf.f.sub, kSub, &L.n_sub);
-        });
+        auto take = [&](float v) { wave_append(v >= lo && v < x_hi, v, L.buf.f.sub, kSub, &L.n_sub); };
+        if (cand && bin < kCandBins) for_each_candidate(cand, a.S, a.seg, L, take);
+        else for_each_logit<T, VEC, 4>(x, a.V, take);
     }
     __syncthreads();
     sort_desc(L.buf.f.sub, uniform(L.n_sub));
@@ -819,6 +889,45 @@ __device__ inline Walk walk_sub(SelLds& L, int ns, float m, const FilterArgs& a,
                                 double base, double target) {
     const double unit = unit_of(bin);
     const float* v = L.buf.f.sub;
+    if (ns <= 64) {  // one wave: its scan replaces the workgroup's barriers
+        if (threadIdx.x < 64) {
+            const int lane = threadIdx.x;
+            const bool in = lane < ns;
+            const float x = in ? v[lane] : -INFINITY;
+            const float next = lane + 1 < ns ? v[lane + 1] : -INFINITY;
+            const unsigned long long q = in ? qweight(x, m, a.c64, bin, true) : 0ull;
+            const unsigned long long run = wave_inclusive_scan_u64(q);
+            const bool group_end = in && (lane == ns - 1 || next != x);
+            const unsigned long long hits =
+                __ballot(group_end && base + (double)run * unit >= target);
+            double found = 0.0, tau = -INFINITY, mass = 0.0, margin = 0.0;
+            if (hits) {
+                const int h = __ffsll((long long)hits) - 1;
+                const float th = __shfl(x, h);
+                const unsigned long long end = __shfl(run, h);
+                const unsigned long long eq = (unsigned long long)__popcll(__ballot(in && x == th));
+                const unsigned long long start = end - eq * qweight(th, m, a.c64, bin, true);
+                found = 1.0;
+                tau = th;
+                mass = base + (double)end * unit;
+                margin = fmin(mass - target, target - (base + (double)start * unit));
+            }
+            if (lane == 0) {
+                L.bscan[0] = found;
+                L.bscan[1] = tau;
+                L.bscan[2] = mass;
+                L.bscan[3] = margin;
+            }
+        }
+        __syncthreads();
+        Walk w;
+        w.found = uniform(L.bscan[0]) != 0.0;
+        w.tau = (float)uniform(L.bscan[1]);
+        w.mass = uniform(L.bscan[2]);
+        w.margin = uniform(L.bscan[3]);
+        __syncthreads();
+        return w;
+    }
     const int per = (ns + kSelThreads - 1) / kSelThreads;
     const int lo = threadIdx.x * per;
     unsigned long long own = 0;
@@ -899,20 +1008,8 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
             }
         };
         if (cand && lim <= kCandBins) {
-            // Every logit of bins < kCandBins is among the row's candidates:
-            // chunk c's in slots [c seg, c seg + tcnt[c]).
-            const int nslots = a.S * a.seg;
-            for (int i0 = 0; i0 < nslots; i0 += 4 * kSelThreads) {
-                float v[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = i0 + j * kSelThreads + (int)threadIdx.x;
-                    const bool ok = i < nslots && (uint32_t)(i & (a.seg - 1)) < L.tcnt[i / a.seg];
-                    v[j] = ok ? cand[i] : -INFINITY;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) put(v[j] >= x_lo && v[j] < x_hi, v[j]);
-            }
+            // every logit of bins < kCandBins is among the row's candidates
+            for_each_candidate(cand, a.S, a.seg, L, [&](float v) { put(v >= x_lo && v < x_hi, v); });
         } else {
             for_each_logit<T, VEC, 4>(x, a.V, [&](float v) { put(v >= x_lo && v < x_hi, v); });
         }
@@ -945,17 +1042,37 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
     if (topk) {
         bk = sc.bin;
         const int r = (int)(a.top_k - sc.cnt_ex);
-        if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bk, -INFINITY)) return false;
+        if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bk, -INFINITY, cand)) return false;
         const int ns = uniform(L.n_sub);
         tau_k = uniform(L.buf.f.sub[max(min(r, ns), 1) - 1]);
         unsigned long long c = 0, q = 0;
-        for (int i = threadIdx.x; i < ns; i += kSelThreads)
-            if (L.buf.f.sub[i] >= tau_k) {
-                ++c;
-                q += qweight(L.buf.f.sub[i], m, a.c64, bk, true);
+        if (ns <= 64) {  // one wave
+            if (threadIdx.x < 64) {
+                const float v = (int)threadIdx.x < ns ? L.buf.f.sub[threadIdx.x] : -INFINITY;
+                const bool keep = (int)threadIdx.x < ns && v >= tau_k;
+                const unsigned long long kept = __ballot(keep);
+                const unsigned long long qs =
+                    wave_inclusive_scan_u64(keep ? qweight(v, m, a.c64, bk, true) : 0ull);
+                if (threadIdx.x == 63) {
+                    L.red_u[0] = (unsigned long long)__popcll(kept);
+                    L.red_u[1] = qs;
+                }
             }
-        nk = (int)sel_sum_u64(c, L);
-        s_k = sc.mass_ex + (double)sel_sum_u64(q, L) * unit_of(bk);
+            __syncthreads();
+            c = uniform(L.red_u[0]);
+            q = uniform(L.red_u[1]);
+            __syncthreads();
+            nk = (int)c;
+            s_k = sc.mass_ex + (double)q * unit_of(bk);
+        } else {
+            for (int i = threadIdx.x; i < ns; i += kSelThreads)
+                if (L.buf.f.sub[i] >= tau_k) {
+                    ++c;
+                    q += qweight(L.buf.f.sub[i], m, a.c64, bk, true);
+                }
+            nk = (int)sel_sum_u64(c, L);
+            s_k = sc.mass_ex + (double)sel_sum_u64(q, L) * unit_of(bk);
+        }
     }
     if (topp) {
         // With the gather kernel's candidates (and top-k off), the first
@@ -978,7 +1095,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
         if (topk && bp == bk) {
             ns = nk;  // sub holds bin bk sorted: its first nk entries are >= tau_k
         } else {
-            if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bp, -INFINITY)) return false;
+            if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bp, -INFINITY, cand)) return false;
             ns = uniform(L.n_sub);
         }
         Walk w = walk_sub(L, ns, m, a, bp, sp.mass_ex, target);
@@ -1008,7 +1125,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
                 const BinScan sq = scan_find(L, lim, false, 0ull, target_b);
                 if (sq.bin == lim) return false;
                 if (sq.bin != in_sub) {
-                    if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, sq.bin, -INFINITY))
+                    if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, sq.bin, -INFINITY, cand))
                         return false;
                     ns = uniform(L.n_sub);
                     in_sub = sq.bin;
@@ -1032,7 +1149,7 @@ __device__ __attribute__((always_inline)) bool fast_filter(const T* x, const Fil
         // (at or before the bin of a threshold below tau).
         const int bt = bin_of(tau, m, a.bin_scale);
         const BinScan st = scan_find(L, bt, true, ~0ull, 0.0);
-        if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bt, tau)) return false;
+        if (!gather_bin<T, VEC>(L, x, complete, ntop, m, a, bt, tau, cand)) return false;
         unsigned long long q = 0;
         const int nb_sub = uniform(L.n_sub);
         for (int i = threadIdx.x; i < nb_sub; i += kSelThreads)
@@ -1123,6 +1240,24 @@ __global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
             over |= c > (uint32_t)a.seg;
         }
     over = __syncthreads_or(over);
+    if (cand) {  // the counts to an inclusive prefix over the chunks (one wave, S <= 256)
+        if (threadIdx.x < 64) {
+            const int base = threadIdx.x * 4;
+            uint32_t c[4], sum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[i] = base + i < a.S ? L.tcnt[base + i] : 0u;
+                sum += c[i];
+            }
+            uint32_t run = (uint32_t)wave_inclusive_scan_u64(sum) - sum;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                run += c[i];
+                if (base + i < a.S) L.tcnt[base + i] = run;
+            }
+        }
+        __syncthreads();
+    }
     const float* usable = (cand && !over) ? cand : nullptr;
     double rest_cand = 0.0;
     if (cand)
@@ -1173,7 +1308,8 @@ __global__ __launch_bounds__(kSelThreads, 8) void filter_kernel(FilterArgs a) {
         __syncthreads();
         const int nslots = a.S * a.seg;
         for (int i = threadIdx.x; i < nslots; i += kSelThreads) {
-            const uint32_t c = L.tcnt[i / a.seg];
+            const int ch = i / a.seg;
+            const uint32_t c = L.tcnt[ch] - (ch ? L.tcnt[ch - 1] : 0u);
             if (c <= (uint32_t)a.seg && (uint32_t)(i & (a.seg - 1)) < c) cand[i] = 0.f;
         }
         for (int ch = threadIdx.x; ch < a.S; ch += kSelThreads) {
