@@ -160,26 +160,6 @@ __device__ inline double unit_of(int bin) { return ldexp(1.0, -(octave_of(bin) +
 // fp64 2^a, out of line: it sits on a rare branch of the per-logit loops.
 __device__ __noinline__ double exp2_f64(double a) { return exp2(a); }
 
-// 2^a in fp64 for a in [-1100, 0]: 2^n 2^(j/64) 2^r with n = floor(a), j the
-// next six bits, r in [0, 1/64); 2^(j/64) from `tab` (64 entries, each the
-// library's fp64 exponential), 2^r by its Taylor polynomial to degree 5
-// (truncation below (ln2 / 64)^6 / 720 < 2e-15 relative).  Within a few fp64
-// ulp; about a third of the library call's instructions.
-__device__ inline double exp2_tab64(double a, const double* tab) {
-    const double t = a * 64.0;         // exact (a power of two)
-    const double kd = floor(t);
-    const int k = (int)kd;             // a in [-1100, 0]: k fits easily
-    const double r = (t - kd) * (1.0 / 64.0);  // exact, in [0, 1/64)
-    const double l = 0.69314718055994530942;
-    double p = l * l * l * l * l / 120.0;
-    p = fma(p, r, l * l * l * l / 24.0);
-    p = fma(p, r, l * l * l / 6.0);
-    p = fma(p, r, l * l / 2.0);
-    p = fma(p, r, l);
-    p = fma(p, r, 1.0);
-    return ldexp(tab[k & 63] * p, k >> 6);  // k = 64 n + j, j in [0, 64)
-}
-
 // 2^((x - m) c) for x <= m, fp64.  Accurate (acc): the fp64 exponential for
 // every logit.  Otherwise the fp64 exponential above 2^-8 and below it 2^n
 // times the fp32 exponential of the fractional part, n = floor of the fp64
@@ -268,17 +248,37 @@ struct CandArgs {
     int seg;
 };
 
+// 2^(t / 256) in fp64 for t <= 0 (-inf excluded): 2^n 2^(j/256) 2^(f/256)
+// with k = floor(t) = 256 n + j, f = t - k in [0, 1) (exact); 2^(j/256) from
+// `tab` (256 entries, each the library's fp64 exponential), 2^(f/256) by its
+// Taylor polynomial to degree 4 (truncation below (ln2 / 256)^5 / 120 < 2e-15
+// relative).  Within a few fp64 ulp; below 2^-1074 it underflows to 0.
+__device__ inline double exp2_256(double t, const double* tab) {
+    const double kd = floor(fmax(t, -300000.0));  // keeps k in int range; 2^(-300000/256) is 0
+    const int k = (int)kd;
+    const double f = fmax(t, -300000.0) - kd;
+    constexpr double u = 0.69314718055994530942 / 256.0;
+    double p = u * u * u * u / 24.0;
+    p = fma(p, f, u * u * u / 6.0);
+    p = fma(p, f, u * u / 2.0);
+    p = fma(p, f, u);
+    p = fma(p, f, 1.0);
+    return ldexp(tab[k & 255] * p, k >> 8);
+}
+
 // TAIL: also sum the chunk's tail mass, with fp64 weights (the selection uses
 // it for top-p without top-k only, and then decides against it as against the
 // whole row's mass).
 template <typename T, int U, bool TAIL>
 __global__ __launch_bounds__(kThreads) void cand_kernel(CandArgs a) {
     constexpr int EPV = Elem<T>::kPerVec;
+    static_assert(kThreads >= 256, "one table entry per thread");
     __shared__ float red_f[kWaves];
     __shared__ double red_d[kWaves];
     __shared__ int wsum[kWaves];
-    __shared__ double tab[64];
-    if (TAIL && threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x / 64.0);
+    __shared__ double tab[256];
+    if (TAIL && threadIdx.x < 256) tab[threadIdx.x] = exp2((double)threadIdx.x / 256.0);
+    const double c256 = a.c64 * 256.0;  // exact: a power-of-two multiple
     const int t = blockIdx.x, ch = t % a.S, row = t / a.S;
     const int b = row / a.R, r = row % a.R;
     // The tile's loads go out first; the row maximum and the floor are worked
@@ -309,10 +309,8 @@ __global__ __launch_bounds__(kThreads) void cand_kernel(CandArgs a) {
         for (int e = 0; e < EPV; ++e) {
             const bool c = ok && x[e] >= x_lo;
             n += c ? 1 : 0;
-            if (TAIL && ok && !c && x[e] != -INFINITY) {
-                const double w = ((double)x[e] - (double)m) * a.c64;
-                if (w > -1100.0) tail += exp2_tab64(w, tab);
-            }
+            if (TAIL && ok && !c && x[e] != -INFINITY)
+                tail += exp2_256(((double)x[e] - (double)m) * c256, tab);
         }
     }
     if (TAIL) {
