@@ -254,3 +254,38 @@ def test_filtered_output_distributed_as_filtered_p():
     case = wl.StochasticCase("chi2", trials, 1, V, "f32", 1.0, t, d, x, u)
     gpu = run_filtered(case, 5, 0.9, 0.0)
     assert chi2_stat(np.bincount(gpu["out_tokens"][:, 0], minlength=V), pf) < CHI2_DF7_P001
+
+
+def _top_p_at_group_edge(case, b, row, near=0.9):
+    """A float32 top_p whose target mass for target row `row` of request b lies
+    1e-9 .. 1e-7 (relative to the row's mass) from a group edge: the fp64
+    cumulative masses of the row's descending groups of equal logits, the
+    group end nearest `near`, and the nearest float32 to it at least 2e-9
+    away."""
+    r = case.target[b, row]
+    x = (wl.bits_to_float(r) if case.dtype == "bf16" else r).astype(np.float64)
+    w = np.exp2((x - x.max()) * (np.log2(np.e) / float(np.float32(case.temperature))))
+    vals, inv = np.unique(-x, return_inverse=True)  # ascending -x: descending logits
+    cum = np.cumsum(np.bincount(inv, weights=w)) / w.sum()
+    f = float(cum[np.argmin(np.abs(cum - near))])
+    p = np.float32(f)
+    if abs(float(p) - f) < 2e-9:
+        p = np.nextafter(p, np.float32(1.0 if float(p) >= f else 0.0))
+    return float(p)
+
+
+@pytest.mark.parametrize("mode", [_lib.MODE_STOCHASTIC, _lib.MODE_STOCHASTIC_FILTERED])
+def test_top_p_decided_near_a_group_edge(mode):
+    """Top-p alone with the target 1e-9 .. 1e-7 from a group edge on one row:
+    closer than the statistics' row mass can tell (~1e-5), so the decision
+    comes from the candidate gather's fp64 tail masses (large workspace) or the
+    selection's own fp64 tail pass (small workspace); both must agree with the
+    oracle on that request."""
+    case = wl.c3(8, B=4)
+    top_p = _top_p_at_group_edge(case, 1, 0)
+    ref = oracle_filtered(case, 0, top_p, 0.0)
+    assert 1e-9 <= ref["filter_margins"][1] < 1e-6  # the hard case is really there
+    gpu = run_filtered(case, 0, top_p, 0.0, workspace=_workspace(case, mode))
+    H.compare_stochastic(gpu, ref, label=f"edge-{mode}", filter_band=FILTER_GUARD)
+    assert gpu["num_accepted"][1] == ref["num_accepted"][1]
+    np.testing.assert_array_equal(gpu["out_tokens"][1], ref["out_tokens"][1])
