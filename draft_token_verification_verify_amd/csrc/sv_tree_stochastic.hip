@@ -57,6 +57,7 @@ struct TsLds {
     double red_d[kTsWaves];
     float red_f[kTsWaves];
     double tile_sum[kTsTiles];
+    double wsum[kTsTiles][kTsWaves];  // per-wave sums of each tile of a weight pass
     int red_i;
     int pick_tile;
     double pick_base;
@@ -146,6 +147,37 @@ __device__ inline void ts_load(const T* row, int V, int tile, float* x) {
     for (int e = 0; e < kTsPer; ++e) x[e] = (j0 + e < V) ? Elem<T>::load(row, j0 + e) : -INFINITY;
 }
 
+// One tile's 16-byte vectors of this thread, loaded ahead of their use (the
+// next tile's loads are in flight while the current one is summed).  A tile
+// that is not whole, or a row that is not 16-byte aligned, is read when used.
+template <typename T, bool VEC>
+struct TileBuf {
+    static constexpr int kVecs = VEC ? kTsPer / Elem<T>::kPerVec : 1;
+    uint4 raw[kVecs];
+    bool whole = false;
+    __device__ inline void fetch(const T* row, int V, int tile) {
+        if constexpr (VEC) {
+            constexpr int EPV = Elem<T>::kPerVec;
+            const int j0 = tile * kTsTile + (int)threadIdx.x * kTsPer;
+            whole = j0 + kTsPer <= V;
+            if (whole)
+#pragma unroll
+                for (int v = 0; v < kVecs; ++v) raw[v] = load16(row + j0 + v * EPV);
+        }
+    }
+    __device__ inline void get(const T* row, int V, int tile, float* x) const {
+        if constexpr (VEC) {
+            constexpr int EPV = Elem<T>::kPerVec;
+            if (whole) {
+#pragma unroll
+                for (int v = 0; v < kVecs; ++v) Elem<T>::widen(raw[v], x + v * EPV);
+                return;
+            }
+        }
+        ts_load<T, false>(row, V, tile, x);
+    }
+};
+
 // Softmax statistics of a row: maximum m and s = sum of 2^((x - m) c), in one
 // pass: each thread sums against its running maximum, rescaling its sum (fp64
 // exponential) when the maximum grows; threads are then merged in fixed order.
@@ -187,12 +219,24 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
                              TsLds& L, RowStats* st, RowStats* sd) {
     const int tiles = (V + kTsTile - 1) / kTsTile;
     RunStats rt, rd;
+    TileBuf<T, VEC> bt, bd;
+    bt.fetch(trow, V, 0);
+    if (both) bd.fetch(drow, V, 0);
     for (int k = 0; k < tiles; ++k) {
+        TileBuf<T, VEC> nt, nd;
+        if (k + 1 < tiles) {
+            nt.fetch(trow, V, k + 1);
+            if (both) nd.fetch(drow, V, k + 1);
+        }
         float xt[kTsPer], xd[kTsPer];
-        ts_load<T, VEC>(trow, V, k, xt);
-        if (both) ts_load<T, VEC>(drow, V, k, xd);
+        bt.get(trow, V, k, xt);
         rt.add_tile(xt, sc);
-        if (both) rd.add_tile(xd, sc);
+        if (both) {
+            bd.get(drow, V, k, xd);
+            rd.add_tile(xd, sc);
+        }
+        bt = nt;
+        bd = nd;
     }
     *st = ts_merge(rt, sc, L);
     if (both) *sd = ts_merge(rd, sc, L);
@@ -233,11 +277,18 @@ template <typename T, bool VEC>
 __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist& D, bool residual,
                                  TsLds& L) {
     const int tiles = (V + kTsTile - 1) / kTsTile;
-    double total = 0.0;
+    TileBuf<T, VEC> bt, bd;
+    bt.fetch(trow, V, 0);
+    if (residual) bd.fetch(drow, V, 0);
     for (int k = 0; k < tiles; ++k) {
+        TileBuf<T, VEC> nt, nd;
+        if (k + 1 < tiles) {
+            nt.fetch(trow, V, k + 1);
+            if (residual) nd.fetch(drow, V, k + 1);
+        }
         float xt[kTsPer], xd[kTsPer];
-        ts_load<T, VEC>(trow, V, k, xt);
-        if (residual) ts_load<T, VEC>(drow, V, k, xd);
+        bt.get(trow, V, k, xt);
+        if (residual) bd.get(drow, V, k, xd);
         double own = 0.0;
 #pragma unroll
         for (int e = 0; e < kTsPer; ++e) {
@@ -245,11 +296,23 @@ __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist
             const double p = D.chain(D.p0(xt[e]), qv, D.nrej);
             own += residual ? fmax(p - qv, 0.0) : p;
         }
-        const double s = ts_block_sum(own, L);
-        if (threadIdx.x == 0) L.tile_sum[k] = s;
-        total += s;
+        // The wave's sum now, the waves' sums after the loop (the same order
+        // as a workgroup sum per tile, without its barriers).
+        own = wave_reduce_sum(own);
+        if ((threadIdx.x & 63) == 0) L.wsum[k][threadIdx.x >> 6] = own;
+        bt = nt;
+        bd = nd;
     }
     __syncthreads();
+    if ((int)threadIdx.x < tiles) {
+        double r = L.wsum[threadIdx.x][0];
+#pragma unroll
+        for (int w = 1; w < kTsWaves; ++w) r += L.wsum[threadIdx.x][w];
+        L.tile_sum[threadIdx.x] = r;
+    }
+    __syncthreads();
+    double total = 0.0;
+    for (int k = 0; k < tiles; ++k) total += L.tile_sum[k];
     return total;
 }
 
