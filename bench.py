@@ -164,7 +164,7 @@ def make_step(case, sets, filt=None):
             s = sets[i % len(sets)]
             sv.spec_verify_tree_stochastic(s["target"], s["draft"], s["node_tokens"], s["paths"],
                                            s["uniforms"], case.temperature, out_tokens=out,
-                                           num_accepted=acc, accepted_nodes=nodes)
+                                           num_accepted=acc, accepted_nodes=nodes, workspace=ws)
         step.nodes = nodes
         return step, out, acc
     out = torch.empty((case.B, case.L), dtype=torch.int32, device=dev)
@@ -418,7 +418,7 @@ def main():
             "bound": "hbm",
             "kernel": ("filter selection kernel (filtered call)" if filt is not None else
                        "statistics kernel (two-kernel schedule)" if mode_of(case) == "stochastic"
-                       else "tree walk kernel (one workgroup per request)"
+                       else "tree walk kernel (each request's walk split over workgroups)"
                        if mode_of(case) == "tree-stochastic" else "argmax kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,

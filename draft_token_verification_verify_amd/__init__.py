@@ -17,7 +17,7 @@ import torch
 
 from . import _lib
 from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_STOCHASTIC_FILTERED, MODE_TREE,
-                   SpecVerifyError)
+                   MODE_TREE_STOCHASTIC, SpecVerifyError)
 
 __all__ = [
     "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
@@ -26,6 +26,7 @@ __all__ = [
     "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
     "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE", "MODE_STOCHASTIC_FILTERED",
+    "MODE_TREE_STOCHASTIC",
 ]
 
 
@@ -307,11 +308,15 @@ def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,
 def spec_verify_tree_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                                 node_tokens: torch.Tensor, paths: torch.Tensor,
                                 uniforms: torch.Tensor, temperature: float, *, out_tokens=None,
-                                num_accepted=None, accepted_nodes=None, stream=None):
+                                num_accepted=None, accepted_nodes=None, workspace=None,
+                                split=True, stream=None):
     """Stochastic tree verification (each accepted node's children tested in
     ascending order against the residual of their rejected siblings); returns
     ``(out_tokens[B,L], num_accepted[B], accepted_nodes[B,L])``.  ``uniforms``
-    is float32 [B, N+1]: entry c-1 drives node c's test, entry N the final draw."""
+    is float32 [B, N+1]: entry c-1 drives node c's test, entry N the final draw.
+    With ``split`` (and a workspace, allocated here when not given) each
+    request's walk may be shared by several workgroups; ``split=False`` passes
+    no workspace (one workgroup per request)."""
     device = target_logits.device
     dt = _dtype_code(target_logits)
     if target_logits.dim() != 3 or paths.dim() != 3:
@@ -330,10 +335,14 @@ def spec_verify_tree_stochastic(target_logits: torch.Tensor, draft_logits: torch
         if t is None:
             t = torch.empty(shape, dtype=torch.int32, device=device)
         outs.append(_dev(t, name, device, torch.int32, shape))
+    ws = None
+    if split:
+        ws = _workspace(workspace, spec_verify_workspace_bytes(MODE_TREE_STOCHASTIC, B, N1, V, dt),
+                        device)
     st = _lib.load().spec_verify_tree_stochastic(
         _ptr(target_logits), _ptr(draft_logits), dt, _ptr(node_tokens), _ptr(paths),
         _ptr(uniforms), float(temperature), B, N1 - 1, P, L, V, _ptr(outs[0]), _ptr(outs[1]),
-        _ptr(outs[2]), _stream(device, stream))
+        _ptr(outs[2]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(device, stream))
     _lib.check("spec_verify_tree_stochastic", st)
     return tuple(outs)
 

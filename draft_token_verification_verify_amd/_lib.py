@@ -9,7 +9,7 @@ LIB_PATH = os.path.join(HERE, "libspec_verify.so")
 
 # Stable enums, same values as include/spec_verify.h.
 F32, BF16 = 0, 1
-MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE, MODE_STOCHASTIC_FILTERED = 0, 1, 2, 3
+MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE, MODE_STOCHASTIC_FILTERED, MODE_TREE_STOCHASTIC = range(5)
 OK, INVALID_ARGUMENT, UNSUPPORTED_DTYPE, WORKSPACE_TOO_SMALL, LIMIT_EXCEEDED, HIP_ERROR = range(6)
 SCHEDULE_AUTO, SCHEDULE_TWO_KERNELS, SCHEDULE_SELF_COMPUTE = 0, 1, 2
 
@@ -84,7 +84,7 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_tree.argtypes = [P, I, P, P, I, I, I, I, I, P, P, P, P, P, Z, P]
     lib.spec_verify_tree.restype = I
     lib.spec_verify_tree_stochastic.argtypes = [P, P, I, P, P, P, ctypes.c_float, I, I, I, I, I,
-                                                P, P, P, P]
+                                                P, P, P, P, Z, P]
     lib.spec_verify_tree_stochastic.restype = I
     lib.spec_verify_gather_rows.argtypes = [P, P, Z, P, P, I, I, I, P]
     lib.spec_verify_gather_rows.restype = I

@@ -65,9 +65,11 @@ const char* spec_verify_status_string(int status) {
 
 size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype) {
     const int eb = elem_bytes_of(dtype);
-    if (eb == 0 || mode < 0 || mode > 3 || V > SPEC_VERIFY_MAX_VOCAB) return 0;
-    if (mode != 2 && rows_per_request - 1 > SPEC_VERIFY_MAX_K) return 0;
-    if (mode == 2 && rows_per_request > SPEC_VERIFY_MAX_TREE_ROWS) return 0;
+    if (eb == 0 || mode < 0 || mode > 4 || V > SPEC_VERIFY_MAX_VOCAB) return 0;
+    const bool tree = mode == 2 || mode == 4;
+    if (!tree && rows_per_request - 1 > SPEC_VERIFY_MAX_K) return 0;
+    if (tree && rows_per_request > SPEC_VERIFY_MAX_TREE_ROWS) return 0;
+    if (mode == 4 && V > SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB) return 0;
     sv::Geometry g;
     if (!sv::make_geometry(mode, B, rows_per_request, V, eb, &g)) return 0;
     return g.bytes;
@@ -281,7 +283,8 @@ int spec_verify_tree_stochastic(const void* target_logits, const void* draft_log
                                 const int32_t* node_tokens, const int32_t* paths,
                                 const float* uniforms, float temperature, int B, int N, int P,
                                 int L, int V, int32_t* out_tokens, int32_t* num_accepted,
-                                int32_t* accepted_nodes, void* stream) {
+                                int32_t* accepted_nodes, void* workspace, size_t workspace_bytes,
+                                void* stream) {
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || N < 0 || P < 0 || L < 1 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
@@ -313,6 +316,8 @@ int spec_verify_tree_stochastic(const void* target_logits, const void* draft_log
     c.out_tokens = out_tokens;
     c.num_accepted = num_accepted;
     c.accepted_nodes = accepted_nodes;
+    c.workspace = workspace;
+    c.workspace_bytes = workspace ? workspace_bytes : 0;
     return finish(sv::run_tree_stochastic(c, (hipStream_t)stream, next_events()));
 }
 

@@ -70,6 +70,10 @@ constexpr int kCandBins = 256;
 constexpr int kCandCap = 16384;
 constexpr int kCandMaxChunks = 256;  // rows of more streaming chunks keep no candidates
 
+// Stochastic tree walk split over several workgroups per request: their
+// exchange area in the workspace (mode 4), per request.
+constexpr size_t kTreeSyncBytes = 1280;
+
 // Bins per unit of logit, 16 log2(e) / T, rounded to fp32 once: one value for
 // every kernel that bins.
 inline float filter_bin_scale(float temperature) {
@@ -93,13 +97,20 @@ struct Scale {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // mode: 0 stochastic, 1 greedy, 2 tree, 3 stochastic with filter candidates
-// (mode 0's layout plus a candidate buffer at the end); rows_per_request: k+1
-// or N+1.
+// (mode 0's layout plus a candidate buffer at the end), 4 stochastic tree walk
+// (its exchange area only); rows_per_request: k+1 or N+1.
 inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem_bytes,
                           Geometry* g) {
     if (B < 1 || rows_per_request < 1 || V < 1 || (elem_bytes != 2 && elem_bytes != 4))
         return false;
     const int epv = 16 / elem_bytes;  // elements per 16-byte vector
+    if (mode == 4) {  // stochastic tree walk: only the exchange area
+        if (B < 1 || rows_per_request < 1 || V < 1 || (elem_bytes != 2 && elem_bytes != 4))
+            return false;
+        *g = Geometry{};
+        g->bytes = kTreeSyncBytes * (size_t)B;
+        return true;
+    }
     bool cand = mode == 3;
     if (cand) mode = 0;
     g->R = (mode == 0) ? 2 * rows_per_request - 1 : rows_per_request;

@@ -76,6 +76,8 @@ struct TreeStochCall {
     int32_t* out_tokens;
     int32_t* num_accepted;
     int32_t* accepted_nodes;
+    void* workspace;          // exchange areas (mode 4 size), or null: one workgroup per request
+    size_t workspace_bytes;
 };
 
 // Accepted-row gather.

@@ -24,6 +24,8 @@
 // residual's mass, and the final draw one pass for the weights' running total
 // by tiles plus one tile for the token.  Every sum runs in a fixed order, so
 // results do not change between runs.
+#include <algorithm>
+
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 
@@ -36,6 +38,26 @@ constexpr int kMaxRejections = kMaxTreeNodes;  // a node has at most N children
 constexpr int kTsPer = 16;                     // logits per thread per tile
 constexpr int kTsTile = kTsThreads * kTsPer;   // logits per tile
 constexpr int kTsTiles = 32;                   // tiles per row: V <= 524288
+constexpr int kTsMaxSplit = 8;                 // workgroups per request, at most
+constexpr int kTsSpinLimit = 1 << 20;          // polls of one exchange before giving up
+
+// Exchange area of one request whose walk is split over G workgroups (in the
+// workspace; zero before the call and after it).  Workgroup g takes the
+// row tiles k with k % G == g; every workgroup runs the same walk, so they
+// all make the same exchanges in the same order.  Round r's data sits in
+// slot r & 1; flag[g] = r + 1 says workgroup g has published round r.  A
+// workgroup reaches round r + 2 only after every workgroup has published
+// r + 1, that is, has read round r: two slots suffice.
+struct TsSync {
+    uint32_t flag[kTsMaxSplit];
+    uint32_t exit;      // workgroups done; the last one clears the area
+    uint32_t failed;    // an exchange gave up waiting
+    uint32_t pad[6];
+    double stat[2][kTsMaxSplit][4];  // (target max, mass, draft max, mass) per workgroup
+    double tile[2][kTsTiles];        // weight-pass tile sums, by the tiles' owners
+    int32_t token[2];                // the final draw's token, by its tile's owner
+};
+static_assert(sizeof(TsSync) <= kTreeSyncBytes, "exchange area");
 
 struct TreeStochArgs {
     const void* target;
@@ -48,7 +70,41 @@ struct TreeStochArgs {
     int32_t* out_tokens;      // [B, L]
     int32_t* num_accepted;    // [B]
     int32_t* accepted_nodes;  // [B, L] or null
+    int G;                    // workgroups per request
+    char* sync;               // [B] exchange areas of kTreeSyncBytes (G > 1)
 };
+
+// This workgroup's place in its request's group.
+struct TsGroup {
+    int G, g;
+    TsSync* sy;
+    int round;
+};
+
+// Round `round` of the group: this workgroup's data, already stored with
+// store_coherent by thread 0, is published by its flag; then every
+// workgroup's flag is awaited (bounded: after kTsSpinLimit polls the request
+// is marked failed and the walk goes on, so the kernel always ends).
+__device__ inline void ts_exchange(TsGroup& grp) {
+    const uint32_t want = (uint32_t)grp.round + 1u;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __threadfence();
+        store_coherent(&grp.sy->flag[grp.g], want);
+    }
+    if ((int)threadIdx.x < grp.G) {  // one thread per workgroup's flag (all in wave 0)
+        int spins = 0;
+        while (load_coherent(&grp.sy->flag[threadIdx.x]) < want) {
+            if (++spins > kTsSpinLimit) {
+                store_coherent(&grp.sy->failed, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        __threadfence();
+    }
+    __syncthreads();
+}
 
 struct TsLds {
     int first[kMaxTreeNodes];   // first occurrence (row * L + t) of each node in paths
@@ -58,6 +114,7 @@ struct TsLds {
     float red_f[kTsWaves];
     double tile_sum[kTsTiles];
     double wsum[kTsTiles][kTsWaves];  // per-wave sums of each tile of a weight pass
+    double xstat[kTsMaxSplit * 4];    // the group's row statistics, as exchanged
     int red_i;
     int pick_tile;
     double pick_base;
@@ -213,20 +270,24 @@ __device__ inline RowStats ts_merge(const RunStats& r, const Scale& sc, TsLds& L
     return out;
 }
 
-// Statistics of the target row and, when `both`, of the draft row, in one pass.
+// Statistics of the target row and, when `both`, of the draft row, in one
+// pass (over this workgroup's tiles; with G > 1 the workgroups' statistics are
+// then merged in workgroup order).
 template <typename T, bool VEC>
 __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, const Scale& sc,
-                             TsLds& L, RowStats* st, RowStats* sd) {
+                             TsLds& L, RowStats* st, RowStats* sd, TsGroup& grp) {
     const int tiles = (V + kTsTile - 1) / kTsTile;
     RunStats rt, rd;
     TileBuf<T, VEC> bt, bd;
-    bt.fetch(trow, V, 0);
-    if (both) bd.fetch(drow, V, 0);
-    for (int k = 0; k < tiles; ++k) {
+    if (grp.g < tiles) {
+        bt.fetch(trow, V, grp.g);
+        if (both) bd.fetch(drow, V, grp.g);
+    }
+    for (int k = grp.g; k < tiles; k += grp.G) {
         TileBuf<T, VEC> nt, nd;
-        if (k + 1 < tiles) {
-            nt.fetch(trow, V, k + 1);
-            if (both) nd.fetch(drow, V, k + 1);
+        if (k + grp.G < tiles) {
+            nt.fetch(trow, V, k + grp.G);
+            if (both) nd.fetch(drow, V, k + grp.G);
         }
         float xt[kTsPer], xd[kTsPer];
         bt.get(trow, V, k, xt);
@@ -240,6 +301,33 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
     }
     *st = ts_merge(rt, sc, L);
     if (both) *sd = ts_merge(rd, sc, L);
+    if (grp.G > 1) {
+        double* slot = grp.sy->stat[grp.round & 1][0];
+        if (threadIdx.x == 0) {
+            store_coherent(&slot[grp.g * 4 + 0], (double)st->m);
+            store_coherent(&slot[grp.g * 4 + 1], st->s);
+            store_coherent(&slot[grp.g * 4 + 2], both ? (double)sd->m : 0.0);
+            store_coherent(&slot[grp.g * 4 + 3], both ? sd->s : 0.0);
+        }
+        ts_exchange(grp);
+        if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = load_coherent(&slot[threadIdx.x]);
+        __syncthreads();
+        for (int side = 0; side < (both ? 2 : 1); ++side) {
+            float M = -INFINITY;
+            for (int w = 0; w < grp.G; ++w) M = fmaxf(M, (float)L.xstat[w * 4 + 2 * side]);
+            double S = 0.0;
+            if (M != -INFINITY)
+                for (int w = 0; w < grp.G; ++w) {
+                    const float mw = (float)L.xstat[w * 4 + 2 * side];
+                    if (mw != -INFINITY) S += L.xstat[w * 4 + 2 * side + 1] * exp2_accurate(mw, M, sc);
+                }
+            RowStats& out = side == 0 ? *st : *sd;
+            out.m = M;
+            out.s = S;
+        }
+        __syncthreads();  // xstat is read before the next exchange refills it
+        ++grp.round;
+    }
 }
 
 // The current distribution at token x: p after nrej rejections,
@@ -275,16 +363,18 @@ struct Dist {
 // the total.
 template <typename T, bool VEC>
 __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist& D, bool residual,
-                                 TsLds& L) {
+                                 TsLds& L, TsGroup& grp) {
     const int tiles = (V + kTsTile - 1) / kTsTile;
     TileBuf<T, VEC> bt, bd;
-    bt.fetch(trow, V, 0);
-    if (residual) bd.fetch(drow, V, 0);
-    for (int k = 0; k < tiles; ++k) {
+    if (grp.g < tiles) {
+        bt.fetch(trow, V, grp.g);
+        if (residual) bd.fetch(drow, V, grp.g);
+    }
+    for (int k = grp.g; k < tiles; k += grp.G) {
         TileBuf<T, VEC> nt, nd;
-        if (k + 1 < tiles) {
-            nt.fetch(trow, V, k + 1);
-            if (residual) nd.fetch(drow, V, k + 1);
+        if (k + grp.G < tiles) {
+            nt.fetch(trow, V, k + grp.G);
+            if (residual) nd.fetch(drow, V, k + grp.G);
         }
         float xt[kTsPer], xd[kTsPer];
         bt.get(trow, V, k, xt);
@@ -304,13 +394,23 @@ __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist
         bd = nd;
     }
     __syncthreads();
-    if ((int)threadIdx.x < tiles) {
-        double r = L.wsum[threadIdx.x][0];
+    const int t = threadIdx.x;
+    if (t < tiles && t % grp.G == grp.g) {
+        double r = L.wsum[t][0];
 #pragma unroll
-        for (int w = 1; w < kTsWaves; ++w) r += L.wsum[threadIdx.x][w];
-        L.tile_sum[threadIdx.x] = r;
+        for (int w = 1; w < kTsWaves; ++w) r += L.wsum[t][w];
+        L.tile_sum[t] = r;
     }
     __syncthreads();
+    if (grp.G > 1) {  // every tile's sum, from its owner
+        double* slot = grp.sy->tile[grp.round & 1];
+        if (t == 0)
+            for (int k = grp.g; k < tiles; k += grp.G) store_coherent(&slot[k], L.tile_sum[k]);
+        ts_exchange(grp);
+        if (t < tiles) L.tile_sum[t] = load_coherent(&slot[t]);
+        __syncthreads();
+        ++grp.round;
+    }
     double total = 0.0;
     for (int k = 0; k < tiles; ++k) total += L.tile_sum[k];
     return total;
@@ -320,8 +420,12 @@ __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist
 // whose running weight exceeds u * Z (Z = that pass's total), else the last
 // token with positive weight.
 template <typename T, bool VEC>
+__device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& D, bool residual,
+                               double target, int k, TsLds& L);
+
+template <typename T, bool VEC>
 __device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool residual, double Z,
-                       double u, TsLds& L) {
+                       double u, TsLds& L, TsGroup& grp) {
     const int tiles = (V + kTsTile - 1) / kTsTile;
     const double target = u * Z;
     if (threadIdx.x == 0) {
@@ -349,6 +453,25 @@ __device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool 
     }
     __syncthreads();
     const int k = L.pick_tile;
+    if (grp.G > 1) {  // the tile's owner finds the token; the others wait for it
+        int* slot = &grp.sy->token[grp.round & 1];
+        if (k % grp.G == grp.g) {
+            const int tk = ts_draw_in_tile<T, VEC>(trow, drow, V, D, residual, target, k, L);
+            if (threadIdx.x == 0) store_coherent(slot, (int32_t)tk);
+        }
+        ts_exchange(grp);
+        const int tk = (int)load_coherent(slot);
+        ++grp.round;
+        return tk;
+    }
+    return ts_draw_in_tile<T, VEC>(trow, drow, V, D, residual, target, k, L);
+}
+
+// The token inside tile k: the running weight from the tiles before it plus
+// this tile's weights in order, first above the target.
+template <typename T, bool VEC>
+__device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& D, bool residual,
+                               double target, int k, TsLds& L) {
     const double base = L.pick_base;
     float xt[kTsPer], xd[kTsPer];
     ts_load<T, VEC>(trow, V, k, xt);
@@ -381,7 +504,13 @@ __device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochArgs a) {
     __shared__ TsLds L;
-    const int b = blockIdx.x, N = a.N, V = a.V, Lp = a.L;
+    const int b = blockIdx.x / a.G, N = a.N, V = a.V, Lp = a.L;
+    TsGroup grp;
+    grp.G = a.G;
+    grp.g = blockIdx.x % a.G;
+    grp.sy = a.G > 1 ? reinterpret_cast<TsSync*>(a.sync + (size_t)b * kTreeSyncBytes) : nullptr;
+    grp.round = 0;
+    const bool lead = grp.g == 0;  // writes the outputs
     const int32_t* tok = a.node_tokens + (size_t)b * (N + 1);
     const float* u = a.uniforms + (size_t)b * (N + 1);
     const int32_t* paths = a.paths + (size_t)b * a.P * Lp;
@@ -410,10 +539,11 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
 
     int32_t* out = a.out_tokens + (size_t)b * Lp;
     int32_t* nodes = a.accepted_nodes ? a.accepted_nodes + (size_t)b * Lp : nullptr;
-    for (int t = threadIdx.x; t < Lp; t += kTsThreads) {
-        out[t] = -1;
-        if (nodes) nodes[t] = -1;
-    }
+    if (lead)
+        for (int t = threadIdx.x; t < Lp; t += kTsThreads) {
+            out[t] = -1;
+            if (nodes) nodes[t] = -1;
+        }
 
     int n = 0, depth = 0;
     for (;;) {
@@ -428,7 +558,7 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
         D.nrej = 0;
         D.inv_z = L.inv_z;
         RowStats st, sd;
-        ts_row_stats<T, VEC>(trow, drow, test, V, a.sc, L, &st, &sd);
+        ts_row_stats<T, VEC>(trow, drow, test, V, a.sc, L, &st, &sd, grp);
         D.set(st.m, st.s, test ? sd.m : -INFINITY, test ? sd.s : 0.0);
         int next = -1;
         double Zlast = 0.0;
@@ -447,7 +577,7 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
                     break;
                 }
                 // Rejected: the residual's mass, then the next sibling against it.
-                Zlast = ts_weight_pass<T, VEC>(trow, drow, V, D, true, L);
+                Zlast = ts_weight_pass<T, VEC>(trow, drow, V, D, true, L, grp);
                 if (threadIdx.x == 0) L.inv_z[D.nrej] = Zlast > 0.0 ? 1.0 / Zlast : 0.0;
                 __syncthreads();
                 ++D.nrej;
@@ -462,15 +592,27 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
             // (For a residual, the last rejection's pass left exactly these
             // weights' tile sums in L.tile_sum.)
             const double Z = residual ? Zlast
-                                      : ts_weight_pass<T, VEC>(trow, drow, V, F, false, L);
-            const int token = ts_draw<T, VEC>(trow, drow, V, F, residual, Z, (double)u[N], L);
-            if (threadIdx.x == 0) {
+                                      : ts_weight_pass<T, VEC>(trow, drow, V, F, false, L, grp);
+            const int token = ts_draw<T, VEC>(trow, drow, V, F, residual, Z, (double)u[N], L, grp);
+            if (threadIdx.x == 0 && lead) {
                 out[depth] = token;
                 a.num_accepted[b] = depth;
             }
+            if (grp.G > 1) {  // the last workgroup out clears the exchange area
+                __syncthreads();
+                if (threadIdx.x == 0) {
+                    __threadfence();
+                    if (atomicAdd(&grp.sy->exit, 1u) == (uint32_t)grp.G - 1u) {
+                        __threadfence();
+                        if (load_coherent(&grp.sy->failed)) a.num_accepted[b] = -2;
+                        uint32_t* w = reinterpret_cast<uint32_t*>(grp.sy);
+                        for (size_t i = 0; i < sizeof(TsSync) / 4; ++i) store_coherent(&w[i], 0u);
+                    }
+                }
+            }
             return;
         }
-        if (threadIdx.x == 0) {
+        if (threadIdx.x == 0 && lead) {
             out[depth] = tok[next];
             if (nodes) nodes[depth] = next;
         }
@@ -514,6 +656,61 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherArgs g) {
     }
 }
 
+// Workgroups of the walk kernel that fit on the device at once (cached per
+// device): a split walk needs every workgroup resident, as its exchanges wait
+// on each other.
+template <typename T, bool VEC>
+static int ts_resident_capacity() {
+    static int cached[64][4];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    const int slot = (sizeof(T) == 2 ? 2 : 0) + (VEC ? 1 : 0);
+    if (cached[dev][slot] == 0) {
+        int coop = 0, cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(tree_stochastic_kernel<T, VEC>), kTsThreads,
+                0) != hipSuccess)
+            return 0;
+        cached[dev][slot] = coop ? std::max(cus * per_cu, 1) : -1;
+    }
+    return cached[dev][slot];
+}
+
+template <typename T, bool VEC>
+static hipError_t launch_tree(TreeStochArgs a, const TreeStochCall& c, hipStream_t st,
+                              const KernelEvents& ev) {
+    // Split each request's walk over G workgroups when the workspace holds the
+    // exchange areas and B * G workgroups can all be resident; G is at most
+    // one per row tile.
+    const int tiles = (c.V + kTsTile - 1) / kTsTile;
+    int G = 1;
+    if (c.workspace && c.workspace_bytes >= kTreeSyncBytes * (size_t)c.B) {
+        const int cap = ts_resident_capacity<T, VEC>();
+        if (cap > 0) G = std::min(std::min(kTsMaxSplit, tiles), cap / c.B);
+        if (G < 2) G = 1;
+    }
+    a.G = G;
+    a.sync = G > 1 ? static_cast<char*>(c.workspace) : nullptr;
+    if (G > 1) {
+        void* args[] = {&a};
+        if (ev.begin) (void)hipEventRecord(static_cast<hipEvent_t>(ev.begin), st);
+        const hipError_t e = hipLaunchCooperativeKernel(
+            reinterpret_cast<const void*>(tree_stochastic_kernel<T, VEC>),
+            dim3((unsigned)(c.B * G)), dim3(kTsThreads), args, 0, st);
+        if (ev.end) (void)hipEventRecord(static_cast<hipEvent_t>(ev.end), st);
+        if (e == hipSuccess) return hipSuccess;
+        (void)hipGetLastError();  // not launched: one workgroup per request instead
+        a.G = 1;
+        a.sync = nullptr;
+    }
+    // The events (when set) take the kernel's own start and end timestamps.
+    hipExtLaunchKernelGGL(tree_stochastic_kernel<T, VEC>, dim3((unsigned)c.B), dim3(kTsThreads), 0,
+                          st, ev.begin, ev.end, 0, a);
+    return hipGetLastError();
+}
+
 hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st, const KernelEvents& ev) {
     TreeStochArgs a;
     a.target = c.target;
@@ -530,24 +727,11 @@ hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st, const Ker
     a.out_tokens = c.out_tokens;
     a.num_accepted = c.num_accepted;
     a.accepted_nodes = c.accepted_nodes;
-    const dim3 grid((unsigned)c.B), block(kTsThreads);
-    // The events (when set) take the kernel's own start and end timestamps.
-    if (c.dtype == 1) {
-        if (c.vec)
-            hipExtLaunchKernelGGL(tree_stochastic_kernel<bf16_t, true>, grid, block, 0, st,
-                                  ev.begin, ev.end, 0, a);
-        else
-            hipExtLaunchKernelGGL(tree_stochastic_kernel<bf16_t, false>, grid, block, 0, st,
-                                  ev.begin, ev.end, 0, a);
-    } else {
-        if (c.vec)
-            hipExtLaunchKernelGGL(tree_stochastic_kernel<float, true>, grid, block, 0, st,
-                                  ev.begin, ev.end, 0, a);
-        else
-            hipExtLaunchKernelGGL(tree_stochastic_kernel<float, false>, grid, block, 0, st,
-                                  ev.begin, ev.end, 0, a);
-    }
-    return hipGetLastError();
+    a.G = 1;
+    a.sync = nullptr;
+    if (c.dtype == 1)
+        return c.vec ? launch_tree<bf16_t, true>(a, c, st, ev) : launch_tree<bf16_t, false>(a, c, st, ev);
+    return c.vec ? launch_tree<float, true>(a, c, st, ev) : launch_tree<float, false>(a, c, st, ev);
 }
 
 hipError_t run_gather_rows(const GatherCall& c, hipStream_t st) {

@@ -62,7 +62,11 @@ enum spec_verify_mode {
      * pass, so that its per-row selection reads those instead of the row.
      * spec_verify_stochastic_filtered accepts a workspace of either size and
      * gives the same bits with both; this one is faster. */
-    SPEC_VERIFY_MODE_STOCHASTIC_FILTERED = 3
+    SPEC_VERIFY_MODE_STOCHASTIC_FILTERED = 3,
+    /* Sizing only: the exchange areas (1280 bytes per request) that let
+     * spec_verify_tree_stochastic split each request's walk over several
+     * workgroups (rows_per_request = N + 1). */
+    SPEC_VERIFY_MODE_TREE_STOCHASTIC = 4
 };
 
 enum spec_verify_status {
@@ -365,16 +369,32 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *node_t
  *
  * Limits: N + 1 <= SPEC_VERIFY_MAX_TREE_ROWS, P <= SPEC_VERIFY_MAX_PATHS,
  * L <= SPEC_VERIFY_MAX_PATH_LEN, P * L <= SPEC_VERIFY_MAX_PATH_TABLE,
- * V <= SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB.  No workspace.  Draft ids outside
- * [0, V) are rejected.  One workgroup per request walks its tree: each visited
- * node reads its two rows once for their statistics, once more per rejected
- * child, and once for the final draw.
+ * V <= SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB.  Draft ids outside [0, V) are
+ * rejected.  Each request's walk reads, per visited node, its two rows once
+ * for their statistics, once more per rejected child, and once for the final
+ * draw.
+ *
+ *   workspace      device, zero-filled before first use (left zero), of at
+ *                  least spec_verify_workspace_bytes(SPEC_VERIFY_MODE_TREE_-
+ *                  STOCHASTIC, B, N + 1, V, dtype) bytes, or NULL.  With it,
+ *                  each request's walk is split over up to 8 workgroups (the
+ *                  row tiles shared out, their sums exchanged through it) when
+ *                  all of them fit on the device at once (a cooperative
+ *                  launch); otherwise, or with NULL, one workgroup per request
+ *                  walks its tree.  The two give the same tokens except where
+ *                  a decision lies within rounding of its boundary (the row
+ *                  statistics are merged in a different order).  Calls sharing
+ *                  a workspace must be ordered on one stream.  num_accepted[b]
+ *                  = -2 marks a request whose split walk gave up waiting for
+ *                  one of its workgroups (not expected; its outputs are then
+ *                  not valid).
  */
 int spec_verify_tree_stochastic(const void *target_logits, const void *draft_logits, int dtype,
                                 const int32_t *node_tokens, const int32_t *paths,
                                 const float *uniforms, float temperature, int B, int N, int P,
                                 int L, int V, int32_t *out_tokens, int32_t *num_accepted,
-                                int32_t *accepted_nodes, void *stream);
+                                int32_t *accepted_nodes, void *workspace, size_t workspace_bytes,
+                                void *stream);
 
 /*
  * Gather of the accepted rows (page "TensorRT-LLM source teardown (10)", KV

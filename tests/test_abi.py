@@ -51,7 +51,11 @@ def test_workspace_sizing(lib):
     assert ws(_lib.MODE_GREEDY, 8, 5, 32000, _lib.BF16) > 0
     assert ws(_lib.MODE_TREE, 32, 61, 128256, _lib.BF16) > 0
     assert ws(_lib.MODE_STOCHASTIC, 1, 1, 1, _lib.F32) > 0  # k = 0, V = 1
-    assert ws(4, 1, 2, 10, _lib.F32) == 0           # unknown mode
+    assert ws(5, 1, 2, 10, _lib.F32) == 0           # unknown mode
+    # the stochastic tree walk: one 1280-byte exchange area per request
+    assert ws(_lib.MODE_TREE_STOCHASTIC, 32, 61, 128256, _lib.BF16) == 32 * 1280
+    assert ws(_lib.MODE_TREE_STOCHASTIC, 1, 1025, 100, _lib.BF16) == 0  # N + 1 > 1024
+    assert ws(_lib.MODE_TREE_STOCHASTIC, 1, 5, (1 << 19) + 1, _lib.BF16) == 0
     # the filtered call's size: the stochastic one plus, per logits row
     # (B (2k + 1) rows), 16384 candidate slots of 4 bytes and, per 16384-element
     # chunk (8 at V = 128256), a count and an fp64 tail mass; fewer slots for a
@@ -146,11 +150,12 @@ def test_filtered_rejects(lib, kw, code):
 
 def tree_stoch(lib, **kw):
     a = dict(t=FAKE, d=FAKE, dtype=_lib.BF16, nt=FAKE, paths=FAKE, u=FAKE, T=1.0, B=2, N=5, P=3,
-             L=4, V=100, out=FAKE, acc=FAKE, nodes=None, stream=None)
+             L=4, V=100, out=FAKE, acc=FAKE, nodes=None, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.spec_verify_tree_stochastic(a["t"], a["d"], a["dtype"], a["nt"], a["paths"],
                                            a["u"], a["T"], a["B"], a["N"], a["P"], a["L"],
-                                           a["V"], a["out"], a["acc"], a["nodes"], a["stream"])
+                                           a["V"], a["out"], a["acc"], a["nodes"], a["ws"],
+                                           a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [

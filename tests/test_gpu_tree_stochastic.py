@@ -22,13 +22,14 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def run_tree_stochastic(case):
+def run_tree_stochastic(case, split=True, workspace=None):
     t = wl.to_device(case.target, case.dtype)
     d = wl.to_device(case.draft, case.dtype)
     nt = wl.to_device(case.node_tokens.astype(np.int32))
     pa = wl.to_device(case.paths.astype(np.int32))
     u = wl.to_device(case.uniforms.astype(np.float32))
-    out, acc, nodes = sv.spec_verify_tree_stochastic(t, d, nt, pa, u, case.temperature)
+    out, acc, nodes = sv.spec_verify_tree_stochastic(t, d, nt, pa, u, case.temperature,
+                                                     split=split, workspace=workspace)
     torch.cuda.synchronize()
     return dict(out_tokens=out.cpu().numpy(), num_accepted=acc.cpu().numpy(),
                 accepted_nodes=nodes.cpu().numpy())
@@ -176,3 +177,27 @@ def test_gather_rows(row_shape, dtype):
     sv.spec_verify_gather_rows(src.to(dev), nodes, acc, dst)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(dst.cpu().view(B, L, -1).float().numpy(), want)
+
+
+@pytest.mark.parametrize("name,make", [CASES[1], CASES[3]], ids=[CASES[1][0], CASES[3][0]])
+def test_tree_stochastic_parity_one_workgroup(name, make):
+    """Without a workspace every request's walk runs in one workgroup."""
+    case = make(0)
+    gpu = run_tree_stochastic(case, split=False)
+    compare(gpu, oracle_tree_stochastic(case), name + "-1wg", case.rows)
+
+
+def test_split_walk_leaves_the_workspace_zero():
+    """Split walks of two shapes in a row through one workspace: the exchange
+    areas are cleared by each call's last workgroup (and no request gave up
+    waiting: num_accepted >= 0)."""
+    from draft_token_verification_verify_amd import _lib
+    dev = torch.device("cuda", 0)
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(_lib.MODE_TREE_STOCHASTIC, 16, 61, 32000,
+                                                    _lib.BF16), dtype=torch.uint8, device=dev)
+    for case in (wl.stochastic_tree_case(4, 16, 60, 6, 32000, "bf16"),
+                 wl.stochastic_tree_case(5, 8, 30, 5, 20000, "bf16")):
+        gpu = run_tree_stochastic(case, workspace=ws)
+        assert np.all(gpu["num_accepted"] >= 0)
+        compare(gpu, oracle_tree_stochastic(case), "ws", case.rows)
+        assert int(torch.count_nonzero(ws)) == 0
