@@ -22,7 +22,8 @@ from ._lib import (BF16, F32, MODE_GREEDY, MODE_STOCHASTIC, MODE_STOCHASTIC_FILT
 __all__ = [
     "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
     "spec_verify_stochastic_filtered", "spec_verify_greedy", "spec_verify_greedy_ragged",
-    "spec_verify_tree", "spec_verify_tree_stochastic", "spec_verify_gather_rows",
+    "spec_verify_tree", "spec_verify_tree_stochastic", "spec_verify_tree_stochastic_split",
+    "spec_verify_gather_rows",
     "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
     "MODE_STOCHASTIC", "MODE_GREEDY", "MODE_TREE", "MODE_STOCHASTIC_FILTERED",
@@ -345,6 +346,12 @@ def spec_verify_tree_stochastic(target_logits: torch.Tensor, draft_logits: torch
         _ptr(outs[2]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(device, stream))
     _lib.check("spec_verify_tree_stochastic", st)
     return tuple(outs)
+
+
+def spec_verify_tree_stochastic_split(B: int, V: int, dtype: int = BF16) -> int:
+    """Workgroups per request that spec_verify_tree_stochastic would use on the
+    current device (1: not split; 0: arguments it would reject)."""
+    return int(_lib.load().spec_verify_tree_stochastic_split(B, V, dtype))
 
 
 def spec_verify_gather_rows(src: torch.Tensor, accepted_nodes: torch.Tensor,

@@ -28,6 +28,7 @@ EXPORTED = (
     "spec_verify_greedy_ragged",
     "spec_verify_tree",
     "spec_verify_tree_stochastic",
+    "spec_verify_tree_stochastic_split",
     "spec_verify_gather_rows",
 )
 
@@ -85,6 +86,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_tree.restype = I
     lib.spec_verify_tree_stochastic.argtypes = [P, P, I, P, P, P, ctypes.c_float, I, I, I, I, I,
                                                 P, P, P, P, Z, P]
+    lib.spec_verify_tree_stochastic_split.argtypes = [I, I, I]
+    lib.spec_verify_tree_stochastic_split.restype = I
     lib.spec_verify_tree_stochastic.restype = I
     lib.spec_verify_gather_rows.argtypes = [P, P, Z, P, P, I, I, I, P]
     lib.spec_verify_gather_rows.restype = I

@@ -321,6 +321,12 @@ int spec_verify_tree_stochastic(const void* target_logits, const void* draft_log
     return finish(sv::run_tree_stochastic(c, (hipStream_t)stream, next_events()));
 }
 
+int spec_verify_tree_stochastic_split(int B, int V, int dtype) {
+    if (elem_bytes_of(dtype) == 0 || B < 1 || V < 1 || V > SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB)
+        return 0;
+    return sv::tree_stochastic_split(B, V, dtype);
+}
+
 int spec_verify_gather_rows(const void* src, void* dst, size_t row_bytes,
                             const int32_t* accepted_nodes, const int32_t* num_accepted, int B,
                             int N1, int L, void* stream) {

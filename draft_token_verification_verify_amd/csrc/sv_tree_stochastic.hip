@@ -678,19 +678,28 @@ static int ts_resident_capacity() {
     return cached[dev][slot];
 }
 
+// Workgroups per request for B requests over V tokens: at most one per row
+// tile and kTsMaxSplit, and B * G must all be resident at once; 1 when no
+// split fits.
+template <typename T, bool VEC>
+static int ts_split(int B, int V) {
+    const int tiles = (V + kTsTile - 1) / kTsTile;
+    const int cap = ts_resident_capacity<T, VEC>();
+    const int G = cap > 0 ? std::min(std::min(kTsMaxSplit, tiles), cap / B) : 1;
+    return G < 2 ? 1 : G;
+}
+
+int tree_stochastic_split(int B, int V, int dtype) {
+    return dtype == 1 ? ts_split<bf16_t, true>(B, V) : ts_split<float, true>(B, V);
+}
+
 template <typename T, bool VEC>
 static hipError_t launch_tree(TreeStochArgs a, const TreeStochCall& c, hipStream_t st,
                               const KernelEvents& ev) {
     // Split each request's walk over G workgroups when the workspace holds the
-    // exchange areas and B * G workgroups can all be resident; G is at most
-    // one per row tile.
-    const int tiles = (c.V + kTsTile - 1) / kTsTile;
+    // exchange areas (ts_split).
     int G = 1;
-    if (c.workspace && c.workspace_bytes >= kTreeSyncBytes * (size_t)c.B) {
-        const int cap = ts_resident_capacity<T, VEC>();
-        if (cap > 0) G = std::min(std::min(kTsMaxSplit, tiles), cap / c.B);
-        if (G < 2) G = 1;
-    }
+    if (c.workspace && c.workspace_bytes >= kTreeSyncBytes * (size_t)c.B) G = ts_split<T, VEC>(c.B, c.V);
     a.G = G;
     a.sync = G > 1 ? static_cast<char*>(c.workspace) : nullptr;
     if (G > 1) {

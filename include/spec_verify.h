@@ -397,6 +397,16 @@ int spec_verify_tree_stochastic(const void *target_logits, const void *draft_log
                                 void *stream);
 
 /*
+ * Workgroups per request that spec_verify_tree_stochastic would use, with a
+ * workspace of the right size and 16-byte aligned rows, for B requests over a
+ * vocabulary of V on the current device: at most 8 and one per 16384-token row
+ * tile, and B times it must fit on the device at once; 1 when the walk is not
+ * split.  0 for arguments that call would reject.  Initialises the device's
+ * HIP context if needed; no GPU work.
+ */
+int spec_verify_tree_stochastic_split(int B, int V, int dtype);
+
+/*
  * Gather of the accepted rows (page "TensorRT-LLM source teardown (10)", KV
  * rewind, fourth step: the accepted draft tokens' KV rows, scattered when the
  * draft was a tree, are moved to contiguous logical positions):

@@ -177,6 +177,12 @@ def test_tree_stochastic_rejects(lib, kw, code):
     assert tree_stoch(lib, **kw) == code
 
 
+@pytest.mark.parametrize("B,V,dtype", [(0, 100, _lib.BF16), (4, 0, _lib.BF16), (4, 100, 7),
+                                       (4, (1 << 19) + 1, _lib.F32)])
+def test_tree_split_query_rejects(lib, B, V, dtype):
+    assert lib.spec_verify_tree_stochastic_split(B, V, dtype) == 0
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(B=0), _lib.INVALID_ARGUMENT),
     (dict(N1=0), _lib.INVALID_ARGUMENT),

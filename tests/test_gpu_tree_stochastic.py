@@ -181,7 +181,10 @@ def test_gather_rows(row_shape, dtype):
 
 @pytest.mark.parametrize("name,make", [CASES[1], CASES[3]], ids=[CASES[1][0], CASES[3][0]])
 def test_tree_stochastic_parity_one_workgroup(name, make):
-    """Without a workspace every request's walk runs in one workgroup."""
+    """Without a workspace every request's walk runs in one workgroup (with
+    one, the C5-shaped case is split over 8)."""
+    from draft_token_verification_verify_amd import _lib
+    assert sv.spec_verify_tree_stochastic_split(6, 128256, _lib.BF16) == 8
     case = make(0)
     gpu = run_tree_stochastic(case, split=False)
     compare(gpu, oracle_tree_stochastic(case), name + "-1wg", case.rows)
@@ -197,7 +200,24 @@ def test_split_walk_leaves_the_workspace_zero():
                                                     _lib.BF16), dtype=torch.uint8, device=dev)
     for case in (wl.stochastic_tree_case(4, 16, 60, 6, 32000, "bf16"),
                  wl.stochastic_tree_case(5, 8, 30, 5, 20000, "bf16")):
+        assert sv.spec_verify_tree_stochastic_split(case.B, case.V, _lib.BF16) == 2  # 2 tiles
         gpu = run_tree_stochastic(case, workspace=ws)
         assert np.all(gpu["num_accepted"] >= 0)
         compare(gpu, oracle_tree_stochastic(case), "ws", case.rows)
         assert int(torch.count_nonzero(ws)) == 0
+
+
+def test_split_walk_with_several_tiles_per_workgroup():
+    """Enough requests over a 128256-token vocabulary (8 tiles per row) that
+    fewer workgroups per request fit on the device than there are tiles, so
+    each takes several (k = g, g + G, ...)."""
+    from draft_token_verification_verify_amd import _lib
+    V = 128256
+    B = next((b for b in (64, 96, 128, 192, 256)
+              if 2 <= sv.spec_verify_tree_stochastic_split(b, V, _lib.BF16) < 8), None)
+    if B is None:
+        pytest.skip("no batch size gives 2..7 workgroups per request on this device")
+    case = wl.stochastic_tree_case(17, B, 6, 3, V, "bf16", target_sd=3.0, draft_noise_sd=1.0)
+    gpu = run_tree_stochastic(case)
+    assert np.all(gpu["num_accepted"] >= 0)
+    compare(gpu, oracle_tree_stochastic(case), "64req", case.rows)
