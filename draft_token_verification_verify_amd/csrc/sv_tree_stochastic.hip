@@ -44,18 +44,21 @@ constexpr int kTsSpinLimit = 1 << 20;          // polls of one exchange before g
 // Exchange area of one request whose walk is split over G workgroups (in the
 // workspace; zero before the call and after it).  Workgroup g takes the
 // row tiles k with k % G == g; every workgroup runs the same walk, so they
-// all make the same exchanges in the same order.  Round r's data sits in
-// slot r & 1; flag[g] = r + 1 says workgroup g has published round r.  A
-// workgroup reaches round r + 2 only after every workgroup has published
-// r + 1, that is, has read round r: two slots suffice.
+// all make the same exchanges in the same order.  Every exchanged value is
+// published as 64-bit words that each carry, in their upper half, the round
+// that wrote them (round + 1, so never the cleared 0): a reader polls the
+// words it needs until their tag is the round's, with no fence between data
+// and a flag (a device-scope acquire fence would invalidate the L2 and with
+// it the row tiles every workgroup keeps there).  Round r's words sit in slot
+// r & 1; a workgroup publishes round r + 1 only after reading all of round r,
+// so round r + 2 never overwrites words still to be read.
 struct TsSync {
-    uint32_t flag[kTsMaxSplit];
     uint32_t exit;      // workgroups done; the last one clears the area
     uint32_t failed;    // an exchange gave up waiting
-    uint32_t pad[6];
-    double stat[2][kTsMaxSplit][4];  // (target max, mass, draft max, mass) per workgroup
-    double tile[2][kTsTiles];        // weight-pass tile sums, by the tiles' owners
-    int32_t token[2];                // the final draw's token, by its tile's owner
+    uint32_t pad[2];
+    unsigned long long stat[2][kTsMaxSplit * 4][2];  // (target max, mass, draft max, mass) per workgroup
+    unsigned long long tile[2][kTsTiles][2];         // weight-pass tile sums, by the tiles' owners
+    unsigned long long token[2];                     // the final draw's token, by its tile's owner
 };
 static_assert(sizeof(TsSync) <= kTreeSyncBytes, "exchange area");
 
@@ -81,29 +84,35 @@ struct TsGroup {
     int round;
 };
 
-// Round `round` of the group: this workgroup's data, already stored with
-// store_coherent by thread 0, is published by its flag; then every
-// workgroup's flag is awaited (bounded: after kTsSpinLimit polls the request
-// is marked failed and the walk goes on, so the kernel always ends).
-__device__ inline void ts_exchange(TsGroup& grp) {
-    const uint32_t want = (uint32_t)grp.round + 1u;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __threadfence();
-        store_coherent(&grp.sy->flag[grp.g], want);
-    }
-    if ((int)threadIdx.x < grp.G) {  // one thread per workgroup's flag (all in wave 0)
-        int spins = 0;
-        while (load_coherent(&grp.sy->flag[threadIdx.x]) < want) {
-            if (++spins > kTsSpinLimit) {
-                store_coherent(&grp.sy->failed, 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
+// Publishing and reading tagged words.  A double is two words (low and high
+// halves of its bits), each tagged.
+__device__ inline uint32_t ts_tag(const TsGroup& grp) { return (uint32_t)grp.round + 1u; }
+
+__device__ inline void ts_put(unsigned long long* w, double v, uint32_t tag) {
+    const unsigned long long bits = (unsigned long long)__double_as_longlong(v);
+    store_coherent(&w[0], ((unsigned long long)tag << 32) | (bits & 0xffffffffull));
+    store_coherent(&w[1], ((unsigned long long)tag << 32) | (bits >> 32));
+}
+
+// Poll one tagged word until it carries `tag` (bounded: after kTsSpinLimit
+// polls the request is marked failed and the word taken as it is).
+__device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t tag, TsSync* sy) {
+    unsigned long long v = load_coherent(w);
+    for (int spins = 0; (uint32_t)(v >> 32) != tag; ++spins) {
+        if (spins > kTsSpinLimit) {
+            store_coherent(&sy->failed, 1u);
+            break;
         }
-        __threadfence();
+        __builtin_amdgcn_s_sleep(2);
+        v = load_coherent(w);
     }
-    __syncthreads();
+    return (uint32_t)v;
+}
+
+__device__ inline double ts_get(const unsigned long long* w, uint32_t tag, TsSync* sy) {
+    const unsigned long long lo = ts_wait_word(&w[0], tag, sy);
+    const unsigned long long hi = ts_wait_word(&w[1], tag, sy);
+    return __longlong_as_double((long long)((hi << 32) | lo));
 }
 
 struct TsLds {
@@ -302,15 +311,15 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
     *st = ts_merge(rt, sc, L);
     if (both) *sd = ts_merge(rd, sc, L);
     if (grp.G > 1) {
-        double* slot = grp.sy->stat[grp.round & 1][0];
+        unsigned long long(*slot)[2] = grp.sy->stat[grp.round & 1];
+        const uint32_t tag = ts_tag(grp);
         if (threadIdx.x == 0) {
-            store_coherent(&slot[grp.g * 4 + 0], (double)st->m);
-            store_coherent(&slot[grp.g * 4 + 1], st->s);
-            store_coherent(&slot[grp.g * 4 + 2], both ? (double)sd->m : 0.0);
-            store_coherent(&slot[grp.g * 4 + 3], both ? sd->s : 0.0);
+            ts_put(slot[grp.g * 4 + 0], (double)st->m, tag);
+            ts_put(slot[grp.g * 4 + 1], st->s, tag);
+            ts_put(slot[grp.g * 4 + 2], both ? (double)sd->m : 0.0, tag);
+            ts_put(slot[grp.g * 4 + 3], both ? sd->s : 0.0, tag);
         }
-        ts_exchange(grp);
-        if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = load_coherent(&slot[threadIdx.x]);
+        if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = ts_get(slot[threadIdx.x], tag, grp.sy);
         __syncthreads();
         for (int side = 0; side < (both ? 2 : 1); ++side) {
             float M = -INFINITY;
@@ -403,11 +412,12 @@ __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist
     }
     __syncthreads();
     if (grp.G > 1) {  // every tile's sum, from its owner
-        double* slot = grp.sy->tile[grp.round & 1];
+        unsigned long long(*slot)[2] = grp.sy->tile[grp.round & 1];
+        const uint32_t tag = ts_tag(grp);
         if (t == 0)
-            for (int k = grp.g; k < tiles; k += grp.G) store_coherent(&slot[k], L.tile_sum[k]);
-        ts_exchange(grp);
-        if (t < tiles) L.tile_sum[t] = load_coherent(&slot[t]);
+            for (int k = grp.g; k < tiles; k += grp.G) ts_put(slot[k], L.tile_sum[k], tag);
+        __syncthreads();  // own sums read from LDS before they are overwritten below
+        if (t < tiles && t % grp.G != grp.g) L.tile_sum[t] = ts_get(slot[t], tag, grp.sy);
         __syncthreads();
         ++grp.round;
     }
@@ -454,13 +464,19 @@ __device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool 
     __syncthreads();
     const int k = L.pick_tile;
     if (grp.G > 1) {  // the tile's owner finds the token; the others wait for it
-        int* slot = &grp.sy->token[grp.round & 1];
+        unsigned long long* slot = &grp.sy->token[grp.round & 1];
+        const uint32_t tag = ts_tag(grp);
+        int tk = 0;
         if (k % grp.G == grp.g) {
-            const int tk = ts_draw_in_tile<T, VEC>(trow, drow, V, D, residual, target, k, L);
-            if (threadIdx.x == 0) store_coherent(slot, (int32_t)tk);
+            tk = ts_draw_in_tile<T, VEC>(trow, drow, V, D, residual, target, k, L);
+            if (threadIdx.x == 0)
+                store_coherent(slot, ((unsigned long long)tag << 32) | (uint32_t)tk);
+        } else {
+            if (threadIdx.x == 0) L.red_i = (int)ts_wait_word(slot, tag, grp.sy);
+            __syncthreads();
+            tk = L.red_i;
+            __syncthreads();
         }
-        ts_exchange(grp);
-        const int tk = (int)load_coherent(slot);
         ++grp.round;
         return tk;
     }
