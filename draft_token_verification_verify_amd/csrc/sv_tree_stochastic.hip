@@ -124,6 +124,9 @@ struct TsLds {
     double tile_sum[kTsTiles];
     double wsum[kTsTiles][kTsWaves];  // per-wave sums of each tile of a weight pass
     double xstat[kTsMaxSplit * 4];    // the group's row statistics, as exchanged
+    double xterm[2 * kTsMaxSplit];    // their masses at the common maximum
+    float child_t[kMaxTreeNodes];     // target and draft logits at each child's token,
+    float child_d[kMaxTreeNodes];     // loaded once per node
     int red_i;
     int pick_tile;
     double pick_base;
@@ -321,20 +324,29 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
         }
         if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = ts_get(slot[threadIdx.x], tag, grp.sy);
         __syncthreads();
+        // Each workgroup's mass rescaled to the common maximum: one thread per
+        // (side, workgroup), then summed in workgroup order by every thread.
+        float M[2];
+        for (int side = 0; side < 2; ++side) {
+            M[side] = -INFINITY;
+            for (int w = 0; w < grp.G; ++w) M[side] = fmaxf(M[side], (float)L.xstat[w * 4 + 2 * side]);
+        }
+        if ((int)threadIdx.x < 2 * grp.G) {
+            const int side = threadIdx.x / grp.G, w = threadIdx.x % grp.G;
+            const float mw = (float)L.xstat[w * 4 + 2 * side];
+            L.xterm[threadIdx.x] = (mw == -INFINITY || M[side] == -INFINITY)
+                                       ? 0.0
+                                       : L.xstat[w * 4 + 2 * side + 1] * exp2_accurate(mw, M[side], sc);
+        }
+        __syncthreads();
         for (int side = 0; side < (both ? 2 : 1); ++side) {
-            float M = -INFINITY;
-            for (int w = 0; w < grp.G; ++w) M = fmaxf(M, (float)L.xstat[w * 4 + 2 * side]);
             double S = 0.0;
-            if (M != -INFINITY)
-                for (int w = 0; w < grp.G; ++w) {
-                    const float mw = (float)L.xstat[w * 4 + 2 * side];
-                    if (mw != -INFINITY) S += L.xstat[w * 4 + 2 * side + 1] * exp2_accurate(mw, M, sc);
-                }
+            for (int w = 0; w < grp.G; ++w) S += L.xterm[side * grp.G + w];
             RowStats& out = side == 0 ? *st : *sd;
-            out.m = M;
+            out.m = M[side];
             out.s = S;
         }
-        __syncthreads();  // xstat is read before the next exchange refills it
+        __syncthreads();  // xstat and xterm are read before the next exchange refills them
         ++grp.round;
     }
 }
@@ -498,11 +510,13 @@ __device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& 
         return residual ? fmax(p - qv, 0.0) : p;
     };
     double own = 0.0;
+#pragma unroll
     for (int e = 0; e < kTsPer; ++e) own += weight(e);
     double tile_total;
     double run = base + ts_block_scan(own, L, &tile_total);
     const int j0 = k * kTsTile + (int)threadIdx.x * kTsPer;
     int hit = 0x7fffffff, lastpos = -1;
+#pragma unroll
     for (int e = 0; e < kTsPer; ++e) {  // the same weights, in the same order
         const double w = weight(e);
         if (w > 0.0) {
@@ -573,6 +587,14 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
         D.sc = a.sc;
         D.nrej = 0;
         D.inv_z = L.inv_z;
+        if (test)  // the children's two logits, loaded while the statistics pass runs
+            for (int c = 1 + (int)threadIdx.x; c <= N; c += kTsThreads)
+                if (L.parent[c] == n) {
+                    const int32_t x = tok[c];
+                    const bool ok = x >= 0 && x < V;
+                    L.child_t[c] = ok ? Elem<T>::load(trow, x) : 0.f;
+                    L.child_d[c] = ok ? Elem<T>::load(drow, x) : 0.f;
+                }
         RowStats st, sd;
         ts_row_stats<T, VEC>(trow, drow, test, V, a.sc, L, &st, &sd, grp);
         D.set(st.m, st.s, test ? sd.m : -INFINITY, test ? sd.s : 0.0);
@@ -584,8 +606,8 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
                 const int32_t x = tok[c];
                 bool accepted = false;
                 if (x >= 0 && x < V) {
-                    const double qv = D.q(Elem<T>::load(drow, x));
-                    const double pv = D.chain(D.p0(Elem<T>::load(trow, x)), qv, D.nrej);
+                    const double qv = D.q(L.child_d[c]);
+                    const double pv = D.chain(D.p0(L.child_t[c]), qv, D.nrej);
                     accepted = (pv >= qv) || ((double)u[c - 1] * qv < pv);
                 }
                 if (accepted) {
