@@ -127,6 +127,8 @@ struct TsLds {
     double xterm[2 * kTsMaxSplit];    // their masses at the common maximum
     float child_t[kMaxTreeNodes];     // target and draft logits at each child's token,
     float child_d[kMaxTreeNodes];     // loaded once per node
+    float child_u[kMaxTreeNodes];     // and each child's token and uniform
+    int child_x[kMaxTreeNodes];
     int red_i;
     int pick_tile;
     double pick_base;
@@ -543,6 +545,7 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
     const bool lead = grp.g == 0;  // writes the outputs
     const int32_t* tok = a.node_tokens + (size_t)b * (N + 1);
     const float* u = a.uniforms + (size_t)b * (N + 1);
+    const float u_draw = u[N];  // the final draw's uniform
     const int32_t* paths = a.paths + (size_t)b * a.P * Lp;
 
     // Parents: the first occurrence (row-major) of a node in a usable row.
@@ -587,11 +590,13 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
         D.sc = a.sc;
         D.nrej = 0;
         D.inv_z = L.inv_z;
-        if (test)  // the children's two logits, loaded while the statistics pass runs
+        if (test)  // each child's token, uniform and logits, loaded while the statistics pass runs
             for (int c = 1 + (int)threadIdx.x; c <= N; c += kTsThreads)
                 if (L.parent[c] == n) {
                     const int32_t x = tok[c];
                     const bool ok = x >= 0 && x < V;
+                    L.child_x[c] = x;
+                    L.child_u[c] = u[c - 1];
                     L.child_t[c] = ok ? Elem<T>::load(trow, x) : 0.f;
                     L.child_d[c] = ok ? Elem<T>::load(drow, x) : 0.f;
                 }
@@ -603,12 +608,12 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
         if (test) {
             for (int c = 1; c <= N; ++c) {
                 if (L.parent[c] != n) continue;  // uniform: LDS, same for every thread
-                const int32_t x = tok[c];
+                const int32_t x = L.child_x[c];
                 bool accepted = false;
                 if (x >= 0 && x < V) {
                     const double qv = D.q(L.child_d[c]);
                     const double pv = D.chain(D.p0(L.child_t[c]), qv, D.nrej);
-                    accepted = (pv >= qv) || ((double)u[c - 1] * qv < pv);
+                    accepted = (pv >= qv) || ((double)L.child_u[c] * qv < pv);
                 }
                 if (accepted) {
                     next = c;
@@ -631,7 +636,7 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
             // weights' tile sums in L.tile_sum.)
             const double Z = residual ? Zlast
                                       : ts_weight_pass<T, VEC>(trow, drow, V, F, false, L, grp);
-            const int token = ts_draw<T, VEC>(trow, drow, V, F, residual, Z, (double)u[N], L, grp);
+            const int token = ts_draw<T, VEC>(trow, drow, V, F, residual, Z, (double)u_draw, L, grp);
             if (threadIdx.x == 0 && lead) {
                 out[depth] = token;
                 a.num_accepted[b] = depth;
