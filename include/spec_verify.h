@@ -379,15 +379,18 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *node_t
  *                  STOCHASTIC, B, N + 1, V, dtype) bytes, or NULL.  With it,
  *                  each request's walk is split over up to 8 workgroups (the
  *                  row tiles shared out, their sums exchanged through it) when
- *                  all of them fit on the device at once (a cooperative
- *                  launch); otherwise, or with NULL, one workgroup per request
- *                  walks its tree.  The two give the same tokens except where
- *                  a decision lies within rounding of its boundary (the row
- *                  statistics are merged in a different order).  Calls sharing
- *                  a workspace must be ordered on one stream.  num_accepted[b]
- *                  = -2 marks a request whose split walk gave up waiting for
- *                  one of its workgroups (not expected; its outputs are then
- *                  not valid).
+ *                  all of them fit on the device at once (by the kernel's
+ *                  occupancy); otherwise, or with NULL, one workgroup per
+ *                  request walks its tree.  The two give the same tokens
+ *                  except where a decision lies within rounding of its
+ *                  boundary (the row statistics are merged in a different
+ *                  order).  Calls sharing a workspace must be ordered on one
+ *                  stream.  The split walk's workgroups wait on each other: a
+ *                  kernel that holds compute units for good on another stream
+ *                  can keep some from starting, and every wait is bounded, so
+ *                  num_accepted[b] = -2 then marks a request whose walk gave
+ *                  up waiting for one of its workgroups (its outputs are not
+ *                  valid).
  */
 int spec_verify_tree_stochastic(const void *target_logits, const void *draft_logits, int dtype,
                                 const int32_t *node_tokens, const int32_t *paths,
