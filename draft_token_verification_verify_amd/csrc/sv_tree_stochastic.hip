@@ -129,6 +129,7 @@ struct TsLds {
     float child_d[kMaxTreeNodes];     // loaded once per node
     float child_u[kMaxTreeNodes];     // and each child's token and uniform
     int child_x[kMaxTreeNodes];
+    unsigned long long kids[kMaxTreeNodes / 64];  // the current node's children: bit c of word c / 64
     int red_i;
     int pick_tile;
     double pick_base;
@@ -582,32 +583,48 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
     for (;;) {
         const T* trow = static_cast<const T*>(a.target) + ((size_t)b * (N + 1) + n) * (size_t)V;
         const T* drow = static_cast<const T*>(a.draft) + ((size_t)b * (N + 1) + n) * (size_t)V;
-        // Does n have a child (tested only while depth + 1 < L)?
-        int has = 0;
-        for (int c = 1 + (int)threadIdx.x; c <= N; c += kTsThreads) has |= L.parent[c] == n;
-        const bool test = __syncthreads_or(has) && depth + 1 < Lp;
+        // n's children (tested only while depth + 1 < L) as a bit mask over
+        // node ids, one ballot per wave; each child's token, uniform and two
+        // logits are loaded here, while the statistics pass runs.
+        static_assert(kTsThreads == kMaxTreeNodes, "one thread per node id");
+        {
+            const int c = threadIdx.x;
+            const bool kid = c >= 1 && c <= N && L.parent[c] == n;
+            const unsigned long long m = __ballot(kid);
+            if ((threadIdx.x & 63) == 0) L.kids[threadIdx.x >> 6] = m;
+            if (kid && depth + 1 < Lp) {
+                const int32_t x = tok[c];
+                const bool ok = x >= 0 && x < V;
+                L.child_x[c] = x;
+                L.child_u[c] = u[c - 1];
+                L.child_t[c] = ok ? Elem<T>::load(trow, x) : 0.f;
+                L.child_d[c] = ok ? Elem<T>::load(drow, x) : 0.f;
+            }
+        }
+        __syncthreads();
+        const int kid_words = (N >> 6) + 1;  // words covering ids 0..N
+        bool has = false;
+        for (int w = 0; w < kid_words; ++w) has |= L.kids[w] != 0ull;
+        const bool test = has && depth + 1 < Lp;
         Dist D;
         D.sc = a.sc;
         D.nrej = 0;
         D.inv_z = L.inv_z;
-        if (test)  // each child's token, uniform and logits, loaded while the statistics pass runs
-            for (int c = 1 + (int)threadIdx.x; c <= N; c += kTsThreads)
-                if (L.parent[c] == n) {
-                    const int32_t x = tok[c];
-                    const bool ok = x >= 0 && x < V;
-                    L.child_x[c] = x;
-                    L.child_u[c] = u[c - 1];
-                    L.child_t[c] = ok ? Elem<T>::load(trow, x) : 0.f;
-                    L.child_d[c] = ok ? Elem<T>::load(drow, x) : 0.f;
-                }
         RowStats st, sd;
         ts_row_stats<T, VEC>(trow, drow, test, V, a.sc, L, &st, &sd, grp);
         D.set(st.m, st.s, test ? sd.m : -INFINITY, test ? sd.s : 0.0);
         int next = -1;
         double Zlast = 0.0;
         if (test) {
-            for (int c = 1; c <= N; ++c) {
-                if (L.parent[c] != n) continue;  // uniform: LDS, same for every thread
+            // The children in ascending id order, from the mask (the same
+            // for every thread).
+            int w = 0;
+            unsigned long long m = L.kids[0];
+            for (;;) {
+                while (m == 0ull && ++w < kid_words) m = L.kids[w];
+                if (m == 0ull) break;
+                const int c = (w << 6) + __builtin_ctzll(m);
+                m &= m - 1ull;
                 const int32_t x = L.child_x[c];
                 bool accepted = false;
                 if (x >= 0 && x < V) {
