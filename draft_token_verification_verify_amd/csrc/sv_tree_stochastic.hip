@@ -119,8 +119,6 @@ struct TsLds {
     int first[kMaxTreeNodes];   // first occurrence (row * L + t) of each node in paths
     int parent[kMaxTreeNodes];
     double inv_z[kMaxRejections];  // reciprocal residual masses at the current node
-    double red_d[kTsWaves];
-    float red_f[kTsWaves];
     double tile_sum[kTsTiles];
     double wsum[kTsTiles][kTsWaves];  // per-wave sums of each tile of a weight pass
     double xstat[kTsMaxSplit * 4];    // the group's row statistics, as exchanged
@@ -129,6 +127,10 @@ struct TsLds {
     float child_d[kMaxTreeNodes];     // loaded once per node
     float child_u[kMaxTreeNodes];     // and each child's token and uniform
     int child_x[kMaxTreeNodes];
+    float mrg_m[kTsWaves][2];  // per-wave maxima of both rows (statistics merge)
+    double mrg_s[kTsWaves][2];  // per-wave rescaled sums of both rows
+    double scan_w[kTsWaves];    // per-wave totals (draw scan)
+    int pick_w[kTsWaves][2];    // per-wave first hit and last positive token (draw)
     unsigned long long kids[kMaxTreeNodes / 64];  // the current node's children: bit c of word c / 64
     int red_i;
     int pick_tile;
@@ -142,59 +144,6 @@ __device__ inline double ts_weight(float x, float m, const Scale& sc) {
     const float a = scaled(x - m, sc);
     if (a > -8.f) return exp2_accurate(x, m, sc);
     return (double)fast_exp2(a);
-}
-
-__device__ inline float ts_block_max(float v, TsLds& L) {
-    v = wave_max(v);
-    if ((threadIdx.x & 63) == 0) L.red_f[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = L.red_f[0];
-#pragma unroll
-    for (int w = 1; w < kTsWaves; ++w) r = fmaxf(r, L.red_f[w]);
-    __syncthreads();
-    return r;
-}
-
-__device__ inline double ts_block_sum(double v, TsLds& L) {
-    v = wave_reduce_sum(v);
-    if ((threadIdx.x & 63) == 0) L.red_d[threadIdx.x >> 6] = v;
-    __syncthreads();
-    double r = L.red_d[0];
-#pragma unroll
-    for (int w = 1; w < kTsWaves; ++w) r += L.red_d[w];
-    __syncthreads();
-    return r;
-}
-
-// Workgroup minimum of an int (one LDS atomic per wave).
-__device__ inline int ts_block_min(int v, TsLds& L) {
-    if (threadIdx.x == 0) L.red_i = 0x7fffffff;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v = min(v, __shfl_xor(v, d));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) atomicMin(&L.red_i, v);
-    __syncthreads();
-    const int r = L.red_i;
-    __syncthreads();
-    return r;
-}
-
-// Exclusive prefix in thread order (fixed order); *total = the sum.
-__device__ inline double ts_block_scan(double v, TsLds& L, double* total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const double inc = wave_inclusive_scan(v);
-    if (lane == 63) L.red_d[wave] = inc;
-    __syncthreads();
-    double before = 0.0, all = 0.0;
-#pragma unroll
-    for (int w = 0; w < kTsWaves; ++w) {
-        const double t = L.red_d[w];
-        if (w < wave) before += t;
-        all += t;
-    }
-    __syncthreads();
-    *total = all;
-    return before + (inc - v);
 }
 
 // The row is read in tiles of kTsThreads * 16 logits; thread t takes the 16
@@ -277,12 +226,52 @@ struct RunStats {
     }
 };
 
-__device__ inline RowStats ts_merge(const RunStats& r, const Scale& sc, TsLds& L) {
-    RowStats out;
-    out.m = ts_block_max(r.m, L);
-    const double f = (r.m == -INFINITY || out.m == -INFINITY) ? 0.0 : exp2_accurate(r.m, out.m, sc);
-    out.s = ts_block_sum(r.m == -INFINITY ? 0.0 : r.s * f, L);
-    return out;
+// The workgroup's statistics of the target row and, when `both`, of the draft
+// row: the maxima in one reduction, then the sums rescaled to them in a
+// second (waves combined in wave order).  Each reduction has LDS slots of its
+// own that no other code touches, so one barrier apiece suffices: a thread
+// reads the maxima before it reaches the second barrier, and the sums before
+// the first barrier of the next merge.
+__device__ inline void ts_merge(const RunStats& rt, const RunStats& rd, bool both, const Scale& sc,
+                                TsLds& L, RowStats* st, RowStats* sd) {
+    const int wave = threadIdx.x >> 6;
+    const float wt = wave_max(rt.m);
+    const float wd = both ? wave_max(rd.m) : -INFINITY;
+    if ((threadIdx.x & 63) == 0) {
+        L.mrg_m[wave][0] = wt;
+        L.mrg_m[wave][1] = wd;
+    }
+    __syncthreads();
+    float mt = L.mrg_m[0][0], md = L.mrg_m[0][1];
+#pragma unroll
+    for (int w = 1; w < kTsWaves; ++w) {
+        mt = fmaxf(mt, L.mrg_m[w][0]);
+        md = fmaxf(md, L.mrg_m[w][1]);
+    }
+    const double ft = (rt.m == -INFINITY || mt == -INFINITY) ? 0.0 : exp2_accurate(rt.m, mt, sc);
+    const double vt = wave_reduce_sum(rt.m == -INFINITY ? 0.0 : rt.s * ft);
+    double vd = 0.0;
+    if (both) {
+        const double fd = (rd.m == -INFINITY || md == -INFINITY) ? 0.0 : exp2_accurate(rd.m, md, sc);
+        vd = wave_reduce_sum(rd.m == -INFINITY ? 0.0 : rd.s * fd);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        L.mrg_s[wave][0] = vt;
+        L.mrg_s[wave][1] = vd;
+    }
+    __syncthreads();
+    double s_t = L.mrg_s[0][0], s_d = L.mrg_s[0][1];
+#pragma unroll
+    for (int w = 1; w < kTsWaves; ++w) {
+        s_t += L.mrg_s[w][0];
+        s_d += L.mrg_s[w][1];
+    }
+    st->m = mt;
+    st->s = s_t;
+    if (both) {
+        sd->m = md;
+        sd->s = s_d;
+    }
 }
 
 // Statistics of the target row and, when `both`, of the draft row, in one
@@ -314,8 +303,7 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
         bt = nt;
         bd = nd;
     }
-    *st = ts_merge(rt, sc, L);
-    if (both) *sd = ts_merge(rd, sc, L);
+    ts_merge(rt, rd, both, sc, L, st, sd);
     if (grp.G > 1) {
         unsigned long long(*slot)[2] = grp.sy->stat[grp.round & 1];
         const uint32_t tag = ts_tag(grp);
@@ -515,8 +503,17 @@ __device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& 
     double own = 0.0;
 #pragma unroll
     for (int e = 0; e < kTsPer; ++e) own += weight(e);
-    double tile_total;
-    double run = base + ts_block_scan(own, L, &tile_total);
+    // Exclusive prefix of the threads' sums in thread order (slots of its own,
+    // written once per walk: one barrier).
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const double inc = wave_inclusive_scan(own);
+    if (lane == 63) L.scan_w[wave] = inc;
+    __syncthreads();
+    double before = 0.0;
+#pragma unroll
+    for (int w = 0; w < kTsWaves; ++w)
+        if (w < wave) before += L.scan_w[w];
+    double run = base + (before + (inc - own));
     const int j0 = k * kTsTile + (int)threadIdx.x * kTsPer;
     int hit = 0x7fffffff, lastpos = -1;
 #pragma unroll
@@ -528,9 +525,25 @@ __device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& 
         }
         run += w;
     }
-    int tok = ts_block_min(hit, L);
-    if (tok == 0x7fffffff)  // rounding left every running weight at or below u * Z
-        tok = max(-ts_block_min(-lastpos, L), 0);
+    // The first hit and the last positive token over the workgroup, in one
+    // reduction (slots of their own, written once per walk: one barrier).
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        hit = min(hit, __shfl_xor(hit, d));
+        lastpos = max(lastpos, __shfl_xor(lastpos, d));
+    }
+    if (lane == 0) {
+        L.pick_w[wave][0] = hit;
+        L.pick_w[wave][1] = lastpos;
+    }
+    __syncthreads();
+    int tok = L.pick_w[0][0], last = L.pick_w[0][1];
+#pragma unroll
+    for (int w = 1; w < kTsWaves; ++w) {
+        tok = min(tok, L.pick_w[w][0]);
+        last = max(last, L.pick_w[w][1]);
+    }
+    if (tok == 0x7fffffff) tok = max(last, 0);  // rounding left every running weight at or below u * Z
     return tok;
 }
 
