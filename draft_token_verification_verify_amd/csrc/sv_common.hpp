@@ -72,7 +72,7 @@ constexpr int kCandMaxChunks = 256;  // rows of more streaming chunks keep no ca
 
 // Stochastic tree walk split over several workgroups per request: their
 // exchange area in the workspace (mode 4), per request.
-constexpr size_t kTreeSyncBytes = 2304;
+constexpr size_t kTreeSyncBytes = 3328;
 
 // Bins per unit of logit, 16 log2(e) / T, rounded to fp32 once: one value for
 // every kernel that bins.

@@ -35,9 +35,9 @@ constexpr int kTsThreads = 1024;
 constexpr int kTsWaves = kTsThreads / 64;
 constexpr int kMaxTreeNodes = 1024;            // N + 1
 constexpr int kMaxRejections = kMaxTreeNodes;  // a node has at most N children
-constexpr int kTsPer = 16;                     // logits per thread per tile
+constexpr int kTsPer = 8;                      // logits per thread per tile (16 would spill registers)
 constexpr int kTsTile = kTsThreads * kTsPer;   // logits per tile
-constexpr int kTsTiles = 32;                   // tiles per row: V <= 524288
+constexpr int kTsTiles = 64;                   // tiles per row: V <= 524288
 constexpr int kTsMaxSplit = 8;                 // workgroups per request, at most
 constexpr int kTsSpinLimit = 1 << 20;          // polls of one exchange before giving up
 
@@ -146,8 +146,8 @@ __device__ inline double ts_weight(float x, float m, const Scale& sc) {
     return (double)fast_exp2(a);
 }
 
-// The row is read in tiles of kTsThreads * 16 logits; thread t takes the 16
-// consecutive logits at tile * 16384 + 16 t (all of its 16-byte loads issued
+// The row is read in tiles of kTsThreads * 8 logits; thread t takes the 8
+// consecutive logits at tile * 8192 + 8 t (all of its 16-byte loads issued
 // together when the row is aligned).  Tile-major, thread-minor order is
 // ascending vocabulary order.
 template <typename T, bool VEC>
@@ -210,7 +210,7 @@ struct RowStats {
 struct RunStats {
     float m = -INFINITY;
     double s = 0.0;
-    // The 16 logits of one tile: the running maximum first (one rescale at
+    // The 8 logits of one tile: the running maximum first (one rescale at
     // most), then their terms against it.
     __device__ inline void add_tile(const float* x, const Scale& sc) {
         float tm = m;

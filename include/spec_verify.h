@@ -63,7 +63,7 @@ enum spec_verify_mode {
      * spec_verify_stochastic_filtered accepts a workspace of either size and
      * gives the same bits with both; this one is faster. */
     SPEC_VERIFY_MODE_STOCHASTIC_FILTERED = 3,
-    /* Sizing only: the exchange areas (2304 bytes per request) that let
+    /* Sizing only: the exchange areas (3328 bytes per request) that let
      * spec_verify_tree_stochastic split each request's walk over several
      * workgroups (rows_per_request = N + 1). */
     SPEC_VERIFY_MODE_TREE_STOCHASTIC = 4

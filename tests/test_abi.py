@@ -52,8 +52,8 @@ def test_workspace_sizing(lib):
     assert ws(_lib.MODE_TREE, 32, 61, 128256, _lib.BF16) > 0
     assert ws(_lib.MODE_STOCHASTIC, 1, 1, 1, _lib.F32) > 0  # k = 0, V = 1
     assert ws(5, 1, 2, 10, _lib.F32) == 0           # unknown mode
-    # the stochastic tree walk: one 2304-byte exchange area per request
-    assert ws(_lib.MODE_TREE_STOCHASTIC, 32, 61, 128256, _lib.BF16) == 32 * 2304
+    # the stochastic tree walk: one 3328-byte exchange area per request
+    assert ws(_lib.MODE_TREE_STOCHASTIC, 32, 61, 128256, _lib.BF16) == 32 * 3328
     assert ws(_lib.MODE_TREE_STOCHASTIC, 1, 1025, 100, _lib.BF16) == 0  # N + 1 > 1024
     assert ws(_lib.MODE_TREE_STOCHASTIC, 1, 5, (1 << 19) + 1, _lib.BF16) == 0
     # the filtered call's size: the stochastic one plus, per logits row

@@ -200,7 +200,8 @@ def test_split_walk_leaves_the_workspace_zero():
                                                     _lib.BF16), dtype=torch.uint8, device=dev)
     for case in (wl.stochastic_tree_case(4, 16, 60, 6, 32000, "bf16"),
                  wl.stochastic_tree_case(5, 8, 30, 5, 20000, "bf16")):
-        assert sv.spec_verify_tree_stochastic_split(case.B, case.V, _lib.BF16) == 2  # 2 tiles
+        tiles = -(-case.V // 8192)  # the walk reads rows in tiles of 8192 logits
+        assert sv.spec_verify_tree_stochastic_split(case.B, case.V, _lib.BF16) == tiles  # 4, then 3
         gpu = run_tree_stochastic(case, workspace=ws)
         assert np.all(gpu["num_accepted"] >= 0)
         compare(gpu, oracle_tree_stochastic(case), "ws", case.rows)
@@ -208,7 +209,7 @@ def test_split_walk_leaves_the_workspace_zero():
 
 
 def test_split_walk_with_several_tiles_per_workgroup():
-    """Enough requests over a 128256-token vocabulary (8 tiles per row) that
+    """Enough requests over a 128256-token vocabulary (16 tiles per row) that
     fewer workgroups per request fit on the device than there are tiles, so
     each takes several (k = g, g + G, ...)."""
     from draft_token_verification_verify_amd import _lib
