@@ -227,6 +227,24 @@ __device__ __noinline__ double exp2_accurate(float x, float m, const Scale& k) {
     return exp2(((double)x - (double)m) * k.c64);
 }
 
+// 2^(t / 256) in fp64 for t <= 0 (-inf excluded): 2^n 2^(j/256) 2^(f/256)
+// with k = floor(t) = 256 n + j, f = t - k in [0, 1) (exact); 2^(j/256) from
+// `tab` (256 entries, each the library's fp64 exponential), 2^(f/256) by its
+// Taylor polynomial to degree 4 (truncation below (ln2 / 256)^5 / 120 < 2e-15
+// relative).  Within a few fp64 ulp; below 2^-1074 it underflows to 0.
+__device__ inline double exp2_256(double t, const double* tab) {
+    const double kd = floor(fmax(t, -300000.0));  // keeps k in int range; 2^(-300000/256) is 0
+    const int k = (int)kd;
+    const double f = fmax(t, -300000.0) - kd;
+    constexpr double u = 0.69314718055994530942 / 256.0;
+    double p = u * u * u * u / 24.0;
+    p = fma(p, f, u * u * u / 6.0);
+    p = fma(p, f, u * u / 2.0);
+    p = fma(p, f, u);
+    p = fma(p, f, 1.0);
+    return ldexp(tab[k & 255] * p, k >> 8);
+}
+
 // Argmax pairs: larger value wins, the lower index wins a tie.
 __device__ inline void merge_argmax(float& v, int& i, float v2, int i2) {
     bool take = (v2 > v) || (v2 == v && i2 < i);

@@ -131,18 +131,21 @@ struct TsLds {
     double mrg_s[kTsWaves][2];  // per-wave rescaled sums of both rows
     double scan_w[kTsWaves];    // per-wave totals (draw scan)
     int pick_w[kTsWaves][2];    // per-wave first hit and last positive token (draw)
+    double exp_tab[256];  // 2^(j / 256): the fp64 token weights
     unsigned long long kids[kMaxTreeNodes / 64];  // the current node's children: bit c of word c / 64
     int red_i;
     int pick_tile;
     double pick_base;
 };
 
-// Weight 2^((x - m) c) of a logit in fp64: the fp64 exponential within 2^-8
-// of the row maximum (most of the mass), fp32 below.
-__device__ inline double ts_weight(float x, float m, const Scale& sc) {
+// Weight 2^((x - m) c) of a logit in fp64: within 2^-8 of the row maximum
+// (most of the mass) the fp64 exponential, exp2_256 on the table `tab` with
+// c256 = 256 c; the fp32 one below.
+__device__ inline double ts_weight(float x, float m, const Scale& sc, double c256,
+                                   const double* tab) {
     if (x == -INFINITY) return 0.0;
     const float a = scaled(x - m, sc);
-    if (a > -8.f) return exp2_accurate(x, m, sc);
+    if (a > -8.f) return exp2_256(((double)x - (double)m) * c256, tab);
     return (double)fast_exp2(a);
 }
 
@@ -358,8 +361,10 @@ struct Dist {
         inv_st = (m_t == -INFINITY || !(s_t > 0.0)) ? 0.0 : 1.0 / s_t;
         inv_sd = (m_d == -INFINITY || !(s_d > 0.0)) ? 0.0 : 1.0 / s_d;
     }
-    __device__ inline double p0(float xt) const { return ts_weight(xt, mt, sc) * inv_st; }
-    __device__ inline double q(float xd) const { return ts_weight(xd, md, sc) * inv_sd; }
+    double c256;            // 256 c (exact: c times a power of two)
+    const double* tab;      // 2^(j / 256), j < 256
+    __device__ inline double p0(float xt) const { return ts_weight(xt, mt, sc, c256, tab) * inv_st; }
+    __device__ inline double q(float xd) const { return ts_weight(xd, md, sc, c256, tab) * inv_sd; }
     // p after the first `upto` rejections, given p0 and q at a token.
     __device__ inline double chain(double p, double qv, int upto) const {
         for (int i = 0; i < upto; ++i) {
@@ -562,6 +567,8 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
     const float u_draw = u[N];  // the final draw's uniform
     const int32_t* paths = a.paths + (size_t)b * a.P * Lp;
 
+    static_assert(kTsThreads >= 256, "one table entry per thread");
+    if (threadIdx.x < 256) L.exp_tab[threadIdx.x] = exp2((double)threadIdx.x / 256.0);
     // Parents: the first occurrence (row-major) of a node in a usable row.
     for (int n = threadIdx.x; n <= N; n += kTsThreads) {
         L.first[n] = 0x7fffffff;
@@ -623,6 +630,8 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
         D.sc = a.sc;
         D.nrej = 0;
         D.inv_z = L.inv_z;
+        D.c256 = a.sc.c64 * 256.0;
+        D.tab = L.exp_tab;
         RowStats st, sd;
         ts_row_stats<T, VEC>(trow, drow, test, V, a.sc, L, &st, &sd, grp);
         D.set(st.m, st.s, test ? sd.m : -INFINITY, test ? sd.s : 0.0);
