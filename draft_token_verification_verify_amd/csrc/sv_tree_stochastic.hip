@@ -138,6 +138,12 @@ struct TsLds {
     double pick_base;
 };
 
+// 2^((x - m) c) in fp64 for x <= m (finite), from the table `tab` of
+// exp2_256, with c256 = 256 c.
+__device__ inline double ts_exp2(float x, float m, double c256, const double* tab) {
+    return exp2_256(((double)x - (double)m) * c256, tab);
+}
+
 // Weight 2^((x - m) c) of a logit in fp64: within 2^-8 of the row maximum
 // (most of the mass) the fp64 exponential, exp2_256 on the table `tab` with
 // c256 = 256 c; the fp32 one below.
@@ -145,7 +151,7 @@ __device__ inline double ts_weight(float x, float m, const Scale& sc, double c25
                                    const double* tab) {
     if (x == -INFINITY) return 0.0;
     const float a = scaled(x - m, sc);
-    if (a > -8.f) return exp2_256(((double)x - (double)m) * c256, tab);
+    if (a > -8.f) return ts_exp2(x, m, c256, tab);
     return (double)fast_exp2(a);
 }
 
@@ -215,12 +221,12 @@ struct RunStats {
     double s = 0.0;
     // The 8 logits of one tile: the running maximum first (one rescale at
     // most), then their terms against it.
-    __device__ inline void add_tile(const float* x, const Scale& sc) {
+    __device__ inline void add_tile(const float* x, const Scale& sc, double c256, const double* tab) {
         float tm = m;
 #pragma unroll
         for (int e = 0; e < kTsPer; ++e) tm = fmaxf(tm, x[e]);
         if (tm > m) {
-            if (m != -INFINITY) s *= exp2_accurate(m, tm, sc);
+            if (m != -INFINITY) s *= ts_exp2(m, tm, c256, tab);
             m = tm;
         }
         const float ms = (m == -INFINITY) ? 0.f : m;
@@ -251,11 +257,12 @@ __device__ inline void ts_merge(const RunStats& rt, const RunStats& rd, bool bot
         mt = fmaxf(mt, L.mrg_m[w][0]);
         md = fmaxf(md, L.mrg_m[w][1]);
     }
-    const double ft = (rt.m == -INFINITY || mt == -INFINITY) ? 0.0 : exp2_accurate(rt.m, mt, sc);
+    const double c256 = sc.c64 * 256.0;
+    const double ft = (rt.m == -INFINITY || mt == -INFINITY) ? 0.0 : ts_exp2(rt.m, mt, c256, L.exp_tab);
     const double vt = wave_reduce_sum(rt.m == -INFINITY ? 0.0 : rt.s * ft);
     double vd = 0.0;
     if (both) {
-        const double fd = (rd.m == -INFINITY || md == -INFINITY) ? 0.0 : exp2_accurate(rd.m, md, sc);
+        const double fd = (rd.m == -INFINITY || md == -INFINITY) ? 0.0 : ts_exp2(rd.m, md, c256, L.exp_tab);
         vd = wave_reduce_sum(rd.m == -INFINITY ? 0.0 : rd.s * fd);
     }
     if ((threadIdx.x & 63) == 0) {
@@ -298,10 +305,10 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
         }
         float xt[kTsPer], xd[kTsPer];
         bt.get(trow, V, k, xt);
-        rt.add_tile(xt, sc);
+        rt.add_tile(xt, sc, sc.c64 * 256.0, L.exp_tab);
         if (both) {
             bd.get(drow, V, k, xd);
-            rd.add_tile(xd, sc);
+            rd.add_tile(xd, sc, sc.c64 * 256.0, L.exp_tab);
         }
         bt = nt;
         bd = nd;
@@ -330,7 +337,8 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
             const float mw = (float)L.xstat[w * 4 + 2 * side];
             L.xterm[threadIdx.x] = (mw == -INFINITY || M[side] == -INFINITY)
                                        ? 0.0
-                                       : L.xstat[w * 4 + 2 * side + 1] * exp2_accurate(mw, M[side], sc);
+                                       : L.xstat[w * 4 + 2 * side + 1] *
+                                             ts_exp2(mw, M[side], sc.c64 * 256.0, L.exp_tab);
         }
         __syncthreads();
         for (int side = 0; side < (both ? 2 : 1); ++side) {
@@ -505,9 +513,12 @@ __device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& 
         const double p = D.chain(D.p0(xt[e]), qv, D.nrej);
         return residual ? fmax(p - qv, 0.0) : p;
     };
-    double own = 0.0;
+    double w[kTsPer], own = 0.0;
 #pragma unroll
-    for (int e = 0; e < kTsPer; ++e) own += weight(e);
+    for (int e = 0; e < kTsPer; ++e) {
+        w[e] = weight(e);
+        own += w[e];
+    }
     // Exclusive prefix of the threads' sums in thread order (slots of its own,
     // written once per walk: one barrier).
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -523,12 +534,11 @@ __device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& 
     int hit = 0x7fffffff, lastpos = -1;
 #pragma unroll
     for (int e = 0; e < kTsPer; ++e) {  // the same weights, in the same order
-        const double w = weight(e);
-        if (w > 0.0) {
+        if (w[e] > 0.0) {
             lastpos = j0 + e;
-            if (run + w > target && hit == 0x7fffffff) hit = j0 + e;
+            if (run + w[e] > target && hit == 0x7fffffff) hit = j0 + e;
         }
-        run += w;
+        run += w[e];
     }
     // The first hit and the last positive token over the workgroup, in one
     // reduction (slots of their own, written once per walk: one barrier).
