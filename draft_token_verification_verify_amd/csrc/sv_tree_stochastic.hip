@@ -123,9 +123,11 @@ struct TsLds {
     double wsum[kTsTiles][kTsWaves];  // per-wave sums of each tile of a weight pass
     double xstat[kTsMaxSplit * 4];    // the group's row statistics, as exchanged
     double xterm[2 * kTsMaxSplit];    // their masses at the common maximum
-    float child_t[kMaxTreeNodes];     // target and draft logits at each child's token,
-    float child_d[kMaxTreeNodes];     // loaded once per node
-    float child_u[kMaxTreeNodes];     // and each child's token and uniform
+    // Per child of the current node, loaded once per node: the target and
+    // draft logits at its token, its uniform and its token.
+    float child_t[kMaxTreeNodes];
+    float child_d[kMaxTreeNodes];
+    float child_u[kMaxTreeNodes];
     int child_x[kMaxTreeNodes];
     float mrg_m[kTsWaves][2];  // per-wave maxima of both rows (statistics merge)
     double mrg_s[kTsWaves][2];  // per-wave rescaled sums of both rows
