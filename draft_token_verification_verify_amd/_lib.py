@@ -29,6 +29,7 @@ EXPORTED = (
     "spec_verify_tree",
     "spec_verify_tree_stochastic",
     "spec_verify_tree_stochastic_split",
+    "spec_verify_debug_tree_spin_limit",
     "spec_verify_gather_rows",
 )
 
@@ -88,6 +89,8 @@ def load() -> ctypes.CDLL:
                                                 P, P, P, P, Z, P]
     lib.spec_verify_tree_stochastic_split.argtypes = [I, I, I]
     lib.spec_verify_tree_stochastic_split.restype = I
+    lib.spec_verify_debug_tree_spin_limit.argtypes = [I]
+    lib.spec_verify_debug_tree_spin_limit.restype = I
     lib.spec_verify_tree_stochastic.restype = I
     lib.spec_verify_gather_rows.argtypes = [P, P, Z, P, P, I, I, I, P]
     lib.spec_verify_gather_rows.restype = I

@@ -114,6 +114,7 @@ hipError_t run_tree(const TreeCall& call, const Geometry& g, hipStream_t st,
                     const KernelEvents& ev);
 hipError_t run_fill_zero(void* ptr, size_t bytes, hipStream_t st);
 int tree_stochastic_split(int B, int V, int dtype);
+int tree_stochastic_spin_limit(int polls);
 hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st, const KernelEvents& ev);
 hipError_t run_gather_rows(const GatherCall& c, hipStream_t st);
 

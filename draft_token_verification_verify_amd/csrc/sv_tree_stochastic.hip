@@ -25,6 +25,7 @@
 // by tiles plus one tile for the token.  Every sum runs in a fixed order, so
 // results do not change between runs.
 #include <algorithm>
+#include <atomic>
 
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
@@ -39,7 +40,7 @@ constexpr int kTsPer = 8;                      // logits per thread per tile (16
 constexpr int kTsTile = kTsThreads * kTsPer;   // logits per tile
 constexpr int kTsTiles = 64;                   // tiles per row: V <= 524288
 constexpr int kTsMaxSplit = 8;                 // workgroups per request, at most
-constexpr int kTsSpinLimit = 1 << 20;          // polls of one exchange before giving up
+constexpr int kTsSpinLimit = 1 << 20;          // polls of one exchange word before giving up (default)
 
 // Exchange area of one request whose walk is split over G workgroups (in the
 // workspace; zero before the call and after it).  Workgroup g takes the
@@ -75,6 +76,7 @@ struct TreeStochArgs {
     int32_t* accepted_nodes;  // [B, L] or null
     int G;                    // workgroups per request
     char* sync;               // [B] exchange areas of kTreeSyncBytes (G > 1)
+    int spin_limit;           // polls of one exchange word before giving up
 };
 
 // This workgroup's place in its request's group.
@@ -82,6 +84,7 @@ struct TsGroup {
     int G, g;
     TsSync* sy;
     int round;
+    int spin_limit;  // polls of one word before giving up
 };
 
 // Publishing and reading tagged words.  A double is two words (low and high
@@ -94,13 +97,15 @@ __device__ inline void ts_put(unsigned long long* w, double v, uint32_t tag) {
     store_coherent(&w[1], ((unsigned long long)tag << 32) | (bits >> 32));
 }
 
-// Poll one tagged word until it carries `tag` (bounded: after kTsSpinLimit
-// polls the request is marked failed and the word taken as it is).
-__device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t tag, TsSync* sy) {
+// Poll one tagged word until it carries `tag` (bounded: after the group's
+// spin limit of polls the request is marked failed and the word taken as it
+// is).
+__device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t tag,
+                                        const TsGroup& grp) {
     unsigned long long v = load_coherent(w);
     for (int spins = 0; (uint32_t)(v >> 32) != tag; ++spins) {
-        if (spins > kTsSpinLimit) {
-            store_coherent(&sy->failed, 1u);
+        if (spins > grp.spin_limit) {
+            store_coherent(&grp.sy->failed, 1u);
             break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -109,9 +114,9 @@ __device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t ta
     return (uint32_t)v;
 }
 
-__device__ inline double ts_get(const unsigned long long* w, uint32_t tag, TsSync* sy) {
-    const unsigned long long lo = ts_wait_word(&w[0], tag, sy);
-    const unsigned long long hi = ts_wait_word(&w[1], tag, sy);
+__device__ inline double ts_get(const unsigned long long* w, uint32_t tag, const TsGroup& grp) {
+    const unsigned long long lo = ts_wait_word(&w[0], tag, grp);
+    const unsigned long long hi = ts_wait_word(&w[1], tag, grp);
     return __longlong_as_double((long long)((hi << 32) | lo));
 }
 
@@ -325,7 +330,7 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
             ts_put(slot[grp.g * 4 + 2], both ? (double)sd->m : 0.0, tag);
             ts_put(slot[grp.g * 4 + 3], both ? sd->s : 0.0, tag);
         }
-        if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = ts_get(slot[threadIdx.x], tag, grp.sy);
+        if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = ts_get(slot[threadIdx.x], tag, grp);
         __syncthreads();
         // Each workgroup's mass rescaled to the common maximum: one thread per
         // (side, workgroup), then summed in workgroup order by every thread.
@@ -435,7 +440,7 @@ __device__ double ts_weight_pass(const T* trow, const T* drow, int V, const Dist
         if (t == 0)
             for (int k = grp.g; k < tiles; k += grp.G) ts_put(slot[k], L.tile_sum[k], tag);
         __syncthreads();  // own sums read from LDS before they are overwritten below
-        if (t < tiles && t % grp.G != grp.g) L.tile_sum[t] = ts_get(slot[t], tag, grp.sy);
+        if (t < tiles && t % grp.G != grp.g) L.tile_sum[t] = ts_get(slot[t], tag, grp);
         __syncthreads();
         ++grp.round;
     }
@@ -490,7 +495,7 @@ __device__ int ts_draw(const T* trow, const T* drow, int V, const Dist& D, bool 
             if (threadIdx.x == 0)
                 store_coherent(slot, ((unsigned long long)tag << 32) | (uint32_t)tk);
         } else {
-            if (threadIdx.x == 0) L.red_i = (int)ts_wait_word(slot, tag, grp.sy);
+            if (threadIdx.x == 0) L.red_i = (int)ts_wait_word(slot, tag, grp);
             __syncthreads();
             tk = L.red_i;
             __syncthreads();
@@ -573,6 +578,7 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
     grp.g = blockIdx.x % a.G;
     grp.sy = a.G > 1 ? reinterpret_cast<TsSync*>(a.sync + (size_t)b * kTreeSyncBytes) : nullptr;
     grp.round = 0;
+    grp.spin_limit = a.spin_limit;
     const bool lead = grp.g == 0;  // writes the outputs
     const int32_t* tok = a.node_tokens + (size_t)b * (N + 1);
     const float* u = a.uniforms + (size_t)b * (N + 1);
@@ -812,8 +818,17 @@ static hipError_t launch_tree(TreeStochArgs a, const TreeStochCall& c, hipStream
     return hipGetLastError();
 }
 
+// Polls of one exchange word before a split walk's workgroup gives up; tests
+// lower it to force the give-up path from the host.
+static std::atomic<int> g_spin_limit{kTsSpinLimit};
+
+int tree_stochastic_spin_limit(int polls) {
+    return g_spin_limit.exchange(polls < 0 ? kTsSpinLimit : polls);
+}
+
 hipError_t run_tree_stochastic(const TreeStochCall& c, hipStream_t st, const KernelEvents& ev) {
     TreeStochArgs a;
+    a.spin_limit = g_spin_limit.load();
     a.target = c.target;
     a.draft = c.draft;
     a.node_tokens = c.node_tokens;

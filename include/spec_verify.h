@@ -402,12 +402,23 @@ int spec_verify_tree_stochastic(const void *target_logits, const void *draft_log
 /*
  * Workgroups per request that spec_verify_tree_stochastic would use, with a
  * workspace of the right size and 16-byte aligned rows, for B requests over a
- * vocabulary of V on the current device: at most 8 and one per 16384-token row
+ * vocabulary of V on the current device: at most 8 and one per 8192-token row
  * tile, and B times it must fit on the device at once; 1 when the walk is not
  * split.  0 for arguments that call would reject.  Initialises the device's
  * HIP context if needed; no GPU work.
  */
 int spec_verify_tree_stochastic_split(int B, int V, int dtype);
+
+/*
+ * Testing hook for the split walk's failure path: sets how many times a
+ * workgroup polls one exchange word before it gives up and the request is
+ * marked num_accepted = -2 (default 1048576; a negative value restores it),
+ * for calls of spec_verify_tree_stochastic made from then on, process-wide.
+ * Returns the previous value.  A tiny value makes split walks give up on
+ * purpose, so tests can check that the kernel still ends, marks the requests
+ * and clears its workspace; it has no use outside tests.
+ */
+int spec_verify_debug_tree_spin_limit(int polls);
 
 /*
  * Gather of the accepted rows (page "TensorRT-LLM source teardown (10)", KV

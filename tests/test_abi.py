@@ -38,6 +38,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_tree_spin_limit_hook_sets_and_restores(lib):
+    """Host-only: the testing hook swaps the split walk's poll limit and a
+    negative value restores the default (2^20 polls)."""
+    hook = lib.spec_verify_debug_tree_spin_limit
+    assert hook(7) == 1 << 20
+    assert hook(-1) == 7
+    assert hook(-5) == 1 << 20
+    assert hook(-1) == 1 << 20
+
+
 def test_version_and_status_strings(lib):
     assert lib.spec_verify_version() >= 100
     for code in range(6):

@@ -208,6 +208,41 @@ def test_split_walk_leaves_the_workspace_zero():
         assert int(torch.count_nonzero(ws)) == 0
 
 
+def test_split_walk_gives_up_cleanly_when_forced():
+    """The split walk's failure path, forced from the host: with the poll limit
+    of an exchange word at 0, the workgroups of a request give up waiting for
+    each other.  The kernel still ends; every request is either marked
+    num_accepted = -2 (at least one is) or, having given up on no exchange,
+    matches the oracle; and the workspace is zero afterwards.  With the default
+    limit back, the same workspace gives full parity again."""
+    from draft_token_verification_verify_amd import _lib
+    lib = _lib.load()
+    case = wl.stochastic_tree_case(3, 6, 60, 6, 128256, "bf16", target_sd=3.0, draft_noise_sd=1.0)
+    assert sv.spec_verify_tree_stochastic_split(case.B, case.V, _lib.BF16) == 8
+    n1 = case.node_tokens.shape[1]
+    ws = torch.zeros(sv.spec_verify_workspace_bytes(_lib.MODE_TREE_STOCHASTIC, case.B, n1, case.V,
+                                                    _lib.BF16), dtype=torch.uint8, device="cuda")
+    ref = oracle_tree_stochastic(case)
+    prev = lib.spec_verify_debug_tree_spin_limit(0)
+    try:
+        gpu = run_tree_stochastic(case, workspace=ws)
+    finally:
+        assert lib.spec_verify_debug_tree_spin_limit(-1) == 0
+    assert prev == 1 << 20
+    acc = gpu["num_accepted"]
+    assert np.all((acc == -2) | (acc >= 0)), acc
+    assert np.any(acc == -2), acc
+    amb = oracle.ambiguous_requests(ref["margins"], H.GUARD)
+    for b in np.nonzero((acc >= 0) & ~amb)[0]:
+        assert acc[b] == ref["num_accepted"][b], b
+        assert np.array_equal(gpu["out_tokens"][b], ref["out_tokens"][b]), b
+    assert int(torch.count_nonzero(ws)) == 0
+    gpu = run_tree_stochastic(case, workspace=ws)
+    assert np.all(gpu["num_accepted"] >= 0)
+    compare(gpu, ref, "after", case.rows)
+    assert int(torch.count_nonzero(ws)) == 0
+
+
 def test_split_walk_with_several_tiles_per_workgroup():
     """Enough requests over a 128256-token vocabulary (16 tiles per row) that
     fewer workgroups per request fit on the device than there are tiles, so
