@@ -114,10 +114,21 @@ __device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t ta
     return (uint32_t)v;
 }
 
+// A double's two words, polled together (both loads in flight at once, each
+// reloaded until it carries `tag`; bounded like ts_wait_word).
 __device__ inline double ts_get(const unsigned long long* w, uint32_t tag, const TsGroup& grp) {
-    const unsigned long long lo = ts_wait_word(&w[0], tag, grp);
-    const unsigned long long hi = ts_wait_word(&w[1], tag, grp);
-    return __longlong_as_double((long long)((hi << 32) | lo));
+    unsigned long long lo = load_coherent(&w[0]);
+    unsigned long long hi = load_coherent(&w[1]);
+    for (int spins = 0; (uint32_t)(lo >> 32) != tag || (uint32_t)(hi >> 32) != tag; ++spins) {
+        if (spins > grp.spin_limit) {
+            store_coherent(&grp.sy->failed, 1u);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        if ((uint32_t)(lo >> 32) != tag) lo = load_coherent(&w[0]);
+        if ((uint32_t)(hi >> 32) != tag) hi = load_coherent(&w[1]);
+    }
+    return __longlong_as_double((long long)(((hi & 0xffffffffull) << 32) | (lo & 0xffffffffull)));
 }
 
 struct TsLds {
