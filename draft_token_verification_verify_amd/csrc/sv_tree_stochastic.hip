@@ -26,6 +26,7 @@
 // results do not change between runs.
 #include <algorithm>
 #include <atomic>
+#include <cstddef>
 
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
@@ -56,7 +57,8 @@ constexpr int kTsSpinLimit = 1 << 20;          // polls of one exchange word bef
 struct TsSync {
     uint32_t exit;      // workgroups done; the last one clears the area
     uint32_t failed;    // an exchange gave up waiting
-    uint32_t pad[2];
+    uint32_t ticket;    // request 0's area only: arrival tickets of the whole call
+    uint32_t done;      // request 0's area only: workgroups of the call finished
     unsigned long long stat[2][kTsMaxSplit * 4][2];  // (target max, mass, draft max, mass) per workgroup
     unsigned long long tile[2][kTsTiles][2];         // weight-pass tile sums, by the tiles' owners
     unsigned long long token[2];                     // the final draw's token, by its tile's owner
@@ -583,10 +585,27 @@ __device__ int ts_draw_in_tile(const T* trow, const T* drow, int V, const Dist& 
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochArgs a) {
     __shared__ TsLds L;
-    const int b = blockIdx.x / a.G, N = a.N, V = a.V, Lp = a.L;
+    const int N = a.N, V = a.V, Lp = a.L;
+    // A split walk's groups are formed by arrival, not by workgroup id: the
+    // t-th workgroup to start takes request t / G as its member t % G.  Only
+    // the group holding the latest tickets can then be incomplete, so at most
+    // G - 1 workgroups of a call ever wait for one not yet placed, whatever
+    // else shares the device (two split walks on two streams included).
+    TsSync* const area0 = reinterpret_cast<TsSync*>(a.sync);
+    int ticket = blockIdx.x;
+    if (a.G > 1) {
+        if (threadIdx.x == 0) L.red_i = (int)atomicAdd(&area0->ticket, 1u);
+        __syncthreads();
+        ticket = L.red_i;
+        __syncthreads();  // red_i is reused by the draw
+        // A workspace that was not zero before the call (a broken
+        // precondition) could hand out tickets past the grid: stay in bounds.
+        if ((unsigned)ticket >= (unsigned)(a.B * a.G)) ticket = blockIdx.x;
+    }
+    const int b = ticket / a.G;
     TsGroup grp;
     grp.G = a.G;
-    grp.g = blockIdx.x % a.G;
+    grp.g = ticket % a.G;
     grp.sy = a.G > 1 ? reinterpret_cast<TsSync*>(a.sync + (size_t)b * kTreeSyncBytes) : nullptr;
     grp.round = 0;
     grp.spin_limit = a.spin_limit;
@@ -717,7 +736,16 @@ __global__ __launch_bounds__(kTsThreads) void tree_stochastic_kernel(TreeStochAr
                         __threadfence();
                         if (load_coherent(&grp.sy->failed)) a.num_accepted[b] = -2;
                         uint32_t* w = reinterpret_cast<uint32_t*>(grp.sy);
-                        for (size_t i = 0; i < sizeof(TsSync) / 4; ++i) store_coherent(&w[i], 0u);
+                        constexpr size_t kTicket = offsetof(TsSync, ticket) / 4;
+                        constexpr size_t kDone = offsetof(TsSync, done) / 4;
+                        for (size_t i = 0; i < sizeof(TsSync) / 4; ++i)
+                            if (i != kTicket && i != kDone) store_coherent(&w[i], 0u);
+                    }
+                    // The call's last workgroup (every ticket taken by then)
+                    // clears the call's counters.
+                    if (atomicAdd(&area0->done, 1u) == (uint32_t)(a.B * grp.G) - 1u) {
+                        store_coherent(&area0->ticket, 0u);
+                        store_coherent(&area0->done, 0u);
                     }
                 }
             }

@@ -385,12 +385,13 @@ int spec_verify_tree(const void *target_logits, int dtype, const int32_t *node_t
  *                  except where a decision lies within rounding of its
  *                  boundary (the row statistics are merged in a different
  *                  order).  Calls sharing a workspace must be ordered on one
- *                  stream.  The split walk's workgroups wait on each other: a
- *                  kernel that holds compute units for good on another stream
- *                  can keep some from starting, and every wait is bounded, so
- *                  num_accepted[b] = -2 then marks a request whose walk gave
- *                  up waiting for one of its workgroups (its outputs are not
- *                  valid).
+ *                  stream; calls with their own workspaces may run at once on
+ *                  several streams.  A request's workgroups wait on each other
+ *                  and are grouped by arrival, so only a kernel that holds
+ *                  compute units for good on another stream can keep one from
+ *                  starting; every wait is bounded, and num_accepted[b] = -2
+ *                  then marks a request whose walk gave up waiting for one of
+ *                  its workgroups (its outputs are not valid).
  */
 int spec_verify_tree_stochastic(const void *target_logits, const void *draft_logits, int dtype,
                                 const int32_t *node_tokens, const int32_t *paths,

@@ -243,6 +243,45 @@ def test_split_walk_gives_up_cleanly_when_forced():
     assert int(torch.count_nonzero(ws)) == 0
 
 
+def test_split_walks_on_two_streams_at_once():
+    """Two split walks launched at once on two streams, each with its own
+    workspace and each large enough to fill the device on its own.  A walk's
+    groups are formed by arrival, so neither waits for workgroups that the
+    other keeps from starting: both end without giving up and match the
+    oracle, and both workspaces are zero afterwards."""
+    from draft_token_verification_verify_amd import _lib
+    V = 65536  # 8 tiles per row
+    full = [b for b in range(1, 129) if sv.spec_verify_tree_stochastic_split(b, V, _lib.BF16) == 8]
+    if not full or max(full) > 64:
+        pytest.skip("device capacity outside the range this test sizes for")
+    B = max(full)  # B * 8 workgroups: the most the device holds at once
+    cases = [wl.stochastic_tree_case(s, B, 30, 5, V, "bf16", target_sd=3.0, draft_noise_sd=1.0)
+             for s in (21, 22)]
+    dev = torch.device("cuda", 0)
+    streams = [torch.cuda.Stream(device=dev) for _ in cases]
+    inputs, outs, spaces = [], [], []
+    for case in cases:
+        inputs.append((wl.to_device(case.target, case.dtype), wl.to_device(case.draft, case.dtype),
+                       wl.to_device(case.node_tokens.astype(np.int32)),
+                       wl.to_device(case.paths.astype(np.int32)),
+                       wl.to_device(case.uniforms.astype(np.float32))))
+        spaces.append(torch.zeros(sv.spec_verify_workspace_bytes(
+            _lib.MODE_TREE_STOCHASTIC, B, case.node_tokens.shape[1], V, _lib.BF16),
+            dtype=torch.uint8, device=dev))
+    torch.cuda.synchronize()
+    for case, (t, d, nt, pa, u), ws, st in zip(cases, inputs, spaces, streams):
+        with torch.cuda.stream(st):
+            outs.append(sv.spec_verify_tree_stochastic(t, d, nt, pa, u, case.temperature,
+                                                       workspace=ws))
+    torch.cuda.synchronize()
+    for case, (out, acc, nodes), ws in zip(cases, outs, spaces):
+        gpu = dict(out_tokens=out.cpu().numpy(), num_accepted=acc.cpu().numpy(),
+                   accepted_nodes=nodes.cpu().numpy())
+        assert np.all(gpu["num_accepted"] >= 0)
+        compare(gpu, oracle_tree_stochastic(case), "two-streams", case.rows)
+        assert int(torch.count_nonzero(ws)) == 0
+
+
 def test_split_walk_with_several_tiles_per_workgroup():
     """Enough requests over a 128256-token vocabulary (16 tiles per row) that
     fewer workgroups per request fit on the device than there are tiles, so
