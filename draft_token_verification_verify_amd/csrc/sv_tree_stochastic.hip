@@ -844,9 +844,9 @@ static hipError_t launch_tree(TreeStochArgs a, const TreeStochCall& c, hipStream
         // A plain launch: the grid is at most the device's resident capacity,
         // so on a device running nothing else every workgroup is resident at
         // once.  (hipLaunchCooperativeKernel gives the same guarantee but
-        // costs about 18 us more per call.)  Beside other kernels, workgroups
-        // still waiting for a slot are placed as those kernels' workgroups
-        // finish; every wait is bounded in any case.
+        // costs about 18 us more per call.)  Beside other work, groups formed
+        // by arrival (in the kernel) leave at most G - 1 workgroups waiting
+        // for one not yet placed; every wait is bounded in any case.
         hipExtLaunchKernelGGL(tree_stochastic_kernel<T, VEC>, dim3((unsigned)(c.B * G)),
                               dim3(kTsThreads), 0, st, ev.begin, ev.end, 0, a);
         return hipGetLastError();
