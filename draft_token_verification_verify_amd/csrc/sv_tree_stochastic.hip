@@ -59,7 +59,9 @@ struct TsSync {
     uint32_t failed;    // an exchange gave up waiting
     uint32_t ticket;    // request 0's area only: arrival tickets of the whole call
     uint32_t done;      // request 0's area only: workgroups of the call finished
-    unsigned long long stat[2][kTsMaxSplit * 4][2];  // (target max, mass, draft max, mass) per workgroup
+    // per workgroup, six words: target max, target mass (two words), draft
+    // max, draft mass (two words); a max is an fp32, so one word carries it
+    unsigned long long stat[2][kTsMaxSplit * 6];
     unsigned long long tile[2][kTsTiles][2];         // weight-pass tile sums, by the tiles' owners
     unsigned long long token[2];                     // the final draw's token, by its tile's owner
 };
@@ -118,6 +120,10 @@ __device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t ta
 
 // A double's two words, polled together (both loads in flight at once, each
 // reloaded until it carries `tag`; bounded like ts_wait_word).
+__device__ inline void ts_put_float(unsigned long long* w, float v, uint32_t tag) {
+    store_coherent(w, ((unsigned long long)tag << 32) | (unsigned long long)__float_as_uint(v));
+}
+
 __device__ inline double ts_get(const unsigned long long* w, uint32_t tag, const TsGroup& grp) {
     unsigned long long lo = load_coherent(&w[0]);
     unsigned long long hi = load_coherent(&w[1]);
@@ -139,7 +145,7 @@ struct TsLds {
     double inv_z[kMaxRejections];  // reciprocal residual masses at the current node
     double tile_sum[kTsTiles];
     double wsum[kTsTiles][kTsWaves];  // per-wave sums of each tile of a weight pass
-    double xstat[kTsMaxSplit * 4];    // the group's row statistics, as exchanged
+    uint32_t xw[kTsMaxSplit * 6];     // the group's row statistics, as exchanged (payloads)
     double xterm[2 * kTsMaxSplit];    // their masses at the common maximum
     // Per child of the current node, loaded once per node: the target and
     // draft logits at its token, its uniform and its token.
@@ -335,29 +341,37 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
     }
     ts_merge(rt, rd, both, sc, L, st, sd);
     if (grp.G > 1) {
-        unsigned long long(*slot)[2] = grp.sy->stat[grp.round & 1];
+        unsigned long long* slot = grp.sy->stat[grp.round & 1];
         const uint32_t tag = ts_tag(grp);
         if (threadIdx.x == 0) {
-            ts_put(slot[grp.g * 4 + 0], (double)st->m, tag);
-            ts_put(slot[grp.g * 4 + 1], st->s, tag);
-            ts_put(slot[grp.g * 4 + 2], both ? (double)sd->m : 0.0, tag);
-            ts_put(slot[grp.g * 4 + 3], both ? sd->s : 0.0, tag);
+            unsigned long long* mine = slot + grp.g * 6;
+            ts_put_float(&mine[0], st->m, tag);
+            ts_put(&mine[1], st->s, tag);
+            ts_put_float(&mine[3], both ? sd->m : 0.f, tag);
+            ts_put(&mine[4], both ? sd->s : 0.0, tag);
         }
-        if ((int)threadIdx.x < grp.G * 4) L.xstat[threadIdx.x] = ts_get(slot[threadIdx.x], tag, grp);
+        if ((int)threadIdx.x < grp.G * 6) L.xw[threadIdx.x] = ts_wait_word(&slot[threadIdx.x], tag, grp);
         __syncthreads();
+        // Workgroup w's max and mass of one side, from the exchanged payloads.
+        auto xmax = [&](int w, int side) { return __uint_as_float(L.xw[w * 6 + 3 * side]); };
+        auto xmass = [&](int w, int side) {
+            const int i = w * 6 + 3 * side + 1;
+            return __longlong_as_double(
+                (long long)(((unsigned long long)L.xw[i + 1] << 32) | L.xw[i]));
+        };
         // Each workgroup's mass rescaled to the common maximum: one thread per
         // (side, workgroup), then summed in workgroup order by every thread.
         float M[2];
         for (int side = 0; side < 2; ++side) {
             M[side] = -INFINITY;
-            for (int w = 0; w < grp.G; ++w) M[side] = fmaxf(M[side], (float)L.xstat[w * 4 + 2 * side]);
+            for (int w = 0; w < grp.G; ++w) M[side] = fmaxf(M[side], xmax(w, side));
         }
         if ((int)threadIdx.x < 2 * grp.G) {
             const int side = threadIdx.x / grp.G, w = threadIdx.x % grp.G;
-            const float mw = (float)L.xstat[w * 4 + 2 * side];
+            const float mw = xmax(w, side);
             L.xterm[threadIdx.x] = (mw == -INFINITY || M[side] == -INFINITY)
                                        ? 0.0
-                                       : L.xstat[w * 4 + 2 * side + 1] *
+                                       : xmass(w, side) *
                                              ts_exp2(mw, M[side], sc.c64 * 256.0, L.exp_tab);
         }
         __syncthreads();
@@ -368,7 +382,7 @@ __device__ void ts_row_stats(const T* trow, const T* drow, bool both, int V, con
             out.m = M[side];
             out.s = S;
         }
-        __syncthreads();  // xstat and xterm are read before the next exchange refills them
+        __syncthreads();  // xw and xterm are read before the next exchange refills them
         ++grp.round;
     }
 }
