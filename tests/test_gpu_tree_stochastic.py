@@ -190,6 +190,21 @@ def test_tree_stochastic_parity_one_workgroup(name, make):
     compare(gpu, oracle_tree_stochastic(case), name + "-1wg", case.rows)
 
 
+def test_benchmarked_workload_full_size():
+    """The stochastic-tree workload the benchmark times, at its full size and in
+    its launch configuration: B=32 trees of 60 nodes, depth 6, V=128256 bf16,
+    each request's walk split over 8 workgroups; every request against the
+    oracle."""
+    from draft_token_verification_verify_amd import _lib
+    case = wl.stochastic_tree_case(0, 32, 60, 6, 128256, "bf16", target_sd=3.0,
+                                   draft_noise_sd=1.0)
+    assert sv.spec_verify_tree_stochastic_split(case.B, case.V, _lib.BF16) == 8
+    gpu = run_tree_stochastic(case)
+    assert np.all(gpu["num_accepted"] >= 0)
+    amb = compare(gpu, oracle_tree_stochastic(case), "c5-shape-B32", case.rows)
+    print(f"c5-shape-B32: {amb} ambiguous requests")
+
+
 def test_split_walk_leaves_the_workspace_zero():
     """Split walks of two shapes in a row through one workspace: the exchange
     areas are cleared by each call's last workgroup (and no request gave up
