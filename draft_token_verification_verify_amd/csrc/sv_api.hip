@@ -27,6 +27,10 @@ bool vec_ok(const void* p, int V, int eb) {
                             ((size_t)V * (size_t)eb) % 16 == 0);
 }
 
+// A workspace holds 8- and 16-byte words (counters, partials, exchange
+// words): it must be 256-byte aligned, as every device allocation is.
+bool ws_aligned(const void* p) { return reinterpret_cast<uintptr_t>(p) % 256 == 0; }
+
 int finish(hipError_t e) { return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_HIP_ERROR; }
 
 // Profiling hook state (see spec_verify_profile_events).
@@ -109,7 +113,7 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     if (!(temperature >= SPEC_VERIFY_MIN_TEMPERATURE) ||
         !(temperature <= SPEC_VERIFY_MAX_TEMPERATURE))
         return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (!target_logits || !out_tokens || !num_accepted || !workspace)
+    if (!target_logits || !out_tokens || !num_accepted || !workspace || !ws_aligned(workspace))
         return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!counter_uniforms && !uniforms) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;
@@ -208,7 +212,7 @@ int spec_verify_greedy_ragged(const void* target_logits, int dtype, const int32_
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (!target_logits || !out_tokens || !num_accepted || !workspace)
+    if (!target_logits || !out_tokens || !num_accepted || !workspace || !ws_aligned(workspace))
         return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && !draft_tokens) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
@@ -248,7 +252,8 @@ int spec_verify_tree(const void* target_logits, int dtype, const int32_t* node_t
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || N < 0 || P < 0 || L < 1 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (!target_logits || !node_tokens || !out_tokens || !num_accepted || !workspace)
+    if (!target_logits || !node_tokens || !out_tokens || !num_accepted || !workspace ||
+        !ws_aligned(workspace))
         return SPEC_VERIFY_INVALID_ARGUMENT;
     if (P > 0 && !paths) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (N + 1 > SPEC_VERIFY_MAX_TREE_ROWS || P > SPEC_VERIFY_MAX_PATHS ||
@@ -292,7 +297,7 @@ int spec_verify_tree_stochastic(const void* target_logits, const void* draft_log
         !(temperature <= SPEC_VERIFY_MAX_TEMPERATURE))
         return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!target_logits || !draft_logits || !node_tokens || !uniforms || !out_tokens ||
-        !num_accepted)
+        !num_accepted || (workspace && !ws_aligned(workspace)))
         return SPEC_VERIFY_INVALID_ARGUMENT;
     if (P > 0 && !paths) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (N + 1 > SPEC_VERIFY_MAX_TREE_ROWS || P > SPEC_VERIFY_MAX_PATHS ||

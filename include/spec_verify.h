@@ -108,7 +108,9 @@ const char *spec_verify_status_string(int status);
  * of it zero-filled again when it completes, so one workspace serves any
  * number of later calls of any mode and shape whose size fits, provided calls
  * that share it are ordered on one stream.  (A call cut short by a device
- * fault leaves it undefined: zero it again.)
+ * fault leaves it undefined: zero it again.)  Its address must be 256-byte
+ * aligned, as hipMalloc's and torch's allocations are; calls reject any other
+ * with SPEC_VERIFY_INVALID_ARGUMENT.
  */
 size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype);
 

@@ -12,6 +12,7 @@ from draft_token_verification_verify_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "spec_verify.h")
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p(0x1008)  # 8-byte but not 256-byte aligned
 
 
 @pytest.fixture(scope="module")
@@ -117,6 +118,16 @@ def stoch(lib, **kw):
 ])
 def test_stochastic_rejects(lib, kw, code):
     assert stoch(lib, **kw) == code
+
+
+def test_misaligned_workspace_is_rejected(lib):
+    """Every call that takes a workspace rejects one that is not 256-byte
+    aligned on the host (nothing is launched)."""
+    assert stoch(lib, ws=MISALIGNED) == _lib.INVALID_ARGUMENT
+    assert filtered(lib, ws=MISALIGNED) == _lib.INVALID_ARGUMENT
+    assert greedy(lib, ws=MISALIGNED) == _lib.INVALID_ARGUMENT
+    assert tree(lib, ws=MISALIGNED) == _lib.INVALID_ARGUMENT
+    assert tree_stoch(lib, ws=MISALIGNED, wsb=1 << 30) == _lib.INVALID_ARGUMENT
 
 
 def test_stochastic_k0_needs_no_draft_pointers_but_checks_workspace(lib):
