@@ -23,6 +23,7 @@ __all__ = [
     "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
     "spec_verify_stochastic_filtered", "spec_verify_greedy", "spec_verify_greedy_ragged",
     "spec_verify_tree", "spec_verify_tree_stochastic", "spec_verify_tree_stochastic_split",
+    "check_tree_stochastic_result", "GAVE_UP",
     "spec_verify_gather_rows",
     "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
@@ -78,35 +79,43 @@ def spec_verify_workspace_bytes(mode: int, B: int, rows_per_request: int, V: int
 
 
 class Workspace:
-    """Grow-only, zero-initialised device workspace, one buffer per device.
+    """Grow-only, zero-initialised device workspaces, one buffer per (device,
+    stream).
 
     The library leaves its counters at zero after every completed call, so one
-    buffer serves every later call that is ordered on the same stream.
+    buffer serves every later call ordered on the same stream; calls on other
+    streams get buffers of their own (two calls racing on one buffer would give
+    wrong results).  Each buffer is allocated on the stream that uses it, so when
+    it grows, torch's allocator does not hand the old memory to other work until
+    that stream's pending calls have run.
     """
 
     def __init__(self):
-        self._buf: dict[torch.device, torch.Tensor] = {}
+        self._buf: dict[tuple[torch.device, int], torch.Tensor] = {}
 
-    def get(self, nbytes: int, device: torch.device) -> torch.Tensor:
-        buf = self._buf.get(device)
+    def get(self, nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
+        s = torch.cuda.current_stream(device) if stream is None else stream
+        key = (device, s.cuda_stream)
+        buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
-            # torch.zeros clears with a fill kernel (no memset node).
-            buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
-            self._buf[device] = buf
+            with torch.cuda.stream(s):
+                # torch.zeros clears with a fill kernel (no memset node).
+                buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+            self._buf[key] = buf
         return buf
 
 
 _default_workspace = Workspace()
 
 
-def _workspace(ws, nbytes: int, device: torch.device) -> torch.Tensor:
+def _workspace(ws, nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
     if nbytes == 0:
         raise SpecVerifyError("spec_verify_workspace_bytes", _lib.INVALID_ARGUMENT,
                               "shape rejected by the library")
     if ws is None:
-        return _default_workspace.get(nbytes, device)
+        return _default_workspace.get(nbytes, device, stream)
     if isinstance(ws, Workspace):
-        return ws.get(nbytes, device)
+        return ws.get(nbytes, device, stream)
     _dev(ws, "workspace", device, torch.uint8)
     if ws.numel() < nbytes:
         raise SpecVerifyError("workspace", _lib.WORKSPACE_TOO_SMALL,
@@ -147,7 +156,7 @@ def _stochastic(fn, target_logits, draft_logits, draft_tokens, draft_lens, unifo
     if filtered and (workspace is None or isinstance(workspace, Workspace)):
         # room for the filter candidates (a caller's own tensor may be either size)
         nbytes = spec_verify_workspace_bytes(MODE_STOCHASTIC_FILTERED, B, k + 1, V, dt)
-    ws = _workspace(workspace, nbytes, device)
+    ws = _workspace(workspace, nbytes, device, stream)
     lib = _lib.load()
     head = (_ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens))
     tail = (_ptr(uniforms), float(temperature), B, k, V, _ptr(out_tokens), _ptr(num_accepted),
@@ -246,7 +255,7 @@ def _greedy(fn, target_logits, draft_tokens, draft_lens, out_tokens, num_accepte
     _dev(out_tokens, "out_tokens", device, torch.int32, (B, k + 1))
     _dev(num_accepted, "num_accepted", device, torch.int32, (B,))
     nbytes = spec_verify_workspace_bytes(MODE_GREEDY, B, k + 1, V, dt)
-    ws = _workspace(workspace, nbytes, device)
+    ws = _workspace(workspace, nbytes, device, stream)
     lib = _lib.load()
     tail = (B, k, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(ws), ws.numel(),
             _stream(device, stream))
@@ -297,7 +306,7 @@ def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,
             t = torch.empty(shape, dtype=torch.int32, device=device)
         outs.append(_dev(t, name, device, torch.int32, shape))
     nbytes = spec_verify_workspace_bytes(MODE_TREE, B, N1, V, dt)
-    ws = _workspace(workspace, nbytes, device)
+    ws = _workspace(workspace, nbytes, device, stream)
     st = _lib.load().spec_verify_tree(
         _ptr(target_logits), dt, _ptr(node_tokens), _ptr(paths), B, N1 - 1, P, L, V,
         _ptr(outs[0]), _ptr(outs[1]), _ptr(outs[2]), _ptr(outs[3]), _ptr(ws), ws.numel(),
@@ -306,18 +315,38 @@ def spec_verify_tree(target_logits: torch.Tensor, node_tokens: torch.Tensor,
     return tuple(outs)
 
 
+GAVE_UP = -2  # num_accepted of a stochastic tree request whose split walk gave up waiting
+
+
+def check_tree_stochastic_result(num_accepted: torch.Tensor) -> None:
+    """Raise SpecVerifyError if a request of a stochastic tree call is marked as
+    given up (num_accepted == -2: its workgroups stopped waiting for one another
+    and its outputs are not valid).  Reads the tensor (synchronises with its
+    stream when it lives on the GPU)."""
+    bad = (num_accepted == GAVE_UP).nonzero().flatten().tolist()
+    if bad:
+        raise SpecVerifyError("spec_verify_tree_stochastic", _lib.HIP_ERROR,
+                              f"the split walk of request(s) {bad[:8]} gave up waiting for "
+                              "its workgroups (outputs not valid)")
+
+
 def spec_verify_tree_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tensor,
                                 node_tokens: torch.Tensor, paths: torch.Tensor,
                                 uniforms: torch.Tensor, temperature: float, *, out_tokens=None,
                                 num_accepted=None, accepted_nodes=None, workspace=None,
-                                split=True, stream=None):
+                                split=True, stream=None, check=True):
     """Stochastic tree verification (each accepted node's children tested in
     ascending order against the residual of their rejected siblings); returns
     ``(out_tokens[B,L], num_accepted[B], accepted_nodes[B,L])``.  ``uniforms``
     is float32 [B, N+1]: entry c-1 drives node c's test, entry N the final draw.
     With ``split`` (and a workspace, allocated here when not given) each
     request's walk may be shared by several workgroups; ``split=False`` passes
-    no workspace (one workgroup per request)."""
+    no workspace (one workgroup per request).
+
+    With ``check`` (the default) the call waits for its result and raises
+    SpecVerifyError when a request's walk gave up (num_accepted == -2); a caller
+    that reads num_accepted itself may pass ``check=False`` to stay
+    asynchronous and call ``check_tree_stochastic_result`` when it does."""
     device = target_logits.device
     dt = _dtype_code(target_logits)
     if target_logits.dim() != 3 or paths.dim() != 3:
@@ -339,12 +368,14 @@ def spec_verify_tree_stochastic(target_logits: torch.Tensor, draft_logits: torch
     ws = None
     if split:
         ws = _workspace(workspace, spec_verify_workspace_bytes(MODE_TREE_STOCHASTIC, B, N1, V, dt),
-                        device)
+                        device, stream)
     st = _lib.load().spec_verify_tree_stochastic(
         _ptr(target_logits), _ptr(draft_logits), dt, _ptr(node_tokens), _ptr(paths),
         _ptr(uniforms), float(temperature), B, N1 - 1, P, L, V, _ptr(outs[0]), _ptr(outs[1]),
         _ptr(outs[2]), _ptr(ws), 0 if ws is None else ws.numel(), _stream(device, stream))
     _lib.check("spec_verify_tree_stochastic", st)
+    if check:
+        check_tree_stochastic_result(outs[1])
     return tuple(outs)
 
 

@@ -101,17 +101,26 @@ __device__ inline void ts_put(unsigned long long* w, double v, uint32_t tag) {
     store_coherent(&w[1], ((unsigned long long)tag << 32) | (bits >> 32));
 }
 
-// Poll one tagged word until it carries `tag` (bounded: after the group's
-// spin limit of polls the request is marked failed and the word taken as it
-// is).
+// Whether a poll gives up: past the group's spin limit (the request is then
+// marked failed), or once another workgroup of the group has given up (checked
+// every 32 polls).  After a first give-up the group's members take different
+// paths and later tags never match: without the second test every later wait
+// would run to the full limit.
+__device__ inline bool ts_give_up(int spins, const TsGroup& grp) {
+    if (spins > grp.spin_limit) {
+        store_coherent(&grp.sy->failed, 1u);
+        return true;
+    }
+    return (spins & 31) == 31 && load_coherent(&grp.sy->failed) != 0u;
+}
+
+// Poll one tagged word until it carries `tag` (bounded by ts_give_up; the word
+// is then taken as it is).
 __device__ inline uint32_t ts_wait_word(const unsigned long long* w, uint32_t tag,
                                         const TsGroup& grp) {
     unsigned long long v = load_coherent(w);
     for (int spins = 0; (uint32_t)(v >> 32) != tag; ++spins) {
-        if (spins > grp.spin_limit) {
-            store_coherent(&grp.sy->failed, 1u);
-            break;
-        }
+        if (ts_give_up(spins, grp)) break;
         __builtin_amdgcn_s_sleep(2);
         v = load_coherent(w);
     }
@@ -128,10 +137,7 @@ __device__ inline double ts_get(const unsigned long long* w, uint32_t tag, const
     unsigned long long lo = load_coherent(&w[0]);
     unsigned long long hi = load_coherent(&w[1]);
     for (int spins = 0; (uint32_t)(lo >> 32) != tag || (uint32_t)(hi >> 32) != tag; ++spins) {
-        if (spins > grp.spin_limit) {
-            store_coherent(&grp.sy->failed, 1u);
-            break;
-        }
+        if (ts_give_up(spins, grp)) break;
         __builtin_amdgcn_s_sleep(2);
         if ((uint32_t)(lo >> 32) != tag) lo = load_coherent(&w[0]);
         if ((uint32_t)(hi >> 32) != tag) hi = load_coherent(&w[1]);

@@ -695,6 +695,161 @@ def check_filtered_output_distribution(lib, trials: int = 400_000):
     assert chi2_stat(np.bincount(r["out_tokens"][:, 0], minlength=V), pf) < CHI2_DF7_P001
 
 
+# ---- guard band: the margins that classify a request as ambiguous --------------
+#
+# A request is ambiguous when a decision it actually took lies within 1e-6 of
+# its boundary: test i at u_i against min(1, P/Q) (the strict test
+# u < min(1, p(x)/q(x)) of "02. Speculative Decoding", section 2), the final
+# draw at u*Z against the nearer edge of the chosen token's CDF interval,
+# relative to Z.  The values below come from hand-built rows whose P/Q is
+# known in closed form, and from searchsorted over library cumulative sums.
+
+def _exact_rows():
+    """One target row p = (1/4, 3/4, 0, 0) and draft rows q = (1, 0, 0, 0) and
+    q' = (1/8, 7/8, 0, 0): P/Q = 1/4 for token 0 under q, P/Q = 6/7 for token 1
+    under q', P >= Q for token 1 under q."""
+    t = np.array([0.0, np.log(3.0), -np.inf, -np.inf], np.float32)
+    q = np.array([0.0, -np.inf, -np.inf, -np.inf], np.float32)
+    q2 = np.array([0.0, np.log(7.0), -np.inf, -np.inf], np.float32)
+    p = lib_softmax(t)
+    return t, q, q2, p
+
+
+def check_accept_margin(lib):
+    """margin[i] = |u - min(1, P/Q)| for the test actually taken: u = P/Q +- delta
+    for several delta (P/Q from the library softmax of the float32 rows), u
+    against 1 when P >= Q, and +inf past the stop row."""
+    t, q, q2, p = _exact_rows()
+    pq = lib_softmax(q)
+    pq2 = lib_softmax(q2)
+    cases = [(q, 0, p[0] / pq[0]), (q2, 1, p[1] / pq2[1]), (q, 1, 1.0)]  # (draft, token, threshold)
+    for draft, token, thr in cases:
+        for delta in (0.25e-1, -0.125, 3e-6, -2e-6, 7e-7, -4e-7):
+            u0 = np.float32(min(max(thr + delta, 0.0), 0.99999994))
+            tt = np.stack([t, t])[None]  # k = 1: row 0 tested, row 1 bonus
+            r = oracle.stochastic(tt, draft[None, None], np.array([[token]], np.int32),
+                                  np.array([[u0, 0.5]], np.float32), 1.0, lib=lib)
+            want = abs(float(u0) - min(1.0, thr))
+            assert abs(r["margins"][0, 0] - want) < 1e-12, (token, delta, r["margins"][0, 0], want)
+    # past the stop row: +inf (k = 2, test 0 rejects with u near 1)
+    tt = np.stack([t, t, t])[None]
+    dd = np.stack([q, q])[None]
+    r = oracle.stochastic(tt, dd, np.array([[0, 0]], np.int32),
+                          np.array([[0.9, 0.1, 0.5]], np.float32), 1.0, lib=lib)
+    assert r["num_accepted"][0] == 0 and np.isinf(r["margins"][0, 1])
+
+
+def check_final_margin(lib):
+    """margin[k] = distance from u*Z to the nearest CDF edge divided by Z, from
+    searchsorted over library cumulative sums: residual draws (Z < 1, so the
+    division matters) on rows with zero weights, and bonus draws."""
+    rng = np.random.default_rng(81)
+    B, V = 400, 12
+    tl = rng.normal(0, 1.0, (B, 2, V)).astype(np.float32)
+    dl = rng.normal(0, 1.0, (B, 1, V)).astype(np.float32)
+    tl[:, :, 0] = -np.inf  # token 0 never has weight
+    tl[rng.random((B, 2, V)) < 0.2] = -np.inf
+    tl[:, :, 1] = 0.5      # every row keeps a finite logit
+    x = rng.integers(0, V, (B, 1)).astype(np.int32)
+    u = rng.random((B, 2), dtype=np.float32)
+    r = oracle.stochastic(tl, dl, x, u, 1.0, lib=lib)
+    p = lib_softmax(tl)
+    q = lib_softmax(dl)
+    n_res = 0
+    for b in range(B):
+        s = int(r["num_accepted"][b])
+        if s == 0:
+            w = np.maximum(p[b, 0] - q[b, 0], 0.0)
+            if not w.sum() > 0:
+                continue
+            n_res += 1
+        else:
+            w = p[b, 1]
+        j, dist = lib_inverse_cdf(w, float(u[b, 1]))
+        assert abs(r["margins"][b, 1] - dist) < 1e-9 * max(1.0, dist), (b, s)
+        if dist > 1e-9:
+            assert r["out_tokens"][b, s] == j, b
+    assert n_res > 50
+
+
+def check_top_p_margin(lib):
+    """filter_margins of a top-p row: the distance of the target top_p * mass1
+    from the nearer cumulative edge of the group it falls in, divided by mass1
+    (the mass of the top-k survivors), from a sort of the library softmax."""
+    base = np.log(np.array([0.35, 0.25, 0.2, 0.12, 0.08])).astype(np.float32)
+    p = lib_softmax(base)
+    for top_k, top_p in ((0, 0.5), (0, 0.83), (3, 0.7), (4, 0.95), (3, 0.4)):
+        keep = np.arange(5) < (top_k if top_k else 5)
+        mass1 = p[keep].sum()
+        cum = np.concatenate([[0.0], np.cumsum(p[keep])])
+        target = float(np.float32(top_p)) * mass1
+        g = int(np.searchsorted(cum, target, side="left"))  # first edge >= target
+        want = min(target - cum[g - 1], cum[g] - target) / mass1
+        r = oracle.stochastic(base[None, None], None, np.zeros((1, 0), np.int32),
+                              np.array([[0.3]], np.float32), 1.0, top_k=top_k,
+                              top_p=float(np.float32(top_p)), lib=lib)
+        assert abs(r["filter_margins"][0] - want) < 1e-12, (top_k, top_p,
+                                                            r["filter_margins"][0], want)
+
+
+def check_min_p_margin(lib):
+    """filter_margins of a min-p row: the smallest |x - (max x + T ln(min_p))| over
+    the row's logits (absolute, logit units), at two temperatures."""
+    rng = np.random.default_rng(83)
+    for T, min_p in ((1.0, 0.5), (0.7, 0.05)):
+        x = rng.normal(0, 1.0, 9).astype(np.float32)
+        x[0] = np.float32(2.0)
+        tmin = 2.0 + T * np.log(np.float32(min_p), dtype=np.float64)
+        x[4] = np.float32(tmin + 3e-3)  # one logit a known distance above the threshold
+        want = float(np.min(np.abs(x.astype(np.float64) - tmin)))
+        assert want <= 3.1e-3
+        r = oracle.stochastic(x[None, None], None, np.zeros((1, 0), np.int32),
+                              np.array([[0.3]], np.float32), T, min_p=float(np.float32(min_p)),
+                              lib=lib)
+        assert abs(r["filter_margins"][0] - want) < 1e-12, (T, r["filter_margins"][0], want)
+
+
+def check_ambiguous_requests(lib, fn=None):
+    """The classifier: a request is ambiguous iff its smallest decision margin is
+    strictly below the band (or, for filtered calls, its filter margin below the
+    filter band); +inf margins (decisions not taken) never count."""
+    fn = fn or oracle.ambiguous_requests
+    inf = np.inf
+    margins = np.array([[inf, 5e-7, inf],   # one decision inside the band
+                        [2e-6, 3e-6, inf],  # all outside
+                        [1e-6, inf, 4e-6],  # exactly on the band: outside (strict)
+                        [inf, inf, inf],    # no decision taken
+                        [0.0, 0.5, 0.5]])   # a decision on its boundary
+    np.testing.assert_array_equal(fn(margins, 1e-6), [True, False, False, False, True])
+    fm = np.array([inf, 1e-10, 1e-9, 2.0, inf])
+    np.testing.assert_array_equal(fn(margins, 1e-6, fm, 1e-9), [True, True, False, False, True])
+    del lib
+
+
+def check_tree_sibling_margins(lib):
+    """Stochastic tree margins: the first child's test against min(1, p/q), the
+    second sibling's against min(1, r/q) with r the normalised residual (library
+    softmax), the final draw's from searchsorted over the second residual."""
+    V = 4
+    tl = np.log(np.array([[0.4, 0.1, 0.3, 0.2]] + [[0.25] * V] * 2)).astype(np.float32)
+    dl = np.log(np.array([[0.1, 0.5, 0.25, 0.15]] + [[0.25] * V] * 2)).astype(np.float32)
+    p = lib_softmax(tl[0])
+    q = lib_softmax(dl[0])
+    res = np.maximum(p - q, 0.0)
+    res /= res.sum()
+    res2 = np.maximum(res - q, 0.0)
+    thr1, thr2 = p[1] / q[1], res[2] / q[2]
+    paths = np.array([[[0, 1], [0, 2]]], np.int32)
+    tok = np.array([[0, 1, 2]], np.int32)
+    u = np.array([[0.999, min(thr2 * 1.01, 0.999), 0.6]], np.float32)
+    r = oracle.tree_stochastic(tl[None], dl[None], tok, paths, u, 1.0, lib=lib)
+    assert r["num_accepted"][0] == 0
+    assert abs(r["margins"][0, 0] - abs(float(u[0, 0]) - thr1)) < 1e-12
+    assert abs(r["margins"][0, 1] - abs(float(u[0, 1]) - thr2)) < 1e-12
+    _, dist = lib_inverse_cdf(res2, float(u[0, 2]))
+    assert abs(r["margins"][0, 2] - dist) < 1e-12
+
+
 # ---- stochastic tree ----------------------------------------------------------
 
 def _chain_paths(B, k, P=3):
@@ -852,4 +1007,10 @@ ALL_CHECKS = [
     check_tree_stochastic_output_distribution,
     check_tree_stochastic_identical_draft,
     check_gather_rows_example,
+    check_accept_margin,
+    check_final_margin,
+    check_top_p_margin,
+    check_min_p_margin,
+    check_ambiguous_requests,
+    check_tree_sibling_margins,
 ]

@@ -7,6 +7,8 @@ below 1e-4 of the rows; p(x_i) and q(x_i) within 1e-5 relative.  The ambiguous
 count itself is reported, not bounded: with V ~ 10^5 CDF edges a 1e-6 band
 around each edge covers a few percent of [0, 1) on heavy-tailed rows.
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -112,11 +114,16 @@ def test_c3_disagreements_over_many_seeds():
     assert tot_dis <= 1e-4 * tot_rows
 
 
-def test_c4_full_size_sampled_requests():
-    """B=256, k=5, V=151936 fp32 on the GPU; the oracle checks 40 sampled requests."""
-    case = wl.c4(0)
-    rows = np.sort(np.random.default_rng(5).choice(case.B, 40, replace=False))
-    check(case, rows)
+@functools.lru_cache(maxsize=2)
+def _c4(seed):
+    return wl.c4(seed)  # 1.7 GB of logits: generated once per seed for both schedules
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_c4_full_size(seed):
+    """B=256, k=5, V=151936 fp32 (the low-acceptance workload): every request
+    checked against the oracle."""
+    check(_c4(seed))
 
 
 def test_identical_draft_accepts_everything():

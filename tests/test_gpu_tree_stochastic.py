@@ -22,14 +22,15 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-def run_tree_stochastic(case, split=True, workspace=None):
+def run_tree_stochastic(case, split=True, workspace=None, check=True):
     t = wl.to_device(case.target, case.dtype)
     d = wl.to_device(case.draft, case.dtype)
     nt = wl.to_device(case.node_tokens.astype(np.int32))
     pa = wl.to_device(case.paths.astype(np.int32))
     u = wl.to_device(case.uniforms.astype(np.float32))
     out, acc, nodes = sv.spec_verify_tree_stochastic(t, d, nt, pa, u, case.temperature,
-                                                     split=split, workspace=workspace)
+                                                     split=split, workspace=workspace,
+                                                     check=check)
     torch.cuda.synchronize()
     return dict(out_tokens=out.cpu().numpy(), num_accepted=acc.cpu().numpy(),
                 accepted_nodes=nodes.cpu().numpy())
@@ -240,11 +241,14 @@ def test_split_walk_gives_up_cleanly_when_forced():
     ref = oracle_tree_stochastic(case)
     prev = lib.spec_verify_debug_tree_spin_limit(0)
     try:
-        gpu = run_tree_stochastic(case, workspace=ws)
+        gpu = run_tree_stochastic(case, workspace=ws, check=False)
     finally:
         assert lib.spec_verify_debug_tree_spin_limit(-1) == 0
     assert prev == 1 << 20
     acc = gpu["num_accepted"]
+    # the binding's check reports the given-up requests
+    with pytest.raises(sv.SpecVerifyError, match="gave up"):
+        sv.check_tree_stochastic_result(torch.from_numpy(acc))
     assert np.all((acc == -2) | (acc >= 0)), acc
     assert np.any(acc == -2), acc
     amb = oracle.ambiguous_requests(ref["margins"], H.GUARD)

@@ -6,8 +6,10 @@ index, a dropped term); it is compiled into a temporary library and every pin
 in ``oracle_pins`` runs against it until one fails.  A mutant that passes every
 pin means the pins are too weak to notice that mistake.
 """
+import inspect
 import os
 
+import numpy as np
 import pytest
 
 import oracle
@@ -65,6 +67,33 @@ MUTANTS = {
     "philox words swapped": ("    ctr[1] = lo1;\n", "    ctr[1] = lo0;\n"),
     "philox nine rounds": ("for (int round = 0; round < 10; ++round)", "for (int round = 0; round < 9; ++round)"),
     "philox uniform low bits": ("(block[i % 4] >> 40)", "(block[i % 4] & 0xFFFFFF)"),
+    # guard band: the margins that classify requests as ambiguous
+    "final margin not divided by Z": ("*margin = (lo < hi ? lo : hi) / Z;",
+                                      "*margin = (lo < hi ? lo : hi);"),
+    "accept margin without the min": ("double threshold = (P >= Q) ? 1.0 : P / Q;",
+                                      "double threshold = P / Q;"),
+    "accept margin at the final uniform": (
+        "margin[i] = in_range ? fabs((double)u[i] - threshold) : INFINITY;",
+        "margin[i] = in_range ? fabs((double)u[k] - threshold) : INFINITY;"),
+    "top-p margin not relative to the survivors": ("double m = (lo < hi ? lo : hi) / mass1;",
+                                                   "double m = (lo < hi ? lo : hi);"),
+    "min-p margin from the maximum": (
+        "double d = fabs(logit_at(logits, dtype, row_offset + (size_t)j) - tmin);",
+        "double d = fabs(logit_at(logits, dtype, row_offset + (size_t)j) - xmax);"),
+    "tree margin without the min": ("double threshold = (P_ >= Q_) ? 1.0 : P_ / Q_;",
+                                    "double threshold = P_ / Q_;"),
+    "tree final margin from p": ("out[depth] = inverse_cdf(rejected ? w : p, V, (double)u[N], &final_margin);",
+                                 "out[depth] = inverse_cdf(rejected ? w : p, V, (double)u[N], &final_margin);\n                if (rejected) inverse_cdf(p, V, (double)u[N], &final_margin);"),
+}
+
+# Planted mistakes in the oracle's Python classifier of ambiguous requests.
+PY_MUTANTS = {
+    "ambiguous takes the largest margin": ("amb = np.min(margins, axis=1) < band",
+                                           "amb = np.max(margins, axis=1) < band"),
+    "ambiguous band inclusive": ("amb = np.min(margins, axis=1) < band",
+                                 "amb = np.min(margins, axis=1) <= band"),
+    "filter band ignored": ("amb |= np.asarray(filter_margins) < filter_band",
+                            "amb |= np.asarray(filter_margins) < 0.0"),
 }
 
 
@@ -88,3 +117,14 @@ def test_mutant_is_caught(name, source, tmp_path):
         except AssertionError:
             return  # caught
     pytest.fail(f"planted mistake {name!r} passed every oracle pin")
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS))
+def test_classifier_mutant_is_caught(name):
+    old, new = PY_MUTANTS[name]
+    src = inspect.getsource(oracle.ambiguous_requests)
+    assert src.count(old) == 1, f"mutation anchor for {name!r} not found exactly once"
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    with pytest.raises(AssertionError):
+        oracle_pins.check_ambiguous_requests(None, fn=ns["ambiguous_requests"])
