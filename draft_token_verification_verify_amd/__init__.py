@@ -23,7 +23,7 @@ __all__ = [
     "spec_verify_stochastic", "spec_verify_stochastic_ragged", "spec_verify_stochastic_philox",
     "spec_verify_stochastic_filtered", "spec_verify_greedy", "spec_verify_greedy_ragged",
     "spec_verify_tree", "spec_verify_tree_stochastic", "spec_verify_tree_stochastic_split",
-    "check_tree_stochastic_result", "GAVE_UP",
+    "check_tree_stochastic_result", "GAVE_UP", "spec_verify_stochastic_noalloc",
     "spec_verify_gather_rows",
     "spec_verify_set_schedule",
     "spec_verify_workspace_bytes", "spec_verify_version", "Workspace", "SpecVerifyError",
@@ -187,6 +187,41 @@ def spec_verify_stochastic(target_logits: torch.Tensor, draft_logits: torch.Tens
     return _stochastic("spec_verify_stochastic", target_logits, draft_logits, draft_tokens, None,
                        uniforms, temperature, out_tokens, num_accepted, p_at_draft, q_at_draft,
                        workspace, stream)
+
+
+def spec_verify_stochastic_noalloc(target_logits: torch.Tensor,
+                                   draft_logits: torch.Tensor | None,
+                                   draft_tokens: torch.Tensor | None, uniforms: torch.Tensor,
+                                   temperature: float, *, out_tokens, num_accepted,
+                                   p_at_draft=None, q_at_draft=None, stream=None):
+    """spec_verify_stochastic on the library's fixed per-GPU scratch array instead of a
+    workspace: the call allocates nothing (the caller passes the outputs).  Calls
+    that overlap in time on one GPU race on that array; shapes whose workspace
+    exceeds ``_lib.NOALLOC_SCRATCH_BYTES`` raise (LIMIT_EXCEEDED)."""
+    device = target_logits.device
+    dt = _dtype_code(target_logits)
+    if target_logits.dim() != 3:
+        raise ValueError("target_logits must be [B, k+1, V]")
+    B, k1, V = target_logits.shape
+    k = k1 - 1
+    _dev(target_logits, "target_logits", device)
+    if k > 0:
+        _dev(draft_logits, "draft_logits", device, target_logits.dtype, (B, k, V))
+        _dev(draft_tokens, "draft_tokens", device, torch.int32, (B, k))
+    else:
+        draft_logits = draft_tokens = None
+    _dev(uniforms, "uniforms", device, torch.float32, (B, k + 1))
+    _dev(out_tokens, "out_tokens", device, torch.int32, (B, k + 1))
+    _dev(num_accepted, "num_accepted", device, torch.int32, (B,))
+    for name, t in (("p_at_draft", p_at_draft), ("q_at_draft", q_at_draft)):
+        if t is not None:
+            _dev(t, name, device, torch.float32, (B, k))
+    st = _lib.load().spec_verify_stochastic_noalloc(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(uniforms),
+        float(temperature), B, k, V, _ptr(out_tokens), _ptr(num_accepted), _ptr(p_at_draft),
+        _ptr(q_at_draft), _stream(device, stream))
+    _lib.check("spec_verify_stochastic_noalloc", st)
+    return out_tokens, num_accepted
 
 
 def spec_verify_stochastic_ragged(target_logits: torch.Tensor, draft_logits: torch.Tensor | None,

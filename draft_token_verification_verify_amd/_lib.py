@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libspec_verify.so")
 F32, BF16 = 0, 1
 MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE, MODE_STOCHASTIC_FILTERED, MODE_TREE_STOCHASTIC = range(5)
 OK, INVALID_ARGUMENT, UNSUPPORTED_DTYPE, WORKSPACE_TOO_SMALL, LIMIT_EXCEEDED, HIP_ERROR = range(6)
+NOALLOC_SCRATCH_BYTES = 8 << 20  # SPEC_VERIFY_NOALLOC_SCRATCH_BYTES
 SCHEDULE_AUTO, SCHEDULE_TWO_KERNELS, SCHEDULE_SELF_COMPUTE = 0, 1, 2
 
 EXPORTED = (
@@ -22,6 +23,7 @@ EXPORTED = (
     "spec_verify_set_schedule",
     "spec_verify_stochastic",
     "spec_verify_stochastic_ragged",
+    "spec_verify_stochastic_noalloc",
     "spec_verify_stochastic_philox",
     "spec_verify_stochastic_filtered",
     "spec_verify_greedy",
@@ -71,6 +73,9 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_stochastic_ragged.argtypes = [P, P, I, P, P, P, ctypes.c_float, I, I, I, P,
                                                   P, P, P, P, Z, P]
     lib.spec_verify_stochastic_ragged.restype = I
+    lib.spec_verify_stochastic_noalloc.argtypes = [P, P, I, P, P, ctypes.c_float, I, I, I, P, P,
+                                                   P, P, P]
+    lib.spec_verify_stochastic_noalloc.restype = I
     U64 = ctypes.c_uint64
     lib.spec_verify_stochastic_philox.argtypes = [P, P, I, P, P, U64, U64, ctypes.c_float, I, I,
                                                   I, P, P, P, P, P, Z, P]

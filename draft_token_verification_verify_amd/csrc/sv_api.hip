@@ -9,9 +9,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "spec_verify.h"
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
+
+// Workspace of spec_verify_stochastic_noalloc: a fixed device array, one copy
+// per GPU (each device that loads the library holds its own), kept until the
+// process ends.  Host code never passes the array's name to a kernel or a copy:
+// it looks up each device's address once (hipGetSymbolAddress) and uses that.
+static __device__ __align__(256) unsigned char scratch[SPEC_VERIFY_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -32,6 +40,30 @@ bool vec_ok(const void* p, int V, int eb) {
 bool ws_aligned(const void* p) { return reinterpret_cast<uintptr_t>(p) % 256 == 0; }
 
 int finish(hipError_t e) { return e == hipSuccess ? SPEC_VERIFY_OK : SPEC_VERIFY_HIP_ERROR; }
+
+constexpr size_t kNoAllocBytes = SPEC_VERIFY_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch`: on the first call per device its
+// address is looked up and the array zero-filled by a fill kernel on `st`
+// (ordered before the call that follows on the same stream).
+int noalloc_scratch(hipStream_t st, void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return SPEC_VERIFY_HIP_ERROR;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return SPEC_VERIFY_HIP_ERROR;
+        if (sv::run_fill_zero(p, kNoAllocBytes, st) != hipSuccess) return SPEC_VERIFY_HIP_ERROR;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return SPEC_VERIFY_OK;
+}
 
 // Profiling hook state (see spec_verify_profile_events).
 void* const* g_events = nullptr;
@@ -106,15 +138,17 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
                            uint64_t offset, float temperature, int B, int k, int V,
                            int32_t* out_tokens, int32_t* num_accepted, float* p_at_draft,
                            float* q_at_draft, void* workspace, size_t workspace_bytes,
-                           void* stream, const sv::FilterCall* filter = nullptr) {
+                           void* stream, const sv::FilterCall* filter = nullptr,
+                           bool noalloc = false) {
     const int eb = elem_bytes_of(dtype);
     if (eb == 0) return SPEC_VERIFY_UNSUPPORTED_DTYPE;
     if (B < 1 || k < 0 || V < 1) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!(temperature >= SPEC_VERIFY_MIN_TEMPERATURE) ||
         !(temperature <= SPEC_VERIFY_MAX_TEMPERATURE))
         return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (!target_logits || !out_tokens || !num_accepted || !workspace || !ws_aligned(workspace))
+    if (!target_logits || !out_tokens || !num_accepted)
         return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!noalloc && (!workspace || !ws_aligned(workspace))) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!counter_uniforms && !uniforms) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
@@ -123,6 +157,13 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     if (!sv::make_geometry(0, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
     if ((long long)B * g.R * g.S > 0x7fffffffLL || (long long)B * g.S2 > 0x7fffffffLL)
         return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (noalloc) {
+        // Every check above ran first: a rejected call launches nothing.
+        if (g.bytes > kNoAllocBytes) return SPEC_VERIFY_LIMIT_EXCEEDED;
+        const int st = noalloc_scratch((hipStream_t)stream, &workspace);
+        if (st != SPEC_VERIFY_OK) return st;
+        workspace_bytes = kNoAllocBytes;
+    }
     if (workspace_bytes < g.bytes) return SPEC_VERIFY_WORKSPACE_TOO_SMALL;
     if (filter) {  // room for the filter candidates: the same layout plus their buffer
         sv::Geometry g3;
@@ -192,6 +233,16 @@ int spec_verify_stochastic(const void* target_logits, const void* draft_logits, 
     return stochastic_impl(target_logits, draft_logits, dtype, draft_tokens, nullptr, uniforms,
                            false, 0, 0, temperature, B, k, V, out_tokens, num_accepted,
                            p_at_draft, q_at_draft, workspace, workspace_bytes, stream);
+}
+
+int spec_verify_stochastic_noalloc(const void* target_logits, const void* draft_logits,
+                                   int dtype, const int32_t* draft_tokens, const float* uniforms,
+                                   float temperature, int B, int k, int V, int32_t* out_tokens,
+                                   int32_t* num_accepted, float* p_at_draft, float* q_at_draft,
+                                   void* stream) {
+    return stochastic_impl(target_logits, draft_logits, dtype, draft_tokens, nullptr, uniforms,
+                           false, 0, 0, temperature, B, k, V, out_tokens, num_accepted,
+                           p_at_draft, q_at_draft, nullptr, 0, stream, nullptr, true);
 }
 
 int spec_verify_stochastic_philox(const void* target_logits, const void* draft_logits, int dtype,

@@ -201,6 +201,31 @@ int spec_verify_stochastic(const void *target_logits, const void *draft_logits, 
                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * spec_verify_stochastic without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Arguments, outputs and results are those
+ * of spec_verify_stochastic; the workspace is a fixed array of
+ * SPEC_VERIFY_NOALLOC_SCRATCH_BYTES in the library's device memory, one per
+ * GPU, held until the process ends.  The call allocates and frees nothing.
+ *
+ *   - A shape whose workspace (spec_verify_workspace_bytes of MODE_STOCHASTIC)
+ *     exceeds SPEC_VERIFY_NOALLOC_SCRATCH_BYTES is rejected on the host with
+ *     SPEC_VERIFY_LIMIT_EXCEEDED; nothing is launched.
+ *   - The array belongs to the current device; `stream` must belong to it too.
+ *     The first call on a device looks up the array's address and zero-fills
+ *     it with a fill kernel on `stream`; every completed call leaves it zero.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in time
+ *     on one GPU (several streams, several host threads) race on it and give
+ *     undefined results.  Order them on one stream.
+ */
+#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int spec_verify_stochastic_noalloc(const void *target_logits, const void *draft_logits,
+                                   int dtype, const int32_t *draft_tokens,
+                                   const float *uniforms, float temperature, int B, int k,
+                                   int V, int32_t *out_tokens, int32_t *num_accepted,
+                                   float *p_at_draft, float *q_at_draft, void *stream);
+
+/*
  * Stochastic verification with a draft length per request (page "TensorRT-LLM
  * source teardown (10)", acceptance pipeline, step 2: ragged verification,
  * every request verified over its own window while buffers stay padded to the

@@ -289,3 +289,40 @@ def test_ragged_entry_points_validate_like_the_dense_ones(lib):
               None) == _lib.INVALID_ARGUMENT
     assert gr(FAKE, _lib.F32, FAKE, FAKE, 2, 100, 100, FAKE, FAKE, FAKE, 1 << 30,
               None) == _lib.LIMIT_EXCEEDED
+
+
+def noalloc(lib, **kw):
+    a = dict(t=FAKE, d=FAKE, dtype=_lib.BF16, x=FAKE, u=FAKE, T=1.0, B=2, k=3, V=100,
+             out=FAKE, acc=FAKE, p=None, q=None, stream=None)
+    a.update(kw)
+    return lib.spec_verify_stochastic_noalloc(a["t"], a["d"], a["dtype"], a["x"], a["u"], a["T"],
+                                              a["B"], a["k"], a["V"], a["out"], a["acc"], a["p"],
+                                              a["q"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=5), _lib.UNSUPPORTED_DTYPE),
+    (dict(B=0), _lib.INVALID_ARGUMENT),
+    (dict(T=0.0), _lib.INVALID_ARGUMENT),
+    (dict(t=None), _lib.INVALID_ARGUMENT),
+    (dict(u=None), _lib.INVALID_ARGUMENT),
+    (dict(out=None), _lib.INVALID_ARGUMENT),
+    (dict(d=None), _lib.INVALID_ARGUMENT),
+    (dict(k=65), _lib.LIMIT_EXCEEDED),
+    # a shape whose workspace exceeds the fixed scratch array is refused
+    (dict(B=512, k=5, V=151936, dtype=_lib.F32), _lib.LIMIT_EXCEEDED),
+])
+def test_noalloc_rejects_on_the_host(lib, kw, code):
+    """The allocation-free call runs every host check of spec_verify_stochastic,
+    plus the scratch size, before it touches the device (nothing runs here)."""
+    assert noalloc(lib, **kw) == code
+
+
+def test_noalloc_limit_matches_the_header(lib):
+    need = lib.spec_verify_workspace_bytes(_lib.MODE_STOCHASTIC, 512, 6, 151936, _lib.F32)
+    assert need > _lib.NOALLOC_SCRATCH_BYTES
+    # the largest benchmarked stochastic shape (B=256, k=5, V=151936 fp32) fits
+    assert lib.spec_verify_workspace_bytes(_lib.MODE_STOCHASTIC, 256, 6, 151936,
+                                           _lib.F32) <= _lib.NOALLOC_SCRATCH_BYTES
+    with open(os.path.join(ROOT, "include", "spec_verify.h")) as f:
+        assert "#define SPEC_VERIFY_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)" in f.read()
