@@ -8,11 +8,14 @@ statistics + accept/reject + residual/bonus sampling) on inputs already resident
 in device memory.  Inputs rotate over enough copies (>= 1 GiB in total) that the
 256 MB last-level cache cannot serve a step from the previous one.
 
-Prints ONE JSON line: throughput in verified rows/s (B * (k+1) per step), the
-roofline of the streaming kernel (algorithmic bytes = one read of each logits
-tensor, over that kernel's own start/end event timestamps in a second run of the
-timed steps), and the CPU oracle's rate on a bounded sample of the same
-workload.
+Prints ONE JSON line: throughput in verified rows/s (B * (k+1) per step); the
+roofline of the call's dominant kernel (for the plain stochastic call, the
+one-launch kernel that is the whole call), as algorithmic bytes (one read of each
+logits tensor) over that kernel's own start/end event timestamps in a second run
+of the timed steps, with the whole call's fraction beside it; and the CPU
+oracle on the same workload (one host thread, then one thread per core), which
+also reports how many of the step's requests it finds ambiguous and how many
+differ from the GPU's.
 """
 from __future__ import annotations
 
@@ -54,6 +57,12 @@ def parse():
                     help="stochastic workloads: min-p filter of every row (0: off)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--bare-read", action="store_true",
+                    help="only time plain reads of the workload's logits bytes: the library's "
+                         "argmax stream and torch's amax over the same bytes (the streaming "
+                         "ceiling of this box)")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the parallel oracle leg (0: the host's core count)")
     return ap.parse_args()
 
 
@@ -164,7 +173,8 @@ def make_step(case, sets, filt=None):
             s = sets[i % len(sets)]
             sv.spec_verify_tree_stochastic(s["target"], s["draft"], s["node_tokens"], s["paths"],
                                            s["uniforms"], case.temperature, out_tokens=out,
-                                           num_accepted=acc, accepted_nodes=nodes, workspace=ws)
+                                           num_accepted=acc, accepted_nodes=nodes, workspace=ws,
+                                           check=False)
         step.nodes = nodes
         return step, out, acc
     out = torch.empty((case.B, case.L), dtype=torch.int32, device=dev)
@@ -258,7 +268,7 @@ def tree_walk_bytes(case, nodes, acc) -> int:
 def load_traffic(workload: str, src_hash: str):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were
     taken on the current kernel sources; else None."""
-    path = os.path.join(PROFILES, f"streaming_kernel_{workload}_pmc.json")
+    path = os.path.join(PROFILES, f"dominant_kernel_{workload}_pmc.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -268,40 +278,104 @@ def load_traffic(workload: str, src_hash: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(case, seconds: float, filt=None):
-    """The oracle (single-threaded fp64 C) on whole requests of the same workload
-    until about `seconds` of CPU time has been spent."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_one(case, b, fkw):
+    """The oracle on request b alone (one ctypes call: it releases the GIL)."""
+    import oracle
+
+    sl = slice(b, b + 1)
+    mode = mode_of(case)
+    if mode == "stochastic":
+        return oracle.stochastic(case.target[sl], case.draft[sl] if case.k > 0 else None,
+                                 case.draft_tokens[sl], case.uniforms[sl], case.temperature, **fkw)
+    if mode == "greedy":
+        return oracle.greedy(case.target[sl], case.draft_tokens[sl])
+    if mode == "tree-stochastic":
+        return oracle.tree_stochastic(case.target[sl], case.draft[sl], case.node_tokens[sl],
+                                      case.paths[sl], case.uniforms[sl], case.temperature)
+    return oracle.tree(case.target[sl], case.node_tokens[sl], case.paths[sl])
+
+
+def cpu_baseline(case, seconds: float, gpu_out, gpu_acc, threads: int, filt=None):
+    """The oracle (fp64 C, one request per call) on the same workload: one host
+    thread for about `seconds`, then `threads` host threads (one request per
+    call, calls in parallel) for about the same time.  The oracle's outputs on
+    every request of the step are also compared with the GPU's (the stochastic
+    modes count the requests the oracle finds ambiguous and those that differ)."""
+    import concurrent.futures as cf
+
     import numpy as np
 
     import oracle
 
     fkw = {} if filt is None else dict(top_k=filt[0], top_p=float(np.float32(filt[1])),
                                        min_p=float(np.float32(filt[2])))
-    mode = mode_of(case)
-    done = 0
+    rows_per_req = case.rows // case.B
+    # one thread
+    done, times = 0, []
     t0 = time.perf_counter()
     while True:
-        b = done % case.B
-        sl = slice(b, b + 1)
-        if mode == "stochastic":
-            oracle.stochastic(case.target[sl], case.draft[sl] if case.k > 0 else None,
-                              case.draft_tokens[sl], case.uniforms[sl], case.temperature, **fkw)
-        elif mode == "greedy":
-            oracle.greedy(case.target[sl], case.draft_tokens[sl])
-        elif mode == "tree-stochastic":
-            oracle.tree_stochastic(case.target[sl], case.draft[sl], case.node_tokens[sl],
-                                   case.paths[sl], case.uniforms[sl], case.temperature)
-        else:
-            oracle.tree(case.target[sl], case.node_tokens[sl], case.paths[sl])
+        t1 = time.perf_counter()
+        _oracle_one(case, done % case.B, fkw)
+        times.append(time.perf_counter() - t1)
         done += 1
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    rows_per_req = case.rows // case.B
-    return dict(value=done * rows_per_req / el, unit="rows/s", cores=1, kind="oracle",
-                sample=f"{done} requests of {case.name} (seed {case.meta.get('seed')})"
-                       f"{'' if filt is None else ' with filters ' + str(fkw)}, "
-                       f"one request per call, {el:.1f} s on one host thread")
+    single = done * rows_per_req / el
+    # `threads` threads, about the same time
+    n_par = max(threads * int(round(done / el * seconds / max(threads, 1))), threads)
+    n_par = max(n_par, threads)
+    with cf.ThreadPoolExecutor(max_workers=threads) as ex:
+        t0 = time.perf_counter()
+        list(ex.map(lambda i: _oracle_one(case, i % case.B, fkw), range(n_par)))
+        el_par = time.perf_counter() - t0
+    parallel = n_par * rows_per_req / el_par
+    out = dict(value=single, unit="rows/s", cores=1, kind="oracle",
+               sample=f"{done} requests of {case.name} (seed {case.meta.get('seed')})"
+                      f"{'' if filt is None else ' with filters ' + str(fkw)}, "
+                      f"one request per call, {el:.1f} s on one host thread",
+               per_request_ms_p10_p50_p90=[float(np.percentile(times, q)) * 1e3
+                                           for q in (10, 50, 90)],
+               parallel={"value": parallel, "unit": "rows/s", "cores": threads,
+                         "sample": f"{n_par} requests, {threads} host threads (one request "
+                                   f"per call), {el_par:.1f} s"},
+               host_cpu=cpu_model(), host_threads_available=os.cpu_count())
+    # parity over the step's requests (every request of the workload)
+    mode = mode_of(case)
+    if mode in ("stochastic", "tree-stochastic"):
+        if mode == "stochastic":
+            ref = oracle.stochastic(case.target, case.draft if case.k > 0 else None,
+                                    case.draft_tokens, case.uniforms, case.temperature, **fkw)
+            amb = oracle.ambiguous_requests(ref["margins"], 1e-6,
+                                            ref.get("filter_margins") if filt else None, 1e-9)
+        else:
+            ref = oracle.tree_stochastic(case.target, case.draft, case.node_tokens, case.paths,
+                                         case.uniforms, case.temperature)
+            amb = oracle.ambiguous_requests(ref["margins"], 1e-6)
+    elif mode == "greedy":
+        ref = oracle.greedy(case.target, case.draft_tokens)
+        amb = np.zeros(case.B, bool)
+    else:
+        ref = oracle.tree(case.target, case.node_tokens, case.paths)
+        amb = np.zeros(case.B, bool)
+    same = (gpu_acc == ref["num_accepted"]) & np.all(gpu_out == ref["out_tokens"], axis=1)
+    out["parity"] = {"requests": int(case.B), "rows": int(case.rows),
+                     "ambiguous_requests": int(amb.sum()),
+                     "ambiguous_requests_differing": int((amb & ~same).sum()),
+                     "non_ambiguous_requests_differing": int((~amb & ~same).sum()),
+                     "guard_band": 1e-6}
+    return out
 
 
 def copy_probe():
@@ -317,6 +391,65 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 5}), flush=True)
 
 
+def bare_read(args):
+    """Plain reads of the workload's logits bytes, rotating over >= 1 GiB of
+    copies like the timed workload: the library's argmax stream over every
+    logits row (the tree call with no paths: one 16-byte-vector tile per
+    (row, chunk) with a max and an index per element, then a one-workgroup-per-
+    request epilogue), timed per call and, through the profiling hook, the
+    streaming kernel alone; and torch's amax over the same bytes."""
+    import numpy as np
+    import torch
+
+    import draft_token_verification_verify_amd as sv
+    from draft_token_verification_verify_amd import _lib
+
+    case = make_case(args.workload, args.seed)
+    nbytes = streaming_bytes(case)
+    dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+    esize = 2 if case.dtype == "bf16" else 4
+    V = case.V
+    rows = nbytes // (V * esize)
+    B = case.B
+    R = rows // B
+    copies = max(1, math.ceil((1 << 30) / nbytes))
+    bufs = [torch.randn(B, R, V, device="cuda").to(dt) for _ in range(copies)]
+    nt = torch.zeros((B, R), dtype=torch.int32, device="cuda")
+    paths = torch.zeros((B, 0, 1), dtype=torch.int32, device="cuda")
+    ws = sv.Workspace()
+    outs = [torch.empty((B, 1), dtype=torch.int32, device="cuda"),
+            torch.empty((B,), dtype=torch.int32, device="cuda")]
+
+    def stream(x):
+        sv.spec_verify_tree(x, nt, paths, out_tokens=outs[0], num_accepted=outs[1], workspace=ws)
+
+    res = {}
+    for name, fn in (("argmax_stream_call", stream), ("torch_amax", lambda x: torch.amax(x, dim=2))):
+        for i in range(args.warmup):
+            fn(bufs[i % copies])
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for i in range(args.steps):
+            evs[i][0].record()
+            fn(bufs[i % copies])
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+        res[name] = {"us_median": float(np.median(us)), "us_p10": float(np.percentile(us, 10)),
+                     "us_p90": float(np.percentile(us, 90)),
+                     "gbps_median": nbytes / (np.median(us) * 1e-6) / 1e9}
+    kms = time_streaming_kernel(lambda i: stream(bufs[i % copies]), args.steps, args.warmup)
+    us = np.array(kms) * 1e3
+    res["argmax_stream_kernel"] = {
+        "us_median": float(np.median(us)), "us_p10": float(np.percentile(us, 10)),
+        "us_p90": float(np.percentile(us, 90)),
+        "gbps_median": nbytes / (np.median(us) * 1e-6) / 1e9}
+    print(json.dumps({"bare_read_bytes": nbytes, "workload": case.name, "rows": int(rows),
+                      "copies": copies, "peak_gbps": HBM_PEAK_GBPS, **res}), flush=True)
+    del _lib
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -329,6 +462,9 @@ def main():
 
     if args.copy_probe:
         copy_probe()
+        return
+    if args.bare_read:
+        bare_read(args)
         return
 
     t_gen = time.perf_counter()
@@ -352,25 +488,24 @@ def main():
     from draft_token_verification_verify_amd import _lib
 
     ms = time_steps(step, args.steps, args.warmup)
-    one_launch_ms = None
-    if filt is not None:
-        # Statistics kernel, per-row filter selection, sampler; the events sit
-        # on the selection kernel, the call's longest (its algorithmic read is
-        # one pass over every row, like the statistics kernel's).
-        kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
-    elif mode_of(case) == "stochastic":
-        # The default schedule runs statistics and sampling in one launch; the
-        # streaming roofline is taken on the statistics kernel of the
-        # two-kernel schedule (same workload, same bytes), and the one-launch
-        # kernel's own duration is reported beside it.
-        one_launch_ms = time_streaming_kernel(step, args.steps, args.warmup)
+    # The dominant kernel of the timed call, timed on its own stream through the
+    # library's profiling hook (a second run of the same steps).
+    kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
+    plain = mode_of(case) == "stochastic" and filt is None
+    stats_pass = None
+    if plain:
+        # Beside it: the two-kernel schedule's first kernel (statistics and the
+        # per-request decisions, the algorithmic read), for reference.
         sv.spec_verify_set_schedule(_lib.SCHEDULE_TWO_KERNELS)
         try:
-            kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
+            two_ms = time_streaming_kernel(step, args.steps, args.warmup)
         finally:
             sv.spec_verify_set_schedule(_lib.SCHEDULE_AUTO)
-    else:
-        kernel_ms = time_streaming_kernel(step, args.steps, args.warmup)
+        stats_pass = {
+            "kernel": "sv::plain_tiles_kernel (two-kernel schedule: statistics and decisions)",
+            "us_mean": float(np.mean(two_ms)) * 1e3,
+            "achieved_gbps": nbytes / (float(np.mean(two_ms)) * 1e-3) / 1e9,
+        }
     k_avg = float(np.mean(kernel_ms))
     if mode_of(case) == "tree-stochastic":
         # the walk reads only the visited rows: the same outputs on every copy
@@ -380,6 +515,10 @@ def main():
     achieved = nbytes / (k_avg * 1e-3) / 1e9
     n_acc = acc.cpu().numpy()
     src_hash = source_hash()
+    kname = ("filter selection kernel (filtered call)" if filt is not None else
+             "one-launch kernel (statistics, decisions and sampling: the whole call)" if plain
+             else "tree walk kernel (each request's walk split over workgroups)"
+             if mode_of(case) == "tree-stochastic" else "argmax kernel")
     traffic = load_traffic(args.workload, src_hash) if filt is None else None
     wname = case.name if filt is None else (
         f"{case.name}-topk{args.top_k}-topp{args.top_p:g}-minp{args.min_p:g}")
@@ -414,34 +553,30 @@ def main():
                                         "min_p": args.min_p}),
         },
         "hbm_gbps_whole_call": nbytes / (ms * 1e-3) / 1e9,
+        "whole_call_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("filter selection kernel (filtered call)" if filt is not None else
-                       "statistics kernel (two-kernel schedule)" if mode_of(case) == "stochastic"
-                       else "tree walk kernel (each request's walk split over workgroups)"
-                       if mode_of(case) == "tree-stochastic" else "argmax kernel"),
+            "kernel": kname,
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": traffic,
             "kernel_us_mean": k_avg * 1e3,
-            "kernel_us_p10_p90": [float(np.percentile(kernel_ms, 10)) * 1e3,
-                                  float(np.percentile(kernel_ms, 90)) * 1e3],
+            "kernel_us_p10_p50_p90": [float(np.percentile(kernel_ms, q)) * 1e3
+                                      for q in (10, 50, 90)],
             "algorithmic_bytes_per_launch": nbytes,
             "source_hash": src_hash,
         },
-        "one_launch_kernel": None if one_launch_ms is None else {
-            "us_mean": float(np.mean(one_launch_ms)) * 1e3,
-            "algorithmic_gbps": nbytes / (float(np.mean(one_launch_ms)) * 1e-3) / 1e9,
-            "note": "default schedule: statistics and sampling in one kernel",
-        },
+        "statistics_pass": stats_pass,
         "num_accepted_histogram": np.bincount(n_acc, minlength=(rows // case.B)).tolist(),
         "acceptance_length": float(n_acc.mean() + 1.0),
     }
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle baseline", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, filt)
+        threads = args.cpu_threads or min(os.cpu_count() or 1, 16)
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds, out.cpu().numpy(), n_acc,
+                                            threads, filt)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)

@@ -106,6 +106,7 @@ size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V,
     if (!tree && rows_per_request - 1 > SPEC_VERIFY_MAX_K) return 0;
     if (tree && rows_per_request > SPEC_VERIFY_MAX_TREE_ROWS) return 0;
     if (mode == 4 && V > SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB) return 0;
+    if ((mode == 0 || mode == 3) && V > SPEC_VERIFY_MAX_STOCHASTIC_VOCAB) return 0;
     sv::Geometry g;
     if (!sv::make_geometry(mode, B, rows_per_request, V, eb, &g)) return 0;
     return g.bytes;
@@ -151,7 +152,8 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     if (!noalloc && (!workspace || !ws_aligned(workspace))) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (!counter_uniforms && !uniforms) return SPEC_VERIFY_INVALID_ARGUMENT;
     if (k > 0 && (!draft_logits || !draft_tokens)) return SPEC_VERIFY_INVALID_ARGUMENT;
-    if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_STOCHASTIC_VOCAB)
+        return SPEC_VERIFY_LIMIT_EXCEEDED;
     if (filter && V > SPEC_VERIFY_MAX_FILTER_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
     sv::Geometry g;
     if (!sv::make_geometry(0, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;

@@ -12,12 +12,18 @@
 // parent's row; the branch of paths[b, P, L] with the most nodes accepted from
 // the root down is kept (lowest path row on ties).
 //
-// Two kernels per call: one workgroup per (request, row, vocabulary chunk)
+// One kernel per call.  One workgroup per (request, row, vocabulary chunk)
 // streams its chunk once with 16-byte loads and reduces it to (max, lowest
-// index of the max); then one workgroup per request merges the chunks of every
-// row in chunk order and runs the mode's epilogue: the leading-match count
-// (greedy), or the path walk with the path table, the node tokens and the
-// argmax vector staged in LDS (tree).
+// index of the max), published as one tagged 64-bit word; these take no
+// atomics and wait for nothing.  After them in the grid, one workgroup per
+// request polls its request's words until all are published, merges them in
+// chunk order and runs the mode's epilogue: the leading-match count (greedy),
+// or the path walk with the path table, the node tokens and the argmax vector
+// staged in LDS (tree); it is the words' only reader and clears them.  Its
+// wait is bounded: past the bound it computes the missing rows' maxima itself
+// and marks the workspace stale (a word no call clears), since a late word may
+// then be left behind; from then on the epilogues of every call on that
+// workspace compute the maxima themselves, until the workspace is zeroed.
 #include <limits.h>
 
 #include "sv_common.hpp"
@@ -29,7 +35,9 @@ namespace sv {
 struct ArgmaxArgs {
     const void* target;
     int B, R, V, S, chunk;
-    Partial16* partials;  // [B, R, S]: f0 = chunk max, f1 = its lowest index (int bits)
+    Partial16* partials;  // [B, R, S]: word 0 = 2^63 | lowest index << 32 | bits(chunk max)
+    uint32_t* stale;      // nonzero: published words may be stale (see above)
+    int spin_limit;       // polls before an epilogue computes missing maxima itself
     // greedy
     const int32_t* draft_tokens;  // [B, k]
     const int32_t* lens;          // [B] draft length per request, or null (all k)
@@ -61,12 +69,13 @@ struct ArgmaxOp : ArgmaxArgs {
         publish(dst, -INFINITY, __int_as_float(INT_MAX), 0.0);
     }
 
-    __device__ void publish(Partial16* dst, float f0, float f1, double d) const {
-        Partial16 p;
-        p.f0 = f0;
-        p.f1 = f1;
-        p.d = d;
-        *dst = p;
+    // One 64-bit word per chunk, stored at once: the tag bit tells a published
+    // word from the cleared 0 (indices fit 31 bits).
+    __device__ void publish(Partial16* dst, float f0, float f1, double) const {
+        const unsigned long long w = (1ull << 63) |
+                                     ((unsigned long long)(unsigned)__float_as_int(f1) << 32) |
+                                     (unsigned long long)__float_as_uint(f0);
+        store_coherent(reinterpret_cast<unsigned long long*>(dst), w);
     }
 
     __device__ void finish(float v, int i, float* f0, float* f1, double* d) const {
@@ -138,27 +147,93 @@ struct ArgmaxOp : ArgmaxArgs {
     }
 
     __device__ int row_argmax(int b, int r) const {
-        const Partial16* p = partials + ((size_t)b * R + r) * S;
+        const unsigned long long* p =
+            reinterpret_cast<const unsigned long long*>(partials + ((size_t)b * R + r) * S);
         float v = -INFINITY;
         int i = INT_MAX;
-        for (int ch = 0; ch < S; ++ch)  // fixed chunk order
-            merge_argmax(v, i, p[ch].f0, __float_as_int(p[ch].f1));
+        for (int ch = 0; ch < S; ++ch) {  // fixed chunk order
+            const unsigned long long w = load_coherent(p + 2 * ch);
+            merge_argmax(v, i, __uint_as_float((unsigned)w), (int)((w >> 32) & 0x7fffffffu));
+        }
         return i;
     }
 
-    __device__ void epilogue(int b) const {
-        if constexpr (MODE == 1) greedy_epilogue(b);
-        else tree_epilogue(b);
+    // Argmax of row r of request b computed by this workgroup alone (any order
+    // gives the same maximum and lowest index).
+    __device__ int row_argmax_here(int b, int r) const {
+        const T* p = row(b, r);
+        float bv = -INFINITY;
+        int bi = INT_MAX;
+        for (int j = threadIdx.x; j < V; j += kThreads) {
+            const float x = Elem<T>::load(p, j);
+            if (x > bv || bi == INT_MAX) {
+                bv = x;
+                bi = j;
+            }
+        }
+        wave_reduce_argmax(bv, bi);
+        __shared__ float red_v[kWaves];
+        __shared__ int red_i[kWaves];
+        if ((threadIdx.x & 63) == 0) {
+            red_v[threadIdx.x >> 6] = bv;
+            red_i[threadIdx.x >> 6] = bi;
+        }
         __syncthreads();
-        clear_partials(partials + (size_t)b * R * S, R * S);  // workspace back to zero
+        bv = red_v[0];
+        bi = red_i[0];
+        for (int w = 1; w < kWaves; ++w) merge_argmax(bv, bi, red_v[w], red_i[w]);
+        __syncthreads();
+        return bi;
+    }
+
+    // The epilogue workgroup of request b: the argmax of rows 0 .. rows-1 (into
+    // sh_a), from the published words (all R * S of the request, skipped rows'
+    // too, are awaited, so none is published after they are cleared), or, past
+    // the poll limit or on a stale workspace, computed here.  Returns whether
+    // the words were used.
+    __device__ bool gather_argmax(int b, int rows, int* sh_a) const {
+        __shared__ int sh_ok;
+        const int n = R * S;
+        const unsigned long long* p =
+            reinterpret_cast<const unsigned long long*>(partials + (size_t)b * n);
+        if (threadIdx.x == 0) sh_ok = load_coherent(stale) == 0u;
+        __syncthreads();
+        bool use = sh_ok != 0;
+        for (int it = 0; use; ++it) {
+            int ok = 1;
+            for (int t = threadIdx.x; t < n; t += kThreads)
+                ok &= (load_coherent(p + 2 * t) >> 63) != 0ull;
+            if (__syncthreads_and(ok)) break;
+            if (it >= spin_limit) {
+                use = false;
+                if (threadIdx.x == 0) store_coherent(stale, 1u);
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (use) {
+            for (int r = threadIdx.x; r < rows; r += kThreads) sh_a[r] = row_argmax(b, r);
+        } else {
+            for (int r = 0; r < rows; ++r) {
+                const int i = row_argmax_here(b, r);
+                if (threadIdx.x == 0) sh_a[r] = i;
+            }
+        }
+        __syncthreads();
+        return use;
+    }
+
+    // After the epilogue: the request's words back to zero (this workgroup is
+    // their only reader), unless the workspace is stale.
+    __device__ void clear_words(int b, bool used) const {
+        __syncthreads();
+        if (used) clear_partials(partials + (size_t)b * R * S, R * S);
     }
 
     __device__ void greedy_epilogue(int b) const {
         __shared__ int sh_a[kMaxK + 1];
         __shared__ int sh_s;
         const int kb = kb_of(b);
-        for (int r = threadIdx.x; r <= kb; r += kThreads) sh_a[r] = row_argmax(b, r);
-        __syncthreads();
+        const bool used = gather_argmax(b, kb + 1, sh_a);
         if (threadIdx.x == 0) {
             int s = 0;
             while (s < kb && draft_tokens[(size_t)b * k + s] == sh_a[s]) ++s;
@@ -173,6 +248,7 @@ struct ArgmaxOp : ArgmaxArgs {
             else if (i == s) v = sh_a[s];
             out_tokens[(size_t)b * (k + 1) + i] = v;
         }
+        clear_words(b, used);
     }
 
     __device__ void tree_epilogue(int b) const {
@@ -180,10 +256,9 @@ struct ArgmaxOp : ArgmaxArgs {
         int* sh_a = dyn;              // [N+1] argmax of each node's row
         int* sh_tok = dyn + (N + 1);  // [N+1] node tokens
         int* sh_paths = dyn + 2 * (N + 1);
-        for (int n = threadIdx.x; n <= N; n += kThreads) {
-            sh_a[n] = row_argmax(b, n);
+        for (int n = threadIdx.x; n <= N; n += kThreads)
             sh_tok[n] = node_tokens[(size_t)b * (N + 1) + n];
-        }
+        const bool used = gather_argmax(b, N + 1, sh_a);
         const int32_t* gpaths = paths + (size_t)b * P * L;
         if (paths_in_lds)
             for (int q = threadIdx.x; q < P * L; q += kThreads) sh_paths[q] = gpaths[q];
@@ -250,59 +325,61 @@ struct ArgmaxOp : ArgmaxArgs {
             num_accepted[b] = m;
             if (best_path) best_path[b] = none ? -1 : best_p;
         }
+        clear_words(b, used);
     }
 };
+
+// Polls of an epilogue workgroup for one request's words before it computes
+// the maxima itself: far above any wait seen when workgroups are dispatched in
+// order.
+constexpr int kEpilogueSpin = 1 << 16;
 
 template <typename T, int U, bool VEC, int MODE>
 __global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxArgs a) {
     ArgmaxOp<T, U, MODE> op;
     static_cast<ArgmaxArgs&>(op) = a;
-    if constexpr (VEC) stream_tile_vec<T, U>(op);
-    else stream_tile_scalar<T>(op);
+    const int n_tiles = a.B * a.R * a.S;
+    if ((int)blockIdx.x < n_tiles) {
+        if constexpr (VEC) stream_tile_vec<T, U>(op, blockIdx.x);
+        else stream_tile_scalar<T>(op, blockIdx.x);
+        return;
+    }
+    const int b = (int)blockIdx.x - n_tiles;
+    if constexpr (MODE == 1) op.greedy_epilogue(b);
+    else op.tree_epilogue(b);
 }
 
-// One workgroup per request.  (T and U do not matter to the epilogue.)
-template <int MODE>
-__global__ __launch_bounds__(kThreads) void argmax_epilogue_kernel(ArgmaxArgs a) {
-    ArgmaxOp<float, 1, MODE> op;
-    static_cast<ArgmaxArgs&>(op) = a;
-    op.epilogue(blockIdx.x);
-}
-
+// One kernel: the streaming tiles, then one epilogue workgroup per request (the
+// profiling events, when set, take its start and end).  `lds` is the tree
+// epilogue's dynamic LDS.
 template <typename T, int U, bool VEC, int MODE>
-static hipError_t launch_argmax_u(const ArgmaxArgs& a, hipStream_t st, const KernelEvents& ev) {
-    const unsigned n_tiles = (unsigned)((long long)a.B * a.R * a.S);
-    // The events (when set) take the kernel's own start and end timestamps.
-    hipExtLaunchKernelGGL(argmax_kernel<T, U, VEC, MODE>, dim3(n_tiles), dim3(kThreads), 0, st,
+static hipError_t launch_argmax_u(const ArgmaxArgs& a, size_t lds, hipStream_t st,
+                                  const KernelEvents& ev) {
+    const unsigned grid = (unsigned)((long long)a.B * a.R * a.S + a.B);
+    hipExtLaunchKernelGGL(argmax_kernel<T, U, VEC, MODE>, dim3(grid), dim3(kThreads), lds, st,
                           ev.begin, ev.end, 0, a);
     return hipGetLastError();
 }
 
 template <typename T, bool VEC, int MODE>
-static hipError_t launch_argmax(const ArgmaxArgs& a, int U, hipStream_t st,
+static hipError_t launch_argmax(const ArgmaxArgs& a, int U, size_t lds, hipStream_t st,
                                 const KernelEvents& ev) {
     switch (U) {
-        case 8: return launch_argmax_u<T, 8, VEC, MODE>(a, st, ev);
-        case 4: return launch_argmax_u<T, 4, VEC, MODE>(a, st, ev);
-        case 2: return launch_argmax_u<T, 2, VEC, MODE>(a, st, ev);
-        default: return launch_argmax_u<T, 1, VEC, MODE>(a, st, ev);
+        case 8: return launch_argmax_u<T, 8, VEC, MODE>(a, lds, st, ev);
+        case 4: return launch_argmax_u<T, 4, VEC, MODE>(a, lds, st, ev);
+        case 2: return launch_argmax_u<T, 2, VEC, MODE>(a, lds, st, ev);
+        default: return launch_argmax_u<T, 1, VEC, MODE>(a, lds, st, ev);
     }
 }
 
-// Streaming kernel (timed by the profiling events), then the epilogue kernel.
 template <int MODE>
 static hipError_t dispatch(const ArgmaxArgs& a, int dtype, bool vec, int U, size_t lds,
                            hipStream_t st, const KernelEvents& ev) {
-    hipError_t e;
     if (dtype == 1)
-        e = vec ? launch_argmax<bf16_t, true, MODE>(a, U, st, ev)
-                : launch_argmax<bf16_t, false, MODE>(a, U, st, ev);
-    else
-        e = vec ? launch_argmax<float, true, MODE>(a, U, st, ev)
-                : launch_argmax<float, false, MODE>(a, U, st, ev);
-    if (e != hipSuccess) return e;
-    argmax_epilogue_kernel<MODE><<<dim3((unsigned)a.B), dim3(kThreads), lds, st>>>(a);
-    return hipGetLastError();
+        return vec ? launch_argmax<bf16_t, true, MODE>(a, U, lds, st, ev)
+                   : launch_argmax<bf16_t, false, MODE>(a, U, lds, st, ev);
+    return vec ? launch_argmax<float, true, MODE>(a, U, lds, st, ev)
+               : launch_argmax<float, false, MODE>(a, U, lds, st, ev);
 }
 
 static ArgmaxArgs base_args(const void* target, int B, int R, int V, const Geometry& g,
@@ -316,6 +393,8 @@ static ArgmaxArgs base_args(const void* target, int B, int R, int V, const Geome
     a.S = g.S;
     a.chunk = g.chunk;
     a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
+    a.stale = reinterpret_cast<uint32_t*>(ws + g.off_tickets) + 8;
+    a.spin_limit = kEpilogueSpin;
     return a;
 }
 

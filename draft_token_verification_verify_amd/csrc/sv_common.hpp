@@ -55,7 +55,9 @@ struct Geometry {
     int chunk2;      // elements per stop-row chunk
     int cand_cap;    // filter candidate slots per row (mode 3), else 0: S segments of cand_seg
     int cand_seg;    // slots per streaming chunk (a power of two)
-    size_t off_tickets, off_partials, off_segs, off_rowf, off_ccount, off_tails, off_cand, bytes;
+    size_t off_tickets, off_partials, off_segs, off_rowf, off_ccount, off_tails, off_cand;
+    size_t off_masses;   // per request: S2 stop-row chunk masses (one word each)
+    size_t bytes;
 };
 
 // Sampling filters: weight bins of 1/16 octave below a row's maximum m,
@@ -69,6 +71,10 @@ constexpr int kFilterBinsPerOctave = 16;
 constexpr int kCandBins = 256;
 constexpr int kCandCap = 16384;
 constexpr int kCandMaxChunks = 256;  // rows of more streaming chunks keep no candidates
+
+// Stop-row chunks per request at most (one workgroup-wide scan over their
+// masses): with 16 * 4 tokens per thread, vocabularies up to 2^22.
+constexpr int kMaxChunks2 = 256;
 
 // Stochastic tree walk split over several workgroups per request: their
 // exchange area in the workspace (mode 4), per request.
@@ -129,15 +135,16 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     // Sampler: 16, 32 or 64 consecutive tokens per thread; the smallest that
     // keeps the sampler to about one round of resident workgroups.
     int nsub = 1;
-    while (nsub < 4 && (long long)B * ((V + kThreads * 16 * nsub - 1) / (kThreads * 16 * nsub)) >
-                           SV_SAMPLER_WGS)
+    while (nsub < 4 && ((long long)B * ((V + kThreads * 16 * nsub - 1) / (kThreads * 16 * nsub)) >
+                            SV_SAMPLER_WGS ||
+                        (V + kThreads * 16 * nsub - 1) / (kThreads * 16 * nsub) > kMaxChunks2))
         nsub <<= 1;
     g->chunk2 = kThreads * 16 * nsub;
     g->S2 = (mode == 0) ? (V + g->chunk2 - 1) / g->chunk2 : 0;
 
     size_t off = 0;
-    g->off_tickets = off;  // sampler arrival counters (stochastic only), one line each
-    off = align_up(off + (mode == 0 ? sizeof(uint32_t) * kTicketStride * (size_t)B : 0), 256);
+    g->off_tickets = off;  // per-request counters, one cache line each
+    off = align_up(off + sizeof(uint32_t) * kTicketStride * (size_t)B, 256);
     g->off_partials = off;
     off = align_up(off + 16 * (size_t)rows * (size_t)g->S, 256);
     g->off_segs = off;
@@ -148,6 +155,8 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
                              kThreads, 256);
     g->off_rowf = off;  // per-row sampling filter of the filtered call (stochastic only)
     off = align_up(off + (mode == 0 ? 16 * (size_t)rows : 0), 256);
+    g->off_masses = off;   // stop-row chunk masses, two rounds (stochastic only)
+    off = align_up(off + (mode == 0 ? 16 * (size_t)B * (size_t)g->S2 : 0), 256);
     // Candidates: per row up to kCandCap slots (fewer for a short vocabulary),
     // split into one power-of-two segment per streaming chunk.
     cand = cand && g->S <= kCandMaxChunks;
@@ -220,11 +229,36 @@ inline Scale make_scale(float temperature) {
 // Base-2 exponent of a logit difference d = x - m, rounded once.
 __device__ inline float scaled(float d, const Scale& k) { return fmaf(d, k.hi, d * k.lo); }
 
+// 2^t in fp64, inline (no call, no stack): t = n + f with n = rint(t) and
+// f in [-1/2, 1/2] (exact), 2^f = e^y with y = f ln 2, |y| <= 0.35, from the
+// Taylor series of e^y to degree 13 (truncation below 0.35^14 / 14! < 4e-18
+// relative) in Horner form; then the exponent n.  Within a few ulp of double;
+// below 2^-1074 it underflows to 0, above 2^1023 it overflows to inf.
+__device__ inline double exp2_fp64(double t) {
+    t = fmin(fmax(t, -1100.0), 1100.0);  // keeps n in int range; the ends round to 0 and inf
+    const double n = rint(t);
+    const double y = (t - n) * 0.69314718055994530942;
+    double p = 1.0 / 6227020800.0;  // 1/13!
+    p = fma(p, y, 1.0 / 479001600.0);
+    p = fma(p, y, 1.0 / 39916800.0);
+    p = fma(p, y, 1.0 / 3628800.0);
+    p = fma(p, y, 1.0 / 362880.0);
+    p = fma(p, y, 1.0 / 40320.0);
+    p = fma(p, y, 1.0 / 5040.0);
+    p = fma(p, y, 1.0 / 720.0);
+    p = fma(p, y, 1.0 / 120.0);
+    p = fma(p, y, 1.0 / 24.0);
+    p = fma(p, y, 1.0 / 6.0);
+    p = fma(p, y, 0.5);
+    p = fma(p, y, 1.0);
+    p = fma(p, y, 1.0);
+    return ldexp(p, (int)n);
+}
+
 // 2^((x - m) * c) in fp64 (accurate to a few ulp of double); 0 for x = -inf.
-// Kept out of line: it sits on rare branches of otherwise short loops.
-__device__ __noinline__ double exp2_accurate(float x, float m, const Scale& k) {
+__device__ inline double exp2_accurate(float x, float m, const Scale& k) {
     if (x == -INFINITY) return 0.0;
-    return exp2(((double)x - (double)m) * k.c64);
+    return exp2_fp64(((double)x - (double)m) * k.c64);
 }
 
 // 2^(t / 256) in fp64 for t <= 0 (-inf excluded): 2^n 2^(j/256) 2^(f/256)

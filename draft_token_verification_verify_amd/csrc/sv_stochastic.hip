@@ -64,6 +64,9 @@ struct CallArgs {
     float* p_at_draft;       // [B, k] or null
     float* q_at_draft;       // [B, k] or null
     RowFilter* rowf;         // [B, 2k+1] sampling filter per row (filtered call), else null
+    unsigned long long* masses;   // [B, S2] stop-row chunk masses, bitwise complemented (0: none)
+    int lookahead;           // one-launch grid: items of request b follow the tiles of b + lookahead
+    int self_compute;        // items compute every partial themselves (no tiles in the grid)
 };
 
 // Draft length of request b: lens[b] clamped to [0, k] (per-request windows in
@@ -150,7 +153,7 @@ struct StatsOp : CallArgs {
     // Workgroup reduction of per-thread (max m, fp64 sum s against m) into the
     // tile's (M, S): every thread's sum is rescaled to the common M with an fp64
     // exponential, then summed in fixed order.
-    __device__ void finish(float m, double s, float* f0, float* f1, double* d) const {
+    __device__ __forceinline__ void finish(float m, double s, float* f0, float* f1, double* d) const {
         __shared__ float red_f[kWaves];
         __shared__ double red_d[kWaves];
         const float M = block_max(m, red_f);
@@ -164,8 +167,8 @@ struct StatsOp : CallArgs {
         *d = (M == -INFINITY) ? 1.0 : Ssum;
     }
 
-    __device__ void tile(int b, int r, int lo, int hi, const uint4* raw, int nvec, float* f0,
-                         float* f1, double* d) const {
+    __device__ __forceinline__ void tile(int b, int r, int lo, int hi, const uint4* raw, int nvec,
+                                         float* f0, float* f1, double* d) const {
         constexpr int EPV = Elem<T>::kPerVec;
         float x[U][EPV];
 #pragma unroll
@@ -196,8 +199,8 @@ struct StatsOp : CallArgs {
         finish(m, s, f0, f1, d);
     }
 
-    __device__ void tile_scalar(int b, int r, int lo, int hi, float* f0, float* f1,
-                                double* d) const {
+    __device__ __forceinline__ void tile_scalar(int b, int r, int lo, int hi, float* f0, float* f1,
+                                                double* d) const {
         const T* p = row(b, r);
         float m = -INFINITY;
         for (int j = lo + threadIdx.x; j < hi; j += kThreads) m = fmaxf(m, Elem<T>::load(p, j));
@@ -223,7 +226,7 @@ __device__ inline void publish_partial(Partial16* dst, float f0, float f1, doubl
 // StatsOp::tile (masked slots add exactly 0 there), hence the same bits.  Used
 // by a sampler workgroup that computes partials itself instead of waiting.
 template <typename T>
-__device__ void stats_tile_runtime(const CallArgs& a, int t, float* f0, float* f1, double* d) {
+__device__ __forceinline__ void stats_tile_runtime(const CallArgs& a, int t, float* f0, float* f1, double* d) {
     constexpr int EPV = Elem<T>::kPerVec;
     StatsOp<T, 1> op;
     static_cast<CallArgs&>(op) = a;
@@ -272,8 +275,8 @@ template <typename T, int U, bool VEC>
 __global__ __launch_bounds__(kThreads) void stats_kernel(CallArgs a) {
     StatsOp<T, U> op;
     static_cast<CallArgs&>(op) = a;
-    if constexpr (VEC) stream_tile_vec<T, U>(op);
-    else stream_tile_scalar<T>(op);
+    if constexpr (VEC) stream_tile_vec<T, U>(op, blockIdx.x);
+    else stream_tile_scalar<T>(op, blockIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -291,83 +294,124 @@ struct Decision {
 
 constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the merge
 
-// Make sure every partial of request b is published.  They come from an
-// earlier kernel (then the first check succeeds) or from statistics workgroups
-// of the same launch; after a.spin_limit polls this workgroup computes the
-// still-missing ones itself (same bits as their owners), so no wait depends on
-// another workgroup being scheduled.
-template <typename T>
-__device__ void await_partials(const CallArgs& a, int b) {
-    const int n = a.R * a.S;
-    Partial16* p = a.partials + (size_t)b * n;
-    for (int iter = 0;; ++iter) {
-        int ok = 1;
-        for (int t = threadIdx.x; t < n; t += kThreads) ok &= read_partial(p + t).ok;
-        if (__syncthreads_and(ok)) return;
-        if (iter >= a.spin_limit) break;
-        __builtin_amdgcn_s_sleep(2);
+// Row statistics of request b from its n = R * S partials staged in LDS
+// (pm[t] = chunk max, ps[t] = chunk sum): sh_m[r] = row max, sh_s[r] = sum of
+// 2^((x - max) * c) in fp64, chunks merged in chunk order.  ps is overwritten.
+__device__ __forceinline__ void merge_staged(const CallArgs& a, const float* pm, double* ps,
+                                             float* sh_m, double* sh_s) {
+    const int R = a.R, S = a.S, n = R * S;
+    for (int r = threadIdx.x; r < R; r += kThreads) {
+        float M = -INFINITY;
+        for (int ch = 0; ch < S; ++ch) M = fmaxf(M, pm[r * S + ch]);
+        sh_m[r] = M;
     }
-    __shared__ int sh_missing;
-    for (int t = 0; t < n; ++t) {
-        if (threadIdx.x == 0) sh_missing = !read_partial(p + t).ok;
-        __syncthreads();
-        const int missing = sh_missing;
-        __syncthreads();
-        if (missing) {
-            float f0, f1;
-            double d;
-            stats_tile_runtime<T>(a, b * n + t, &f0, &f1, &d);
-            if (threadIdx.x == 0) publish_partial(p + t, f0, f1, d);
-        }
+    __syncthreads();
+    // every thread takes a few partials: one fp64 exponential each
+    for (int t = threadIdx.x; t < n; t += kThreads) {
+        const float M = sh_m[t / S];
+        ps[t] = (M == -INFINITY) ? 0.0 : ps[t] * exp2_accurate(pm[t], M, a.sc);
     }
-    wait_stores();  // this thread's own reads below see its stores
+    __syncthreads();
+    for (int r = threadIdx.x; r < R; r += kThreads) {
+        double acc = 0.0;
+        for (int ch = 0; ch < S; ++ch) acc += ps[r * S + ch];  // fixed chunk order
+        sh_s[r] = acc;
+    }
     __syncthreads();
 }
 
-// Row statistics of request b: sh_m[r] = row max, sh_s[r] = sum of
-// 2^((x - max) * c) in fp64 (chunks merged in order).
+// The same from partials read in global memory (every one of which the caller
+// has seen published), for requests of more than kMergeLds partials: the same
+// values in the same order, so the same bits.
 template <typename T>
-__device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) {
+__device__ __forceinline__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) {
     const int R = a.R, S = a.S, n = R * S;
     const Partial16* p = a.partials + (size_t)b * n;
-    await_partials<T>(a, b);
-    if (n <= kMergeLds) {
-        // Every thread takes a few partials: one fp64 exponential each.
-        __shared__ float pm[kMergeLds];
-        __shared__ double ps[kMergeLds];
-        for (int t = threadIdx.x; t < n; t += kThreads) {
-            const PartialRead q = read_partial(p + t);
-            pm[t] = q.f0;
-            ps[t] = q.d;
-        }
-        __syncthreads();
-        for (int r = threadIdx.x; r < R; r += kThreads) {
-            float M = -INFINITY;
-            for (int ch = 0; ch < S; ++ch) M = fmaxf(M, pm[r * S + ch]);
-            sh_m[r] = M;
-        }
-        __syncthreads();
-        for (int t = threadIdx.x; t < n; t += kThreads) {
-            const float M = sh_m[t / S];
-            ps[t] = (M == -INFINITY) ? 0.0 : ps[t] * exp2_accurate(pm[t], M, a.sc);
-        }
-        __syncthreads();
-        for (int r = threadIdx.x; r < R; r += kThreads) {
-            double acc = 0.0;
-            for (int ch = 0; ch < S; ++ch) acc += ps[r * S + ch];  // fixed chunk order
-            sh_s[r] = acc;
-        }
+    for (int r = threadIdx.x; r < R; r += kThreads) {
+        const Partial16* q = p + (size_t)r * S;
+        float M = -INFINITY;
+        for (int ch = 0; ch < S; ++ch) M = fmaxf(M, read_partial(q + ch).f0);
+        double acc = 0.0;
+        if (M != -INFINITY)
+            for (int ch = 0; ch < S; ++ch) {
+                const PartialRead e = read_partial(q + ch);
+                acc += e.d * exp2_accurate(e.f0, M, a.sc);
+            }
+        sh_m[r] = M;
+        sh_s[r] = acc;
+    }
+    __syncthreads();
+}
+
+// Statistics tile t (request-major numbering) computed by this workgroup, with
+// the element-to-thread mapping and operation order of the streaming tile, so
+// the same bits as the partial its owner publishes.  Every thread gets them.
+template <typename T, bool VEC>
+__device__ __forceinline__ void stats_tile_any(const CallArgs& a, int t, float* m, double* s) {
+    float f1;
+    if constexpr (VEC) {
+        stats_tile_runtime<T>(a, t, m, &f1, s);
     } else {
-        for (int r = threadIdx.x; r < R; r += kThreads) {
-            const Partial16* q = p + (size_t)r * S;
-            float M = -INFINITY;
-            for (int ch = 0; ch < S; ++ch) M = fmaxf(M, read_partial(q + ch).f0);
-            double acc = 0.0;
-            if (M != -INFINITY)
-                for (int ch = 0; ch < S; ++ch) {
-                    const PartialRead e = read_partial(q + ch);
-                    acc += e.d * exp2_accurate(e.f0, M, a.sc);
-                }
+        StatsOp<T, 1> op;
+        static_cast<CallArgs&>(op) = a;
+        const int ch = t % a.S, rr = t / a.S;
+        const int r = rr % a.R, b = rr / a.R;
+        if (op.skip(b, r)) {
+            *m = -INFINITY;
+            *s = 1.0;
+            return;
+        }
+        const int lo = ch * a.chunk, hi = min(a.V, lo + a.chunk);
+        op.tile_scalar(b, r, lo, hi, m, &f1, s);
+    }
+}
+
+// Partial t of request b as every thread sees it: the published one (when
+// use_published), or, where it is not (yet, or any more) published, computed
+// here.  Nothing is written.
+template <typename T, bool VEC>
+__device__ __forceinline__ void partial_here(const CallArgs& a, int b, int t, bool use_published, float* m,
+                             double* s) {
+    __shared__ float sh_pm;
+    __shared__ double sh_ps;
+    __shared__ int sh_ok;
+    const int n = a.R * a.S;
+    if (threadIdx.x == 0) {
+        const PartialRead q = use_published ? read_partial(a.partials + (size_t)b * n + t)
+                                            : PartialRead{0.f, false, 0.0};
+        sh_ok = q.ok;
+        sh_pm = q.f0;
+        sh_ps = q.d;
+    }
+    __syncthreads();
+    const bool ok = sh_ok != 0;
+    *m = sh_pm;
+    *s = sh_ps;
+    __syncthreads();
+    if (!ok) stats_tile_any<T, VEC>(a, b * n + t, m, s);
+}
+
+// merge_rows computed by one workgroup: the same maxima and sums in the same
+// order, each partial taken as published (when use_published) or computed here
+// (partial_here), so the same bits.  Slow (one partial at a time).
+template <typename T, bool VEC>
+__device__ __forceinline__ void merge_rows_here(const CallArgs& a, int b, float* sh_m, double* sh_s,
+                                bool use_published) {
+    const int R = a.R, S = a.S;
+    for (int r = 0; r < R; ++r) {
+        float M = -INFINITY, m;
+        double s;
+        for (int ch = 0; ch < S; ++ch) {
+            partial_here<T, VEC>(a, b, r * S + ch, use_published, &m, &s);
+            M = fmaxf(M, m);
+        }
+        double acc = 0.0;
+        if (M != -INFINITY)
+            for (int ch = 0; ch < S; ++ch) {
+                partial_here<T, VEC>(a, b, r * S + ch, use_published, &m, &s);
+                acc += s * exp2_accurate(m, M, a.sc);
+            }
+        if (threadIdx.x == 0) {
             sh_m[r] = M;
             sh_s[r] = acc;
         }
@@ -375,16 +419,12 @@ __device__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) 
     __syncthreads();
 }
 
-template <typename T, bool FILT>
-__device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
-    __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1], sh_tau[2 * kMaxK + 1];
-    __shared__ double sh_s[2 * kMaxK + 1];
-    __shared__ int sh_acc[kMaxK];
-    __shared__ int sh_stop;
+// Wave 1 loads the tested logits target[b, i, x_i] and draft[b, i, x_i]
+// (i < kb) into sh_g[i] and sh_g[k + 1 + i]; they are read after the next
+// barrier.  An id outside [0, V) leaves -inf (the test rejects it).
+template <typename T>
+__device__ inline void gather_tested(const CallArgs& a, int b, int kb, float* sh_g) {
     const int k = a.k;
-    const int kb = draft_len(a, b);
-    // Wave 1 gathers the tested logits target[b, i, x_i] and draft[b, i, x_i]
-    // while wave 0 merges the partials.
     if (threadIdx.x >= 64 && threadIdx.x < 64 + kb) {
         const int i = threadIdx.x - 64;
         const int32_t x = a.draft_tokens[(size_t)b * k + i];
@@ -396,25 +436,34 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
         sh_g[i] = gt;
         sh_g[k + 1 + i] = gd;
     }
-    const int i = threadIdx.x;  // test i runs in thread i (k <= 64)
-    int32_t x = 0;
-    float u = 0.f;
+}
+
+// Test i's draft token and uniform, loaded by thread i (i < kb) ahead of the
+// statistics they are compared with.
+__device__ inline void load_test_inputs(const CallArgs& a, int b, int kb, int32_t* x, float* u) {
+    const int i = threadIdx.x;
+    *x = 0;
+    *u = 0.f;
     if (i < kb) {
-        x = a.draft_tokens[(size_t)b * k + i];
-        u = uniform_at(a, b, i);
+        *x = a.draft_tokens[(size_t)b * a.k + i];
+        *u = uniform_at(a, b, i);
     }
-    if constexpr (FILT) {
-        // Filtered rows: maximum, kept mass and threshold from the selection kernel.
-        for (int r = threadIdx.x; r < a.R; r += kThreads) {
-            const RowFilter f = a.rowf[(size_t)b * a.R + r];
-            sh_m[r] = f.m;
-            sh_s[r] = f.s;
-            sh_tau[r] = f.tau;
-        }
-        __syncthreads();
-    } else {
-        merge_rows<T>(a, b, sh_m, sh_s);
-    }
+}
+
+// The tests of request b, all at once (thread i runs test i; they are
+// independent given the uniforms), from its rows' maxima sh_m and masses sh_s
+// (with FILT, thresholds sh_tau) and the tested logits sh_g.  Returns the stop
+// row: the first rejected i, or kb.  With write_outputs it also writes the
+// accepted drafts, the -1 padding, num_accepted, P and Q (out_tokens[b, s] is
+// the final draw's).
+template <bool FILT>
+__device__ int run_tests(const CallArgs& a, int b, int kb, int32_t x, float u, const float* sh_m,
+                         const double* sh_s, const float* sh_tau, const float* sh_g,
+                         bool write_outputs) {
+    __shared__ int sh_acc[kMaxK];
+    __shared__ int sh_stop;
+    const int k = a.k;
+    const int i = threadIdx.x;
     if (i < k) {  // past the window (i >= kb): no test, P = Q = 0 reported
         double P = 0.0, Q = 0.0;
         int acc = 0;
@@ -445,8 +494,35 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
         for (int j = threadIdx.x; j <= k; j += kThreads) {
             if (j < s) a.out_tokens[(size_t)b * (k + 1) + j] = a.draft_tokens[(size_t)b * k + j];
             else if (j > s) a.out_tokens[(size_t)b * (k + 1) + j] = -1;
-            // out_tokens[b, s] is written by the final draw.
         }
+    __syncthreads();
+    return s;
+}
+
+template <typename T, bool FILT>
+__device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
+    __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1], sh_tau[2 * kMaxK + 1];
+    __shared__ double sh_s[2 * kMaxK + 1];
+    const int k = a.k;
+    const int kb = draft_len(a, b);
+    // Wave 1 gathers the tested logits while wave 0 merges the partials.
+    gather_tested<T>(a, b, kb, sh_g);
+    int32_t x;
+    float u;
+    load_test_inputs(a, b, kb, &x, &u);
+    if constexpr (FILT) {
+        // Filtered rows: maximum, kept mass and threshold from the selection kernel.
+        for (int r = threadIdx.x; r < a.R; r += kThreads) {
+            const RowFilter f = a.rowf[(size_t)b * a.R + r];
+            sh_m[r] = f.m;
+            sh_s[r] = f.s;
+            sh_tau[r] = f.tau;
+        }
+        __syncthreads();
+    } else {
+        merge_rows<T>(a, b, sh_m, sh_s);
+    }
+    const int s = run_tests<FILT>(a, b, kb, x, u, sh_m, sh_s, sh_tau, sh_g, write_outputs);
     out->s = s;
     out->kb = kb;
     out->mt = sh_m[s];
@@ -775,24 +851,395 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(CallArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// One-launch schedule (16-byte aligned rows): the grid holds the statistics
-// tiles first, then the sampler items.  Workgroups are dispatched in index
-// order, so items start as statistics workgroups retire and sample the early
-// requests while the late requests are still streaming.  An item polls for its
-// request's partials and, past a bounded number of polls, computes the missing
-// ones itself (await_partials), so no wait depends on dispatch order.
+// The plain call.
+//
+// Tiles (one workgroup per (request, row, chunk)) compute the softmax
+// statistics as above and publish their partials; they take no atomics and
+// wait for nothing.
+//
+// Items (one workgroup per (request, stop-row chunk)) each read their
+// request's partials (polling until all are published), merge them in chunk
+// order and run the k tests, so every item of a request reaches the same
+// decision (the chunk-0 item writes the accepted drafts, num_accepted, P and
+// Q).  Each weighs its chunk of the final distribution (residual
+// max(0, p_s - q_s) or bonus p_k, as Weigher does) into per-thread sums and
+// publishes the chunk's mass; then reads every chunk mass of its request
+// (computing here any that is late), and all find the same owner chunk: the
+// first whose running mass exceeds u_k * Z.  The owner finds the token from
+// its per-thread sums and one 64-lane scan of one thread's tokens.  Each item
+// then takes its request's ticket; the last clears the partials and masses.
+//
+// Waits are bounded.  An item that gives up on a partial computes the
+// request's statistics itself and marks the workspace stale (a word no call
+// clears): a tile that publishes late may then leave a stale partial behind,
+// so from then on every call on that workspace computes its statistics in the
+// items and ignores published partials, until the workspace is zeroed again.
+//
+// One launch (rows 16-byte aligned): the grid holds the tiles request by
+// request, and the items of request b follow the tiles of request
+// b + lookahead (all items last when lookahead >= B).  Two kernels: all tiles,
+// then all items.  Self-compute (testing): items alone, each computing its
+// request's statistics.
 // ---------------------------------------------------------------------------
+
+__device__ inline unsigned long long enc_f64(double v) {
+    return ~(unsigned long long)__double_as_longlong(v);
+}
+__device__ inline double dec_f64(unsigned long long w) {
+    return __longlong_as_double((long long)~w);
+}
+
+// Per-request counters, each request on its own cache line: [0] item tickets.
+// Word kStaleWord of request 0's line marks a stale workspace.
+constexpr int kStaleWord = 8;
+__device__ inline uint32_t* req_counter(const CallArgs& a, int b, int which) {
+    return ticket_of(a.tickets, b) + which;
+}
+__device__ inline uint32_t* stale_word(const CallArgs& a) { return a.tickets + kStaleWord; }
+
+// Request b's decision, in every item: the rows' statistics from the published
+// partials (polled, bounded) merged in chunk order, or computed here (the
+// self-compute schedule, a stale workspace, or a partial that never came: the
+// workspace is then marked stale); then the tests.  With write_outputs the
+// accepted drafts, num_accepted, P and Q are written.
+template <typename T, bool VEC>
+__device__ __forceinline__ void item_decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
+    __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1];
+    __shared__ double sh_s[2 * kMaxK + 1];
+    __shared__ int sh_stale;
+    const int k = a.k, n = a.R * a.S;
+    const int kb = draft_len(a, b);
+    gather_tested<T>(a, b, kb, sh_g);
+    int32_t x;
+    float u;
+    load_test_inputs(a, b, kb, &x, &u);
+    // The stale word is read alongside the first poll of the partials; up to
+    // kMergeLds partials are kept in LDS as they are read.
+    __shared__ float pm[kMergeLds];
+    __shared__ double ps[kMergeLds];
+    const bool staged = n <= kMergeLds;
+    bool here = a.self_compute != 0;
+    if (!here) {
+        const Partial16* p = a.partials + (size_t)b * n;
+        for (int it = 0;; ++it) {
+            if (it == 0 && threadIdx.x == 0) sh_stale = load_coherent(stale_word(a)) != 0u;
+            int ok = 1;
+            for (int t = threadIdx.x; t < n; t += kThreads) {
+                const PartialRead q = read_partial(p + t);
+                ok &= q.ok;
+                if (staged) {
+                    pm[t] = q.f0;
+                    ps[t] = q.d;
+                }
+            }
+            ok = __syncthreads_and(ok);
+            if (sh_stale) {
+                here = true;
+                break;
+            }
+            if (ok) break;
+            if (it >= a.spin_limit) {
+                here = true;
+                if (threadIdx.x == 0) store_coherent(stale_word(a), 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+    } else if (threadIdx.x == 0) {
+        sh_stale = 1;
+    }
+    __syncthreads();
+    if (here) merge_rows_here<T, VEC>(a, b, sh_m, sh_s, !a.self_compute && !sh_stale);
+    else if (staged) merge_staged(a, pm, ps, sh_m, sh_s);
+    else merge_rows<T>(a, b, sh_m, sh_s);
+    const int s = run_tests<false>(a, b, kb, x, u, sh_m, sh_s, nullptr, sh_g, write_outputs);
+    out->s = s;
+    out->kb = kb;
+    out->mt = sh_m[s];
+    out->st = sh_s[s];
+    out->md = (s < kb) ? sh_m[k + 1 + s] : 0.f;
+    out->sd = (s < kb) ? sh_s[k + 1 + s] : 1.0;
+    out->taut = -INFINITY;
+    out->taud = -INFINITY;
+    __syncthreads();
+}
+
+// Weights of request b's final draw (Weigher) and its stop rows.
+template <typename T>
+struct FinalRows {
+    Weigher W;
+    const T* trow;
+    const T* drow;
+};
+
+// Workgroup-uniform values moved to scalar registers (every lane holds the
+// same value): they then take no vector registers.
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline float uni(float v) { return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v))); }
+__device__ inline double uni(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ inline Decision uni(const Decision& d) {
+    Decision u;
+    u.s = uni(d.s);
+    u.kb = uni(d.kb);
+    u.mt = uni(d.mt);
+    u.md = uni(d.md);
+    u.st = uni(d.st);
+    u.sd = uni(d.sd);
+    u.taut = uni(d.taut);
+    u.taud = uni(d.taud);
+    return u;
+}
+
+template <typename T>
+__device__ inline FinalRows<T> final_rows(const CallArgs& a, int b, const Decision& d) {
+    FinalRows<T> f;
+    f.W.mt = d.mt;
+    f.W.md = d.md;
+    f.W.set_ratio(d.st / d.sd);
+    f.W.sc = a.sc;
+    f.W.residual = d.s < d.kb;
+    f.W.taut = -INFINITY;
+    f.W.taud = -INFINITY;
+    f.trow = static_cast<const T*>(a.target) + ((size_t)b * (a.k + 1) + d.s) * (size_t)a.V;
+    f.drow = f.W.residual
+        ? static_cast<const T*>(a.draft) + ((size_t)b * a.k + d.s) * (size_t)a.V
+        : f.trow;
+    return f;
+}
+
+// Mass of chunk c of the final distribution: every thread's sum over its
+// 16 * NSUB tokens (segment_sum), and their inclusive prefix in thread order;
+// *total is the chunk's mass (the same additions as the last prefix).
+template <typename T, bool VEC, int NSUB>
+__device__ __forceinline__ double chunk_sums(const CallArgs& a, const FinalRows<T>& f, int c, double* incl,
+                                    double* total) {
+    __shared__ double sh_wave[kWaves];
+    const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
+    const double seg = segment_sum_any<T, VEC, NSUB, false>(f.trow, f.drow, f.W, lo, hi);
+    *incl = block_inclusive_scan(seg, sh_wave, total);
+    return seg;
+}
+
+// Across the workgroup: the first thread whose flag is set (kThreads if none)
+// and the last thread whose second flag is set (-1 if none).
+__device__ inline void block_first_last(bool first_flag, bool last_flag, int* first, int* last) {
+    __shared__ int sh_first[kWaves], sh_last[kWaves];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long fm = __ballot(first_flag);
+    const unsigned long long lm = __ballot(last_flag);
+    if (lane == 0) {
+        sh_first[wave] = fm ? wave * 64 + __ffsll((long long)fm) - 1 : kThreads;
+        sh_last[wave] = lm ? wave * 64 + 63 - __clzll((long long)lm) : -1;
+    }
+    __syncthreads();
+    int fi = kThreads, la = -1;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        fi = min(fi, sh_first[w]);
+        la = max(la, sh_last[w]);
+    }
+    __syncthreads();
+    *first = fi;
+    *last = la;
+}
+
+// The token inside chunk c: the first thread with positive mass whose running
+// mass (prev + its inclusive prefix) exceeds tau, else the last with positive
+// mass; then that thread's 16 * NSUB tokens, one per lane of wave 0, the first
+// with positive weight whose running mass exceeds tau, else the last with
+// positive weight.  Written to out_tokens[b, s_row] by lane 0 of wave 0.
+template <typename T, bool VEC, int NSUB>
+__device__ __forceinline__ void draw_in_chunk(const CallArgs& a, int b, int s_row, const FinalRows<T>& f, int c,
+                              double seg, double incl, double prev, double tau) {
+    __shared__ double sh_ti[kThreads];
+    sh_ti[threadIdx.x] = incl;
+    __syncthreads();
+    int fi, la;
+    block_first_last(seg > 0.0 && prev + incl > tau, seg > 0.0, &fi, &la);
+    const bool over = fi < kThreads;
+    const int tsel = over ? fi : max(la, 0);
+    const double base_run = prev + (tsel > 0 ? sh_ti[tsel - 1] : 0.0);
+    if (threadIdx.x < 64) {
+        constexpr int SEG = NSUB * kSub;
+        const int lane = threadIdx.x;
+        const int lo = c * a.chunk2, hi = min(a.V, lo + a.chunk2);
+        const int j = lo + tsel * SEG + lane;
+        double w = 0.0;
+        if (lane < SEG && j < hi)
+            w = f.W.template weigh<false>(Elem<T>::load(f.trow, j), Elem<T>::load(f.drow, j));
+        const double run = base_run + wave_inclusive_scan(w);
+        const unsigned long long hit = __ballot(over && w > 0.0 && run > tau);
+        const unsigned long long pos = __ballot(w > 0.0);
+        int sel;
+        if (hit) sel = __ffsll((long long)hit) - 1;
+        else if (pos) sel = 63 - __clzll((long long)pos);
+        else sel = 0;
+        if (lane == 0) a.out_tokens[(size_t)b * (a.k + 1) + s_row] = lo + tsel * SEG + sel;
+    }
+    __syncthreads();
+}
+
+// One item of the plain call: chunk c of request b's final draw.
+template <typename T, bool VEC, int NSUB>
+__device__ __forceinline__ void item_plain(const CallArgs& a, int b, int c) {
+    __shared__ double sh_incl[kThreads];
+    __shared__ double sh_scan[kWaves];
+    __shared__ int sh_last, sh_stale;
+    // 1. The request's decision.
+    Decision d;
+    item_decide<T, VEC>(a, b, c == 0, &d);
+    d = uni(d);
+    FinalRows<T> f = final_rows<T>(a, b, d);
+    f.W.set_ratio(uni(f.W.r));
+    const double u = uni((double)uniform_at(a, b, d.kb));  // the final draw's uniform
+
+    // Round 0 draws from the request's final distribution.  Its masses are all
+    // zero only when the residual vanished (p_s == q_s exactly, which a strict
+    // test with u < 1 never rejects); round 1 then draws from p_s instead, with
+    // a second set of chunk masses.
+    __shared__ int sh_miss[kMaxChunks2];
+    __shared__ int sh_nmiss;
+    int owner = -1;
+    double seg = 0.0, incl = 0.0, Z = 0.0, prev_incl = 0.0;
+    for (int round = 0; round < 2 && owner < 0; ++round) {
+        if (round == 1) {
+            f.W.residual = false;
+            f.drow = f.trow;
+        }
+        unsigned long long* masses = a.masses + (size_t)(round * a.B + b) * a.S2;
+        // 2. This chunk's sums and mass, published; then every chunk's mass,
+        //    thread t holding chunk t's (at most kMaxChunks2 chunks): as
+        //    published by its item, or, past the poll limit, weighed here by
+        //    the same code (the same bits).
+        double m = 0.0;
+        int job = c, jn = 0;
+        for (;;) {
+            double incl_j, mass_j;
+            const double seg_j = chunk_sums<T, VEC, NSUB>(a, f, job, &incl_j, &mass_j);
+            if (job == c && jn == 0) {
+                seg = seg_j;
+                incl = incl_j;
+                if (threadIdx.x == 0) {
+                    sh_nmiss = 0;
+                    if (a.S2 > 1) store_coherent(&masses[c], enc_f64(mass_j));
+                }
+                const int t = threadIdx.x;
+                bool have = t >= a.S2 || t == c;
+                if (t == c) m = mass_j;
+                for (int it = 0; !have; ++it) {
+                    const unsigned long long v = load_coherent(&masses[t]);
+                    if (v != 0ull) {
+                        m = dec_f64(v);
+                        have = true;
+                    } else if (it >= a.spin_limit) {
+                        break;
+                    } else {
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                __syncthreads();
+                if (!have) sh_miss[atomicAdd(&sh_nmiss, 1)] = t;
+                __syncthreads();
+            } else if ((int)threadIdx.x == job) {
+                m = mass_j;
+            }
+            if (jn >= sh_nmiss) break;
+            job = sh_miss[jn++];
+        }
+
+        // 3. Z and the owner chunk: the first with positive mass whose running
+        //    mass (chunks in order, one workgroup-wide scan: the same values in
+        //    every item) exceeds u Z, else the last with positive mass.
+        const double ci = block_inclusive_scan(m, sh_scan, &Z);
+        const double tau = u * Z;
+        sh_incl[threadIdx.x] = ci;
+        __syncthreads();
+        int fi, la;
+        block_first_last(m > 0.0 && ci > tau, m > 0.0, &fi, &la);
+        owner = fi < kThreads ? fi : la;  // la: rounding left u Z at or past the total
+        prev_incl = owner > 0 ? sh_incl[owner - 1] : 0.0;
+        __syncthreads();
+        owner = uni(owner);
+        prev_incl = uni(prev_incl);
+        Z = uni(Z);
+    }
+
+    // 4. Ticket (its value is used last): this item has read all it needs.
+    uint32_t prev = 0;
+    if (threadIdx.x == 0) prev = atomicAdd(req_counter(a, b, 0), 1u);
+
+    // 5. The owner draws.
+    if (owner == c) draw_in_chunk<T, VEC, NSUB>(a, b, d.s, f, c, seg, incl, prev_incl, u * Z);
+
+    // 6. The last item clears both rounds' masses and, unless the workspace is
+    //    stale, the partials.
+    if (threadIdx.x == 0) {
+        sh_last = prev == (uint32_t)a.S2 - 1u;
+        sh_stale = sh_last && load_coherent(stale_word(a)) != 0u;
+    }
+    __syncthreads();
+    if (sh_last) {
+        for (int i = threadIdx.x; i < a.S2; i += kThreads) {
+            store_coherent(&a.masses[(size_t)b * a.S2 + i], 0ull);
+            store_coherent(&a.masses[(size_t)(a.B + b) * a.S2 + i], 0ull);
+        }
+        if (!sh_stale && !a.self_compute) clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
+        if (threadIdx.x == 0) atomicExch(req_counter(a, b, 0), 0u);
+    }
+}
+
+// Block index -> work of the one-launch grid: the tiles of requests
+// 0 .. L-1, then for b = L .. B-1 the tiles of b followed by the items of
+// b - L, then the items of the last L requests (L = min(lookahead, B)).
+// Returns true for a tile (*idx its request-major tile index), false for an
+// item (*idx = request * S2 + chunk).
+__device__ inline bool plain_block(const CallArgs& a, int x, int* idx) {
+    const int tpr = a.R * a.S, ipr = a.S2;
+    const int L = min(a.lookahead, a.B);
+    const int head = L * tpr;
+    if (x < head) {
+        *idx = x;
+        return true;
+    }
+    x -= head;
+    const int per = tpr + ipr, nmid = a.B - L;
+    if (x < nmid * per) {
+        const int seg = x / per, off = x % per;
+        if (off < tpr) {
+            *idx = (L + seg) * tpr + off;
+            return true;
+        }
+        *idx = seg * ipr + (off - tpr);
+        return false;
+    }
+    x -= nmid * per;
+    *idx = nmid * ipr + x;
+    return false;
+}
+
+#ifndef SV_PLAIN_WAVES
+#define SV_PLAIN_WAVES 1
+#endif
 template <typename T, int U, int NSUB>
-__global__ __launch_bounds__(kThreads) void onepass_kernel(CallArgs a) {
-    const int n_tiles = a.B * a.R * a.S;
-    if ((int)blockIdx.x < n_tiles) {
+__global__ __launch_bounds__(kThreads, SV_PLAIN_WAVES) void plain_kernel(CallArgs a) {
+    int idx;
+    if (plain_block(a, (int)blockIdx.x, &idx)) {
         StatsOp<T, U> op;
         static_cast<CallArgs&>(op) = a;
-        stream_tile_vec<T, U>(op);
-        return;
+        stream_tile_vec<T, U>(op, idx);
+    } else {
+        item_plain<T, true, NSUB>(a, idx / a.S2, idx % a.S2);
     }
-    const int j = (int)blockIdx.x - n_tiles;
-    sample_item<T, true, NSUB, false>(a, j / a.S2, j % a.S2);
+}
+
+template <typename T, bool VEC, int NSUB>
+__global__ __launch_bounds__(kThreads) void plain_items_kernel(CallArgs a) {
+    item_plain<T, VEC, NSUB>(a, (int)blockIdx.x / a.S2, (int)blockIdx.x % a.S2);
 }
 
 // ---------------------------------------------------------------------------
@@ -816,52 +1263,88 @@ static hipError_t launch_stats(const CallArgs& a, int U, hipStream_t st, const K
     }
 }
 
-template <typename T, bool VEC, bool FILT = false>
-static hipError_t launch_sample(const CallArgs& a, hipStream_t st) {
+template <typename T, bool VEC>
+static hipError_t launch_sample_filtered(const CallArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
     switch (a.chunk2 / (kThreads * kSub)) {
-        case 4: sample_kernel<T, VEC, 4, FILT><<<grid, block, 0, st>>>(a); break;
-        case 2: sample_kernel<T, VEC, 2, FILT><<<grid, block, 0, st>>>(a); break;
-        default: sample_kernel<T, VEC, 1, FILT><<<grid, block, 0, st>>>(a); break;
+        case 4: sample_kernel<T, VEC, 4, true><<<grid, block, 0, st>>>(a); break;
+        case 2: sample_kernel<T, VEC, 2, true><<<grid, block, 0, st>>>(a); break;
+        default: sample_kernel<T, VEC, 1, true><<<grid, block, 0, st>>>(a); break;
     }
     return hipGetLastError();
 }
 
-template <typename T, int U>
-static hipError_t launch_onepass_u(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
+// One launch: tiles and items in one grid.
+template <typename T, int U, int NSUB>
+static hipError_t launch_plain_u(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
     const unsigned grid = (unsigned)((long long)a.B * a.R * a.S + (long long)a.B * a.S2);
-    switch (a.chunk2 / (kThreads * kSub)) {
-        case 4:
-            hipExtLaunchKernelGGL(onepass_kernel<T, U, 4>, dim3(grid), dim3(kThreads), 0, st,
-                                  ev.begin, ev.end, 0, a);
-            break;
-        case 2:
-            hipExtLaunchKernelGGL(onepass_kernel<T, U, 2>, dim3(grid), dim3(kThreads), 0, st,
-                                  ev.begin, ev.end, 0, a);
-            break;
-        default:
-            hipExtLaunchKernelGGL(onepass_kernel<T, U, 1>, dim3(grid), dim3(kThreads), 0, st,
-                                  ev.begin, ev.end, 0, a);
-            break;
-    }
+    hipExtLaunchKernelGGL(plain_kernel<T, U, NSUB>, dim3(grid), dim3(kThreads), 0, st, ev.begin,
+                          ev.end, 0, a);
     return hipGetLastError();
+}
+
+template <typename T, int NSUB>
+static hipError_t launch_plain_n(const CallArgs& a, int U, hipStream_t st, const KernelEvents& ev) {
+    switch (U) {
+        case 8: return launch_plain_u<T, 8, NSUB>(a, st, ev);
+        case 4: return launch_plain_u<T, 4, NSUB>(a, st, ev);
+        case 2: return launch_plain_u<T, 2, NSUB>(a, st, ev);
+        default: return launch_plain_u<T, 1, NSUB>(a, st, ev);
+    }
 }
 
 template <typename T>
-static hipError_t launch_onepass(const CallArgs& a, int U, hipStream_t st,
-                                 const KernelEvents& ev) {
-    switch (U) {
-        case 8: return launch_onepass_u<T, 8>(a, st, ev);
-        case 4: return launch_onepass_u<T, 4>(a, st, ev);
-        case 2: return launch_onepass_u<T, 2>(a, st, ev);
-        default: return launch_onepass_u<T, 1>(a, st, ev);
+static hipError_t launch_plain(const CallArgs& a, int U, hipStream_t st, const KernelEvents& ev) {
+    switch (a.chunk2 / (kThreads * kSub)) {
+        case 4: return launch_plain_n<T, 4>(a, U, st, ev);
+        case 2: return launch_plain_n<T, 2>(a, U, st, ev);
+        default: return launch_plain_n<T, 1>(a, U, st, ev);
     }
+}
+
+// Items alone (after the statistics kernel, or computing the statistics
+// themselves under the self-compute schedule).
+template <typename T, bool VEC>
+static hipError_t launch_plain_items(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
+    const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
+    switch (a.chunk2 / (kThreads * kSub)) {
+        case 4:
+            hipExtLaunchKernelGGL(plain_items_kernel<T, VEC, 4>, grid, block, 0, st, ev.begin,
+                                  ev.end, 0, a);
+            break;
+        case 2:
+            hipExtLaunchKernelGGL(plain_items_kernel<T, VEC, 2>, grid, block, 0, st, ev.begin,
+                                  ev.end, 0, a);
+            break;
+        default:
+            hipExtLaunchKernelGGL(plain_items_kernel<T, VEC, 1>, grid, block, 0, st, ev.begin,
+                                  ev.end, 0, a);
+            break;
+    }
+    return hipGetLastError();
+}
+
+// Two kernels: every tile, then every item (the events, when set, on the
+// statistics kernel).
+template <typename T, bool VEC>
+static hipError_t launch_plain_two(const CallArgs& a, int U, hipStream_t st,
+                                   const KernelEvents& ev) {
+    const hipError_t e = launch_stats<T, VEC>(a, U, st, ev);
+    if (e != hipSuccess) return e;
+    return launch_plain_items<T, VEC>(a, st, KernelEvents{});
 }
 
 int g_stochastic_schedule = 0;
 
-// Polls of an unpublished partial before an item computes it itself: far above
-// any wait seen when workgroups are dispatched in order (a few microseconds).
+// One-launch grid: items of request b follow the tiles of request
+// b + SV_LOOKAHEAD (< 0: every item after every tile).
+#ifndef SV_LOOKAHEAD
+#define SV_LOOKAHEAD -1
+#endif
+
+// Polls of a decision record or chunk mass before an item derives it itself:
+// far above any wait seen when workgroups are dispatched in order (a few
+// microseconds).
 constexpr int kSpinLimit = 1 << 16;
 
 static CallArgs make_args(const StochasticCall& call, const Geometry& g) {
@@ -886,32 +1369,34 @@ static CallArgs make_args(const StochasticCall& call, const Geometry& g) {
     a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
     a.tickets = reinterpret_cast<uint32_t*>(ws + g.off_tickets);
     a.segs = reinterpret_cast<double*>(ws + g.off_segs);
+    a.masses = reinterpret_cast<unsigned long long*>(ws + g.off_masses);
     a.out_tokens = call.out_tokens;
     a.num_accepted = call.num_accepted;
     a.p_at_draft = call.p_at_draft;
     a.q_at_draft = call.q_at_draft;
     a.rowf = nullptr;
-    a.spin_limit = (g_stochastic_schedule == 2) ? 0 : kSpinLimit;
+    a.spin_limit = kSpinLimit;
+    a.self_compute = g_stochastic_schedule == 2;
+    a.lookahead = SV_LOOKAHEAD < 0 ? call.B : SV_LOOKAHEAD;
     return a;
 }
 
 hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
                           const KernelEvents& ev) {
     const CallArgs a = make_args(call, g);
-    hipError_t e;
+    if (a.self_compute)
+        return call.dtype == 1 ? (call.vec ? launch_plain_items<bf16_t, true>(a, st, ev)
+                                           : launch_plain_items<bf16_t, false>(a, st, ev))
+                               : (call.vec ? launch_plain_items<float, true>(a, st, ev)
+                                           : launch_plain_items<float, false>(a, st, ev));
     if (call.vec && g_stochastic_schedule != 1)
-        return call.dtype == 1 ? launch_onepass<bf16_t>(a, g.U, st, ev)
-                               : launch_onepass<float>(a, g.U, st, ev);
+        return call.dtype == 1 ? launch_plain<bf16_t>(a, g.U, st, ev)
+                               : launch_plain<float>(a, g.U, st, ev);
     if (call.dtype == 1)
-        e = call.vec ? launch_stats<bf16_t, true>(a, g.U, st, ev)
-                     : launch_stats<bf16_t, false>(a, g.U, st, ev);
-    else
-        e = call.vec ? launch_stats<float, true>(a, g.U, st, ev)
-                     : launch_stats<float, false>(a, g.U, st, ev);
-    if (e != hipSuccess) return e;
-    if (call.dtype == 1)
-        return call.vec ? launch_sample<bf16_t, true>(a, st) : launch_sample<bf16_t, false>(a, st);
-    return call.vec ? launch_sample<float, true>(a, st) : launch_sample<float, false>(a, st);
+        return call.vec ? launch_plain_two<bf16_t, true>(a, g.U, st, ev)
+                        : launch_plain_two<bf16_t, false>(a, g.U, st, ev);
+    return call.vec ? launch_plain_two<float, true>(a, g.U, st, ev)
+                    : launch_plain_two<float, false>(a, g.U, st, ev);
 }
 
 hipError_t run_stochastic_filtered(const StochasticCall& call, const FilterCall& f,
@@ -930,9 +1415,10 @@ hipError_t run_stochastic_filtered(const StochasticCall& call, const FilterCall&
     e = run_filter(call, f, g, st, ev);
     if (e != hipSuccess) return e;
     if (call.dtype == 1)
-        return call.vec ? launch_sample<bf16_t, true, true>(a, st)
-                        : launch_sample<bf16_t, false, true>(a, st);
-    return call.vec ? launch_sample<float, true, true>(a, st) : launch_sample<float, false, true>(a, st);
+        return call.vec ? launch_sample_filtered<bf16_t, true>(a, st)
+                        : launch_sample_filtered<bf16_t, false>(a, st);
+    return call.vec ? launch_sample_filtered<float, true>(a, st)
+                    : launch_sample_filtered<float, false>(a, st);
 }
 
 }  // namespace sv

@@ -52,7 +52,7 @@ struct RowFilter {
 };
 static_assert(sizeof(RowFilter) == 16, "RowFilter layout");
 
-// One workgroup per tile, rows 16-byte aligned (V a whole number of vectors).
+// Tile t, rows 16-byte aligned (V a whole number of vectors).
 //   Op::row(b, r) -> const T* row start
 //   Op::skip(b, r) -> true for a row that is not read (its partial is
 //     Op::publish_skipped's)
@@ -60,9 +60,8 @@ static_assert(sizeof(RowFilter) == 16, "RowFilter layout");
 //     raw[U] (this thread's vectors; slots >= nvec are padding); thread 0 then
 //     calls Op::publish(&partials[t], f0, f1, d).
 template <typename T, int U, class Op>
-__device__ void stream_tile_vec(const Op& op) {
+__device__ __forceinline__ void stream_tile_vec(const Op& op, int t) {
     constexpr int EPV = Elem<T>::kPerVec;
-    const int t = blockIdx.x;
     const int ch = t % op.S, rr = t / op.S;
     const int r = rr % op.R, b = rr / op.R;
     if (op.skip(b, r)) {  // row outside the request's window: nothing to read
@@ -85,8 +84,7 @@ __device__ void stream_tile_vec(const Op& op) {
 
 // Same for rows that are not 16-byte aligned: scalar loads.
 template <typename T, class Op>
-__device__ void stream_tile_scalar(const Op& op) {
-    const int t = blockIdx.x;
+__device__ __forceinline__ void stream_tile_scalar(const Op& op, int t) {
     const int ch = t % op.S, rr = t / op.S;
     const int r = rr % op.R, b = rr / op.R;
     if (op.skip(b, r)) {

@@ -85,6 +85,7 @@ enum spec_verify_status {
 #define SPEC_VERIFY_MAX_PATH_LEN 64   /* L */
 #define SPEC_VERIFY_MAX_PATH_TABLE 16384 /* P * L */
 #define SPEC_VERIFY_MAX_VOCAB (1 << 30)
+#define SPEC_VERIFY_MAX_STOCHASTIC_VOCAB (1 << 22) /* V of the linear stochastic calls */
 #define SPEC_VERIFY_MAX_FILTER_VOCAB (1 << 22) /* V of a filtered call with a filter on */
 #define SPEC_VERIFY_MAX_TREE_SAMPLING_VOCAB (1 << 19) /* V of spec_verify_tree_stochastic */
 #define SPEC_VERIFY_MIN_TEMPERATURE 1e-20f /* keeps log2(e)/T finite in fp32 */
@@ -115,25 +116,37 @@ const char *spec_verify_status_string(int status);
 size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V, int dtype);
 
 /*
+ * Waits inside a call are bounded.  Workgroups of a call wait only for
+ * workgroups of the same launch that come before them in the grid, so the
+ * bounds (tens of milliseconds) are reached only when other work holds the
+ * device's compute units for that long.  A stochastic sampling workgroup, or a
+ * greedy or tree epilogue, that reaches its bound computes what it waited for
+ * itself (the same result) and marks the workspace stale: a late workgroup may
+ * then still write into it, so every later call on a stale workspace computes
+ * its statistics without reading them from the workspace (slower, same
+ * results) until the workspace is zeroed again (spec_verify_workspace_init).
+ */
+
+/*
  * Zero-fill `workspace_bytes` bytes of a fresh workspace on `stream` with a fill
  * kernel (no memset node).  Call once after allocating it.
  */
 int spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * Stochastic schedule (process-wide, not thread-safe; default AUTO).  All
- * schedules give bit-identical results.
+ * Stochastic schedule of the plain, ragged, counter-based and allocation-free
+ * calls (process-wide, not thread-safe; default AUTO).  All schedules give
+ * bit-identical results.
  *
  *   AUTO          rows 16-byte aligned (pointers and V * element size): one
  *                 launch whose grid holds the statistics workgroups and then
  *                 the sampling workgroups, which start as statistics
  *                 workgroups retire and wait (bounded polling) for their
  *                 request's statistics; otherwise TWO_KERNELS.
- *   TWO_KERNELS   a statistics kernel, then a sampling kernel; no waits inside
- *                 a kernel.
- *   SELF_COMPUTE  like AUTO, but every sampling workgroup computes its
- *                 request's statistics itself instead of waiting (slow; the
- *                 fallback path of AUTO, exposed for testing).
+ *   TWO_KERNELS   a statistics kernel, then a sampling kernel.
+ *   SELF_COMPUTE  the sampling kernel alone, every sampling workgroup
+ *                 computing its request's statistics itself (slow; for
+ *                 testing: the same bits with no statistics exchanged).
  *
  * Returns INVALID_ARGUMENT for any other value.
  */
@@ -192,6 +205,7 @@ int spec_verify_profile_events(void *const *events, int n_pairs);
  * Work: one streaming pass that reads every logits row once (softmax
  * statistics), then a sampler that reads only each request's stop row(s); in
  * one launch or two kernels (see spec_verify_set_schedule).
+ * V <= SPEC_VERIFY_MAX_STOCHASTIC_VOCAB (else LIMIT_EXCEEDED).
  */
 int spec_verify_stochastic(const void *target_logits, const void *draft_logits, int dtype,
                            const int32_t *draft_tokens, const float *uniforms,

@@ -114,6 +114,7 @@ def stoch(lib, **kw):
     (dict(d=None), _lib.INVALID_ARGUMENT),
     (dict(x=None), _lib.INVALID_ARGUMENT),
     (dict(k=65), _lib.LIMIT_EXCEEDED),
+    (dict(V=(1 << 22) + 1), _lib.LIMIT_EXCEEDED),  # SPEC_VERIFY_MAX_STOCHASTIC_VOCAB
     (dict(wsb=16), _lib.WORKSPACE_TOO_SMALL),
 ])
 def test_stochastic_rejects(lib, kw, code):
@@ -162,8 +163,9 @@ def filtered(lib, **kw):
     (dict(k=65), _lib.LIMIT_EXCEEDED),
     (dict(V=(1 << 22) + 1), _lib.LIMIT_EXCEEDED),
     (dict(wsb=16), _lib.WORKSPACE_TOO_SMALL),
-    # every filter off: the plain call's checks (no vocabulary limit of the filters)
-    (dict(top_k=0, top_p=1.0, min_p=0.0, V=(1 << 22) + 1, wsb=16), _lib.WORKSPACE_TOO_SMALL),
+    # every filter off: the plain call's checks (its vocabulary limit is the same)
+    (dict(top_k=0, top_p=1.0, min_p=0.0, V=1 << 22, wsb=16), _lib.WORKSPACE_TOO_SMALL),
+    (dict(top_k=0, top_p=1.0, min_p=0.0, V=(1 << 22) + 1, wsb=16), _lib.LIMIT_EXCEEDED),
 ])
 def test_filtered_rejects(lib, kw, code):
     assert filtered(lib, **kw) == code

@@ -151,6 +151,34 @@ def test_out_of_range_drafts_are_rejected():
     assert np.all(gpu["num_accepted"] <= 1)
 
 
+def test_two_streams_with_the_default_workspace():
+    """Two calls in flight at once on two streams, both with the binding's
+    default workspace (one buffer per stream): both match the oracle."""
+    cases = [wl.c3(31, B=16), wl.c3(32, B=16)]
+    dev = torch.device("cuda", 0)
+    ins = []
+    for c in cases:
+        ins.append((wl.to_device(c.target, c.dtype), wl.to_device(c.draft, c.dtype),
+                    wl.to_device(c.draft_tokens.astype(np.int32)),
+                    wl.to_device(c.uniforms.astype(np.float32))))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for rep in range(3):
+        for c, (t, d, x, u), st in zip(cases, ins, streams):
+            with torch.cuda.stream(st):
+                outs.append((c, *sv.spec_verify_stochastic(t, d, x, u, c.temperature)))
+    torch.cuda.synchronize()
+    for c, out, acc in outs:
+        gpu = dict(out_tokens=out.cpu().numpy(), num_accepted=acc.cpu().numpy(),
+                   p_at_draft=np.zeros((c.B, c.k)), q_at_draft=np.zeros((c.B, c.k)))
+        ref = H.oracle_stochastic(c)
+        ref = dict(ref, p_at_draft=np.zeros((c.B, c.k)), q_at_draft=np.zeros((c.B, c.k)))
+        amb, dis = H.compare_stochastic(gpu, ref, label=c.name)
+        assert dis <= 1e-4 * c.rows
+    del dev
+
+
 def test_repeat_calls_are_bit_identical():
     case = wl.c3(7, B=16)
     a = H.run_stochastic(case)
