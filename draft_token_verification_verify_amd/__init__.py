@@ -69,7 +69,8 @@ def spec_verify_version() -> int:
 
 def spec_verify_set_schedule(schedule: int) -> None:
     """Process-wide stochastic schedule: ``_lib.SCHEDULE_AUTO``,
-    ``_lib.SCHEDULE_TWO_KERNELS`` or ``_lib.SCHEDULE_SELF_COMPUTE``."""
+    ``_lib.SCHEDULE_TWO_KERNELS``, ``_lib.SCHEDULE_SELF_COMPUTE`` or
+    ``_lib.SCHEDULE_INTERLEAVED``."""
     _lib.check("spec_verify_set_schedule", _lib.load().spec_verify_set_schedule(int(schedule)))
 
 

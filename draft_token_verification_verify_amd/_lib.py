@@ -12,7 +12,7 @@ F32, BF16 = 0, 1
 MODE_STOCHASTIC, MODE_GREEDY, MODE_TREE, MODE_STOCHASTIC_FILTERED, MODE_TREE_STOCHASTIC = range(5)
 OK, INVALID_ARGUMENT, UNSUPPORTED_DTYPE, WORKSPACE_TOO_SMALL, LIMIT_EXCEEDED, HIP_ERROR = range(6)
 NOALLOC_SCRATCH_BYTES = 8 << 20  # SPEC_VERIFY_NOALLOC_SCRATCH_BYTES
-SCHEDULE_AUTO, SCHEDULE_TWO_KERNELS, SCHEDULE_SELF_COMPUTE = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_TWO_KERNELS, SCHEDULE_SELF_COMPUTE, SCHEDULE_INTERLEAVED = 0, 1, 2, 3
 
 EXPORTED = (
     "spec_verify_version",

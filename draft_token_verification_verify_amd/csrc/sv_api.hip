@@ -114,7 +114,7 @@ size_t spec_verify_workspace_bytes(int mode, int B, int rows_per_request, int V,
 
 int spec_verify_set_schedule(int schedule) {
     if (schedule != SPEC_VERIFY_SCHEDULE_AUTO && schedule != SPEC_VERIFY_SCHEDULE_TWO_KERNELS &&
-        schedule != SPEC_VERIFY_SCHEDULE_SELF_COMPUTE)
+        schedule != SPEC_VERIFY_SCHEDULE_SELF_COMPUTE && schedule != SPEC_VERIFY_SCHEDULE_INTERLEAVED)
         return SPEC_VERIFY_INVALID_ARGUMENT;
     sv::g_stochastic_schedule = schedule;
     return SPEC_VERIFY_OK;

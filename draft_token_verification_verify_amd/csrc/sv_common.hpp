@@ -279,6 +279,21 @@ __device__ inline double exp2_256(double t, const double* tab) {
     return ldexp(tab[k & 255] * p, k >> 8);
 }
 
+// The table exp2_256 reads: tab[j] = 2^(j / 256), j < 256, each the library's
+// fp64 exponential; written by the first 256 threads, read after a barrier.
+__device__ inline void fill_exp_table(double* tab) {
+    for (int j = threadIdx.x; j < 256; j += blockDim.x) tab[j] = exp2((double)j / 256.0);
+}
+
+// 2^((x - m) c) in fp64 for x <= m from the table `tab` (exp2_256), with
+// c256 = 256 c; 0 for x = -inf.  A few fp64 ulp, like exp2_accurate, with four
+// polynomial constants instead of its thirteen: in a loop the compiler keeps
+// those in registers, and fewer of them leave room for more waves.
+__device__ inline double exp2_table(float x, float m, double c256, const double* tab) {
+    if (x == -INFINITY) return 0.0;
+    return exp2_256(((double)x - (double)m) * c256, tab);
+}
+
 // Argmax pairs: larger value wins, the lower index wins a tie.
 __device__ inline void merge_argmax(float& v, int& i, float v2, int i2) {
     bool take = (v2 > v) || (v2 == v && i2 < i);

@@ -38,9 +38,17 @@
 // ~10^5 CDF edges, so a relative error e in the cumulative weights moves the
 // drawn token on a fraction ~V * e of the draws.  The fp64 paths above keep e
 // near 1e-10.
+#include <algorithm>
+#include <atomic>
+
 #include "sv_common.hpp"
 #include "sv_launch.hpp"
 #include "sv_stream.hpp"
+
+// Lookahead of the one-launch grid, fixed for tuning (< 0: chosen per call).
+#ifndef SV_LOOKAHEAD
+#define SV_LOOKAHEAD -1
+#endif
 
 namespace sv {
 
@@ -126,9 +134,9 @@ __device__ inline float uniform_at(const CallArgs& a, int b, int i) {
 }
 
 // p(x) = 2^((x - M) * c) / S in fp64; 0 when x or the whole row is -inf.
-__device__ inline double prob_of(float x, float M, double S, const Scale& k) {
+__device__ inline double prob_of(float x, float M, double S, double c256, const double* tab) {
     if (M == -INFINITY || !(S > 0.0)) return 0.0;
-    return exp2_accurate(x, M, k) / S;
+    return exp2_table(x, M, c256, tab) / S;
 }
 
 // ---------------------------------------------------------------------------
@@ -298,7 +306,7 @@ constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the m
 // (pm[t] = chunk max, ps[t] = chunk sum): sh_m[r] = row max, sh_s[r] = sum of
 // 2^((x - max) * c) in fp64, chunks merged in chunk order.  ps is overwritten.
 __device__ __forceinline__ void merge_staged(const CallArgs& a, const float* pm, double* ps,
-                                             float* sh_m, double* sh_s) {
+                                             float* sh_m, double* sh_s, const double* tab) {
     const int R = a.R, S = a.S, n = R * S;
     for (int r = threadIdx.x; r < R; r += kThreads) {
         float M = -INFINITY;
@@ -309,7 +317,7 @@ __device__ __forceinline__ void merge_staged(const CallArgs& a, const float* pm,
     // every thread takes a few partials: one fp64 exponential each
     for (int t = threadIdx.x; t < n; t += kThreads) {
         const float M = sh_m[t / S];
-        ps[t] = (M == -INFINITY) ? 0.0 : ps[t] * exp2_accurate(pm[t], M, a.sc);
+        ps[t] = (M == -INFINITY) ? 0.0 : ps[t] * exp2_table(pm[t], M, a.sc.c64 * 256.0, tab);
     }
     __syncthreads();
     for (int r = threadIdx.x; r < R; r += kThreads) {
@@ -324,7 +332,8 @@ __device__ __forceinline__ void merge_staged(const CallArgs& a, const float* pm,
 // has seen published), for requests of more than kMergeLds partials: the same
 // values in the same order, so the same bits.
 template <typename T>
-__device__ __forceinline__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s) {
+__device__ __forceinline__ void merge_rows(const CallArgs& a, int b, float* sh_m, double* sh_s,
+                                           const double* tab) {
     const int R = a.R, S = a.S, n = R * S;
     const Partial16* p = a.partials + (size_t)b * n;
     for (int r = threadIdx.x; r < R; r += kThreads) {
@@ -335,7 +344,7 @@ __device__ __forceinline__ void merge_rows(const CallArgs& a, int b, float* sh_m
         if (M != -INFINITY)
             for (int ch = 0; ch < S; ++ch) {
                 const PartialRead e = read_partial(q + ch);
-                acc += e.d * exp2_accurate(e.f0, M, a.sc);
+                acc += e.d * exp2_table(e.f0, M, a.sc.c64 * 256.0, tab);
             }
         sh_m[r] = M;
         sh_s[r] = acc;
@@ -396,7 +405,7 @@ __device__ __forceinline__ void partial_here(const CallArgs& a, int b, int t, bo
 // (partial_here), so the same bits.  Slow (one partial at a time).
 template <typename T, bool VEC>
 __device__ __forceinline__ void merge_rows_here(const CallArgs& a, int b, float* sh_m, double* sh_s,
-                                bool use_published) {
+                                bool use_published, const double* tab) {
     const int R = a.R, S = a.S;
     for (int r = 0; r < R; ++r) {
         float M = -INFINITY, m;
@@ -409,7 +418,7 @@ __device__ __forceinline__ void merge_rows_here(const CallArgs& a, int b, float*
         if (M != -INFINITY)
             for (int ch = 0; ch < S; ++ch) {
                 partial_here<T, VEC>(a, b, r * S + ch, use_published, &m, &s);
-                acc += s * exp2_accurate(m, M, a.sc);
+                acc += s * exp2_table(m, M, a.sc.c64 * 256.0, tab);
             }
         if (threadIdx.x == 0) {
             sh_m[r] = M;
@@ -459,7 +468,7 @@ __device__ inline void load_test_inputs(const CallArgs& a, int b, int kb, int32_
 template <bool FILT>
 __device__ int run_tests(const CallArgs& a, int b, int kb, int32_t x, float u, const float* sh_m,
                          const double* sh_s, const float* sh_tau, const float* sh_g,
-                         bool write_outputs) {
+                         bool write_outputs, const double* tab) {
     __shared__ int sh_acc[kMaxK];
     __shared__ int sh_stop;
     const int k = a.k;
@@ -470,8 +479,9 @@ __device__ int run_tests(const CallArgs& a, int b, int kb, int32_t x, float u, c
         if (i < kb && x >= 0 && x < a.V) {
             const float gt = sh_g[i], gd = sh_g[k + 1 + i];
             // A token below its row's filter threshold has probability 0.
-            if (!FILT || gt >= sh_tau[i]) P = prob_of(gt, sh_m[i], sh_s[i], a.sc);
-            if (!FILT || gd >= sh_tau[k + 1 + i]) Q = prob_of(gd, sh_m[k + 1 + i], sh_s[k + 1 + i], a.sc);
+            const double c256 = a.sc.c64 * 256.0;
+            if (!FILT || gt >= sh_tau[i]) P = prob_of(gt, sh_m[i], sh_s[i], c256, tab);
+            if (!FILT || gd >= sh_tau[k + 1 + i]) Q = prob_of(gd, sh_m[k + 1 + i], sh_s[k + 1 + i], c256, tab);
             acc = (P >= Q) || ((double)u * Q < P);  // strict u < min(1, P/Q), no division
         }
         sh_acc[i] = acc;
@@ -500,7 +510,7 @@ __device__ int run_tests(const CallArgs& a, int b, int kb, int32_t x, float u, c
 }
 
 template <typename T, bool FILT>
-__device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
+__device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* out, const double* tab) {
     __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1], sh_tau[2 * kMaxK + 1];
     __shared__ double sh_s[2 * kMaxK + 1];
     const int k = a.k;
@@ -520,9 +530,9 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
         }
         __syncthreads();
     } else {
-        merge_rows<T>(a, b, sh_m, sh_s);
+        merge_rows<T>(a, b, sh_m, sh_s, tab);
     }
-    const int s = run_tests<FILT>(a, b, kb, x, u, sh_m, sh_s, sh_tau, sh_g, write_outputs);
+    const int s = run_tests<FILT>(a, b, kb, x, u, sh_m, sh_s, sh_tau, sh_g, write_outputs, tab);
     out->s = s;
     out->kb = kb;
     out->mt = sh_m[s];
@@ -545,6 +555,8 @@ __device__ void decide(const CallArgs& a, int b, bool write_outputs, Decision* o
 struct Weigher {
     float mt, md;
     double r;
+    double c256;         // 256 log2(e) / T
+    const double* tab;   // 2^(j / 256), j < 256 (exp2_table)
     float r32;     // r rounded to fp32
     float ad_big;  // draft exponent above which r e_d may pass 2^-8: -8 - log2(r)
     Scale sc;
@@ -557,7 +569,7 @@ struct Weigher {
     }
     __device__ inline double e_of(float x, float m) const {
         const float a = scaled(x - m, sc);
-        if (a > -8.f) return exp2_accurate(x, m, sc);
+        if (a > -8.f) return exp2_table(x, m, c256, tab);
         return (double)fast_exp2(a);
     }
     template <bool RESID, bool FILT>
@@ -581,7 +593,7 @@ struct Weigher {
         const float at = scaled(xt - mt, sc);
         if constexpr (!RESID) {
             if (!kt) return;
-            if (at > -8.f) big += exp2_accurate(xt, mt, sc);
+            if (at > -8.f) big += exp2_table(xt, mt, c256, tab);
             else small += fast_exp2(at);
         } else {
             const bool kd = !FILT || xd >= taud;
@@ -819,9 +831,14 @@ __device__ void sample_final(const CallArgs& a, int b, int s_row, int kb, const 
 template <typename T, bool VEC, int NSUB, bool FILT>
 __device__ void sample_item(const CallArgs& a, int b, int ch) {
     const int k = a.k;
+    __shared__ double exp_tab[256];
+    fill_exp_table(exp_tab);
+    __syncthreads();
     Decision dc;
-    decide<T, FILT>(a, b, ch == 0, &dc);
+    decide<T, FILT>(a, b, ch == 0, &dc, exp_tab);
     Weigher W;
+    W.c256 = a.sc.c64 * 256.0;
+    W.tab = exp_tab;
     W.mt = dc.mt;
     W.md = dc.md;
     W.set_ratio(dc.st / dc.sd);
@@ -903,12 +920,12 @@ __device__ inline uint32_t* stale_word(const CallArgs& a) { return a.tickets + k
 // workspace is then marked stale); then the tests.  With write_outputs the
 // accepted drafts, num_accepted, P and Q are written.
 template <typename T, bool VEC>
-__device__ __forceinline__ void item_decide(const CallArgs& a, int b, bool write_outputs, Decision* out) {
+__device__ __forceinline__ void item_decide(const CallArgs& a, int b, int kb, bool write_outputs,
+                                            Decision* out, const double* tab) {
     __shared__ float sh_m[2 * kMaxK + 1], sh_g[2 * kMaxK + 1];
     __shared__ double sh_s[2 * kMaxK + 1];
     __shared__ int sh_stale;
     const int k = a.k, n = a.R * a.S;
-    const int kb = draft_len(a, b);
     gather_tested<T>(a, b, kb, sh_g);
     int32_t x;
     float u;
@@ -949,10 +966,10 @@ __device__ __forceinline__ void item_decide(const CallArgs& a, int b, bool write
         sh_stale = 1;
     }
     __syncthreads();
-    if (here) merge_rows_here<T, VEC>(a, b, sh_m, sh_s, !a.self_compute && !sh_stale);
-    else if (staged) merge_staged(a, pm, ps, sh_m, sh_s);
-    else merge_rows<T>(a, b, sh_m, sh_s);
-    const int s = run_tests<false>(a, b, kb, x, u, sh_m, sh_s, nullptr, sh_g, write_outputs);
+    if (here) merge_rows_here<T, VEC>(a, b, sh_m, sh_s, !a.self_compute && !sh_stale, tab);
+    else if (staged) merge_staged(a, pm, ps, sh_m, sh_s, tab);
+    else merge_rows<T>(a, b, sh_m, sh_s, tab);
+    const int s = run_tests<false>(a, b, kb, x, u, sh_m, sh_s, nullptr, sh_g, write_outputs, tab);
     out->s = s;
     out->kb = kb;
     out->mt = sh_m[s];
@@ -996,8 +1013,10 @@ __device__ inline Decision uni(const Decision& d) {
 }
 
 template <typename T>
-__device__ inline FinalRows<T> final_rows(const CallArgs& a, int b, const Decision& d) {
+__device__ inline FinalRows<T> final_rows(const CallArgs& a, int b, const Decision& d, const double* tab) {
     FinalRows<T> f;
+    f.W.c256 = a.sc.c64 * 256.0;
+    f.W.tab = tab;
     f.W.mt = d.mt;
     f.W.md = d.md;
     f.W.set_ratio(d.st / d.sd);
@@ -1090,13 +1109,19 @@ __device__ __forceinline__ void item_plain(const CallArgs& a, int b, int c) {
     __shared__ double sh_incl[kThreads];
     __shared__ double sh_scan[kWaves];
     __shared__ int sh_last, sh_stale;
-    // 1. The request's decision.
+    // 1. The request's decision (the final draw's uniform is loaded first, so
+    //    that its latency overlaps the decision's).
+    const int kb = draft_len(a, b);
+    const float u_final = uniform_at(a, b, kb);
+    __shared__ double exp_tab[256];
+    fill_exp_table(exp_tab);
+    __syncthreads();
     Decision d;
-    item_decide<T, VEC>(a, b, c == 0, &d);
+    item_decide<T, VEC>(a, b, kb, c == 0, &d, exp_tab);
     d = uni(d);
-    FinalRows<T> f = final_rows<T>(a, b, d);
+    FinalRows<T> f = final_rows<T>(a, b, d, exp_tab);
     f.W.set_ratio(uni(f.W.r));
-    const double u = uni((double)uniform_at(a, b, d.kb));  // the final draw's uniform
+    const double u = uni((double)u_final);
 
     // Round 0 draws from the request's final distribution.  Its masses are all
     // zero only when the residual vanished (p_s == q_s exactly, which a strict
@@ -1274,9 +1299,52 @@ static hipError_t launch_sample_filtered(const CallArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Workgroups of plain_kernel<T, U, NSUB> resident on the current device at
+// once (cached per device); 0 when the runtime cannot say.
+template <typename T, int U, int NSUB>
+static int plain_resident() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(plain_kernel<T, U, NSUB>), kThreads, 0) !=
+                hipSuccess)
+            return 0;
+        v = std::max(cus * per_cu, 1);
+        cached[dev].store(v, std::memory_order_relaxed);
+    }
+    return v;
+}
+
+// The one-launch grid's lookahead L (items of request b follow the tiles of
+// request b + L).  A call whose logits fit the last-level cache (256 MiB)
+// puts every item last (L = B): the stop rows are still resident when the
+// stream ends, and items amid the stream would take ALU time from the tiles.
+// A larger call would find its early stop rows evicted by then, so its items
+// run amid the stream, three resident windows behind their tiles (a window is
+// the requests whose workgroups are resident at once), late enough that the
+// request's tiles have finished and its rows are still cached.
+constexpr size_t kLastLevelCacheBytes = (size_t)256 << 20;
+
+static int plain_lookahead(const CallArgs& a, size_t elem_bytes, int resident) {
+    if (SV_LOOKAHEAD >= 0) return std::min(SV_LOOKAHEAD, a.B);
+    if (g_stochastic_schedule == 3) return 1;
+    const size_t logits = (size_t)a.B * (size_t)a.R * (size_t)a.V * elem_bytes;
+    if (logits <= kLastLevelCacheBytes || resident <= 0) return a.B;
+    const long long per_request = (long long)a.R * a.S + a.S2;
+    const long long L = (3LL * resident + per_request - 1) / per_request;
+    return (int)std::min<long long>(std::max<long long>(L, 1), a.B);
+}
+
 // One launch: tiles and items in one grid.
 template <typename T, int U, int NSUB>
-static hipError_t launch_plain_u(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
+static hipError_t launch_plain_u(const CallArgs& args, hipStream_t st, const KernelEvents& ev) {
+    CallArgs a = args;
+    a.lookahead = plain_lookahead(a, sizeof(T), plain_resident<T, U, NSUB>());
     const unsigned grid = (unsigned)((long long)a.B * a.R * a.S + (long long)a.B * a.S2);
     hipExtLaunchKernelGGL(plain_kernel<T, U, NSUB>, dim3(grid), dim3(kThreads), 0, st, ev.begin,
                           ev.end, 0, a);
@@ -1336,12 +1404,6 @@ static hipError_t launch_plain_two(const CallArgs& a, int U, hipStream_t st,
 
 int g_stochastic_schedule = 0;
 
-// One-launch grid: items of request b follow the tiles of request
-// b + SV_LOOKAHEAD (< 0: every item after every tile).
-#ifndef SV_LOOKAHEAD
-#define SV_LOOKAHEAD -1
-#endif
-
 // Polls of a decision record or chunk mass before an item derives it itself:
 // far above any wait seen when workgroups are dispatched in order (a few
 // microseconds).
@@ -1377,7 +1439,7 @@ static CallArgs make_args(const StochasticCall& call, const Geometry& g) {
     a.rowf = nullptr;
     a.spin_limit = kSpinLimit;
     a.self_compute = g_stochastic_schedule == 2;
-    a.lookahead = SV_LOOKAHEAD < 0 ? call.B : SV_LOOKAHEAD;
+    a.lookahead = call.B;  // the one-launch grid sets its own (plain_lookahead)
     return a;
 }
 

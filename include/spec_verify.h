@@ -139,21 +139,29 @@ int spec_verify_workspace_init(void *workspace, size_t workspace_bytes, void *st
  * bit-identical results.
  *
  *   AUTO          rows 16-byte aligned (pointers and V * element size): one
- *                 launch whose grid holds the statistics workgroups and then
- *                 the sampling workgroups, which start as statistics
- *                 workgroups retire and wait (bounded polling) for their
- *                 request's statistics; otherwise TWO_KERNELS.
+ *                 launch whose grid holds each request's statistics
+ *                 workgroups, with the sampling workgroups of request b after
+ *                 those of request b + L; sampling workgroups wait (bounded
+ *                 polling) for their request's statistics.  L = B (every
+ *                 sampling workgroup last) when the call's logits fit the
+ *                 256 MiB last-level cache; otherwise three times the
+ *                 requests whose workgroups are resident at once, so that a
+ *                 request's stop rows are read again while still cached.
+ *                 Unaligned rows: TWO_KERNELS.
  *   TWO_KERNELS   a statistics kernel, then a sampling kernel.
  *   SELF_COMPUTE  the sampling kernel alone, every sampling workgroup
  *                 computing its request's statistics itself (slow; for
  *                 testing: the same bits with no statistics exchanged).
+ *   INTERLEAVED   AUTO's one launch with L = 1 at every size (for testing:
+ *                 sampling workgroups poll statistics still being computed).
  *
  * Returns INVALID_ARGUMENT for any other value.
  */
 enum {
     SPEC_VERIFY_SCHEDULE_AUTO = 0,
     SPEC_VERIFY_SCHEDULE_TWO_KERNELS = 1,
-    SPEC_VERIFY_SCHEDULE_SELF_COMPUTE = 2
+    SPEC_VERIFY_SCHEDULE_SELF_COMPUTE = 2,
+    SPEC_VERIFY_SCHEDULE_INTERLEAVED = 3
 };
 int spec_verify_set_schedule(int schedule);
 

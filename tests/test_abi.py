@@ -271,9 +271,10 @@ def test_workspace_init_rejects_null(lib):
 
 
 def test_schedule_switch(lib):
-    for code in (_lib.SCHEDULE_TWO_KERNELS, _lib.SCHEDULE_SELF_COMPUTE, _lib.SCHEDULE_AUTO):
+    for code in (_lib.SCHEDULE_TWO_KERNELS, _lib.SCHEDULE_SELF_COMPUTE, _lib.SCHEDULE_INTERLEAVED,
+                 _lib.SCHEDULE_AUTO):
         assert lib.spec_verify_set_schedule(code) == _lib.OK
-    assert lib.spec_verify_set_schedule(3) == _lib.INVALID_ARGUMENT
+    assert lib.spec_verify_set_schedule(4) == _lib.INVALID_ARGUMENT
     assert lib.spec_verify_set_schedule(-1) == _lib.INVALID_ARGUMENT
 
 

@@ -15,10 +15,11 @@ import oracle
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(autouse=True, params=["auto", "two-kernels"])
+@pytest.fixture(autouse=True, params=["auto", "two-kernels", "interleaved"])
 def schedule(request):
-    sv.spec_verify_set_schedule(_lib.SCHEDULE_AUTO if request.param == "auto"
-                                else _lib.SCHEDULE_TWO_KERNELS)
+    sv.spec_verify_set_schedule({"auto": _lib.SCHEDULE_AUTO,
+                                 "two-kernels": _lib.SCHEDULE_TWO_KERNELS,
+                                 "interleaved": _lib.SCHEDULE_INTERLEAVED}[request.param])
     yield request.param
     sv.spec_verify_set_schedule(_lib.SCHEDULE_AUTO)
 
