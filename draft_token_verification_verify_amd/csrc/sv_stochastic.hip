@@ -300,6 +300,7 @@ struct Decision {
     float taut, taud;  // filter thresholds of the stop rows (-inf: unfiltered)
 };
 
+static_assert(kMaxK < kThreads, "one test per thread");
 constexpr int kMergeLds = 1024;  // partials per request staged in LDS for the merge
 
 // Row statistics of request b from its n = R * S partials staged in LDS
@@ -500,11 +501,12 @@ __device__ int run_tests(const CallArgs& a, int b, int kb, int32_t x, float u, c
     }
     __syncthreads();
     const int s = sh_stop;
-    if (write_outputs)
-        for (int j = threadIdx.x; j <= k; j += kThreads) {
-            if (j < s) a.out_tokens[(size_t)b * (k + 1) + j] = a.draft_tokens[(size_t)b * k + j];
-            else if (j > s) a.out_tokens[(size_t)b * (k + 1) + j] = -1;
-        }
+    if (write_outputs) {
+        // Thread j holds draft token j (x, for j < kb) already: k < kThreads.
+        const int j = threadIdx.x;
+        if (j < s) a.out_tokens[(size_t)b * (k + 1) + j] = x;
+        else if (j > s && j <= k) a.out_tokens[(size_t)b * (k + 1) + j] = -1;
+    }
     __syncthreads();
     return s;
 }
@@ -1103,12 +1105,45 @@ __device__ __forceinline__ void draw_in_chunk(const CallArgs& a, int b, int s_ro
     __syncthreads();
 }
 
+// An arrival ticket on request b (thread 0's value; 0 elsewhere), taken once
+// this workgroup has read all it needs and thread 0's stores (a published mass
+// or partial) have completed, so that the last arrival's clearing cannot
+// overtake them.
+__device__ inline uint32_t take_ticket(const CallArgs& a, int b) {
+    uint32_t prev = 0;
+    if (threadIdx.x == 0) {
+        wait_stores();
+        prev = atomicAdd(req_counter(a, b, 0), 1u);
+    }
+    return prev;
+}
+
+// The last of the request's S2 arrivals (prev from take_ticket) clears both
+// rounds' masses, the partials (unless the workspace is stale) and the
+// counter.
+__device__ __forceinline__ void close_request(const CallArgs& a, int b, uint32_t prev) {
+    __shared__ int sh_last, sh_stale;
+    if (threadIdx.x == 0) {
+        sh_last = prev == (uint32_t)a.S2 - 1u;
+        sh_stale = sh_last && load_coherent(stale_word(a)) != 0u;
+    }
+    __syncthreads();
+    if (sh_last) {
+        for (int i = threadIdx.x; i < a.S2; i += kThreads) {
+            store_coherent(&a.masses[(size_t)b * a.S2 + i], 0ull);
+            store_coherent(&a.masses[(size_t)(a.B + b) * a.S2 + i], 0ull);
+        }
+        if (!sh_stale && !a.self_compute)
+            clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
+        if (threadIdx.x == 0) atomicExch(req_counter(a, b, 0), 0u);
+    }
+}
+
 // One item of the plain call: chunk c of request b's final draw.
 template <typename T, bool VEC, int NSUB>
 __device__ __forceinline__ void item_plain(const CallArgs& a, int b, int c) {
     __shared__ double sh_incl[kThreads];
     __shared__ double sh_scan[kWaves];
-    __shared__ int sh_last, sh_stale;
     // 1. The request's decision (the final draw's uniform is loaded first, so
     //    that its latency overlaps the decision's).
     const int kb = draft_len(a, b);
@@ -1195,27 +1230,13 @@ __device__ __forceinline__ void item_plain(const CallArgs& a, int b, int c) {
     }
 
     // 4. Ticket (its value is used last): this item has read all it needs.
-    uint32_t prev = 0;
-    if (threadIdx.x == 0) prev = atomicAdd(req_counter(a, b, 0), 1u);
+    const uint32_t prev = take_ticket(a, b);
 
     // 5. The owner draws.
     if (owner == c) draw_in_chunk<T, VEC, NSUB>(a, b, d.s, f, c, seg, incl, prev_incl, u * Z);
 
-    // 6. The last item clears both rounds' masses and, unless the workspace is
-    //    stale, the partials.
-    if (threadIdx.x == 0) {
-        sh_last = prev == (uint32_t)a.S2 - 1u;
-        sh_stale = sh_last && load_coherent(stale_word(a)) != 0u;
-    }
-    __syncthreads();
-    if (sh_last) {
-        for (int i = threadIdx.x; i < a.S2; i += kThreads) {
-            store_coherent(&a.masses[(size_t)b * a.S2 + i], 0ull);
-            store_coherent(&a.masses[(size_t)(a.B + b) * a.S2 + i], 0ull);
-        }
-        if (!sh_stale && !a.self_compute) clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
-        if (threadIdx.x == 0) atomicExch(req_counter(a, b, 0), 0u);
-    }
+    // 6. The last arrival clears the request's part of the workspace.
+    close_request(a, b, prev);
 }
 
 // Block index -> work of the one-launch grid: the tiles of requests
