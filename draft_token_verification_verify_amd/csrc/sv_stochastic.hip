@@ -1275,6 +1275,9 @@ template <typename T, int U, int NSUB>
 __global__ __launch_bounds__(kThreads, SV_PLAIN_WAVES) void plain_kernel(CallArgs a) {
     int idx;
     if (plain_block(a, (int)blockIdx.x, &idx)) {
+        // Tiles issue ahead of the items that share their compute unit: an
+        // item amid the stream then takes only the cycles the tiles leave.
+        __builtin_amdgcn_s_setprio(3);
         StatsOp<T, U> op;
         static_cast<CallArgs&>(op) = a;
         stream_tile_vec<T, U>(op, idx);
