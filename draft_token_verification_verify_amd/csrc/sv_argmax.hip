@@ -340,7 +340,8 @@ __global__ __launch_bounds__(kThreads) void argmax_kernel(ArgmaxArgs a) {
     static_cast<ArgmaxArgs&>(op) = a;
     const int n_tiles = a.B * a.R * a.S;
     if ((int)blockIdx.x < n_tiles) {
-        if constexpr (VEC) stream_tile_vec<T, U>(op, blockIdx.x);
+        // Rows are read once (the epilogues read only the published maxima).
+        if constexpr (VEC) stream_tile_vec<T, U, true>(op, blockIdx.x);
         else stream_tile_scalar<T>(op, blockIdx.x);
         return;
     }

@@ -74,6 +74,7 @@ struct CallArgs {
     RowFilter* rowf;         // [B, 2k+1] sampling filter per row (filtered call), else null
     unsigned long long* masses;   // [B, S2] stop-row chunk masses, bitwise complemented (0: none)
     int lookahead;           // one-launch grid: items of request b follow the tiles of b + lookahead
+    int nontemporal;         // one-launch grid: tiles load with non-temporal hints
     int self_compute;        // items compute every partial themselves (no tiles in the grid)
 };
 
@@ -1280,7 +1281,8 @@ __global__ __launch_bounds__(kThreads, SV_PLAIN_WAVES) void plain_kernel(CallArg
         __builtin_amdgcn_s_setprio(3);
         StatsOp<T, U> op;
         static_cast<CallArgs&>(op) = a;
-        stream_tile_vec<T, U>(op, idx);
+        if (a.nontemporal) stream_tile_vec<T, U, true>(op, idx);
+        else stream_tile_vec<T, U, false>(op, idx);
     } else {
         item_plain<T, true, NSUB>(a, idx / a.S2, idx % a.S2);
     }
@@ -1354,11 +1356,14 @@ static int plain_resident() {
 // request's tiles have finished and its rows are still cached.
 constexpr size_t kLastLevelCacheBytes = (size_t)256 << 20;
 
+static bool beyond_last_level_cache(const CallArgs& a, size_t elem_bytes) {
+    return (size_t)a.B * (size_t)a.R * (size_t)a.V * elem_bytes > kLastLevelCacheBytes;
+}
+
 static int plain_lookahead(const CallArgs& a, size_t elem_bytes, int resident) {
     if (SV_LOOKAHEAD >= 0) return std::min(SV_LOOKAHEAD, a.B);
     if (g_stochastic_schedule == 3) return 1;
-    const size_t logits = (size_t)a.B * (size_t)a.R * (size_t)a.V * elem_bytes;
-    if (logits <= kLastLevelCacheBytes || resident <= 0) return a.B;
+    if (!beyond_last_level_cache(a, elem_bytes) || resident <= 0) return a.B;
     const long long per_request = (long long)a.R * a.S + a.S2;
     const long long L = (3LL * resident + per_request - 1) / per_request;
     return (int)std::min<long long>(std::max<long long>(L, 1), a.B);
@@ -1369,6 +1374,11 @@ template <typename T, int U, int NSUB>
 static hipError_t launch_plain_u(const CallArgs& args, hipStream_t st, const KernelEvents& ev) {
     CallArgs a = args;
     a.lookahead = plain_lookahead(a, sizeof(T), plain_resident<T, U, NSUB>());
+    // Tiles of a call beyond the last-level cache stream with non-temporal
+    // loads (the faster choice there: most of their rows are never read
+    // again); a smaller call's tiles leave their rows cached for the items,
+    // which re-read the stop rows after the stream.
+    a.nontemporal = beyond_last_level_cache(a, sizeof(T)) ? 1 : 0;
     const unsigned grid = (unsigned)((long long)a.B * a.R * a.S + (long long)a.B * a.S2);
     hipExtLaunchKernelGGL(plain_kernel<T, U, NSUB>, dim3(grid), dim3(kThreads), 0, st, ev.begin,
                           ev.end, 0, a);
@@ -1464,6 +1474,7 @@ static CallArgs make_args(const StochasticCall& call, const Geometry& g) {
     a.spin_limit = kSpinLimit;
     a.self_compute = g_stochastic_schedule == 2;
     a.lookahead = call.B;  // the one-launch grid sets its own (plain_lookahead)
+    a.nontemporal = 0;
     return a;
 }
 

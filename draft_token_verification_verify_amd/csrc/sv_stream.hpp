@@ -59,7 +59,16 @@ static_assert(sizeof(RowFilter) == 16, "RowFilter layout");
 //   Op::tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d): reduce the tile held in
 //     raw[U] (this thread's vectors; slots >= nvec are padding); thread 0 then
 //     calls Op::publish(&partials[t], f0, f1, d).
-template <typename T, int U, class Op>
+// A 16-byte load that asks the caches not to keep the line (for rows read once).
+__device__ inline uint4 load16_nontemporal(const uint4* p) {
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u w = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    return make_uint4(w.x, w.y, w.z, w.w);
+}
+
+// NT: non-temporal loads, for rows that nothing in the call reads again while
+// they could still be cached.
+template <typename T, int U, bool NT = false, class Op>
 __device__ __forceinline__ void stream_tile_vec(const Op& op, int t) {
     constexpr int EPV = Elem<T>::kPerVec;
     const int ch = t % op.S, rr = t / op.S;
@@ -75,7 +84,10 @@ __device__ __forceinline__ void stream_tile_vec(const Op& op, int t) {
     // vector (in bounds) and are masked by the op.
     uint4 raw[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) raw[j] = base[min((int)threadIdx.x + j * kThreads, nvec - 1)];
+    for (int j = 0; j < U; ++j) {
+        const uint4* p = base + min((int)threadIdx.x + j * kThreads, nvec - 1);
+        raw[j] = NT ? load16_nontemporal(p) : *p;
+    }
     float f0, f1;
     double d;
     op.tile(b, r, lo, hi, raw, nvec, &f0, &f1, &d);
