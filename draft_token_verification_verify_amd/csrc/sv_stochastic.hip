@@ -1281,7 +1281,13 @@ __global__ __launch_bounds__(kThreads, SV_PLAIN_WAVES) void plain_kernel(CallArg
         __builtin_amdgcn_s_setprio(3);
         StatsOp<T, U> op;
         static_cast<CallArgs&>(op) = a;
-        if (a.nontemporal) stream_tile_vec<T, U, true>(op, idx);
+        // With non-temporal loads on, the rows a request most likely stops
+        // at stay cached for the items' re-read: with per-position acceptance
+        // a the stop row s has probability a^s (1 - a) below k and a^k at the
+        // bonus row k, so target rows 0, 1 and k and draft rows 0 and 1.
+        const int r = (idx / a.S) % a.R;
+        const bool likely_stop = r <= 1 || r == a.k || r == a.k + 1 || r == a.k + 2;
+        if (a.nontemporal && !likely_stop) stream_tile_vec<T, U, true>(op, idx);
         else stream_tile_vec<T, U, false>(op, idx);
     } else {
         item_plain<T, true, NSUB>(a, idx / a.S2, idx % a.S2);
