@@ -64,17 +64,32 @@ def parse():
     ap.add_argument("--graph", action="store_true",
                     help="time replays of a HIP graph holding one call per input copy "
                          "(how a serving loop issues launch-bound calls) instead of eager calls")
+    ap.add_argument("--pmc-summary", nargs=4, metavar="CSV",
+                    help="write profiles/dominant_kernel_<workload>_pmc.json from four rocprofv3 "
+                         "--pmc counter_collection.csv files: FETCH_SIZE and WRITE_SIZE of this "
+                         "workload's run, then of a --copy-probe run (the calibration)")
+    ap.add_argument("--pmc-kernel", default="sv::plain_kernel",
+                    help="name fragment of the kernel the --pmc-summary figures are for")
     ap.add_argument("--cpu-threads", type=int, default=0,
                     help="threads of the parallel oracle leg (0: the host's core count)")
     return ap.parse_args()
 
 
-def source_hash() -> str:
+# The source file of each mode's timed kernel (with every shared header).
+KERNEL_SOURCE = {"stochastic": "sv_stochastic.hip", "filtered": "sv_filter.hip",
+                 "greedy": "sv_argmax.hip", "tree": "sv_argmax.hip",
+                 "tree-stochastic": "sv_tree_stochastic.hip"}
+
+
+def source_hash(kernel_file: str) -> str:
+    """Hash of the timed kernel's source file and the shared headers: counters
+    taken on other sources no longer describe it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "draft_token_verification_verify_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        if name == kernel_file or name.endswith(".hpp"):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
@@ -301,6 +316,64 @@ def tree_walk_bytes(case, nodes, acc) -> int:
     return total
 
 
+WORKLOAD_MODE = {"c1": "stochastic", "c2-stochastic": "stochastic", "c3": "stochastic",
+                 "c4": "stochastic", "c2-greedy": "greedy", "c5": "tree",
+                 "c5-stochastic": "tree-stochastic"}
+
+
+def pmc_summary(args):
+    """HBM bytes per launch of one kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counters (KiB per dispatch), each scaled by what the same counter reads for
+    the plain 1 GiB device copy of --copy-probe (1 GiB read, 1 GiB written)."""
+    import csv
+
+    import numpy as np
+
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.pmc_summary
+
+    def values(path, counter, match):
+        with open(path) as f:
+            return [float(r["Counter_Value"]) for r in csv.DictReader(f)
+                    if r["Counter_Name"] == counter and match(r["Kernel_Name"])]
+
+    def kernel(name):
+        return args.pmc_kernel in name
+
+    def copy(name):
+        return name.startswith("__amd_rocclr_copyBuffer")
+
+    fetch = values(fetch_csv, "FETCH_SIZE", kernel)
+    write = values(write_csv, "WRITE_SIZE", kernel)
+    cf = values(cfetch_csv, "FETCH_SIZE", copy)
+    cw = values(cwrite_csv, "WRITE_SIZE", copy)
+    if not (fetch and write and cf and cw):
+        raise SystemExit("pmc-summary: a counter file holds no dispatch of the kernel or the copy")
+    # the 1 GiB copies (the probe's largest dispatches)
+    cf = [v for v in cf if v >= 0.9 * max(cf)]
+    cw = [v for v in cw if v >= 0.9 * max(cw)]
+    kib = float(1 << 20)  # 1 GiB in KiB
+    f_kib, w_kib = float(np.mean(fetch)), float(np.mean(write))
+    ff, wf = kib / float(np.mean(cf)), kib / float(np.mean(cw))
+    mode = WORKLOAD_MODE[args.workload]
+    rec = {
+        "workload": args.workload,
+        "kernel": args.pmc_kernel,
+        "source_hash": source_hash(KERNEL_SOURCE[mode]),
+        "fetch_kib_per_dispatch": f_kib,
+        "write_kib_per_dispatch": w_kib,
+        "dispatches": [len(fetch), len(write)],
+        "copy_probe": {"bytes": 1 << 30, "fetch_kib": float(np.mean(cf)),
+                       "write_kib": float(np.mean(cw)), "fetch_factor": ff, "write_factor": wf},
+        "hbm_read_bytes_per_launch": f_kib * ff * 1024.0,
+        "hbm_write_bytes_per_launch": w_kib * wf * 1024.0,
+        "hbm_bytes_per_launch": (f_kib * ff + w_kib * wf) * 1024.0,
+    }
+    path = os.path.join(PROFILES, f"dominant_kernel_{args.workload}_pmc.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec), flush=True)
+
+
 def load_traffic(workload: str, src_hash: str):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, if they were
     taken on the current kernel sources; else None."""
@@ -496,6 +569,9 @@ def main():
     import numpy as np
     import torch
 
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
     if args.copy_probe:
         copy_probe()
         return
@@ -554,7 +630,7 @@ def main():
     value = rows / (ms * 1e-3)
     achieved = nbytes / (k_avg * 1e-3) / 1e9
     n_acc = acc.cpu().numpy()
-    src_hash = source_hash()
+    src_hash = source_hash(KERNEL_SOURCE["filtered" if filt is not None else mode_of(case)])
     kname = ("filter selection kernel (filtered call)" if filt is not None else
              "one-launch kernel (statistics, decisions and sampling: the whole call)" if plain
              else "tree walk kernel (each request's walk split over workgroups)"
