@@ -223,10 +223,14 @@ SCHEDULE_CASES = [
     lambda: wl.gaussian_stochastic(23, 3, 0, 33000, "f32", target_sd=2.0, draft_noise_sd=1.0),
     lambda: wl.gaussian_stochastic(24, 64, 5, 8, "f32", target_sd=1.0, draft_noise_sd=1.0),
     lambda: wl.c4(25, B=6),
+    # small requests: a few one-vector tiles and one stop-row chunk
+    lambda: wl.gaussian_stochastic(26, 4, 3, 1000, "f32", target_sd=2.0, draft_noise_sd=1.0),
+    lambda: wl.gaussian_stochastic(27, 3, 2, 2048, "bf16", target_sd=3.0, draft_noise_sd=1.0),
 ]
 
 
-@pytest.mark.parametrize("make", SCHEDULE_CASES, ids=["c3", "bf16-V40000", "k0", "V8", "c4-B6"])
+@pytest.mark.parametrize("make", SCHEDULE_CASES, ids=["c3", "bf16-V40000", "k0", "V8", "c4-B6",
+                                                      "f32-V1000", "bf16-V2048"])
 def test_schedules_are_bit_identical(make, schedule):
     """The one-launch schedule, the two-kernel schedule, the sampling kernel
     whose workgroups compute the statistics themselves, and the one-launch
