@@ -32,6 +32,7 @@ EXPORTED = (
     "spec_verify_tree_stochastic",
     "spec_verify_tree_stochastic_split",
     "spec_verify_debug_tree_spin_limit",
+    "spec_verify_debug_spin_limit",
     "spec_verify_gather_rows",
 )
 
@@ -96,6 +97,8 @@ def load() -> ctypes.CDLL:
     lib.spec_verify_tree_stochastic_split.restype = I
     lib.spec_verify_debug_tree_spin_limit.argtypes = [I]
     lib.spec_verify_debug_tree_spin_limit.restype = I
+    lib.spec_verify_debug_spin_limit.argtypes = [I]
+    lib.spec_verify_debug_spin_limit.restype = I
     lib.spec_verify_tree_stochastic.restype = I
     lib.spec_verify_gather_rows.argtypes = [P, P, Z, P, P, I, I, I, P]
     lib.spec_verify_gather_rows.restype = I

@@ -387,6 +387,8 @@ int spec_verify_tree_stochastic_split(int B, int V, int dtype) {
 
 int spec_verify_debug_tree_spin_limit(int polls) { return sv::tree_stochastic_spin_limit(polls); }
 
+int spec_verify_debug_spin_limit(int polls) { return sv::set_debug_spin_limit(polls, 1 << 16); }
+
 int spec_verify_gather_rows(const void* src, void* dst, size_t row_bytes,
                             const int32_t* accepted_nodes, const int32_t* num_accepted, int B,
                             int N1, int L, void* stream) {

@@ -395,7 +395,7 @@ static ArgmaxArgs base_args(const void* target, int B, int R, int V, const Geome
     a.chunk = g.chunk;
     a.partials = reinterpret_cast<Partial16*>(ws + g.off_partials);
     a.stale = reinterpret_cast<uint32_t*>(ws + g.off_tickets) + 8;
-    a.spin_limit = kEpilogueSpin;
+    a.spin_limit = debug_spin_limit(kEpilogueSpin);
     return a;
 }
 

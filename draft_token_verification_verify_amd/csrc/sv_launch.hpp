@@ -99,6 +99,9 @@ struct KernelEvents {
 // kernels), 1 two kernels, 2 one launch whose sampler items compute their
 // request's statistics themselves instead of waiting (for tests).
 extern int g_stochastic_schedule;
+// Poll limit of the linear calls' bounded waits (testing hook; < 0: default).
+int debug_spin_limit(int fallback);
+int set_debug_spin_limit(int polls, int fallback);
 
 hipError_t run_stochastic(const StochasticCall& call, const Geometry& g, hipStream_t st,
                           const KernelEvents& ev);

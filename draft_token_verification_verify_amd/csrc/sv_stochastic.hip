@@ -1444,6 +1444,16 @@ static hipError_t launch_plain_two(const CallArgs& a, int U, hipStream_t st,
 
 int g_stochastic_schedule = 0;
 
+static std::atomic<int> g_debug_spin{-1};
+int debug_spin_limit(int fallback) {
+    const int v = g_debug_spin.load(std::memory_order_relaxed);
+    return v < 0 ? fallback : v;
+}
+int set_debug_spin_limit(int polls, int fallback) {
+    const int prev = g_debug_spin.exchange(polls < 0 ? -1 : polls);
+    return prev < 0 ? fallback : prev;
+}
+
 // Polls of a decision record or chunk mass before an item derives it itself:
 // far above any wait seen when workgroups are dispatched in order (a few
 // microseconds).
@@ -1477,7 +1487,7 @@ static CallArgs make_args(const StochasticCall& call, const Geometry& g) {
     a.p_at_draft = call.p_at_draft;
     a.q_at_draft = call.q_at_draft;
     a.rowf = nullptr;
-    a.spin_limit = kSpinLimit;
+    a.spin_limit = debug_spin_limit(kSpinLimit);
     a.self_compute = g_stochastic_schedule == 2;
     a.lookahead = call.B;  // the one-launch grid sets its own (plain_lookahead)
     a.nontemporal = 0;

@@ -471,6 +471,18 @@ int spec_verify_tree_stochastic_split(int B, int V, int dtype);
 int spec_verify_debug_tree_spin_limit(int polls);
 
 /*
+ * Testing hook for the bounded waits of the linear calls: sets how many times
+ * a sampling workgroup of the stochastic calls, or an epilogue workgroup of
+ * the greedy and tree calls, polls its request's published statistics before
+ * it computes what is missing itself and marks the workspace stale (default
+ * 65536; a negative value restores it), for calls made from then on,
+ * process-wide.  Returns the previous value.  A tiny value makes waits give
+ * up on purpose, so tests can check that results still match and that later
+ * calls on the stale workspace do too; it has no use outside tests.
+ */
+int spec_verify_debug_spin_limit(int polls);
+
+/*
  * Gather of the accepted rows (page "TensorRT-LLM source teardown (10)", KV
  * rewind, fourth step: the accepted draft tokens' KV rows, scattered when the
  * draft was a tree, are moved to contiguous logical positions):

@@ -49,6 +49,15 @@ def test_tree_spin_limit_hook_sets_and_restores(lib):
     assert hook(-1) == 1 << 20
 
 
+def test_spin_limit_hook_sets_and_restores(lib):
+    """Host-only: the linear calls' poll limit hook, default 2^16 polls."""
+    hook = lib.spec_verify_debug_spin_limit
+    assert hook(3) == 1 << 16
+    assert hook(0) == 3
+    assert hook(-1) == 0
+    assert hook(-1) == 1 << 16
+
+
 def test_version_and_status_strings(lib):
     assert lib.spec_verify_version() >= 100
     for code in range(6):
