@@ -48,6 +48,9 @@ def test_stochastic_gives_up_and_stays_correct(poll_limit, schedule):
             gpu = H.run_stochastic(case, workspace=ws)
             amb, dis = H.compare_stochastic(gpu, ref, label=f"limit 0, call {rep}")
             assert dis <= 1e-4 * case.rows
+            if rep == 0:  # a give-up leaves the stale flag set (and partials behind)
+                torch.cuda.synchronize()
+                assert int(torch.count_nonzero(ws)) > 0, "no wait gave up"
         poll_limit(-1)
         gpu = H.run_stochastic(case, workspace=ws)
         amb, dis = H.compare_stochastic(gpu, ref, label="default limit after give-ups")
@@ -72,6 +75,9 @@ def test_greedy_gives_up_and_stays_exact(poll_limit):
         gpu = H.run_greedy(case, workspace=ws)
         np.testing.assert_array_equal(gpu["out_tokens"], ref["out_tokens"], f"call {rep}")
         np.testing.assert_array_equal(gpu["num_accepted"], ref["num_accepted"], f"call {rep}")
+        if rep == 0:  # a give-up leaves the stale flag set (and maxima behind)
+            torch.cuda.synchronize()
+            assert int(torch.count_nonzero(ws)) > 0, "no wait gave up"
     poll_limit(-1)
     gpu = H.run_greedy(case, workspace=ws)
     np.testing.assert_array_equal(gpu["out_tokens"], ref["out_tokens"])
