@@ -1119,24 +1119,21 @@ __device__ inline uint32_t take_ticket(const CallArgs& a, int b) {
     return prev;
 }
 
-// The last of the request's S2 arrivals (prev from take_ticket) clears both
-// rounds' masses, the partials (unless the workspace is stale) and the
-// counter.
+// The last of the request's S2 arrivals (prev from take_ticket; a request of
+// one item takes no ticket) clears both rounds' masses, the partials and the
+// counter.  On a stale workspace a tile of this call may still publish after
+// the clearing; later calls ignore published partials there in any case.
 __device__ __forceinline__ void close_request(const CallArgs& a, int b, uint32_t prev) {
-    __shared__ int sh_last, sh_stale;
-    if (threadIdx.x == 0) {
-        sh_last = prev == (uint32_t)a.S2 - 1u;
-        sh_stale = sh_last && load_coherent(stale_word(a)) != 0u;
-    }
+    __shared__ int sh_last;
+    if (threadIdx.x == 0) sh_last = prev == (uint32_t)a.S2 - 1u;
     __syncthreads();
     if (sh_last) {
         for (int i = threadIdx.x; i < a.S2; i += kThreads) {
             store_coherent(&a.masses[(size_t)b * a.S2 + i], 0ull);
             store_coherent(&a.masses[(size_t)(a.B + b) * a.S2 + i], 0ull);
         }
-        if (!sh_stale && !a.self_compute)
-            clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
-        if (threadIdx.x == 0) atomicExch(req_counter(a, b, 0), 0u);
+        if (!a.self_compute) clear_partials(a.partials + (size_t)b * a.R * a.S, a.R * a.S);
+        if (threadIdx.x == 0 && a.S2 > 1) atomicExch(req_counter(a, b, 0), 0u);
     }
 }
 
@@ -1231,7 +1228,7 @@ __device__ __forceinline__ void item_plain(const CallArgs& a, int b, int c) {
     }
 
     // 4. Ticket (its value is used last): this item has read all it needs.
-    const uint32_t prev = take_ticket(a, b);
+    const uint32_t prev = a.S2 > 1 ? take_ticket(a, b) : 0u;
 
     // 5. The owner draws.
     if (owner == c) draw_in_chunk<T, VEC, NSUB>(a, b, d.s, f, c, seg, incl, prev_incl, u * Z);
