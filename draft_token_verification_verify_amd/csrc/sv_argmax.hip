@@ -366,6 +366,7 @@ template <typename T, bool VEC, int MODE>
 static hipError_t launch_argmax(const ArgmaxArgs& a, int U, size_t lds, hipStream_t st,
                                 const KernelEvents& ev) {
     switch (U) {
+        case 16: return launch_argmax_u<T, 16, VEC, MODE>(a, lds, st, ev);
         case 8: return launch_argmax_u<T, 8, VEC, MODE>(a, lds, st, ev);
         case 4: return launch_argmax_u<T, 4, VEC, MODE>(a, lds, st, ev);
         case 2: return launch_argmax_u<T, 2, VEC, MODE>(a, lds, st, ev);

@@ -10,10 +10,16 @@
 #ifndef SV_COHERENT_TICKETS
 #define SV_COHERENT_TICKETS 1
 #endif
-// Tile shape: the largest per-thread vector count (at most SV_MAX_U) whose tile
-// count reaches SV_MIN_TILES.
+// Tile shape: the largest per-thread vector count (at most SV_MAX_U, or
+// SV_MAX_U_ARGMAX for the greedy and tree argmax stream) whose tile count
+// reaches SV_MIN_TILES.  The argmax tile keeps no statistics, so 16 vectors
+// per thread (64 KB tiles, three workgroups per compute unit) hold as many bytes
+// in flight as 8 with six, from half as many workgroups.
 #ifndef SV_MAX_U
 #define SV_MAX_U 8
+#endif
+#ifndef SV_MAX_U_ARGMAX
+#define SV_MAX_U_ARGMAX 16
 #endif
 #ifndef SV_MIN_TILES
 #define SV_MIN_TILES 2048
@@ -50,7 +56,7 @@ struct Geometry {
     int R;           // logits rows streamed per request
     int S;           // chunks per row in the streaming kernel
     int chunk;       // elements per chunk (multiple of 2048)
-    int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8
+    int U;           // 16-byte vectors per thread per chunk: 1, 2, 4 or 8 (16: argmax)
     int S2;          // stop-row chunks per request (stochastic sampler)
     int chunk2;      // elements per stop-row chunk
     int cand_cap;    // filter candidate slots per row (mode 3), else 0: S segments of cand_seg
@@ -123,7 +129,7 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     const long long rows = (long long)B * g->R;
     // Largest per-thread vector count whose tile count still fills the chip
     // several times over; small problems fall back to smaller tiles.
-    int U = SV_MAX_U;
+    int U = (mode == 1 || mode == 2) ? SV_MAX_U_ARGMAX : SV_MAX_U;
     for (; U > 1; U >>= 1) {
         long long ce = (long long)kThreads * U * epv;
         long long tiles = rows * ((V + ce - 1) / ce);
