@@ -53,6 +53,18 @@ def test_tied_logits(B, k, V, dtype):
         check_greedy(tied_greedy(seed, B, k, V, dtype))
 
 
+@pytest.mark.parametrize("B,k,V,dtype", [
+    (128, 7, 65552, "bf16"),  # 3 tiles per row; the last holds 2 vectors
+    (96, 7, 32772, "f32"),    # 3 tiles per row; the last holds 1 vector
+])
+def test_tied_logits_large_tiles(B, k, V, dtype):
+    """Shapes whose argmax tiles are 16 vectors per thread (64 KB: B (k+1)
+    tiles per row-chunk reach 2048 at that size), each row ending in a tile of
+    one or two vectors: the lowest index among equal maxima across tiles and
+    inside the ragged tile."""
+    check_greedy(tied_greedy(2, B, k, V, dtype))
+
+
 def test_no_draft_accepted_reads_row_zero_only():
     case = tied_greedy(3, 8, 4, 1000, "f32", corrupt=0.0)
     tf = case.target
