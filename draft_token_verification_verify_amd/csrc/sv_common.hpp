@@ -12,9 +12,12 @@
 #endif
 // Tile shape: the largest per-thread vector count (at most SV_MAX_U, or
 // SV_MAX_U_ARGMAX for the greedy and tree argmax stream) whose tile count
-// reaches SV_MIN_TILES.  The argmax tile keeps no statistics, so 16 vectors
-// per thread (64 KB tiles, three workgroups per compute unit) hold as many bytes
-// in flight as 8 with six, from half as many workgroups.
+// reaches SV_MIN_TILES (SV_MIN_TILES_ARGMAX).  The argmax tile keeps no
+// statistics, so 16 vectors per thread (64 KB tiles, three workgroups per
+// compute unit) hold as many bytes in flight as 8 with six, from half as many
+// workgroups.  Fewer, larger tiles also shorten small calls: a tile's fixed
+// costs (its reductions and publication, and the merge of one more partial)
+// outweigh the parallelism of more tiles well before the chip is full.
 #ifndef SV_MAX_U
 #define SV_MAX_U 8
 #endif
@@ -22,7 +25,10 @@
 #define SV_MAX_U_ARGMAX 16
 #endif
 #ifndef SV_MIN_TILES
-#define SV_MIN_TILES 2048
+#define SV_MIN_TILES 512
+#endif
+#ifndef SV_MIN_TILES_ARGMAX
+#define SV_MIN_TILES_ARGMAX 128
 #endif
 // Distance in uint32 words between two requests' arrival counters: each counter
 // gets its own cache line, so atomics on different requests do not queue on one
@@ -127,13 +133,13 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     if (cand) mode = 0;
     g->R = (mode == 0) ? 2 * rows_per_request - 1 : rows_per_request;
     const long long rows = (long long)B * g->R;
-    // Largest per-thread vector count whose tile count still fills the chip
-    // several times over; small problems fall back to smaller tiles.
+    // Largest per-thread vector count whose tile count reaches the floor;
+    // small problems fall back to smaller tiles.
     int U = (mode == 1 || mode == 2) ? SV_MAX_U_ARGMAX : SV_MAX_U;
     for (; U > 1; U >>= 1) {
         long long ce = (long long)kThreads * U * epv;
         long long tiles = rows * ((V + ce - 1) / ce);
-        if (tiles >= SV_MIN_TILES) break;
+        if (tiles >= ((mode == 1 || mode == 2) ? SV_MIN_TILES_ARGMAX : SV_MIN_TILES)) break;
     }
     g->U = U;
     g->chunk = kThreads * U * epv;
