@@ -155,8 +155,11 @@ static int stochastic_impl(const void* target_logits, const void* draft_logits, 
     if (k > SPEC_VERIFY_MAX_K || V > SPEC_VERIFY_MAX_STOCHASTIC_VOCAB)
         return SPEC_VERIFY_LIMIT_EXCEEDED;
     if (filter && V > SPEC_VERIFY_MAX_FILTER_VOCAB) return SPEC_VERIFY_LIMIT_EXCEEDED;
+    // A filtered call's sampler chunks are its own (geometry mode 5, or 3 when
+    // the workspace also holds the candidates); mode 5 never needs more bytes
+    // than mode 0.
     sv::Geometry g;
-    if (!sv::make_geometry(0, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
+    if (!sv::make_geometry(filter ? 5 : 0, B, k + 1, V, eb, &g)) return SPEC_VERIFY_INVALID_ARGUMENT;
     if ((long long)B * g.R * g.S > 0x7fffffffLL || (long long)B * g.S2 > 0x7fffffffLL)
         return SPEC_VERIFY_LIMIT_EXCEEDED;
     if (noalloc) {

@@ -87,6 +87,7 @@ constexpr int kCandMaxChunks = 256;  // rows of more streaming chunks keep no ca
 // Stop-row chunks per request at most (one workgroup-wide scan over their
 // masses): with 16 * 4 tokens per thread, vocabularies up to 2^22.
 constexpr int kMaxChunks2 = 256;
+constexpr int kSamplerOneRound = 256;  // sampler workgroups that fit one per compute unit
 
 // Stochastic tree walk split over several workgroups per request: their
 // exchange area in the workspace (mode 4), per request.
@@ -115,7 +116,8 @@ struct Scale {
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // mode: 0 stochastic, 1 greedy, 2 tree, 3 stochastic with filter candidates
-// (mode 0's layout plus a candidate buffer at the end), 4 stochastic tree walk
+// (mode 0's layout plus a candidate buffer at the end), 5 (internal) mode 0's
+// layout with the filtered call's sampler chunks, 4 stochastic tree walk
 // (its exchange area only); rows_per_request: k+1 or N+1.
 inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem_bytes,
                           Geometry* g) {
@@ -129,8 +131,12 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
         g->bytes = kTreeSyncBytes * (size_t)B;
         return true;
     }
+    // Mode 5 (internal): the stochastic layout for a filtered call whose
+    // workspace has no room for the candidates.  Modes 3 and 5 size the
+    // sampler alike, so both give a filtered call the same bits.
     bool cand = mode == 3;
-    if (cand) mode = 0;
+    const bool filtered = mode == 3 || mode == 5;
+    if (filtered) mode = 0;
     g->R = (mode == 0) ? 2 * rows_per_request - 1 : rows_per_request;
     const long long rows = (long long)B * g->R;
     // Largest per-thread vector count whose tile count reaches the floor;
@@ -144,14 +150,23 @@ inline bool make_geometry(int mode, int B, int rows_per_request, int V, int elem
     g->U = U;
     g->chunk = kThreads * U * epv;
     g->S = (V + g->chunk - 1) / g->chunk;
-    // Sampler: 16, 32 or 64 consecutive tokens per thread; the smallest that
-    // keeps the sampler to about one round of resident workgroups.
-    int nsub = 1;
-    while (nsub < 4 && ((long long)B * ((V + kThreads * 16 * nsub - 1) / (kThreads * 16 * nsub)) >
-                            SV_SAMPLER_WGS ||
-                        (V + kThreads * 16 * nsub - 1) / (kThreads * 16 * nsub) > kMaxChunks2))
-        nsub <<= 1;
-    g->chunk2 = kThreads * 16 * nsub;
+    // Sampler: 8, 16, 32 or 64 consecutive tokens per thread.  8 while the
+    // call's sampler workgroups fit one per compute unit (each then runs its
+    // chain alone, and a shorter chunk shortens the chain); otherwise the
+    // smallest of 16, 32 and 64 that keeps the sampler to about one round of
+    // resident workgroups (there the weighing is bound by the chip's ALU
+    // throughput and more workgroups only add decisions).  The filtered call's
+    // sampler takes at least 16 (its stored 64-token segments are summed by at
+    // most 4 threads).
+    auto items = [&](int tpt) {
+        return (long long)B * ((V + (long long)kThreads * tpt - 1) / ((long long)kThreads * tpt));
+    };
+    int tpt = 8;
+    if (filtered || items(8) > kSamplerOneRound) {
+        tpt = 16;
+        while (tpt < 64 && (items(tpt) > SV_SAMPLER_WGS || items(tpt) / B > kMaxChunks2)) tpt <<= 1;
+    }
+    g->chunk2 = kThreads * tpt;
     g->S2 = (mode == 0) ? (V + g->chunk2 - 1) / g->chunk2 : 0;
 
     size_t off = 0;

@@ -612,7 +612,7 @@ struct Weigher {
     }
 };
 
-constexpr int kSub = 16;  // tokens per sampler sub-step
+constexpr int kSub = 8;  // tokens per sampler sub-step
 
 // Sum of the weights of this thread's segment of the chunk [lo, hi): the
 // NSUB * 16 consecutive tokens from lo + t * NSUB * 16.  Each pass issues up to
@@ -1035,7 +1035,7 @@ __device__ inline FinalRows<T> final_rows(const CallArgs& a, int b, const Decisi
 }
 
 // Mass of chunk c of the final distribution: every thread's sum over its
-// 16 * NSUB tokens (segment_sum), and their inclusive prefix in thread order;
+// kSub * NSUB tokens (segment_sum), and their inclusive prefix in thread order;
 // *total is the chunk's mass (the same additions as the last prefix).
 template <typename T, bool VEC, int NSUB>
 __device__ __forceinline__ double chunk_sums(const CallArgs& a, const FinalRows<T>& f, int c, double* incl,
@@ -1072,7 +1072,7 @@ __device__ inline void block_first_last(bool first_flag, bool last_flag, int* fi
 
 // The token inside chunk c: the first thread with positive mass whose running
 // mass (prev + its inclusive prefix) exceeds tau, else the last with positive
-// mass; then that thread's 16 * NSUB tokens, one per lane of wave 0, the first
+// mass; then that thread's kSub * NSUB tokens, one per lane of wave 0, the first
 // with positive weight whose running mass exceeds tau, else the last with
 // positive weight.  Written to out_tokens[b, s_row] by lane 0 of wave 0.
 template <typename T, bool VEC, int NSUB>
@@ -1321,6 +1321,7 @@ template <typename T, bool VEC>
 static hipError_t launch_sample_filtered(const CallArgs& a, hipStream_t st) {
     const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
     switch (a.chunk2 / (kThreads * kSub)) {
+        case 8: sample_kernel<T, VEC, 8, true><<<grid, block, 0, st>>>(a); break;
         case 4: sample_kernel<T, VEC, 4, true><<<grid, block, 0, st>>>(a); break;
         case 2: sample_kernel<T, VEC, 2, true><<<grid, block, 0, st>>>(a); break;
         default: sample_kernel<T, VEC, 1, true><<<grid, block, 0, st>>>(a); break;
@@ -1401,6 +1402,7 @@ static hipError_t launch_plain_n(const CallArgs& a, int U, hipStream_t st, const
 template <typename T>
 static hipError_t launch_plain(const CallArgs& a, int U, hipStream_t st, const KernelEvents& ev) {
     switch (a.chunk2 / (kThreads * kSub)) {
+        case 8: return launch_plain_n<T, 8>(a, U, st, ev);
         case 4: return launch_plain_n<T, 4>(a, U, st, ev);
         case 2: return launch_plain_n<T, 2>(a, U, st, ev);
         default: return launch_plain_n<T, 1>(a, U, st, ev);
@@ -1413,6 +1415,10 @@ template <typename T, bool VEC>
 static hipError_t launch_plain_items(const CallArgs& a, hipStream_t st, const KernelEvents& ev) {
     const dim3 grid((unsigned)((long long)a.B * a.S2)), block(kThreads);
     switch (a.chunk2 / (kThreads * kSub)) {
+        case 8:
+            hipExtLaunchKernelGGL(plain_items_kernel<T, VEC, 8>, grid, block, 0, st, ev.begin,
+                                  ev.end, 0, a);
+            break;
         case 4:
             hipExtLaunchKernelGGL(plain_items_kernel<T, VEC, 4>, grid, block, 0, st, ev.begin,
                                   ev.end, 0, a);
