@@ -13,6 +13,8 @@ library every call raises.
 """
 from __future__ import annotations
 
+import functools
+
 import torch
 
 from . import _lib
@@ -47,7 +49,7 @@ def _dev(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=Non
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
@@ -58,9 +60,18 @@ def _ptr(t):
     return None if t is None else t.data_ptr()
 
 
+# The current stream's raw handle without building a Stream object (about a
+# tenth of torch.cuda.current_stream's cost per call); the public call where
+# torch lacks the accessor.
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device: torch.device, stream=None) -> int:
-    s = torch.cuda.current_stream(device) if stream is None else stream
-    return s.cuda_stream
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(device.index if device.index is not None else torch.cuda.current_device())
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def spec_verify_version() -> int:
@@ -74,8 +85,10 @@ def spec_verify_set_schedule(schedule: int) -> None:
     _lib.check("spec_verify_set_schedule", _lib.load().spec_verify_set_schedule(int(schedule)))
 
 
+@functools.lru_cache(maxsize=1024)
 def spec_verify_workspace_bytes(mode: int, B: int, rows_per_request: int, V: int,
                                 dtype: int) -> int:
+    """Workspace bytes for a call shape (a pure function of the shape, so cached)."""
     return int(_lib.load().spec_verify_workspace_bytes(mode, B, rows_per_request, V, dtype))
 
 
@@ -95,10 +108,10 @@ class Workspace:
         self._buf: dict[tuple[torch.device, int], torch.Tensor] = {}
 
     def get(self, nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
-        s = torch.cuda.current_stream(device) if stream is None else stream
-        key = (device, s.cuda_stream)
+        key = (device, _stream(device, stream))
         buf = self._buf.get(key)
         if buf is None or buf.numel() < nbytes:
+            s = torch.cuda.current_stream(device) if stream is None else stream
             with torch.cuda.stream(s):
                 # torch.zeros clears with a fill kernel (no memset node).
                 buf = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
